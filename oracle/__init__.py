@@ -1,0 +1,132 @@
+"""CPU oracle for sink attention.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  The library (attention_sink_softmax_amd) never does, and this package never
+imports the library: the two share no code.  The arithmetic lives in oracle.c (fp64,
+plain loops, OpenMP over output rows) and, for tiny brute-force checks, oracle_np.py.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py against the
+worked example of the paper-notes page (§4.3), torch's CPU scaled_dot_product_attention
+in float64, closed forms and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+GLOBAL = 0
+SWA = 1
+RING = 0
+PAGED = 1
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB, extra: tuple = ()) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP) into a shared library."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *extra, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str = LIB):
+    """Load (building first if absent) the compiled oracle and declare its signatures."""
+    global _lib
+    if path == LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path) or (path == LIB and os.path.getmtime(path) < os.path.getmtime(SRC)):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_prefill.restype = I
+    lib.oracle_prefill.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P,
+                                   ctypes.c_int64, P, P]
+    lib.oracle_decode.restype = I
+    lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
+                                  P, P, P]
+    lib.oracle_threads.restype = I
+    lib.oracle_threads.argtypes = []
+    if path == LIB:
+        _lib = lib
+    return lib
+
+
+def _arr(x, dtype):
+    """Contiguous array and its storage flag: uint16 -> bf16 bits, else float32."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), BF16
+    return np.ascontiguousarray(x, dtype=np.float32), F32
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=None) -> np.ndarray:
+    """q [B,Hq,L,dqk], k [B,Hkv,L,dqk], v [B,Hkv,L,dv]: all float32, or all uint16 bf16 bits.
+    sink: [Hq] floats or None.  rows: optional int array [n,3] of (b, h, i).
+    Returns float64 [B,Hq,L,dv] (rows None) or [n,dv]."""
+    lib = lib or load()
+    qa, dt = _arr(q, None)
+    ka, dt2 = _arr(k, None)
+    va, dt3 = _arr(v, None)
+    if not (dt == dt2 == dt3):
+        raise TypeError("q, k, v must share one storage type")
+    B, Hq, L, dqk = qa.shape
+    Hkv, dv = ka.shape[1], va.shape[3]
+    if ka.shape != (B, Hkv, L, dqk) or va.shape != (B, Hkv, L, dv):
+        raise ValueError("shape mismatch")
+    s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    if rows is None:
+        out = np.empty((B, Hq, L, dv), np.float64)
+        n, rp = 0, None
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        out = np.empty((r.shape[0], dv), np.float64)
+        n, rp = r.shape[0], r
+    rc = lib.oracle_prefill(mode, window, B, L, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka),
+                            _ptr(va), _ptr(s), n, _ptr(rp), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return out
+
+
+def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout: int,
+           block_table=None, lib=None) -> np.ndarray:
+    """q [B,Hq,dqk]; RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv]; PAGED: k [P,Hkv,page,dqk],
+    v [P,Hkv,page,dv] with block_table [B,max_pages].  Returns float64 [B,Hq,dv]."""
+    lib = lib or load()
+    qa, dt = _arr(q, None)
+    ka, _ = _arr(k, None)
+    va, _ = _arr(v, None)
+    B, Hq, dqk = qa.shape
+    Hkv, dv = ka.shape[1], va.shape[3]
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    if layout == PAGED:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        ps, mp, npg = ka.shape[2], bt.shape[1], ka.shape[0]
+    else:
+        bt, ps, mp, npg = None, 0, 0, 0
+    out = np.empty((B, Hq, dv), np.float64)
+    rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka),
+                           _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return out
+
+
+def threads() -> int:
+    return load().oracle_threads()

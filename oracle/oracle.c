@@ -1,0 +1,202 @@
+/*
+ * oracle.c -- plain, slow, CPU reference for attention with a per-head sink term in the
+ * softmax denominator.  TEST INFRASTRUCTURE ONLY: it is built and called by the tests,
+ * by the smoke check and by the benchmark's CPU-baseline leg, never by the library.
+ * It shares no source with the GPU path.
+ *
+ * What it computes (plain definition; no tiling, no online softmax, no reordering):
+ *
+ *   logits     a_ij = scale * sum_d q[i,d] * k[j,d]
+ *              ("MiMo-V2-Flash 模型架构深度拆解", CH 3.2 and CH 10.3: scaling = head_dim^-0.5)
+ *   max        m_i  = max(max_{j in J(i)} a_ij, sink_h)
+ *              ("MiMo-V2-Flash 架构 QA", Q3.7; paper notes §4.3)
+ *   weights    s_ij = exp(a_ij - m_i) / (exp(sink_h - m_i) + sum_{j' in J(i)} exp(a_ij' - m_i))
+ *              ("MiMo-V2-Flash 架构 QA", Q3.8 formula; paper notes §4.1: the sink sits in
+ *              the denominator only and has no value vector)
+ *   output     o_i  = sum_{j in J(i)} s_ij * v[j,:]
+ *
+ *   visible set J(i):  global  -> { j : 0 <= j <= i }                 (causal lower triangle)
+ *                      sliding -> { j : max(0, i-W+1) <= j <= i }     (the W most recent keys,
+ *                                                                     the query's own included)
+ *              (deep-dive CH 10.3 mask description; paper notes §4.3 counts 128 keys for W=128)
+ *
+ *   GQA: query head h reads KV head h / (Hq/Hkv) (contiguous groups).
+ *   The sink is per query head, in the same units as the scaled logits (it is not
+ *   multiplied by `scale`).  A NULL sink means no sink term (standard softmax).
+ *   sink = +inf: every weight is 0 (the limit of the formula), so the output row is 0.
+ *
+ * Inputs may be float32 or bfloat16 bit patterns (dtype flag); bf16 -> double is exact.
+ * All arithmetic is double precision.  OpenMP parallelises over output rows only.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_GLOBAL = 0, ORACLE_SWA = 1 };
+enum { ORACLE_RING = 0, ORACLE_PAGED = 1 };
+
+static double load(const void *p, size_t idx, int dtype) {
+    if (dtype == ORACLE_BF16) {
+        uint32_t u = ((uint32_t)((const uint16_t *)p)[idx]) << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)p)[idx];
+}
+
+/* One output row.  qrow: index of q[0] of the row; key j of the visible list lives at
+ * kidx[t]*dqk in k and vidx[t]*dv in v.  n keys.  Writes dv doubles to out. */
+static void attend_row(int dtype, const void *q, size_t qrow, const void *k, const void *v,
+                       const size_t *kidx, const size_t *vidx, int n, int dqk, int dv,
+                       double scale, int has_sink, double sink, double *a, double *out) {
+    for (int e = 0; e < dv; ++e) out[e] = 0.0;
+    if (has_sink && isinf(sink) && sink > 0) return; /* all mass on the sink */
+    double m = has_sink ? sink : -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += load(q, qrow + d, dtype) * load(k, kidx[t] + d, dtype);
+        a[t] = scale * dot;
+        if (a[t] > m) m = a[t];
+    }
+    if (n == 0 || isinf(m)) return; /* empty visible set (or only a -inf sink) */
+    double z = has_sink ? exp(sink - m) : 0.0;
+    for (int t = 0; t < n; ++t) z += exp(a[t] - m);
+    for (int t = 0; t < n; ++t) {
+        double s = exp(a[t] - m) / z;
+        for (int e = 0; e < dv; ++e) out[e] += s * load(v, vidx[t] + e, dtype);
+    }
+}
+
+/*
+ * Prefill.  q [B][Hq][L][dqk], k [B][Hkv][L][dqk], v [B][Hkv][L][dv], sink [Hq] or NULL.
+ * rows == NULL: out [B][Hq][L][dv].  Otherwise rows holds nrows triplets (b, h, i) and
+ * out is [nrows][dv].  Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv,
+                   double scale, int dtype, const void *q, const void *k, const void *v,
+                   const double *sink, int64_t nrows, const int64_t *rows, double *out) {
+    if (B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
+    if (mode == ORACLE_SWA && window <= 0) return -1;
+    if (mode != ORACLE_SWA && mode != ORACLE_GLOBAL) return -1;
+    const int G = Hq / Hkv;
+    const int64_t total = rows ? nrows : (int64_t)B * Hq * L;
+#pragma omp parallel
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)(L > 0 ? L : 1));
+        size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)(L > 0 ? L : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < total; ++r) {
+            int64_t b, h, i;
+            if (rows) {
+                b = rows[3 * r];
+                h = rows[3 * r + 1];
+                i = rows[3 * r + 2];
+            } else {
+                b = r / ((int64_t)Hq * L);
+                h = (r / L) % Hq;
+                i = r % L;
+            }
+            const int64_t g = h / G;
+            const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
+            int n = 0;
+            for (int64_t j = jlo; j <= i; ++j, ++n) {
+                ki[n] = (size_t)(((b * Hkv + g) * L + j) * dqk);
+                vi[n] = (size_t)(((b * Hkv + g) * L + j) * dv);
+            }
+            attend_row(dtype, q, (size_t)(((b * Hq + h) * L + i) * dqk), k, v, ki, vi, n, dqk, dv,
+                       scale, sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+        }
+        free(a);
+        free(ki);
+        free(vi);
+    }
+    return 0;
+}
+
+/*
+ * Decode: one new query per sequence at position n_b - 1, where n_b = seq_lens[b] counts
+ * the new token (its key and value are already in the cache).
+ * q [B][Hq][dqk]; sink [Hq] or NULL; out [B][Hq][dv].
+ * RING  (sliding mode only): k [B][Hkv][window][dqk], v [B][Hkv][window][dv]; position p
+ *       lives in slot p mod window.
+ * PAGED (either mode): k [num_pages][Hkv][page_size][dqk], v [num_pages][Hkv][page_size][dv];
+ *       position p of sequence b lives in page block_table[b*max_pages + p/page_size] at
+ *       offset p mod page_size.
+ * Returns 0, or -1 on bad arguments (including a page id outside the pool).
+ */
+int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
+                  double scale, int dtype, const void *q, const void *k, const void *v,
+                  const int32_t *block_table, int page_size, int max_pages, int num_pages,
+                  const int32_t *seq_lens, const double *sink, double *out) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
+    if (mode == ORACLE_SWA && window <= 0) return -1;
+    if (layout == ORACLE_RING && mode != ORACLE_SWA) return -1;
+    if (layout == ORACLE_PAGED && (!block_table || page_size <= 0 || max_pages < 0)) return -1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+    int64_t maxn = 1;
+    for (int b = 0; b < B; ++b) {
+        if (layout == ORACLE_PAGED && seq_lens[b] > (int64_t)max_pages * page_size) bad = 1;
+        if (seq_lens[b] > maxn) maxn = seq_lens[b];
+    }
+    if (bad) return -1;
+#pragma omp parallel
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)maxn);
+        size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
+        size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
+            const int64_t b = r / Hq, h = r % Hq, g = h / G;
+            const int64_t nb = seq_lens[b];
+            const int64_t i = nb - 1;
+            const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
+            int n = 0;
+            int local_bad = 0;
+            for (int64_t j = jlo; j <= i; ++j, ++n) {
+                if (layout == ORACLE_RING) {
+                    const int64_t slot = j % window;
+                    ki[n] = (size_t)(((b * Hkv + g) * window + slot) * dqk);
+                    vi[n] = (size_t)(((b * Hkv + g) * window + slot) * dv);
+                } else {
+                    const int64_t page = block_table[b * max_pages + j / page_size];
+                    if (page < 0 || page >= num_pages) local_bad = 1;
+                    const int64_t off = j % page_size;
+                    ki[n] = (size_t)(((page * Hkv + g) * page_size + off) * dqk);
+                    vi[n] = (size_t)(((page * Hkv + g) * page_size + off) * dv);
+                }
+            }
+            if (local_bad) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            attend_row(dtype, q, (size_t)((b * Hq + h) * dqk), k, v, ki, vi, n, dqk, dv, scale,
+                       sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+        }
+        free(a);
+        free(ki);
+        free(vi);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (reported next to timings). */
+int oracle_threads(void) {
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,51 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Every mutation is applied to a temporary copy of oracle/oracle.c (the real file is never
+touched), compiled with gcc and run through the pins on the CPU."""
+import os
+
+import pytest
+
+import oracle
+
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "sink dropped from the denominator": ("double z = has_sink ? exp(sink - m) : 0.0;", "double z = 0.0;"),
+    "sink multiplied by the logit scale": ("double m = has_sink ? sink : -INFINITY;",
+                                           "sink *= scale; double m = has_sink ? sink : -INFINITY;"),
+    "sink given a unit value": ("if (n == 0 || isinf(m)) return;",
+                                "if (n == 0 || isinf(m)) return; if (has_sink) out[0] += 0.0 + exp(sink - m) / (exp(sink - m) + 1.0) * 0.5;"),
+    "window one key too wide": ("(i - window + 1 > 0 ? i - window + 1 : 0) : 0;\n            int n = 0;\n            for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv",
+                                "(i - window > 0 ? i - window : 0) : 0;\n            int n = 0;\n            for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv"),
+    "causal mask excludes self": ("for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv",
+                                  "for (int64_t j = jlo; j < i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv"),
+    "GQA head interleaved": ("const int64_t g = h / G;\n            const int64_t jlo", "const int64_t g = h % Hkv;\n            const int64_t jlo"),
+    "wrong exponent sign": ("double s = exp(a[t] - m) / z;", "double s = exp(m - a[t]) / z;"),
+    "logit scale dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
+    "max without the row logits": ("if (a[t] > m) m = a[t];", ""),
+    "ring slot off by one": ("const int64_t slot = j % window;", "const int64_t slot = (j + 1) % window;"),
+    "page offset from the wrong end": ("const int64_t off = j % page_size;", "const int64_t off = page_size - 1 - j % page_size;"),
+    "decode query position off by one": ("const int64_t i = nb - 1;", "const int64_t i = nb - 2;"),
+    "value row from the query position": ("vi[n] = (size_t)(((b * Hkv + g) * L + j) * dv);",
+                                          "vi[n] = (size_t)(((b * Hkv + g) * L + i) * dv);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "liboracle_mut.so")
+    oracle.build(str(mutated), lib_path)
+    lib = oracle.load(lib_path)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake: {name}"
