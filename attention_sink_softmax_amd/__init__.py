@@ -1,0 +1,224 @@
+"""Python binding of libsinkattn.so: sink-bias softmax attention on MI355X (gfx950).
+
+The functions named like the C ABI (sinkattn_prefill, sinkattn_decode,
+sinkattn_decode_workspace_bytes, sinkattn_status_string) only marshal arguments: they
+check that torch tensors have the dtype, device, contiguity and shapes the C ABI
+documents, then pass raw device pointers, sizes and the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, the first call raises LibraryMissing.
+
+`prefill` and `decode` are conveniences that allocate the output (and the decode
+workspace) with torch and call the C-ABI functions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsinkattn.so")
+
+GLOBAL = 0
+SWA = 1
+KV_RING = 0
+KV_PAGED = 1
+D_QK = 192
+D_V = 128
+
+STATUS = {0: "SINKATTN_OK", 1: "SINKATTN_E_NULL", 2: "SINKATTN_E_SHAPE", 3: "SINKATTN_E_UNSUPPORTED",
+          4: "SINKATTN_E_ALIGN", 5: "SINKATTN_E_WORKSPACE", 6: "SINKATTN_E_DEVICE"}
+
+
+class LibraryMissing(ImportError):
+    pass
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("hq", ctypes.c_int32),
+                ("hkv", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+EXPORTS = ("sinkattn_prefill", "sinkattn_decode", "sinkattn_decode_workspace_bytes", "sinkattn_status_string")
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libsinkattn.so and declare its C signatures (raises LibraryMissing if absent)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise LibraryMissing(f"{path} is not built; run `python -m attention_sink_softmax_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L.sinkattn_prefill.restype = I
+    L.sinkattn_prefill.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P]
+    L.sinkattn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_decode_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
+    L.sinkattn_decode.restype = I
+    L.sinkattn_decode.argtypes = [I, I, ctypes.POINTER(Dims), P, ctypes.POINTER(KVDesc), P, ctypes.c_int32,
+                                  P, P, P, ctypes.c_size_t, P]
+    L.sinkattn_status_string.restype = ctypes.c_char_p
+    L.sinkattn_status_string.argtypes = [I]
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def sinkattn_status_string(status: int) -> str:
+    return lib().sinkattn_status_string(status).decode()
+
+
+def _raise(rc: int):
+    if rc != 0:
+        raise SinkAttnError(rc, sinkattn_status_string(rc))
+
+
+# ---------------------------------------------------------------------------- marshalling
+def _dev_tensor(t, name, dtype, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream_ptr(stream, device):
+    import torch
+
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sinkattn_prefill(mode: int, window: int, q, k, v, sink, out, scale: float | None = None, stream=None) -> None:
+    """q bf16 [B,Hq,L,192], k bf16 [B,Hkv,L,192], v bf16 [B,Hkv,L,128], sink float32 [Hq] or
+    None, out bf16 [B,Hq,L,128] (written).  Enqueued on `stream` (default: current stream)."""
+    import torch
+
+    B, Hq, L, dqk = q.shape
+    Hkv = k.shape[1]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(k, "k", torch.bfloat16, (B, Hkv, L, dqk))
+    _dev_tensor(v, "v", torch.bfloat16, (B, Hkv, L, v.shape[3]))
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, L, v.shape[3]))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    for t in (k, v, out, sink):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    d = Dims(B, L, Hq, Hkv, dqk, v.shape[3], dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_prefill(mode, window, ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out),
+                                    _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def sinkattn_decode_workspace_bytes(mode: int, window: int, batch: int, hq: int, hkv: int, max_seq_len: int,
+                                    d_qk: int = D_QK, d_v: int = D_V) -> int:
+    d = Dims(batch, 0, hq, hkv, d_qk, d_v, d_qk ** -0.5)
+    n = lib().sinkattn_decode_workspace_bytes(mode, window, ctypes.byref(d), max_seq_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise SinkAttnError(2, "invalid sizes")
+    return n
+
+
+def sinkattn_decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, max_seq_len: int,
+                    sink, out, workspace, block_table=None, scale: float | None = None, stream=None) -> None:
+    """q bf16 [B,Hq,192]; RING: k_cache [B,Hkv,W,192], v_cache [B,Hkv,W,128];
+    PAGED: k_cache [P,Hkv,page,192], v_cache [P,Hkv,page,128], block_table int32 [B,max_pages].
+    seq_lens int32 [B] (device), sink float32 [Hq] or None, out bf16 [B,Hq,128],
+    workspace uint8 tensor of at least sinkattn_decode_workspace_bytes(...) bytes or None."""
+    import torch
+
+    B, Hq, dqk = q.shape
+    Hkv = k_cache.shape[1]
+    dv = v_cache.shape[3]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, dv))
+    _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    if layout == KV_RING:
+        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (B, Hkv, window, dqk))
+        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (B, Hkv, window, dv))
+        desc = KVDesc(KV_RING, k_cache.data_ptr(), v_cache.data_ptr(), None, 0, 0, 0)
+    elif layout == KV_PAGED:
+        P, _, ps, _ = k_cache.shape
+        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (P, Hkv, ps, dqk))
+        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (P, Hkv, ps, dv))
+        _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
+        desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps,
+                      block_table.shape[1], P)
+    else:
+        raise ValueError("layout must be KV_RING or KV_PAGED")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    for t in (k_cache, v_cache, out, seq_lens, sink, block_table, workspace):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode(mode, window, ctypes.byref(d), _ptr(q), ctypes.byref(desc), _ptr(seq_lens),
+                                   max_seq_len, _ptr(sink), _ptr(out), ws_ptr, ws_bytes,
+                                   _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+# ---------------------------------------------------------------------------- conveniences
+def prefill(mode: int, window: int, q, k, v, sink=None, scale: float | None = None, stream=None):
+    """Allocate out (torch) and run sinkattn_prefill."""
+    import torch
+
+    out = torch.empty((*q.shape[:3], v.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_prefill(mode, window, q, k, v, sink, out, scale, stream)
+    return out
+
+
+def decode_workspace(mode: int, window: int, batch: int, hq: int, hkv: int, max_seq_len: int, device):
+    import torch
+
+    n = sinkattn_decode_workspace_bytes(mode, window, batch, hq, hkv, max_seq_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, max_seq_len: int, sink=None,
+           block_table=None, workspace=None, scale: float | None = None, stream=None):
+    """Allocate out (and the workspace if none is given) and run sinkattn_decode."""
+    import torch
+
+    B, Hq, _ = q.shape
+    if workspace is None:
+        workspace = decode_workspace(mode, window, B, Hq, k_cache.shape[1], max_seq_len, q.device)
+    out = torch.empty((B, Hq, v_cache.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_decode(mode, window, q, layout, k_cache, v_cache, seq_lens, max_seq_len, sink, out, workspace,
+                    block_table, scale, stream)
+    return out

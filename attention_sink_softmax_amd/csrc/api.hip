@@ -1,0 +1,167 @@
+// C-ABI entry points of libsinkattn.so: argument validation, work planning and kernel
+// launches.  Every check here runs on the host before anything touches the device, so
+// argument errors are reported synchronously and nothing is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "sinkattn.h"
+
+namespace {
+
+using namespace sinkattn;
+
+constexpr int kDqkSupported = 192;
+constexpr int kDvSupported = 128;
+constexpr int64_t kDecodeTargetWorkgroups = 2048;  // ~8 per CU on a 256-CU MI355X
+constexpr int kDecodeKeyBlock = 128;                // keys per decode workgroup iteration
+constexpr double kLog2eD = 1.4426950408889634;
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_dims(int mode, int window, const sinkattn_dims *d) {
+    if (!d) return SINKATTN_E_NULL;
+    if (mode != SINKATTN_GLOBAL && mode != SINKATTN_SWA) return SINKATTN_E_UNSUPPORTED;
+    if (d->d_qk != kDqkSupported || d->d_v != kDvSupported) return SINKATTN_E_UNSUPPORTED;
+    if (d->batch < 0 || d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv != 0) return SINKATTN_E_SHAPE;
+    if (mode == SINKATTN_SWA && window < 1) return SINKATTN_E_SHAPE;
+    if (!isfinite(d->scale)) return SINKATTN_E_SHAPE;
+    return SINKATTN_OK;
+}
+
+struct DecodePlan {
+    int nsplit, chunk;
+    size_t ws_bytes;
+};
+
+// Keys per split: enough splits that B * Hkv * head-chunks * splits reaches about
+// kDecodeTargetWorkgroups, in whole 128-key blocks.
+DecodePlan plan_decode(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
+    const int64_t G = d->hq / d->hkv;
+    const int64_t hchunks = (G + 15) / 16;
+    const int64_t kmax = mode == SINKATTN_SWA ? (window < max_seq_len ? window : max_seq_len) : max_seq_len;
+    const int64_t units = (int64_t)d->batch * d->hkv * hchunks;
+    int64_t chunk = units > 0 ? (kmax * units + kDecodeTargetWorkgroups - 1) / kDecodeTargetWorkgroups : kmax;
+    chunk = ((chunk + kDecodeKeyBlock - 1) / kDecodeKeyBlock) * kDecodeKeyBlock;
+    if (chunk < kDecodeKeyBlock) chunk = kDecodeKeyBlock;
+    const int64_t nsplit = (kmax + chunk - 1) / chunk;
+    DecodePlan pl;
+    pl.nsplit = (int)(nsplit < 1 ? 1 : nsplit);
+    pl.chunk = (int)chunk;
+    pl.ws_bytes = pl.nsplit > 1 ? (size_t)d->batch * d->hq * pl.nsplit * (kDvSupported + 4) * sizeof(float) : 0;
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sinkattn_status_string(int status) {
+    switch (status) {
+        case SINKATTN_OK: return "ok";
+        case SINKATTN_E_NULL: return "a required pointer is NULL";
+        case SINKATTN_E_SHAPE: return "invalid sizes";
+        case SINKATTN_E_UNSUPPORTED: return "unsupported head size, mode or cache layout";
+        case SINKATTN_E_ALIGN: return "a pointer is not 16-byte aligned";
+        case SINKATTN_E_WORKSPACE: return "decode workspace missing or too small";
+        case SINKATTN_E_DEVICE: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q, const void *k, const void *v,
+                     const float *sink, void *out, void *stream) {
+    int st = check_dims(mode, window, d);
+    if (st) return st;
+    if (d->seqlen < 0) return SINKATTN_E_SHAPE;
+    if (d->batch == 0 || d->seqlen == 0) return SINKATTN_OK;
+    if (!q || !k || !v || !out) return SINKATTN_E_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (sink && misaligned(sink)))
+        return SINKATTN_E_ALIGN;
+
+    PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.sink = sink;
+    p.out = static_cast<uint16_t *>(out);
+    p.B = d->batch;
+    p.L = d->seqlen;
+    p.Hq = d->hq;
+    p.Hkv = d->hkv;
+    p.G = d->hq / d->hkv;
+    p.swa = mode == SINKATTN_SWA;
+    p.window = p.swa ? window : 0;
+    p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    p.hw = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.pw = 4 / p.hw;
+    const int64_t npb = (p.L + 31) / 32;
+    p.n_pbw = (int)((npb + p.pw - 1) / p.pw);
+    p.hgroups = p.G / p.hw;
+    const int64_t items = (int64_t)p.n_pbw * p.B * p.Hkv * p.hgroups;
+    const int64_t grid = ((items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
+    if (grid > INT32_MAX) return SINKATTN_E_SHAPE;
+    p.n_items = (int)items;
+    return launch_prefill(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+size_t sinkattn_decode_workspace_bytes(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
+    if (check_dims(mode, window, d) || max_seq_len < 1) return (size_t)-1;
+    return plan_decode(mode, window, d, max_seq_len).ws_bytes;
+}
+
+int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,
+                    const int32_t *seq_lens, int32_t max_seq_len, const float *sink, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    int st = check_dims(mode, window, d);
+    if (st) return st;
+    if (!kv) return SINKATTN_E_NULL;
+    if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
+    if (kv->layout == SINKATTN_KV_RING && mode != SINKATTN_SWA) return SINKATTN_E_UNSUPPORTED;
+    if (max_seq_len < 1) return SINKATTN_E_SHAPE;
+    if (kv->layout == SINKATTN_KV_PAGED) {
+        if (kv->page_size <= 0 || kv->max_pages <= 0 || kv->num_pages <= 0) return SINKATTN_E_SHAPE;
+        if ((int64_t)max_seq_len > (int64_t)kv->max_pages * kv->page_size) return SINKATTN_E_SHAPE;
+    }
+    if (d->batch == 0) return SINKATTN_OK;
+    if (!q || !out || !seq_lens || !kv->k || !kv->v) return SINKATTN_E_NULL;
+    if (kv->layout == SINKATTN_KV_PAGED && !kv->block_table) return SINKATTN_E_NULL;
+    if (misaligned(q) || misaligned(out) || misaligned(seq_lens) || misaligned(kv->k) || misaligned(kv->v) ||
+        (sink && misaligned(sink)) || (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
+        return SINKATTN_E_ALIGN;
+    const DecodePlan pl = plan_decode(mode, window, d, max_seq_len);
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return SINKATTN_E_WORKSPACE;
+        if (misaligned(workspace)) return SINKATTN_E_ALIGN;
+    }
+
+    DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(kv->k);
+    p.v = static_cast<const uint16_t *>(kv->v);
+    p.block_table = kv->layout == SINKATTN_KV_PAGED ? kv->block_table : nullptr;
+    p.seq_lens = seq_lens;
+    p.sink = sink;
+    p.out = static_cast<uint16_t *>(out);
+    p.ws = static_cast<float *>(workspace);
+    p.B = d->batch;
+    p.Hq = d->hq;
+    p.Hkv = d->hkv;
+    p.G = d->hq / d->hkv;
+    p.hchunks = (p.G + 15) / 16;
+    p.swa = mode == SINKATTN_SWA;
+    p.window = p.swa ? window : 0;
+    p.paged = kv->layout == SINKATTN_KV_PAGED;
+    p.page_size = p.paged ? kv->page_size : 0;
+    p.max_pages = p.paged ? kv->max_pages : 0;
+    p.num_pages = p.paged ? kv->num_pages : 0;
+    p.max_seq_len = max_seq_len;
+    p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    p.nsplit = pl.nsplit;
+    p.chunk = pl.chunk;
+    if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq > INT32_MAX)
+        return SINKATTN_E_SHAPE;
+    return launch_decode(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+}  // extern "C"

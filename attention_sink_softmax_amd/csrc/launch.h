@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+struct PrefillParams {
+    const uint16_t *q, *k, *v;
+    const float *sink;  // [Hq] or nullptr
+    uint16_t *out;
+    int B, L, Hq, Hkv, G;
+    int swa, window;
+    float scale_log2;  // logit scale * log2(e)
+    int hw;            // query heads per workgroup (4, 2 or 1; divides G)
+    int pw;            // 32-position blocks per workgroup (4 / hw)
+    int n_pbw;         // position groups per (batch, kv head)
+    int hgroups;       // head groups per kv head (G / hw)
+    int n_items;       // n_pbw * B * Hkv * hgroups
+};
+
+struct DecodeParams {
+    const uint16_t *q, *k, *v;
+    const int32_t *block_table;  // paged layout only
+    const int32_t *seq_lens;
+    const float *sink;  // [Hq] or nullptr
+    uint16_t *out;
+    float *ws;  // partials [B][Hq][nsplit][kDv + 4] when nsplit > 1
+    int B, Hq, Hkv, G, hchunks;
+    int swa, window, paged, page_size, max_pages, num_pages, max_seq_len;
+    float scale_log2;
+    int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
+};
+
+int launch_prefill(const PrefillParams &p, hipStream_t stream);
+int launch_decode(const DecodeParams &p, hipStream_t stream);
+
+}  // namespace sinkattn

@@ -1,0 +1,237 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step runs every kernel of the path once, each on its benchmark workload:
+  swa_prefill_L32768   sliding-window prefill, L=32768, 64 query / 8 KV heads, W=128
+  ga_prefill_L32768    global causal prefill with sink, L=32768, 64 query / 4 KV heads
+  swa_decode_B128_ring sliding-window decode, 128 sequences, 128-slot ring caches
+  ga_decode_B8_256K    global decode, 8 sequences x 262144 tokens, 64-token permuted pages
+All inputs are synthetic (seeded N(0,1) bf16, sink ~ U[0,6]) and resident in HBM before
+timing starts.  Each call is timed with HIP events recorded on the stream the library
+launches on.
+
+`value` is the prefill throughput over both 32K prefill workloads (algorithmic flops of
+the two / their summed kernel time); the 256K decode KV-read bandwidth is reported next
+to it.  Algorithmic work counts 2*(192+128) flops per (query head, visible key) pair and,
+for decode, the K/V bytes of the visible keys.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s (SWA & GA+sink, 32K) + decode KV-read HBM GB/s at 256K"
+FLOP_PER_PAIR = 2 * (192 + 128)
+
+
+def pairs_prefill(L, mode, W):
+    if mode == 1:
+        n = min(L, W)
+        return n * (n + 1) // 2 + (L - n) * W
+    return L * (L + 1) // 2
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of workloads to run (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import attention_sink_softmax_amd as sa
+    from attention_sink_softmax_amd import inputs
+
+    sa.lib()  # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    only = set(filter(None, args.only.split(",")))
+    runs = {}  # name -> (callable, flops, bytes)
+
+    # --- prefill workloads
+    for w in (inputs.SWA_PREFILL, inputs.GA_PREFILL):
+        if only and w.name not in only:
+            continue
+        d = inputs.prefill_inputs(w)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        out = torch.empty((w.batch, w.hq, w.seqlen, w.d_v), dtype=torch.bfloat16, device=dev)
+        del d
+        flops = pairs_prefill(w.seqlen, w.mode, w.window) * w.hq * w.batch * FLOP_PER_PAIR
+        nbytes = (q.numel() + k.numel() + v.numel() + out.numel()) * 2
+
+        def call(w=w, q=q, k=k, v=v, sink=sink, out=out):
+            sa.sinkattn_prefill(w.mode, w.window, q, k, v, sink, out)
+
+        runs[w.name] = (call, flops, nbytes)
+
+    # --- sliding-window decode: 4 input sets rotate (one set fits the 256 MB Infinity Cache)
+    w = inputs.SWA_DECODE
+    if not only or w.name in only:
+        sets = []
+        for r in range(4):
+            d = inputs.decode_ring_inputs(w, seed=w.seed * 100 + r)
+            lens = d["seq_lens"]
+            sets.append(dict(q=up(d["q"]), k=up(d["k"]), v=up(d["v"]), lens=torch.from_numpy(lens).to(dev),
+                             maxlen=int(lens.max()), sink=torch.from_numpy(d["sink"]).to(dev)))
+        out = torch.empty((w.batch, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, 65536, dev)
+        visible = w.batch * w.window  # every context is longer than the window
+        flops = visible * w.hq * FLOP_PER_PAIR
+        nbytes = visible * w.hkv * (w.d_qk + w.d_v) * 2
+        state = {"i": 0}
+
+        def call(w=w, sets=sets, out=out, ws=ws, state=state):
+            s = sets[state["i"] % len(sets)]
+            state["i"] += 1
+            sa.sinkattn_decode(w.mode, w.window, s["q"], sa.KV_RING, s["k"], s["v"], s["lens"], s["maxlen"],
+                               s["sink"], out, ws)
+
+        runs[w.name] = (call, flops, nbytes)
+
+    # --- global decode at 256K, permuted 64-token pages
+    w = inputs.GA_DECODE
+    if not only or w.name in only:
+        d = inputs.decode_paged_inputs(w)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        bt = torch.from_numpy(d["block_table"]).to(dev)
+        lens = torch.from_numpy(d["seq_lens"]).to(dev)
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        del d
+        out = torch.empty((w.batch, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, w.ctx_hi, dev)
+        visible = w.batch * w.ctx_hi
+        flops = visible * w.hq * FLOP_PER_PAIR
+        nbytes = visible * w.hkv * (w.d_qk + w.d_v) * 2
+
+        def call(w=w, q=q, k=k, v=v, bt=bt, lens=lens, sink=sink, out=out, ws=ws):
+            sa.sinkattn_decode(w.mode, w.window, q, sa.KV_PAGED, k, v, lens, w.ctx_hi, sink, out, ws, bt)
+
+        runs[w.name] = (call, flops, nbytes)
+
+    names = list(runs)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for n in names:
+            runs[n][0]()
+    torch.cuda.synchronize()
+
+    ev = {n: [] for n in names}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for n in names:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            runs[n][0]()
+            e1.record(stream)
+            ev[n].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    comp = {}
+    for n in names:
+        ms = [a.elapsed_time(b) for a, b in ev[n]]
+        avg = float(np.mean(ms))
+        _, flops, nbytes = runs[n]
+        comp[n] = {"ms_avg": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
+                   "ms_max": round(float(np.max(ms)), 5),
+                   "tflops": round(flops / (avg * 1e-3) / 1e12, 3),
+                   "gbps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                   "algorithmic_gflop": round(flops / 1e9, 3), "algorithmic_gb": round(nbytes / 1e9, 4)}
+
+    pre = [n for n in ("swa_prefill_L32768", "ga_prefill_L32768") if n in comp]
+    value = None
+    if pre:
+        fl = sum(runs[n][1] for n in pre)
+        t = sum(comp[n]["ms_avg"] for n in pre) * 1e-3
+        value = round(fl / t / 1e12, 3)
+    dec = comp.get("ga_decode_B8_256K_paged")
+
+    roofline = None
+    if "ga_prefill_L32768" in comp:
+        c = comp["ga_prefill_L32768"]
+        roofline = {"kernel": "prefill_kernel (ga_prefill_L32768)", "bound": "mfma", "achieved": c["tflops"],
+                    "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(c["tflops"] / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roofline_decode = None
+    if dec:
+        roofline_decode = {"kernel": "decode_split_kernel+decode_merge_kernel (ga_decode_B8_256K_paged)",
+                           "bound": "hbm", "achieved": dec["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline and pre:
+        cpu = cpu_baseline()
+
+    step_ms = sum(comp[n]["ms_avg"] for n in names)
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "wall_s_timed": round(wall, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, sink ~ U[0,6]); no weights",
+        "config": {"workload": "sink attention hot path: " + " + ".join(names),
+                   "swa_prefill": "B=1 L=32768 Hq=64 Hkv=8 W=128 d_qk=192 d_v=128",
+                   "ga_prefill": "B=1 L=32768 Hq=64 Hkv=4 causal+sink d_qk=192 d_v=128",
+                   "swa_decode": "B=128 ctx~U[4096,65536] 128-slot ring Hq=64 Hkv=8",
+                   "ga_decode": "B=8 ctx=262144 64-token pages, permuted table, Hq=64 Hkv=4"},
+        "decode_kv_read_GBps": dec["gbps"] if dec else None,
+        "components": comp, "roofline": roofline, "roofline_decode": roofline_decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline():
+    """The CPU oracle (fp64, OpenMP) on a fixed sample of both prefill workloads: all 64 heads
+    at 4096 seeded positions of the sliding workload and 160 seeded positions of the global
+    one (about 128 GFLOP of algorithmic work)."""
+    import oracle
+    from attention_sink_softmax_amd import inputs
+
+    total_flops, total_t = 0, 0.0
+    parts = []
+    for w, npos in ((inputs.SWA_PREFILL, 4096), (inputs.GA_PREFILL, 160)):
+        d = inputs.prefill_inputs(w)
+        rng = np.random.default_rng([w.seed, 123])
+        pos = np.sort(rng.choice(w.seqlen, size=npos, replace=False))
+        rows = np.array([(0, h, i) for h in range(w.hq) for i in pos], np.int64)
+        fl = sum(min(i + 1, w.window) if w.mode == 1 else i + 1 for i in pos) * w.hq * FLOP_PER_PAIR
+        oracle.load()
+        t0 = time.perf_counter()
+        oracle.prefill(d["q"], d["k"], d["v"], d["sink"], w.mode, w.window, w.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        total_flops += fl
+        total_t += dt
+        parts.append(f"{w.name}: {w.hq} heads x {npos} positions, {fl / 1e9:.1f} GFLOP in {dt:.2f} s")
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(total_flops / total_t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "host_cores_visible": cores, "kind": "oracle", "sample": "; ".join(parts)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

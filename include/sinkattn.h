@@ -1,0 +1,146 @@
+/*
+ * sinkattn.h -- C ABI of libsinkattn.so: causal grouped-query softmax attention with a
+ * learnable per-query-head sink term in the softmax denominator, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (the sink softmax of "MiMo-V2-Flash 架构 QA", Q3.7 and Q3.8; the sink is
+ * described on the paper-notes page "MiMo-V2-Flash Technical Report", §4.1 and §4.3, and
+ * its eager form on "MiMo-V2-Flash 模型架构深度拆解", CH 10.1):
+ *
+ *   a_ij = scale * q_i . k_j
+ *   m_i  = max(max_{j in J(i)} a_ij, sink_h)
+ *   o_i  = sum_{j in J(i)} exp(a_ij - m_i) v_j / (exp(sink_h - m_i) + sum_{j in J(i)} exp(a_ij - m_i))
+ *
+ *   J(i) = { 0 <= j <= i }                      SINKATTN_GLOBAL (causal)
+ *        = { max(0, i - window + 1) <= j <= i } SINKATTN_SWA    (the `window` most recent
+ *                                                               keys, the query's own included)
+ *
+ * The sink has no value vector: it only enlarges the denominator, so the weights of a row
+ * sum to less than one.  It is given per QUERY head (the model declares it with
+ * num_attention_heads entries, deep-dive page CH 10.3) and in the units of the scaled
+ * logits (it is not multiplied by `scale`).  A NULL sink pointer means no sink term
+ * (standard softmax attention).  sink = +inf gives an all-zero output row; NaN is a caller
+ * error and is not checked.  GQA: query head h reads KV head h / (hq / hkv).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or synchronises, and keeps no mutable global state (thread-safe).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ *    asynchronously.  Results are valid once the stream has reached that point.
+ *  - Tensors are dense, row-major, in the index order written next to each argument.
+ *    bf16 means IEEE bfloat16 (raw 16-bit storage); sink is float32.
+ *  - Every pointer must be 16-byte aligned.
+ *  - Argument errors return a nonzero status at once and enqueue nothing.  A failed
+ *    kernel launch returns SINKATTN_E_DEVICE.  Faults during execution surface on the
+ *    stream like any other HIP error.
+ *  - Supported head sizes: d_qk = 192 and d_v = 128 (the model's qk/v head dims,
+ *    deep-dive page CH 8.1 and CH 10.3).  Other sizes return SINKATTN_E_UNSUPPORTED.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SINKATTN_GLOBAL = 0, SINKATTN_SWA = 1 } sinkattn_mode;
+typedef enum { SINKATTN_KV_RING = 0, SINKATTN_KV_PAGED = 1 } sinkattn_kv_layout;
+
+enum {
+    SINKATTN_OK = 0,
+    SINKATTN_E_NULL = 1,        /* a required pointer is NULL                         */
+    SINKATTN_E_SHAPE = 2,       /* a size is negative/zero where it must not be, or    */
+                                /* hq % hkv != 0, or a cache is too small for a length */
+    SINKATTN_E_UNSUPPORTED = 3, /* head sizes other than 192/128, unknown mode/layout, */
+                                /* a ring cache in global mode                         */
+    SINKATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+    SINKATTN_E_WORKSPACE = 5,   /* decode workspace NULL or smaller than required      */
+    SINKATTN_E_DEVICE = 6       /* the kernel launch failed                            */
+};
+
+/* Problem sizes.  seqlen: prefill length L (ignored by decode).  scale: logit scale,
+ * normally 1/sqrt(d_qk) (deep-dive page CH 10.3: scaling = head_dim ** -0.5). */
+typedef struct {
+    int32_t batch, seqlen, hq, hkv, d_qk, d_v;
+    float scale;
+} sinkattn_dims;
+
+/*
+ * KV cache descriptor for decode.
+ *  RING  (sliding-window mode only; deep-dive page CH 2.6: sliding layers keep only the
+ *        last `window` tokens): k bf16 [batch][hkv][window][d_qk], v bf16
+ *        [batch][hkv][window][d_v]; the token at position p is in slot p mod window.
+ *        block_table must be NULL; page_size, max_pages, num_pages are ignored.
+ *  PAGED (either mode; global layers keep every token): k bf16
+ *        [num_pages][hkv][page_size][d_qk], v bf16 [num_pages][hkv][page_size][d_v];
+ *        the token at position p of sequence b is in page block_table[b][p / page_size]
+ *        at offset p mod page_size.  block_table int32 [batch][max_pages].  A contiguous
+ *        cache is the identity table.  A page id outside [0, num_pages) is never read:
+ *        that sequence's output row becomes NaN.
+ */
+typedef struct {
+    int32_t layout;
+    const void *k;
+    const void *v;
+    const int32_t *block_table;
+    int32_t page_size, max_pages, num_pages;
+} sinkattn_kv;
+
+/*
+ * Prefill: every position of every sequence attends causally (GLOBAL) or within the
+ * sliding window (SWA) over the same sequence.
+ *   mode   SINKATTN_GLOBAL or SINKATTN_SWA
+ *   window window size W >= 1 (SWA; ignored by GLOBAL).  W >= seqlen equals GLOBAL.
+ *   d      sizes; batch >= 0, seqlen >= 0 (zero-sized work is a no-op), hq % hkv == 0
+ *   q      bf16 [batch][hq][seqlen][d_qk]
+ *   k      bf16 [batch][hkv][seqlen][d_qk]
+ *   v      bf16 [batch][hkv][seqlen][d_v]
+ *   sink   float32 [hq], or NULL for no sink
+ *   out    bf16 [batch][hq][seqlen][d_v]  (written; may not alias the inputs)
+ * Accumulation is float32; the probabilities enter the value product as bf16; out is
+ * rounded to nearest even.
+ */
+int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q, const void *k,
+                     const void *v, const float *sink, void *out, void *stream);
+
+/*
+ * Bytes of device workspace sinkattn_decode needs for these arguments (0 when none).
+ * max_seq_len is the host-side upper bound on seq_lens used to plan the key splits; pass
+ * the same value to sinkattn_decode.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t sinkattn_decode_workspace_bytes(int mode, int window, const sinkattn_dims *d,
+                                       int32_t max_seq_len);
+
+/*
+ * Decode: one new query per sequence, at position seq_lens[b] - 1; its own key and value
+ * must already be in the cache (the cache update precedes attention, deep-dive page
+ * CH 10.3 forward steps 6-7).
+ *   q            bf16 [batch][hq][d_qk]
+ *   kv           cache descriptor (above)
+ *   seq_lens     device int32 [batch]: tokens in each sequence INCLUDING the new one.
+ *                1 <= seq_lens[b] <= max_seq_len (PAGED: also <= max_pages * page_size).
+ *                A value <= 0 yields a zero output row; one above max_seq_len yields NaN.
+ *   max_seq_len  host upper bound on seq_lens (>= 1), used for split planning only
+ *   sink         float32 [hq], or NULL
+ *   out          bf16 [batch][hq][d_v]
+ *   workspace    device scratch of at least sinkattn_decode_workspace_bytes(...) bytes
+ *                (may be NULL when that is 0); its contents need no initialisation.
+ * Long contexts are split across workgroups; the per-split partial results are merged
+ * in a second kernel on the same stream, where the sink term enters exactly once.
+ */
+int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q,
+                    const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len,
+                    const float *sink, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *sinkattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

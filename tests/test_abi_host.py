@@ -1,0 +1,130 @@
+"""The C-ABI library on the host: it loads, exports what include/sinkattn.h declares, plans
+the decode workspace, and rejects bad arguments before touching any device.
+
+No call here reaches a kernel launch: every call has an argument error that the host-side
+checks report first (pointer values are never dereferenced by those checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_sink_softmax_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sa.LIB_PATH):
+        from attention_sink_softmax_amd import build
+        build.build()
+    return sa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*\s*|size_t\s+|int\s+)(sinkattn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(sa.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert sa.sinkattn_status_string(s)
+    assert sa.sinkattn_status_string(99) == "unknown status"
+
+
+def dims(B=1, Lq=64, hq=64, hkv=8, dqk=192, dv=128, scale=192 ** -0.5):
+    return sa.Dims(B, Lq, hq, hkv, dqk, dv, scale)
+
+
+A = 0x10000  # a 16-byte aligned fake address (never dereferenced)
+
+
+def prefill(L, mode=1, window=128, d=None, q=A, k=A, v=A, sink=None, out=A):
+    d = d or dims()
+    return L.sinkattn_prefill(mode, window, ctypes.byref(d), q, k, v, sink, out, None)
+
+
+def test_prefill_argument_errors(L):
+    assert L.sinkattn_prefill(1, 128, None, A, A, A, None, A, None) == E_NULL
+    assert prefill(L, mode=2) == E_UNSUP
+    assert prefill(L, d=dims(dqk=128)) == E_UNSUP
+    assert prefill(L, d=dims(dv=192)) == E_UNSUP
+    assert prefill(L, d=dims(hq=64, hkv=6)) == E_SHAPE
+    assert prefill(L, d=dims(hkv=0)) == E_SHAPE
+    assert prefill(L, d=dims(B=-1)) == E_SHAPE
+    assert prefill(L, d=dims(Lq=-1)) == E_SHAPE
+    assert prefill(L, mode=1, window=0) == E_SHAPE
+    assert prefill(L, d=dims(scale=float("nan"))) == E_SHAPE
+    assert prefill(L, q=None) == E_NULL
+    assert prefill(L, out=None) == E_NULL
+    assert prefill(L, k=A + 8) == E_ALIGN
+    assert prefill(L, sink=A + 4) == E_ALIGN
+    # empty work is a no-op success, even with NULL tensors
+    assert prefill(L, d=dims(Lq=0), q=None, k=None, v=None, out=None) == OK
+    assert prefill(L, d=dims(B=0), q=None, k=None, v=None, out=None) == OK
+
+
+def kv(layout=1, k=A, v=A, bt=A, ps=64, mp=4096, npg=32768):
+    return sa.KVDesc(layout, k, v, bt, ps, mp, npg)
+
+
+def decode(L, mode=0, window=0, d=None, q=A, desc=None, lens=A, maxlen=262144, sink=None, out=A, ws=A,
+           wsb=1 << 30):
+    d = d or dims(B=8, hq=64, hkv=4)
+    desc = desc if desc is not None else kv()
+    return L.sinkattn_decode(mode, window, ctypes.byref(d), q, ctypes.byref(desc), lens, maxlen, sink, out, ws, wsb,
+                             None)
+
+
+def test_decode_argument_errors(L):
+    assert decode(L, desc=kv(layout=0)) == E_UNSUP          # ring needs sliding mode
+    assert decode(L, desc=kv(layout=5)) == E_UNSUP
+    assert decode(L, maxlen=0) == E_SHAPE
+    assert decode(L, maxlen=262145) == E_SHAPE              # beyond max_pages * page_size
+    assert decode(L, desc=kv(ps=0)) == E_SHAPE
+    assert decode(L, desc=kv(npg=0)) == E_SHAPE
+    assert decode(L, q=None) == E_NULL
+    assert decode(L, lens=None) == E_NULL
+    assert decode(L, desc=kv(bt=None)) == E_NULL
+    assert decode(L, desc=kv(k=None)) == E_NULL
+    assert decode(L, out=A + 2) == E_ALIGN
+    assert decode(L, desc=kv(bt=A + 4)) == E_ALIGN
+    assert decode(L, ws=None) == E_WS
+    assert decode(L, wsb=100) == E_WS
+    assert decode(L, ws=A + 8) == E_ALIGN
+    assert decode(L, d=dims(B=8, hq=64, hkv=4, dqk=64)) == E_UNSUP
+    assert decode(L, mode=1, window=0, desc=kv(layout=0)) == E_SHAPE
+    assert L.sinkattn_decode(0, 0, ctypes.byref(dims()), A, None, A, 1, None, A, A, 0, None) == E_NULL
+    # batch 0 is a no-op
+    assert decode(L, d=dims(B=0, hq=64, hkv=4), q=None, out=None) == OK
+
+
+def test_decode_workspace_plan(L):
+    # 256K global decode: 8 sequences x 4 KV heads, split into 64 pieces of 4096 keys
+    n = sa.sinkattn_decode_workspace_bytes(0, 0, 8, 64, 4, 262144)
+    assert n == 8 * 64 * 64 * 132 * 4
+    # sliding ring decode: one split per (sequence, KV head), no workspace
+    assert sa.sinkattn_decode_workspace_bytes(1, 128, 128, 64, 8, 65536) == 0
+    assert sa.sinkattn_decode_workspace_bytes(1, 128, 1, 64, 8, 100) == 0
+    # short global context: single split
+    assert sa.sinkattn_decode_workspace_bytes(0, 0, 1, 64, 4, 100) == 0
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_decode_workspace_bytes(0, 0, 1, 64, 3, 100)
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_decode_workspace_bytes(0, 0, 1, 64, 4, 0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(sa.LibraryMissing):
+        sa.lib(str(tmp_path / "nope.so"))
