@@ -15,6 +15,8 @@ constexpr int kDqkSupported = 192;
 constexpr int kDvSupported = 128;
 constexpr int64_t kDecodeTargetWorkgroups = 2048;  // ~8 per CU on a 256-CU MI355X
 constexpr int kDecodeKeyBlock = 128;                // keys per decode workgroup iteration
+constexpr int kDecodeMaxChunk = 8192;               // keys per split at most (64 slices per wave)
+constexpr int kDecodeSingleSplit = 1024;            // key ranges this short are not split
 constexpr double kLog2eD = 1.4426950408889634;
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -35,15 +37,19 @@ struct DecodePlan {
 };
 
 // Keys per split: enough splits that B * Hkv * head-chunks * splits reaches about
-// kDecodeTargetWorkgroups, in whole 128-key blocks.
+// kDecodeTargetWorkgroups, in whole 128-key blocks.  The kernel walks keys in 32-key
+// slices aligned to absolute positions, so a sliding window of W keys spans up to W + 31
+// aligned keys; short ranges (up to kDecodeSingleSplit keys) stay in one split.
 DecodePlan plan_decode(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
     const int64_t G = d->hq / d->hkv;
     const int64_t hchunks = (G + 15) / 16;
-    const int64_t kmax = mode == SINKATTN_SWA ? (window < max_seq_len ? window : max_seq_len) : max_seq_len;
+    const int64_t kmax = mode == SINKATTN_SWA ? (window < max_seq_len ? window : max_seq_len) + 31 : max_seq_len;
     const int64_t units = (int64_t)d->batch * d->hkv * hchunks;
     int64_t chunk = units > 0 ? (kmax * units + kDecodeTargetWorkgroups - 1) / kDecodeTargetWorkgroups : kmax;
+    if (kmax <= kDecodeSingleSplit) chunk = kmax;
     chunk = ((chunk + kDecodeKeyBlock - 1) / kDecodeKeyBlock) * kDecodeKeyBlock;
     if (chunk < kDecodeKeyBlock) chunk = kDecodeKeyBlock;
+    if (chunk > kDecodeMaxChunk) chunk = kDecodeMaxChunk;
     const int64_t nsplit = (kmax + chunk - 1) / chunk;
     DecodePlan pl;
     pl.nsplit = (int)(nsplit < 1 ? 1 : nsplit);

@@ -25,14 +25,33 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) { return *reinterpret_
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value held by lane (lane ^ 32).
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16, 64); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Pack two floats to two bf16 (round to nearest even) in one dword: lo = a, hi = b.
+// Reductions across lane pairs (lane, lane ^ 32) and (lane, lane ^ 16) with the gfx950
+// lane-swap instructions: after v_permlane32_swap(x, x) one result holds x of the lower
+// half and the other x of the upper half in every lane, so combining the two results
+// combines each lane with its partner.
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Pack two floats to two bf16 (round to nearest even, v_cvt_pk_bf16_f32): lo = a, hi = b.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Byte-select of two dwords (v_perm_b32): result byte i = sel byte i over {hi:lo} bytes

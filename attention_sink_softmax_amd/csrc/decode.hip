@@ -9,15 +9,18 @@
 // exp(sink - M) enters exactly once, in that merge (or in the single-split epilogue), as
 // the sink softmax of "MiMo-V2-Flash 架构 QA" Q3.8 requires.
 //
-// Work of one workgroup (4 waves): keys are taken 128 at a time, 32 per wave.  The G query
-// heads that share the KV head (up to 16) form the N dimension of
+// Work of one workgroup (4 waves, one per SIMD, the whole 160 KB of LDS): each wave walks
+// its own 32-key slices of the split.  A slice's K (12 KB) and V (8 KB) go from HBM
+// straight into a per-wave LDS buffer with 16-byte direct-to-LDS loads (no registers
+// spent on staging), double buffered so the next slice is in flight while this one is
+// computed.  The G query heads that share the KV head (up to 16) form the N dimension of
 // v_mfma_f32_16x16x32_bf16, so every key byte read from HBM serves all of them:
-//   S^T[16 keys][16 heads] = K Q^T    K straight from global memory into the A operand,
+//   S^T[16 keys][16 heads] = K Q^T    K from LDS (one contiguous 1 KB read per operand),
 //                                     Q^T held in registers;
 //   O^T[16 dv][16 heads]  += V^T P^T  P^T is the score tile itself (same lane layout),
-//                                     V^T is V transposed in registers (8x8 bf16 blocks)
-//                                     and staged through a per-wave LDS tile.
-// Row statistics need two lane exchanges (xor 16, xor 32).  At the end the 4 waves'
+//                                     V^T comes from the row-major V slice through the
+//                                     transposing LDS read ds_read_b64_tr_b16.
+// Row statistics need two lane exchanges (lane ^ 16, lane ^ 32).  At the end the 4 waves'
 // states are merged through LDS.
 #include "common.h"
 #include "launch.h"
@@ -27,50 +30,46 @@ namespace sinkattn {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kKeysPerWave = 32;
-constexpr int kBlock = kWaves * kKeysPerWave;  // keys per workgroup iteration
-constexpr int kPart = kDv + 4;                  // partial record: o[128], m, l, 2 pad (16-byte rows)
+constexpr int kSlice = 32;                           // keys per wave step
+constexpr int kKBytes = kSlice * kDqk * 2;           // 12 KB: 12 blocks of 1 KB
+constexpr int kVBytes = kSlice * kDv * 2;            // 8 KB: 8 blocks of 1 KB
+constexpr int kBufBytes = kKBytes + kVBytes;         // one slice
+constexpr int kPart = kDv + 4;                       // partial record: o[128], m, l, 2 pad
+constexpr int kDmaPerSlice = (kKBytes + kVBytes) / 1024;  // 20 wave-wide 1 KB loads
 
-// Per-wave V^T tile [128 dv][32 keys]: 4 chunks of 8 keys per row, chunk c stored at
-// c ^ ((r >> 2) & 3) so the 16 rows of one MFMA operand read hit distinct banks.
-__device__ __forceinline__ int vt_off(int row, int chunk) { return row * 32 + ((chunk ^ (row >> 2)) & 3) * 8; }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Key (0..31 within the wave's slice) supplied as element e by k-group q of the PV product:
-// the 16x16 MFMA output gives lane group q the rows 4q..4q+3 of each 16-key score tile, and
-// the two tiles' registers are concatenated into one 32-key k-step.
-__device__ __forceinline__ int vkey(int q, int e) { return (e < 4) ? (4 * q + e) : (16 + 4 * q + (e - 4)); }
-
-struct KeyAddr {
-    const uint16_t *k;  // row of d_qk values, or nullptr when the key is not readable
-    const uint16_t *v;
-    bool bad;           // page id outside the pool
-};
-
-// Address of visible key number j (0-based within [kbeg, kend)) of sequence b.
-__device__ __forceinline__ KeyAddr key_addr(const DecodeParams &p, int b, int kvh, int j) {
-    KeyAddr a{nullptr, nullptr, false};
-    if (!p.paged) {
-        // ring: the visible keys are slots 0..min(n, W)-1 (position p lives in slot p mod W,
-        // and the W most recent positions occupy distinct slots)
-        const size_t row = ((size_t)b * p.Hkv + kvh) * p.window + j;
-        a.k = p.k + row * kDqk;
-        a.v = p.v + row * kDv;
-        return a;
-    }
-    const int page = p.block_table[(size_t)b * p.max_pages + j / p.page_size];
-    if (page < 0 || page >= p.num_pages) {
-        a.bad = true;
-        return a;
-    }
-    const size_t row = ((size_t)page * p.Hkv + kvh) * p.page_size + (j % p.page_size);
-    a.k = p.k + row * kDqk;
-    a.v = p.v + row * kDv;
-    return a;
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform).
+__device__ __forceinline__ void dma16(const uint16_t *src, char *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kWaves][kDv * kKeysPerWave];
-    __shared__ float red_m[kWaves][16], red_l[kWaves][16];
+// LDS layout of one slice (per wave, per buffer):
+//   K: block (sb, kk) = 16 keys x 64 bytes (d = 32kk .. 32kk+31); slot q*16 + key holds
+//      K[16sb + key][32kk + 8q .. +8], so the A operand of S^T is the 1 KB block itself.
+//   V: block m = keys 4m .. 4m+3, 256 bytes each; row r keeps its 16-byte chunk c in slot
+//      c ^ 2r, so the transposing reads of 4 rows x 32 bytes hit distinct banks.
+
+// Row of key j (general path): ring slot j, or page block_table[b][j / page_size].
+__device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, int kvh, int j, const uint16_t *base,
+                                                  int width, bool &bad) {
+    if (!p.paged) return base + (((size_t)b * p.Hkv + kvh) * p.window + j) * width;
+    const int page = p.block_table[(size_t)b * p.max_pages + j / p.page_size];
+    if (page < 0 || page >= p.num_pages) {
+        bad = true;
+        return base;
+    }
+    return base + (((size_t)page * p.Hkv + kvh) * p.page_size + (j % p.page_size)) * width;
+}
+
+template <bool kFast>
+__global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
+    // two buffer objects (even / odd slices) so that the compiler can tell the loads in
+    // flight into one from the reads of the other
+    __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufBytes];
+    __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kBufBytes];
 
     const int split = blockIdx.x;
     const int kvh = blockIdx.y % p.Hkv, hc = blockIdx.y / p.Hkv;
@@ -82,8 +81,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int h = kvh * p.G + hidx;
 
     const int n = p.seq_lens[b];
-    // visible keys: positions [max(0, n-W), n) (sliding) or [0, n) (global); the ring
-    // enumerates them as slots [0, min(n, W))
+    // visible keys [kbeg, kend): positions [max(0, n-W), n) (sliding) or [0, n) (global);
+    // the ring enumerates them as slots [0, min(n, W)).  Slices are aligned to 32 keys.
     int kbeg, kend;
     if (!p.paged) {
         kbeg = 0;
@@ -93,8 +92,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         kend = n;
     }
     const bool seq_ok = n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
-    const int s_lo = kbeg + split * p.chunk;
+    const int kb0 = kbeg & ~(kSlice - 1);
+    const int s_lo = kb0 + split * p.chunk;
     const int s_hi = seq_ok ? min(kend, s_lo + p.chunk) : s_lo;  // empty when the length is invalid
+    const int nslices = s_hi > s_lo ? (s_hi - s_lo + kSlice - 1) / kSlice : 0;
+    const int nmine = nslices > wave ? (nslices - wave + kWaves - 1) / kWaves : 0;
 
     // Q^T fragments: lane supplies q[h][32kk + 8q .. +8]
     bf16x8 qf[6];
@@ -104,108 +106,170 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         for (int kk = 0; kk < 6; ++kk) qf[kk] = as_bf16x8(head_ok ? ldg16(qrow + 32 * kk) : u32x4{0, 0, 0, 0});
     }
 
+    bool bad = false;
+
+    // Page of each of this wave's slices (lane i: slice i; a split holds at most 8192 keys,
+    // so a wave has at most 64 slices), loaded before the loop so that no table read sits
+    // between the direct-to-LDS loads (fast paged path).
+    int page_reg = 0;
+    if (kFast && p.paged && lane < nmine) {
+        const int j0 = s_lo + kSlice * (wave + kWaves * lane);
+        page_reg = p.block_table[(size_t)b * p.max_pages + j0 / p.page_size];
+    }
+
+    // Issue the 20 direct-to-LDS loads of slice i (of this wave) into `dst`.
+    auto issue = [&](int i, char *dst) {
+        const int j0 = s_lo + kSlice * (wave + kWaves * i);
+        char *kb = dst;
+        char *vb = kb + kKBytes;
+        const int r = lane >> 4, s = lane & 15;
+        if (kFast) {
+            // ring, or pages holding a multiple of 32 keys (one page per slice): rows
+            // j0..j0+31 are contiguous; keys outside [kbeg, kend) read a clamped valid row
+            // (their scores are masked)
+            const uint16_t *kbase, *vbase;
+            int off0;
+            if (p.paged) {
+                const int page = __builtin_amdgcn_readlane(page_reg, i);
+                const bool ok = page >= 0 && page < p.num_pages;
+                bad |= !ok;
+                const size_t row0 = ((size_t)(ok ? page : 0) * p.Hkv + kvh) * p.page_size;
+                kbase = p.k + row0 * kDqk;
+                vbase = p.v + row0 * kDv;
+                off0 = j0 % p.page_size;
+            } else {
+                const size_t row0 = ((size_t)b * p.Hkv + kvh) * p.window;
+                kbase = p.k + row0 * kDqk;
+                vbase = p.v + row0 * kDv;
+                off0 = j0;
+            }
+            const int lo = max(kbeg, j0) - j0, hi = min(kend, j0 + kSlice) - 1 - j0;  // valid key offsets
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int t = min(max(16 * sb + s, lo), hi);
+                const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
+#pragma unroll
+                for (int kk = 0; kk < 6; ++kk) dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int t = min(max(4 * m + r, lo), hi);
+                dma16(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
+            }
+        } else {
+            const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int j = min(max(j0 + 16 * sb + s, lo), hi);
+                const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * r;
+#pragma unroll
+                for (int kk = 0; kk < 6; ++kk) dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int j = min(max(j0 + 4 * m + r, lo), hi);
+                dma16(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
+            }
+        }
+    };
+
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
-    uint16_t *vt = Vt[wave];
 
-    for (int blk = s_lo; blk < s_hi; blk += kBlock) {
-        const int w0 = blk + kKeysPerWave * wave;  // first key of this wave's slice
-        // ---- K operand: two 16-key tiles, lane key = w0 + 16*sb + hl, d chunk 8q + 32kk
-        bf16x8 kf[2][6];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int j = w0 + 16 * sb + hl;
-            const bool in = j < s_hi;
-            const KeyAddr a = in ? key_addr(p, b, kvh, j) : KeyAddr{nullptr, nullptr, false};
-            bad |= a.bad;
-            const bool rd = in && !a.bad;
-#pragma unroll
-            for (int kk = 0; kk < 6; ++kk)
-                kf[sb][kk] = as_bf16x8(rd ? ldg16(a.k + 32 * kk + 8 * q) : u32x4{0, 0, 0, 0});
+    // Slice i: put slice i+1 in flight into `nxt`, wait for slice i, compute it from `cur`.
+    auto step = [&](int i, const char *cur, char *nxt) {
+        if (i + 1 < nmine) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of `nxt` are done
+            issue(i + 1, nxt);
+            // vmcnt(20): the 20 loads just issued may stay in flight; slice i has landed
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerSlice & 15) | ((kDmaPerSlice >> 4) << 14));
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
-        // ---- V: lane owns k-group kq (8 keys) x dv chunk c (8 values); transpose into LDS
-        {
-            const int kq = lane & 3, c = lane >> 2;
-            u32x4 r[8], w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = w0 + vkey(kq, e);
-                const bool in = j < s_hi;
-                const KeyAddr a = in ? key_addr(p, b, kvh, j) : KeyAddr{nullptr, nullptr, false};
-                r[e] = (in && !a.bad) ? ldg16(a.v + 8 * c) : u32x4{0, 0, 0, 0};
-            }
-            transpose8x8_b16(r, w);
-#pragma unroll
-            for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4 *>(&vt[vt_off(8 * c + d, kq)]) = w[d];
-        }
-        // ---- scores
+        const char *kb = cur;
+        const char *vb = kb + kKBytes;
+        const int j0 = s_lo + kSlice * (wave + kWaves * i);
+
+        // ---- scores: S^T tiles of 16 keys x 16 heads
         f32x4 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 6; ++kk)
-                s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[sb][kk], qf[kk], s[sb], 0, 0, 0);
+            for (int kk = 0; kk < 6; ++kk) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
+                s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[sb], 0, 0, 0);
+            }
         }
-        // lane holds keys w0 + 16sb + 4q + i for head hl
+        // lane holds keys j0 + 16sb + 4q + e for head hl
         float x[8];
         float mx = m_run;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = w0 + 16 * sb + 4 * q + i;
-                const float v = j < s_hi ? s[sb][i] * p.scale_log2 : -INFINITY;
-                x[4 * sb + i] = v;
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 16 * sb + 4 * q + e;
+                const float v = (j >= kbeg && j < s_hi) ? s[sb][e] * p.scale_log2 : -INFINITY;
+                x[4 * sb + e] = v;
                 mx = fmaxf(mx, v);
             }
         }
-        mx = fmaxf(mx, xor16(mx));
-        mx = fmaxf(mx, xor32(mx));
+        mx = max_xor32(max_xor16(mx));
         const float mu = (mx == -INFINITY) ? 0.f : mx;
         const float alpha = exp2f_fast(m_run - mu);
         m_run = mx;
         float ps = 0.f;
         uint32_t pk[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p0 = exp2f_fast(x[2 * i] - mu), p1 = exp2f_fast(x[2 * i + 1] - mu);
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = exp2f_fast(x[2 * e] - mu), p1 = exp2f_fast(x[2 * e + 1] - mu);
             ps += p0 + p1;
-            pk[i] = pack_bf16x2(p0, p1);
+            pk[e] = pack_bf16x2(p0, p1);
         }
         l_run = l_run * alpha + ps;
         const bf16x8 pf = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- O^T += V^T P^T; V^T through the transposing read: 16-lane group q, lane
+        // 4r + c4 addresses row r (keys 4q + r, then 16 + 4q + r) at dv 16db + 4c4, and lane i
+        // of the group receives dv 16db + i of the 4 rows
+        const int r = hl >> 2, c4 = lane & 3;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&vt[vt_off(16 * db + hl, q)]);
+            const int c = 2 * db + (c4 >> 1);
+            const int off = r * 256 + ((c ^ (2 * r)) * 16) + (c4 & 1) * 8;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + q * 1024 + off));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (4 + q) * 1024 + off));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[db] * alpha, 0, 0, 0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    if (nmine > 0) issue(0, bufA[wave]);
+    for (int i = 0; i < nmine; i += 2) {
+        step(i, bufA[wave], bufB[wave]);
+        if (i + 1 < nmine) step(i + 1, bufB[wave], bufA[wave]);
     }
 
-    // ---- merge the 4 waves' states through LDS (reusing the V tiles as float storage)
-    float lsum = l_run + xor16(l_run);
-    lsum += xor32(lsum);
-    const bool any_bad = __syncthreads_or(bad) != 0;
-    float *ob = reinterpret_cast<float *>(&Vt[0][0]);  // [4 waves][16 heads][128 dv] floats = 32 KB
+    // ---- merge the 4 waves' states through LDS (reusing the slice buffers)
+    const float lsum = sum_xor32(sum_xor16(l_run));
+    const bool wave_bad = __any(bad);
+    __syncthreads();  // every wave is done with its slice buffers
+    float *ob = reinterpret_cast<float *>(&bufA[0][0]);  // [4 waves][16 heads][128 dv]
+    float *red_m = ob + kWaves * 16 * kDv, *red_l = red_m + kWaves * 16, *red_bad = red_l + kWaves * 16;
     if (q == 0) {
-        red_m[wave][hl] = m_run;
-        red_l[wave][hl] = lsum;
+        red_m[wave * 16 + hl] = m_run;
+        red_l[wave * 16 + hl] = lsum;
     }
+    if (lane == 0) red_bad[wave] = wave_bad ? 1.f : 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ob[(wave * 16 + hl) * kDv + 16 * db + 4 * q + i] = acc[db][i];
+        for (int e = 0; e < 4; ++e) ob[(wave * 16 + hl) * kDv + 16 * db + 4 * q + e] = acc[db][e];
     __syncthreads();
 
+    const bool any_bad = (red_bad[0] + red_bad[1] + red_bad[2] + red_bad[3]) != 0.f;
     // thread -> (head hh, 8 dv values)
     const int hh = tid >> 4, d0 = (tid & 15) * 8;
     const int hidx2 = hc * 16 + hh;
@@ -213,15 +277,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     const int h2 = kvh * p.G + hidx2;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][hh]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        const float sc = exp2f_fast(red_m[w][hh] - Mu);
-        L += sc * red_l[w][hh];
+        const float sc = exp2f_fast(red_m[w * 16 + hh] - Mu);
+        L += sc * red_l[w * 16 + hh];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] += sc * ob[(w * 16 + hh) * kDv + d0 + i];
+        for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
     }
 
     if (p.nsplit == 1) {
@@ -230,15 +294,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
         float res[8];
         if (n <= 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) res[i] = 0.f;
+            for (int e = 0; e < 8; ++e) res[e] = 0.f;
         } else if (!seq_ok || any_bad) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) res[i] = __builtin_nanf("");
+            for (int e = 0; e < 8; ++e) res[e] = __builtin_nanf("");
         } else {
             const float sk = p.sink ? p.sink[h2] : -INFINITY;
             if (sk == INFINITY) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) res[i] = 0.f;
+                for (int e = 0; e < 8; ++e) res[e] = 0.f;
             } else {
                 const float sl = sk * kLog2e;
                 const float M2 = fmaxf(M, sl);
@@ -246,15 +310,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
                 const float Lt = L * sc + (sk == -INFINITY ? 0.f : exp2f_fast(sl - M2));
                 const float inv = 1.f / Lt;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) res[i] = o[i] * sc * inv;
+                for (int e = 0; e < 8; ++e) res[e] = o[e] * sc * inv;
             }
         }
         *reinterpret_cast<u32x4 *>(orow) = u32x4{pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]),
                                                  pack_bf16x2(res[4], res[5]), pack_bf16x2(res[6], res[7])};
     } else {
         float *rec = p.ws + (((size_t)b * p.Hq + h2) * p.nsplit + split) * kPart;
-#pragma unroll
-        for (int i = 0; i < 8; i += 4) *reinterpret_cast<f32x4 *>(rec + d0 + i) = f32x4{o[i], o[i + 1], o[i + 2], o[i + 3]};
+        *reinterpret_cast<f32x4 *>(rec + d0) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4 *>(rec + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
         if ((tid & 15) == 0) {
             rec[kDv] = M;
             rec[kDv + 1] = any_bad ? __builtin_nanf("") : L;
@@ -262,44 +326,74 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
     }
 }
 
-// One wave per (sequence, query head): merge the splits' partials and add the sink once.
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+// One workgroup of 128 threads per (sequence, query head): thread t owns output dim t.
+// Merges the splits' partials and adds the sink term once.
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
+    __shared__ float red[128];
     const int bh = blockIdx.x;
     const int b = bh / p.Hq, h = bh % p.Hq;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x;
     const int n = p.seq_lens[b];
-    uint16_t *orow = p.out + (size_t)bh * kDv + 2 * lane;
+    uint16_t *out = p.out + (size_t)bh * kDv + t;
     const bool seq_ok = n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
     if (n <= 0 || !seq_ok) {
         const float z = n <= 0 ? 0.f : __builtin_nanf("");
-        *reinterpret_cast<uint32_t *>(orow) = pack_bf16x2(z, z);
+        *out = __builtin_bit_cast(uint16_t, (__bf16)z);
         return;
     }
-    const int kbeg = p.paged ? (p.swa ? max(0, n - p.window) : 0) : 0;
-    const int kend = p.paged ? n : min(n, p.window);
-    const int used = (kend - kbeg + p.chunk - 1) / p.chunk;  // splits that saw keys
+    int kbeg, kend;
+    if (!p.paged) {
+        kbeg = 0;
+        kend = min(n, p.window);
+    } else {
+        kbeg = p.swa ? max(0, n - p.window) : 0;
+        kend = n;
+    }
+    const int kb0 = kbeg & ~(kSlice - 1);
+    const int used = (kend - kb0 + p.chunk - 1) / p.chunk;  // splits that saw keys
     const float *base = p.ws + (size_t)bh * p.nsplit * kPart;
 
     const float sk = p.sink ? p.sink[h] : -INFINITY;
     const bool sink_inf = sk == INFINITY;
     const float sl = (sink_inf ? -INFINITY : sk) * kLog2e;  // an infinite sink is applied at the end
     float M = sl;
-    for (int s = lane; s < used; s += 64) M = fmaxf(M, base[(size_t)s * kPart + kDv]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    for (int s = t; s < used; s += 128) M = fmaxf(M, base[(size_t)s * kPart + kDv]);
+    red[t] = M;
+    __syncthreads();
+    for (int w = 64; w >= 1; w >>= 1) {
+        if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+        __syncthreads();
+    }
+    M = red[0];
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float L = (sl == -INFINITY) ? 0.f : exp2f_fast(sl - Mu);
-    float o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < used; ++s) {
-        const float *rec = base + (size_t)s * kPart;
-        const float sc = exp2f_fast(rec[kDv] - Mu);
-        L += sc * rec[kDv + 1];  // a NaN sum marks an unreadable page and poisons L
-        o0 += sc * rec[2 * lane];
-        o1 += sc * rec[2 * lane + 1];
+    float o = 0.f;
+    int s = 0;
+    for (; s + 4 <= used; s += 4) {
+        float sc[4], lv[4], ov[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *rec = base + (size_t)(s + u) * kPart;
+            sc[u] = rec[kDv];
+            lv[u] = rec[kDv + 1];
+            ov[u] = rec[t];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float e = exp2f_fast(sc[u] - Mu);
+            L += e * lv[u];  // a NaN sum marks an unreadable page and poisons L
+            o += e * ov[u];
+        }
     }
-    float r0 = o0 / L, r1 = o1 / L;
-    if (sink_inf && !__builtin_isnan(L)) r0 = r1 = 0.f;
-    *reinterpret_cast<uint32_t *>(orow) = pack_bf16x2(r0, r1);
+    for (; s < used; ++s) {
+        const float *rec = base + (size_t)s * kPart;
+        const float e = exp2f_fast(rec[kDv] - Mu);
+        L += e * rec[kDv + 1];
+        o += e * rec[t];
+    }
+    float r = o / L;
+    if (sink_inf && !__builtin_isnan(L)) r = 0.f;
+    *out = __builtin_bit_cast(uint16_t, (__bf16)r);
 }
 
 }  // namespace
@@ -308,11 +402,12 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     DecodeParams p = prm;
     void *args[] = {&p};
     const dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B);
-    if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_kernel), grid, dim3(256), args, 0, stream) !=
-        hipSuccess)
-        return -1;
+    const bool fast = !p.paged || (p.page_size % kSlice == 0);
+    const void *fn = fast ? reinterpret_cast<const void *>(&decode_split_kernel<true>)
+                          : reinterpret_cast<const void *>(&decode_split_kernel<false>);
+    if (hipLaunchKernel(fn, grid, dim3(256), args, 0, stream) != hipSuccess) return -1;
     if (p.nsplit > 1) {
-        if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_merge_kernel), dim3(p.B * p.Hq), dim3(64), args, 0,
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_merge_kernel), dim3(p.B * p.Hq), dim3(128), args, 0,
                             stream) != hipSuccess)
             return -1;
     }

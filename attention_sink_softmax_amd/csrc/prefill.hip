@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
                 }
                 mx = fmaxf(mx, x[r]);
             }
-            mx = fmaxf(mx, xor32(mx));
+            mx = max_xor32(mx);
             const float mu = (mx == -INFINITY) ? 0.f : mx;
             const float alpha = exp2f_fast(m_run - mu);
             m_run = mx;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
 
     // ---- epilogue: O = acc / l; lane holds dv 32db + 8i + 4g + j of query qi
-    const float lt = l_run + xor32(l_run);
+    const float lt = sum_xor32(l_run);
     if (!wave_live || qi >= p.L) return;
     const float inv = 1.f / lt;
     uint16_t *orow = p.out + ((((size_t)b * p.Hq + h) * p.L) + qi) * kDv + 4 * g;
