@@ -1,14 +1,15 @@
 """Python binding of libsinkattn.so: sink-bias softmax attention on MI355X (gfx950).
 
-The functions named like the C ABI (sinkattn_prefill, sinkattn_decode,
-sinkattn_decode_workspace_bytes, sinkattn_status_string) only marshal arguments: they
+The functions named like the C ABI (sinkattn_prefill, sinkattn_prefill_workspace_bytes,
+sinkattn_decode, sinkattn_decode_workspace_bytes, sinkattn_status_string) only marshal
+arguments: they
 check that torch tensors have the dtype, device, contiguity and shapes the C ABI
 documents, then pass raw device pointers, sizes and the current HIP stream.  Every step
 of the computation runs in the library's HIP kernels; there is no fallback.  If the
 library has not been built, the first call raises LibraryMissing.
 
-`prefill` and `decode` are conveniences that allocate the output (and the decode
-workspace) with torch and call the C-ABI functions.
+`prefill` and `decode` are conveniences that allocate the output and the workspace with
+torch and call the C-ABI functions.
 """
 from __future__ import annotations
 
@@ -51,7 +52,8 @@ class KVDesc(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
-EXPORTS = ("sinkattn_prefill", "sinkattn_decode", "sinkattn_decode_workspace_bytes", "sinkattn_status_string")
+EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_decode",
+           "sinkattn_decode_workspace_bytes", "sinkattn_status_string")
 
 _lib = None
 
@@ -67,7 +69,9 @@ def lib(path: str = LIB_PATH):
     P = ctypes.c_void_p
     I = ctypes.c_int
     L.sinkattn_prefill.restype = I
-    L.sinkattn_prefill.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P]
+    L.sinkattn_prefill.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.sinkattn_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.sinkattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.sinkattn_decode_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
     L.sinkattn_decode.restype = I
@@ -117,9 +121,20 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def sinkattn_prefill(mode: int, window: int, q, k, v, sink, out, scale: float | None = None, stream=None) -> None:
+def sinkattn_prefill_workspace_bytes(batch: int, seqlen: int, hq: int, hkv: int, d_qk: int = D_QK,
+                                     d_v: int = D_V) -> int:
+    d = Dims(batch, seqlen, hq, hkv, d_qk, d_v, d_qk ** -0.5)
+    n = lib().sinkattn_prefill_workspace_bytes(ctypes.byref(d))
+    if n == ctypes.c_size_t(-1).value:
+        raise SinkAttnError(2, "invalid sizes")
+    return n
+
+
+def sinkattn_prefill(mode: int, window: int, q, k, v, sink, out, workspace, scale: float | None = None,
+                     stream=None) -> None:
     """q bf16 [B,Hq,L,192], k bf16 [B,Hkv,L,192], v bf16 [B,Hkv,L,128], sink float32 [Hq] or
-    None, out bf16 [B,Hq,L,128] (written).  Enqueued on `stream` (default: current stream)."""
+    None, out bf16 [B,Hq,L,128] (written), workspace: a GPU tensor of at least
+    sinkattn_prefill_workspace_bytes(...) bytes.  Enqueued on `stream` (default: current)."""
     import torch
 
     B, Hq, L, dqk = q.shape
@@ -130,13 +145,17 @@ def sinkattn_prefill(mode: int, window: int, q, k, v, sink, out, scale: float | 
     _dev_tensor(out, "out", torch.bfloat16, (B, Hq, L, v.shape[3]))
     if sink is not None:
         _dev_tensor(sink, "sink", torch.float32, (Hq,))
-    for t in (k, v, out, sink):
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    for t in (k, v, out, sink, workspace):
         if t is not None and t.device != q.device:
             raise ValueError("all tensors must be on one device")
     d = Dims(B, L, Hq, Hkv, dqk, v.shape[3], dqk ** -0.5 if scale is None else scale)
     with torch.cuda.device(q.device):
         rc = lib().sinkattn_prefill(mode, window, ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out),
-                                    _stream_ptr(stream, q.device))
+                                    ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
     _raise(rc)
 
 
@@ -194,12 +213,23 @@ def sinkattn_decode(mode: int, window: int, q, layout: int, k_cache, v_cache, se
 
 
 # ---------------------------------------------------------------------------- conveniences
-def prefill(mode: int, window: int, q, k, v, sink=None, scale: float | None = None, stream=None):
-    """Allocate out (torch) and run sinkattn_prefill."""
+def prefill_workspace(q, k):
+    """A workspace tensor sized for sinkattn_prefill on these q/k shapes."""
+    import torch
+
+    B, Hq, L, _ = q.shape
+    n = sinkattn_prefill_workspace_bytes(B, L, Hq, k.shape[1])
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def prefill(mode: int, window: int, q, k, v, sink=None, scale: float | None = None, stream=None, workspace=None):
+    """Allocate out (and the workspace if none is given) with torch and run sinkattn_prefill."""
     import torch
 
     out = torch.empty((*q.shape[:3], v.shape[3]), dtype=torch.bfloat16, device=q.device)
-    sinkattn_prefill(mode, window, q, k, v, sink, out, scale, stream)
+    if workspace is None:
+        workspace = prefill_workspace(q, k)
+    sinkattn_prefill(mode, window, q, k, v, sink, out, workspace, scale, stream)
     return out
 
 

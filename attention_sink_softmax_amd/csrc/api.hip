@@ -27,7 +27,7 @@ int check_dims(int mode, int window, const sinkattn_dims *d) {
     if (d->d_qk != kDqkSupported || d->d_v != kDvSupported) return SINKATTN_E_UNSUPPORTED;
     if (d->batch < 0 || d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv != 0) return SINKATTN_E_SHAPE;
     if (mode == SINKATTN_SWA && window < 1) return SINKATTN_E_SHAPE;
-    if (!isfinite(d->scale)) return SINKATTN_E_SHAPE;
+    if (!isfinite(d->scale) || !(d->scale > 0.f)) return SINKATTN_E_SHAPE;
     return SINKATTN_OK;
 }
 
@@ -75,15 +75,24 @@ const char *sinkattn_status_string(int status) {
     }
 }
 
+size_t sinkattn_prefill_workspace_bytes(const sinkattn_dims *d) {
+    if (!d || d->batch < 0 || d->seqlen < 0 || d->hkv <= 0) return (size_t)-1;
+    return prefill_workspace_bytes(d->batch, d->hkv, d->seqlen);
+}
+
 int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q, const void *k, const void *v,
-                     const float *sink, void *out, void *stream) {
+                     const float *sink, void *out, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_dims(mode, window, d);
     if (st) return st;
     if (d->seqlen < 0) return SINKATTN_E_SHAPE;
+    if ((int64_t)d->seqlen * kDqkSupported * 2 > INT32_MAX) return SINKATTN_E_SHAPE;  // 32-bit row offsets
     if (d->batch == 0 || d->seqlen == 0) return SINKATTN_OK;
     if (!q || !k || !v || !out) return SINKATTN_E_NULL;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (sink && misaligned(sink)))
         return SINKATTN_E_ALIGN;
+    const size_t need = prefill_workspace_bytes(d->batch, d->hkv, d->seqlen);
+    if (!workspace || workspace_bytes < need) return SINKATTN_E_WORKSPACE;
+    if (misaligned(workspace)) return SINKATTN_E_ALIGN;
 
     PrefillParams p{};
     p.q = static_cast<const uint16_t *>(q);
@@ -91,6 +100,8 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
     p.v = static_cast<const uint16_t *>(v);
     p.sink = sink;
     p.out = static_cast<uint16_t *>(out);
+    p.vt = static_cast<uint16_t *>(workspace);
+    p.lpad = (d->seqlen + 63) / 64 * 64;
     p.B = d->batch;
     p.L = d->seqlen;
     p.Hq = d->hq;
@@ -99,8 +110,10 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
     p.swa = mode == SINKATTN_SWA;
     p.window = p.swa ? window : 0;
     p.scale_log2 = (float)((double)d->scale * kLog2eD);
-    p.hw = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
-    p.pw = 4 / p.hw;
+    p.hpw = (p.G % 2 == 0) ? 2 : 1;
+    p.hw = p.hpw;
+    while (p.hw * 2 <= 4 * p.hpw && p.G % (p.hw * 2) == 0) p.hw *= 2;
+    p.pw = 4 * p.hpw / p.hw;
     const int64_t npb = (p.L + 31) / 32;
     p.n_pbw = (int)((npb + p.pw - 1) / p.pw);
     p.hgroups = p.G / p.hw;

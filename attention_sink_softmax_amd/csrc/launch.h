@@ -8,13 +8,16 @@ namespace sinkattn {
 
 struct PrefillParams {
     const uint16_t *q, *k, *v;
+    uint16_t *vt;      // workspace: V^T [B][Hkv][kDv][lpad], keys of each 64-key tile in MFMA k-order
+    int lpad;          // L rounded up to a multiple of 64
     const float *sink;  // [Hq] or nullptr
     uint16_t *out;
     int B, L, Hq, Hkv, G;
     int swa, window;
     float scale_log2;  // logit scale * log2(e)
-    int hw;            // query heads per workgroup (4, 2 or 1; divides G)
-    int pw;            // 32-position blocks per workgroup (4 / hw)
+    int hpw;           // query heads per wave (2 when G is even, else 1)
+    int hw;            // query heads per workgroup (a multiple of hpw dividing G, at most 4 * hpw)
+    int pw;            // 32-position blocks per workgroup (4 * hpw / hw)
     int n_pbw;         // position groups per (batch, kv head)
     int hgroups;       // head groups per kv head (G / hw)
     int n_items;       // n_pbw * B * Hkv * hgroups
@@ -33,6 +36,7 @@ struct DecodeParams {
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
 };
 
+size_t prefill_workspace_bytes(int B, int Hkv, int L);
 int launch_prefill(const PrefillParams &p, hipStream_t stream);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 

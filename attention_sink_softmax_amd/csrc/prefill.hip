@@ -10,18 +10,31 @@
 // chunk), causal rows only the tiles at or below the diagonal.
 //
 // Layout of the work (gfx950, wave64):
-//   * A workgroup is 4 waves.  Each wave owns one query head and 32 consecutive query
-//     positions.  The 4 waves share one KV head (grouped-query attention), so one key/value
-//     tile staged in LDS feeds all of them.
+//   * A workgroup is 4 waves.  Each wave owns HPW query heads (2 when the GQA group size
+//     allows it) and 32 consecutive query positions; all waves of a workgroup share one KV
+//     head, so one key/value tile staged in LDS feeds all of them.  With two heads per wave
+//     every K and V fragment read from LDS feeds two MFMAs, which halves LDS read traffic
+//     per flop (LDS bandwidth, ~128 B/clk/CU, would otherwise cap the matrix cores).
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K comes
 //     from LDS as the A operand, Q^T stays in registers as the B operand for the whole
 //     kernel.  In the output layout a lane holds one query column and 16 key rows, so the
 //     row statistics need only one exchange with the partner lane (lane ^ 32), and the
 //     probabilities P^T are already in the B-operand layout of the second product
-//     O^T = V^T P^T (no shuffle of P through LDS).
-//   * V is transposed in registers (8x8 blocks of bf16) on its way into LDS, so the
-//     A operand of O^T = V^T P^T is one 16-byte LDS read per lane.
-//   * LDS tiles are XOR-swizzled so the MFMA operand reads are bank-conflict free.
+//     O^T = V^T P^T.
+//   * A first, HBM-bound kernel writes V^T into the caller's workspace with the keys of
+//     every 16-key group in MFMA k-order, so the A operand of V^T P^T is one 16-byte LDS
+//     read per lane.  K and V^T tiles then travel HBM -> LDS with 16-byte direct-to-LDS
+//     loads (no registers, no transposing in the hot loop) into blocks of 16 rows x 4
+//     chunks stored chunk-major: every 16-lane group of an MFMA operand read is one
+//     contiguous 256-byte run (no bank conflicts) and a lane's operand addresses differ
+//     only by compile-time offsets.  Tiles are double buffered in two distinct LDS objects,
+//     so the loads of tile t+1 overlap the math of tile t.
+//   * Softmax: the logit scale is folded into one FMA per score (exp2 domain), the
+//     running max is taken on raw scores, and the output accumulator is rescaled only
+//     when a row's max grows by more than 2^8 (the result is exact for any reference
+//     max; this only bounds the size of the unnormalised terms).
+//   * Sub-blocks fully inside every row's visible range take a branch-free path; diagonal
+//     and band-edge sub-blocks take a masked path.
 //   * Workgroup ids are remapped so that the workgroups sharing one KV head and position
 //     block land on the same XCD (each XCD has its own L2), heaviest causal rows first.
 #include "common.h"
@@ -33,29 +46,175 @@ namespace {
 
 constexpr int kBQ = 32;    // query positions per wave
 constexpr int kBN = 64;    // keys per LDS tile
+constexpr int kKTileBytes = kBN * kDqk * 2;  // 24 KB
+constexpr int kVTileBytes = kDv * kBN * 2;   // 16 KB
+constexpr float kLazyRescale = 8.f;          // log2 growth of a row max that forces a rescale
 
-// K tile [64 keys][192]: row r holds 24 chunks of 8 bf16; chunk c is stored at
-// (c & ~7) | ((c ^ (r >> 1)) & 7) so 16 consecutive rows read at one column hit distinct banks.
-__device__ __forceinline__ int ks_off(int row, int chunk) {
-    return row * kDqk + ((chunk & ~7) | ((chunk ^ (row >> 1)) & 7)) * 8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---- K tile layout: 24 blocks of 1 KB; block (rg, cg) holds rows 16rg..16rg+15 (keys) and
+// 16-byte chunks 4cg..4cg+3 (8 consecutive d each); chunk c of row r sits in slot 16c + r.
+// A 16-lane group of an MFMA operand read (16 consecutive rows, one chunk) is one
+// contiguous 256-byte run, and for a fixed lane the offsets of all (sub-block, k-step)
+// reads differ only by compile-time constants.
+__device__ __forceinline__ int k_off(int row, int chunk) {
+    return ((row >> 4) * 6 + (chunk >> 2)) * 1024 + ((chunk & 3) * 16 + (row & 15)) * 16;
 }
-// V^T tile [128 dv][64 keys]: row r holds 8 chunks of 8 keys in MFMA k-order; chunk c is
-// stored at (c ^ r ^ (r >> 3)) & 7.
+// ---- V^T tile [128 dv][64 keys] of bf16: 16 blocks of 1 KB; block (rg, kg) holds dv rows
+// 16rg..16rg+15 and key chunks 4kg..4kg+3 (8 keys each, in MFMA k-order); chunk c of row r
+// sits in slot 16c + r.  Byte offsets.
 __device__ __forceinline__ int vt_off(int row, int chunk) {
-    return row * kBN + ((chunk ^ row ^ (row >> 3)) & 7) * 8;
+    return ((row >> 4) * 2 + (chunk >> 2)) * 1024 + ((chunk & 3) * 16 + (row & 15)) * 16;
 }
-
 // Key (within a 64-key tile) supplied as element e by lane group g for the 16-key group gam.
 // In the 32x32 MFMA output a lane of group g holds, for register r, the key row
 // 8*(r/4) + 4*g + r%4 of a 32-key block; the PV product consumes registers 0..7 and 8..15
-// as two 16-key k-steps, so k-step gam, group g, element e is this key:
+// as two 16-key k-steps, so k-step gam, group g, element e is this key.  The transposed V
+// copy stores chunk 2*gam + g of every 64-key tile in this order.
 __device__ __forceinline__ int vkey(int gam, int g, int e) {
     return 16 * gam + ((e < 4) ? (4 * g + e) : (8 + 4 * g + (e - 4)));
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kDqk];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kDv * kBN];
+struct WaveCtx {
+    int L, swa, window;
+    float c;  // logit scale * log2(e)
+    int qpos0, qi, g, lq, lane;
+};
+
+// K tile rows kb..kb+63 -> LDS: block blk (0..23) = (rg, cg) is one wave instruction; lane l
+// fetches row 16rg + (l & 15), chunk 4cg + (l >> 4) (four lanes read 64 contiguous bytes of
+// each of 16 rows).  Rows past the sequence end are clamped to the last row (their scores
+// are masked).
+__device__ __forceinline__ void dma_k_block(char *Kt, const char *kbytes, int kb, int L, int blk, int lane) {
+    const int rg = blk / 6, cg = blk % 6;
+    const int row = min(kb + 16 * rg + (lane & 15), L - 1);
+    __builtin_amdgcn_global_load_lds(kbytes + (uint32_t)(row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16),
+                                     (lds_void *)(Kt + blk * 1024), 16, 0, 0);
+}
+// V^T tile (keys kb..kb+63 of every dv row of the transposed copy, whose rows are padded to
+// a whole number of tiles) -> LDS: block blk (0..15) = (rg, kg); lane l fetches dv row
+// 16rg + (l & 15), key chunk 4kg + (l >> 4).
+__device__ __forceinline__ void dma_vt_block(char *Vt, const char *vtbytes, int lpad, int kb, int blk, int lane) {
+    const int rg = blk >> 1, kg = blk & 1;
+    const int row = 16 * rg + (lane & 15);
+    __builtin_amdgcn_global_load_lds(vtbytes + (uint32_t)(row * lpad * 2 + (kb + 8 * (4 * kg + (lane >> 4))) * 2),
+                                     (lds_void *)(Vt + blk * 1024), 16, 0, 0);
+}
+// Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile (10 per wave).
+__device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const char *kbytes, const char *vtbytes, int lpad,
+                                           int kb, int L, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) dma_k_block(Kt, kbytes, kb, L, wave + 4 * i, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_vt_block(Vt, vtbytes, lpad, kb, wave + 4 * i, lane);
+}
+
+// One 32-key sub-block for one wave: S^T = K Q^T, online softmax with the sink-initialised
+// state, O^T += V^T P^T.  kMask: the sub-block touches a row's causal or window edge (or the
+// sequence end), so scores are masked.
+template <int HPW, bool kMask>
+__device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int kb, int sb,
+                                            const bf16x8 (&qf)[HPW][12], f32x16 (&acc)[HPW][4], float (&m_run)[HPW],
+                                            float (&l_run)[HPW], const WaveCtx &w) {
+    // ---- scores
+    f32x16 s[HPW];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) s[h] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Kt + k_off(32 * sb + w.lq, 2 * kk + w.g));
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[h][kk], s[h], 0, 0, 0);
+    }
+    // ---- masks (key row 8*(r/4) + 4g + r%4 of the sub-block, query column qi)
+    if (kMask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kj = kb + 32 * sb + 8 * (r >> 2) + 4 * w.g + (r & 3);
+            const bool ok = kj <= w.qi && kj < w.L && (!w.swa || kj > w.qi - w.window);
+#pragma unroll
+            for (int h = 0; h < HPW; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
+        }
+    }
+    // ---- running max on raw scores, lazy rescale
+    float mnew[HPW];
+    bool grow = false;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[h][r], s[h][r + 1]));
+        mx = max_xor32(mx) * w.c;
+        mnew[h] = fmaxf(m_run[h], mx);
+        grow |= mnew[h] > m_run[h] + kLazyRescale;
+    }
+    if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+            // unchanged max (including a row with no visible key yet, -inf) keeps alpha = 1;
+            // a first finite max after -inf gives 0
+            const float alpha = (mnew[h] == m_run[h]) ? 1.f : exp2f_fast(m_run[h] - mnew[h]);
+            l_run[h] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) acc[h][db] *= alpha;
+            m_run[h] = mnew[h];
+        }
+    }
+    // ---- probabilities and O^T += V^T P^T
+    bf16x8 pf[HPW][2];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const float neg = (m_run[h] == -INFINITY) ? 0.f : -m_run[h];
+        float ps = 0.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float p0 = exp2f_fast(__builtin_fmaf(s[h][2 * r], w.c, neg));
+            const float p1 = exp2f_fast(__builtin_fmaf(s[h][2 * r + 1], w.c, neg));
+            ps += p0 + p1;
+            pk[r] = pack_bf16x2(p0, p1);
+        }
+        l_run[h] += ps;
+        pf[h][0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+        pf[h][1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + vt_off(32 * db + w.lq, 4 * sb + 2 * k2 + w.g));
+#pragma unroll
+            for (int h = 0; h < HPW; ++h)
+                acc[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h][k2], acc[h][db], 0, 0, 0);
+        }
+    }
+}
+
+// One 64-key tile for one wave, as two 32-key sub-blocks.  Sub-blocks wholly outside this
+// wave's rows are skipped; sub-blocks wholly inside take the unmasked path.
+template <int HPW>
+__device__ __forceinline__ void compute_tile(const char *Kt, const char *Vt, int kb, const bf16x8 (&qf)[HPW][12],
+                                             f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
+                                             const WaveCtx &w) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        const int k0 = kb + 32 * sb;
+        const bool dead = k0 > w.qpos0 + kBQ - 1 || k0 >= w.L || (w.swa && k0 + 31 < w.qpos0 - w.window + 1);
+        if (dead) continue;
+        const bool full = k0 + 31 <= w.qpos0 && k0 + 32 <= w.L && (!w.swa || k0 >= w.qpos0 + kBQ - w.window);
+        if (full)
+            compute_sub<HPW, false>(Kt, Vt, kb, sb, qf, acc, m_run, l_run, w);
+        else
+            compute_sub<HPW, true>(Kt, Vt, kb, sb, qf, acc, m_run, l_run, w);
+    }
+}
+
+template <int HPW>
+__global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) {
+    __shared__ __attribute__((aligned(1024))) char KA[kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char KB[kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char VA[kVTileBytes];
+    __shared__ __attribute__((aligned(1024))) char VB[kVTileBytes];
 
     // ---- workgroup -> (position group, batch, kv head, head group), XCD-aware
     const int C = p.hgroups;
@@ -73,151 +232,150 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     const int pbw = p.n_pbw - 1 - t;  // heaviest (latest) positions first
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int g = lane >> 5, lq = lane & 31;
-    const int h = kvh * p.G + hg * p.hw + (wave % p.hw);
-    const int qpos0 = (pbw * p.pw + wave / p.hw) * kBQ;
+    const int wh = p.hw / HPW;  // waves along heads
+    const int h0 = kvh * p.G + hg * p.hw + (wave % wh) * HPW;
+    const int qpos0 = (pbw * p.pw + wave / wh) * kBQ;
     const int wg_q0 = pbw * p.pw * kBQ;
     const int wg_q1 = min(p.L, wg_q0 + p.pw * kBQ);
-    const int qi = qpos0 + lq;
+
+    WaveCtx w;
+    w.L = p.L;
+    w.swa = p.swa;
+    w.window = p.window;
+    w.c = p.scale_log2;
+    w.qpos0 = qpos0;
+    w.lane = lane;
+    w.g = lane >> 5;
+    w.lq = lane & 31;
+    w.qi = qpos0 + w.lq;
     const bool wave_live = qpos0 < p.L;
 
-    // ---- Q^T fragments (B operand): lane supplies q[qi][16kk + 8g .. +8]
-    bf16x8 qf[12];
+    // ---- Q^T fragments (B operand): lane supplies q[h][qi][16kk + 8g .. +8]
+    bf16x8 qf[HPW][12];
     {
-        const bool ok = qi < p.L;
-        const uint16_t *qrow = p.q + ((((size_t)b * p.Hq + h) * p.L) + (ok ? qi : 0)) * kDqk + 8 * g;
+        const bool ok = w.qi < p.L;
 #pragma unroll
-        for (int kk = 0; kk < 12; ++kk) {
-            u32x4 v = ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0};
-            qf[kk] = as_bf16x8(v);
+        for (int h = 0; h < HPW; ++h) {
+            const uint16_t *qrow = p.q + ((((size_t)b * p.Hq + h0 + h) * p.L) + (ok ? w.qi : 0)) * kDqk + 8 * w.g;
+#pragma unroll
+            for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0});
         }
     }
 
     // ---- running state: the sink starts the max and the denominator
-    const float sk = p.sink ? p.sink[h] : -INFINITY;
-    const bool has_sink = sk != -INFINITY;
-    const bool sink_inf = sk == INFINITY;
-    float m_run = has_sink ? sk * kLog2e : -INFINITY;
-    float l_run = (has_sink && g == 0) ? 1.f : 0.f;  // exp2(sink - m) = 1, counted on one lane of the pair
-    f32x16 acc[4];
+    float m_run[HPW], l_run[HPW];
+    bool sink_inf[HPW];
+    f32x16 acc[HPW][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+    for (int h = 0; h < HPW; ++h) {
+        const float sk = p.sink ? p.sink[h0 + h] : -INFINITY;
+        const bool has_sink = sk != -INFINITY;
+        sink_inf[h] = sk == INFINITY;
+        m_run[h] = has_sink ? sk * kLog2e : -INFINITY;
+        l_run[h] = (has_sink && w.g == 0) ? 1.f : 0.f;  // exp2(sink - m) = 1, counted on one lane of the pair
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[h][db] = f32x16{};
+    }
 
     const size_t kvbase = ((size_t)b * p.Hkv + kvh) * p.L;
-    const uint16_t *kg_base = p.k + kvbase * kDqk;
-    const uint16_t *vg_base = p.v + kvbase * kDv;
+    const char *kbytes = reinterpret_cast<const char *>(p.k + kvbase * kDqk);
+    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)b * p.Hkv + kvh) * kDv * p.lpad);
 
     const int k_lo = p.swa ? max(0, wg_q0 - p.window + 1) : 0;
     const int t0 = k_lo / kBN, t1 = (wg_q1 - 1) / kBN;
 
-    for (int kt = t0; kt <= t1; ++kt) {
-        const int kb = kt * kBN;
-        __syncthreads();  // the previous tile is no longer read
-        if (tid >= 128) {
-            // K tile: 64 rows x 24 chunks of 16 bytes over 128 threads, row-contiguous
-            const int t2 = tid - 128;
-#pragma unroll
-            for (int e = 0; e < 12; ++e) {
-                const int chunk = t2 + 128 * e;
-                const int row = chunk / 24, col = chunk % 24;
-                const int key = kb + row;
-                u32x4 val = key < p.L ? ldg16(kg_base + (size_t)key * kDqk + col * 8) : u32x4{0, 0, 0, 0};
-                *reinterpret_cast<u32x4 *>(&Ks[ks_off(row, col)]) = val;
-            }
-        } else {
-            // V tile: thread owns 8 keys (one MFMA k-chunk) x 8 dv; transpose, store rows of V^T
-            const int c = tid >> 3, kgp = tid & 7;
-            const int gam = kgp >> 1, hh = kgp & 1;
-            u32x4 r[8], w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = kb + vkey(gam, hh, e);
-                r[e] = key < p.L ? ldg16(vg_base + (size_t)key * kDv + 8 * c) : u32x4{0, 0, 0, 0};
-            }
-            transpose8x8_b16(r, w);
-#pragma unroll
-            for (int d = 0; d < 8; ++d) *reinterpret_cast<u32x4 *>(&Vt[vt_off(8 * c + d, kgp)]) = w[d];
-        }
-        __syncthreads();
+    // prologue: tile t0 into buffers A
+    issue_tile(KA, VA, kbytes, vtbytes, p.lpad, t0 * kBN, p.L, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
 
-        if (!wave_live) continue;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int k0 = kb + 32 * sb;
-            const bool skip = k0 > qpos0 + kBQ - 1 || k0 >= p.L || (p.swa && k0 + 31 < qpos0 - p.window + 1);
-            if (skip) continue;
-            const bool need_mask = (k0 + 31 > qpos0) || (k0 + 31 >= p.L) ||
-                                   (p.swa && k0 < qpos0 + kBQ - 1 - p.window + 1);
-            f32x16 s = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < 12; ++kk) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&Ks[ks_off(32 * sb + lq, 2 * kk + g)]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-            }
-            float x[16];
-            float mx = m_run;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                x[r] = s[r] * p.scale_log2;
-                if (need_mask) {
-                    const int kj = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool ok = kj <= qi && kj < p.L && (!p.swa || kj > qi - p.window);
-                    x[r] = ok ? x[r] : -INFINITY;
-                }
-                mx = fmaxf(mx, x[r]);
-            }
-            mx = max_xor32(mx);
-            const float mu = (mx == -INFINITY) ? 0.f : mx;
-            const float alpha = exp2f_fast(m_run - mu);
-            m_run = mx;
-            float ps = 0.f;
-            uint32_t pk[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float p0 = exp2f_fast(x[2 * r] - mu), p1 = exp2f_fast(x[2 * r + 1] - mu);
-                ps += p0 + p1;
-                pk[r] = pack_bf16x2(p0, p1);
-            }
-            l_run = l_run * alpha + ps;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-            const bf16x8 pf0 = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-            const bf16x8 pf1 = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(&Vt[vt_off(32 * db + lq, 4 * sb + g)]);
-                const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(&Vt[vt_off(32 * db + lq, 4 * sb + 2 + g)]);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf0, acc[db], 0, 0, 0);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pf1, acc[db], 0, 0, 0);
-            }
-        }
+    // Tile kt from (Kc, Vc) while tile kt+1 streams into (Kn, Vn).
+    auto step = [&](int kt, const char *Kc, const char *Vc, char *Kn, char *Vn) {
+        const bool more = kt < t1;
+        if (more) issue_tile(Kn, Vn, kbytes, vtbytes, p.lpad, (kt + 1) * kBN, p.L, wave, lane);
+        if (wave_live) compute_tile<HPW>(Kc, Vc, kt * kBN, qf, acc, m_run, l_run, w);
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 has landed
+        __syncthreads();
+    };
+    for (int kt = t0; kt <= t1; kt += 2) {
+        step(kt, KA, VA, KB, VB);
+        if (kt + 1 <= t1) step(kt + 1, KB, VB, KA, VA);
     }
 
     // ---- epilogue: O = acc / l; lane holds dv 32db + 8i + 4g + j of query qi
-    const float lt = sum_xor32(l_run);
-    if (!wave_live || qi >= p.L) return;
-    const float inv = 1.f / lt;
-    uint16_t *orow = p.out + ((((size_t)b * p.Hq + h) * p.L) + qi) * kDv + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int h = 0; h < HPW; ++h) {
+        const float lt = sum_xor32(l_run[h]);
+        if (!wave_live || w.qi >= p.L) continue;
+        const float inv = 1.f / lt;
+        uint16_t *orow = p.out + ((((size_t)b * p.Hq + h0 + h) * p.L) + w.qi) * kDv + 4 * w.g;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o0 = acc[h][db][4 * i] * inv, o1 = acc[h][db][4 * i + 1] * inv;
+                float o2 = acc[h][db][4 * i + 2] * inv, o3 = acc[h][db][4 * i + 3] * inv;
+                if (sink_inf[h]) o0 = o1 = o2 = o3 = 0.f;
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * i) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+            }
+        }
+    }
+}
+
+// V -> V^T with the keys of every 64-key tile in MFMA k-order (chunk 2*gam + g holds the
+// keys vkey(gam, g, 0..7)); rows padded with zeros to lpad keys.  One workgroup per
+// (batch x kv head, 64-key tile).
+__global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uint16_t *vt, int L, int lpad) {
+    __shared__ uint16_t tile[kBN][kDv + 8];
+    const int kb = blockIdx.x * kBN;
+    const size_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const uint16_t *src = v + bh * (size_t)L * kDv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 256 * e;
+        const int key = idx >> 4, c = idx & 15;
+        const u32x4 val = kb + key < L ? ldg16(src + (size_t)(kb + key) * kDv + 8 * c) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x2 *>(&tile[key][8 * c]) = u32x2{val.x, val.y};
+        *reinterpret_cast<u32x2 *>(&tile[key][8 * c + 4]) = u32x2{val.z, val.w};
+    }
+    __syncthreads();
+    uint16_t *dst = vt + bh * kDv * (size_t)lpad;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = tid + 256 * e;
+        const int row = idx >> 3, kc = idx & 7;
+        uint32_t wv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float o0 = acc[db][4 * i] * inv, o1 = acc[db][4 * i + 1] * inv;
-            float o2 = acc[db][4 * i + 2] * inv, o3 = acc[db][4 * i + 3] * inv;
-            if (sink_inf) o0 = o1 = o2 = o3 = 0.f;
-            *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * i) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+            const uint32_t lo = tile[vkey(kc >> 1, kc & 1, 2 * i)][row];
+            const uint32_t hi = tile[vkey(kc >> 1, kc & 1, 2 * i + 1)][row];
+            wv[i] = lo | (hi << 16);
         }
+        *reinterpret_cast<u32x4 *>(dst + (size_t)row * lpad + kb + 8 * kc) = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int B, int Hkv, int L) {
+    const size_t lpad = ((size_t)L + kBN - 1) / kBN * kBN;
+    return (size_t)B * Hkv * kDv * lpad * 2;
+}
+
 int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     PrefillParams p = prm;
+    {
+        void *targs[] = {(void *)&p.v, (void *)&p.vt, (void *)&p.L, (void *)&p.lpad};
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&transpose_v_kernel), dim3(p.lpad / kBN, p.B * p.Hkv),
+                            dim3(256), targs, 0, stream) != hipSuccess)
+            return -1;
+    }
     const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     void *args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel), dim3(grid), dim3(256), args, 0,
-                           stream) == hipSuccess ? 0 : -1;
+    const void *fn = p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
+                                : reinterpret_cast<const void *>(&prefill_kernel<1>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) == hipSuccess ? 0 : -1;
 }
 
 }  // namespace sinkattn

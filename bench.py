@@ -77,12 +77,13 @@ def main() -> int:
         q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
         sink = torch.from_numpy(d["sink"]).to(dev)
         out = torch.empty((w.batch, w.hq, w.seqlen, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.prefill_workspace(q, k)
         del d
         flops = pairs_prefill(w.seqlen, w.mode, w.window) * w.hq * w.batch * FLOP_PER_PAIR
         nbytes = (q.numel() + k.numel() + v.numel() + out.numel()) * 2
 
-        def call(w=w, q=q, k=k, v=v, sink=sink, out=out):
-            sa.sinkattn_prefill(w.mode, w.window, q, k, v, sink, out)
+        def call(w=w, q=q, k=k, v=v, sink=sink, out=out, ws=ws):
+            sa.sinkattn_prefill(w.mode, w.window, q, k, v, sink, out, ws)
 
         runs[w.name] = (call, flops, nbytes)
 

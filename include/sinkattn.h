@@ -57,12 +57,13 @@ enum {
     SINKATTN_E_UNSUPPORTED = 3, /* head sizes other than 192/128, unknown mode/layout, */
                                 /* a ring cache in global mode                         */
     SINKATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
-    SINKATTN_E_WORKSPACE = 5,   /* decode workspace NULL or smaller than required      */
+    SINKATTN_E_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
     SINKATTN_E_DEVICE = 6       /* the kernel launch failed                            */
 };
 
 /* Problem sizes.  seqlen: prefill length L (ignored by decode).  scale: logit scale,
- * normally 1/sqrt(d_qk) (deep-dive page CH 10.3: scaling = head_dim ** -0.5). */
+ * normally 1/sqrt(d_qk) (deep-dive page CH 10.3: scaling = head_dim ** -0.5); it must be a
+ * positive finite number. */
 typedef struct {
     int32_t batch, seqlen, hq, hkv, d_qk, d_v;
     float scale;
@@ -90,21 +91,34 @@ typedef struct {
 } sinkattn_kv;
 
 /*
+ * Bytes of device workspace sinkattn_prefill needs for these sizes (batch, seqlen, hkv are
+ * read): a transposed copy of V, 2 * batch * hkv * 128 * roundup(seqlen, 64) bytes.
+ * Returns (size_t)-1 for invalid sizes.
+ */
+size_t sinkattn_prefill_workspace_bytes(const sinkattn_dims *d);
+
+/*
  * Prefill: every position of every sequence attends causally (GLOBAL) or within the
  * sliding window (SWA) over the same sequence.
- *   mode   SINKATTN_GLOBAL or SINKATTN_SWA
- *   window window size W >= 1 (SWA; ignored by GLOBAL).  W >= seqlen equals GLOBAL.
- *   d      sizes; batch >= 0, seqlen >= 0 (zero-sized work is a no-op), hq % hkv == 0
- *   q      bf16 [batch][hq][seqlen][d_qk]
- *   k      bf16 [batch][hkv][seqlen][d_qk]
- *   v      bf16 [batch][hkv][seqlen][d_v]
- *   sink   float32 [hq], or NULL for no sink
- *   out    bf16 [batch][hq][seqlen][d_v]  (written; may not alias the inputs)
- * Accumulation is float32; the probabilities enter the value product as bf16; out is
- * rounded to nearest even.
+ *   mode      SINKATTN_GLOBAL or SINKATTN_SWA
+ *   window    window size W >= 1 (SWA; ignored by GLOBAL).  W >= seqlen equals GLOBAL.
+ *   d         sizes; batch >= 0, seqlen >= 0 (zero-sized work is a no-op), hq % hkv == 0,
+ *             seqlen * 384 < 2^31
+ *   q         bf16 [batch][hq][seqlen][d_qk]
+ *   k         bf16 [batch][hkv][seqlen][d_qk]
+ *   v         bf16 [batch][hkv][seqlen][d_v]
+ *   sink      float32 [hq], or NULL for no sink
+ *   out       bf16 [batch][hq][seqlen][d_v]  (written; may not alias the inputs)
+ *   workspace device scratch of at least sinkattn_prefill_workspace_bytes(d) bytes; its
+ *             contents need no initialisation and are overwritten.  Concurrent calls need
+ *             separate workspaces.
+ * Two kernels run on `stream`: one writes V transposed into the workspace, the second
+ * computes attention.  Accumulation is float32; the probabilities enter the value product
+ * as bf16; out is rounded to nearest even.
  */
 int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q, const void *k,
-                     const void *v, const float *sink, void *out, void *stream);
+                     const void *v, const float *sink, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of device workspace sinkattn_decode needs for these arguments (0 when none).

@@ -50,13 +50,13 @@ def dims(B=1, Lq=64, hq=64, hkv=8, dqk=192, dv=128, scale=192 ** -0.5):
 A = 0x10000  # a 16-byte aligned fake address (never dereferenced)
 
 
-def prefill(L, mode=1, window=128, d=None, q=A, k=A, v=A, sink=None, out=A):
+def prefill(L, mode=1, window=128, d=None, q=A, k=A, v=A, sink=None, out=A, ws=A, wsb=1 << 40):
     d = d or dims()
-    return L.sinkattn_prefill(mode, window, ctypes.byref(d), q, k, v, sink, out, None)
+    return L.sinkattn_prefill(mode, window, ctypes.byref(d), q, k, v, sink, out, ws, wsb, None)
 
 
 def test_prefill_argument_errors(L):
-    assert L.sinkattn_prefill(1, 128, None, A, A, A, None, A, None) == E_NULL
+    assert L.sinkattn_prefill(1, 128, None, A, A, A, None, A, A, 1 << 40, None) == E_NULL
     assert prefill(L, mode=2) == E_UNSUP
     assert prefill(L, d=dims(dqk=128)) == E_UNSUP
     assert prefill(L, d=dims(dv=192)) == E_UNSUP
@@ -70,6 +70,12 @@ def test_prefill_argument_errors(L):
     assert prefill(L, out=None) == E_NULL
     assert prefill(L, k=A + 8) == E_ALIGN
     assert prefill(L, sink=A + 4) == E_ALIGN
+    assert prefill(L, ws=None) == E_WS
+    assert prefill(L, wsb=1000) == E_WS
+    assert prefill(L, ws=A + 8) == E_ALIGN
+    assert prefill(L, d=dims(scale=-0.1)) == E_SHAPE
+    assert prefill(L, d=dims(scale=0.0)) == E_SHAPE
+    assert prefill(L, d=dims(Lq=6_000_000)) == E_SHAPE  # 32-bit row offsets
     # empty work is a no-op success, even with NULL tensors
     assert prefill(L, d=dims(Lq=0), q=None, k=None, v=None, out=None) == OK
     assert prefill(L, d=dims(B=0), q=None, k=None, v=None, out=None) == OK
@@ -108,6 +114,13 @@ def test_decode_argument_errors(L):
     assert L.sinkattn_decode(0, 0, ctypes.byref(dims()), A, None, A, 1, None, A, A, 0, None) == E_NULL
     # batch 0 is a no-op
     assert decode(L, d=dims(B=0, hq=64, hkv=4), q=None, out=None) == OK
+
+
+def test_prefill_workspace_size(L):
+    # a transposed copy of V, rows padded to 64 keys
+    assert sa.sinkattn_prefill_workspace_bytes(1, 32768, 64, 8) == 8 * 128 * 32768 * 2
+    assert sa.sinkattn_prefill_workspace_bytes(2, 65, 4, 1) == 2 * 128 * 128 * 2
+    assert sa.sinkattn_prefill_workspace_bytes(1, 0, 4, 1) == 0
 
 
 def test_decode_workspace_plan(L):
