@@ -109,15 +109,12 @@ __device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const char *kbyte
     for (int i = 0; i < 4; ++i) dma_vt_block(Vt, vtbytes, lpad, kb, wave + 4 * i, lane);
 }
 
-// One 32-key sub-block for one wave: S^T = K Q^T, online softmax with the sink-initialised
-// state, O^T += V^T P^T.  kMask: the sub-block touches a row's causal or window edge (or the
-// sequence end), so scores are masked.
-template <int HPW, bool kMask>
-__device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int kb, int sb,
-                                            const bf16x8 (&qf)[HPW][12], f32x16 (&acc)[HPW][4], float (&m_run)[HPW],
-                                            float (&l_run)[HPW], const WaveCtx &w) {
-    // ---- scores
-    f32x16 s[HPW];
+// ---- the four steps of a 32-key sub-block (keys kb + 32sb .. +31) for one wave
+
+// S^T = K Q^T for each of the wave's heads.
+template <int HPW>
+__device__ __forceinline__ void qk_scores(const char *Kt, int sb, const bf16x8 (&qf)[HPW][12], f32x16 (&s)[HPW],
+                                          const WaveCtx &w) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) s[h] = f32x16{};
 #pragma unroll
@@ -126,18 +123,26 @@ __device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int 
 #pragma unroll
         for (int h = 0; h < HPW; ++h) s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[h][kk], s[h], 0, 0, 0);
     }
-    // ---- masks (key row 8*(r/4) + 4g + r%4 of the sub-block, query column qi)
-    if (kMask) {
+}
+
+// Scores of keys outside row qi's visible range (or past the sequence end) become -inf.
+// Lane register r holds key row 8*(r/4) + 4g + r%4 of the sub-block.
+template <int HPW>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[HPW], int kb, int sb, const WaveCtx &w) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kj = kb + 32 * sb + 8 * (r >> 2) + 4 * w.g + (r & 3);
-            const bool ok = kj <= w.qi && kj < w.L && (!w.swa || kj > w.qi - w.window);
+    for (int r = 0; r < 16; ++r) {
+        const int kj = kb + 32 * sb + 8 * (r >> 2) + 4 * w.g + (r & 3);
+        const bool ok = kj <= w.qi && kj < w.L && (!w.swa || kj > w.qi - w.window);
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
-        }
+        for (int h = 0; h < HPW; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
     }
-    // ---- running max on raw scores, lazy rescale
-    float mnew[HPW];
+}
+
+// New running max from raw scores (the scale is positive); true when some row's max grew
+// by more than 2^kLazyRescale (branch-free).
+template <int HPW>
+__device__ __forceinline__ bool row_max(const f32x16 (&s)[HPW], const float (&m_run)[HPW], float (&mnew)[HPW],
+                                        const WaveCtx &w) {
     bool grow = false;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
@@ -148,6 +153,19 @@ __device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int 
         mnew[h] = fmaxf(m_run[h], mx);
         grow |= mnew[h] > m_run[h] + kLazyRescale;
     }
+    return grow;
+}
+
+// Lazy rescale: when some row of the wave grew past the threshold, every row moves its
+// reference to its new max and rescales its accumulator and denominator.
+template <int HPW>
+__device__ __forceinline__ void rescale(bool grow, const float (&mnew)[HPW], f32x16 (&acc)[HPW][4],
+                                        float (&m_run)[HPW], float (&l_run)[HPW]) {
+    // keep the accumulators in AGPRs on the common path (the rare rescale moves them)
+#pragma unroll
+    for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) asm volatile("" : "+a"(acc[h][db]));
     if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
@@ -160,8 +178,21 @@ __device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int 
             m_run[h] = mnew[h];
         }
     }
-    // ---- probabilities and O^T += V^T P^T
-    bf16x8 pf[HPW][2];
+}
+
+// Running max and lazy rescale together (general kernel).
+template <int HPW>
+__device__ __forceinline__ void row_update(const f32x16 (&s)[HPW], f32x16 (&acc)[HPW][4], float (&m_run)[HPW],
+                                           float (&l_run)[HPW], const WaveCtx &w) {
+    float mnew[HPW];
+    const bool grow = row_max<HPW>(s, m_run, mnew, w);
+    rescale<HPW>(grow, mnew, acc, m_run, l_run);
+}
+
+// P = 2^(c*s - m) rounded to bf16 in the B-operand layout of the PV product; l += sum(P).
+template <int HPW>
+__device__ __forceinline__ void probs(const f32x16 (&s)[HPW], const float (&m_run)[HPW], float (&l_run)[HPW],
+                                      bf16x8 (&pf)[HPW][2], const WaveCtx &w) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
         const float neg = (m_run[h] == -INFINITY) ? 0.f : -m_run[h];
@@ -177,7 +208,15 @@ __device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int 
         l_run[h] += ps;
         pf[h][0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
         pf[h][1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+        // computed here, not sunk past a following branch towards their use
+        asm volatile("" : "+v"(pf[h][0]), "+v"(pf[h][1]), "+v"(l_run[h]));
     }
+}
+
+// O^T += V^T P^T.
+template <int HPW>
+__device__ __forceinline__ void pv_accum(const char *Vt, int sb, const bf16x8 (&pf)[HPW][2], f32x16 (&acc)[HPW][4],
+                                         const WaveCtx &w) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -190,8 +229,8 @@ __device__ __forceinline__ void compute_sub(const char *Kt, const char *Vt, int 
     }
 }
 
-// One 64-key tile for one wave, as two 32-key sub-blocks.  Sub-blocks wholly outside this
-// wave's rows are skipped; sub-blocks wholly inside take the unmasked path.
+// One 64-key tile for one wave, sub-block by sub-block.  Sub-blocks wholly outside this
+// wave's rows are skipped; sub-blocks wholly inside are not masked.
 template <int HPW>
 __device__ __forceinline__ void compute_tile(const char *Kt, const char *Vt, int kb, const bf16x8 (&qf)[HPW][12],
                                              f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
@@ -202,13 +241,121 @@ __device__ __forceinline__ void compute_tile(const char *Kt, const char *Vt, int
         const bool dead = k0 > w.qpos0 + kBQ - 1 || k0 >= w.L || (w.swa && k0 + 31 < w.qpos0 - w.window + 1);
         if (dead) continue;
         const bool full = k0 + 31 <= w.qpos0 && k0 + 32 <= w.L && (!w.swa || k0 >= w.qpos0 + kBQ - w.window);
-        if (full)
-            compute_sub<HPW, false>(Kt, Vt, kb, sb, qf, acc, m_run, l_run, w);
-        else
-            compute_sub<HPW, true>(Kt, Vt, kb, sb, qf, acc, m_run, l_run, w);
+        f32x16 s[HPW];
+        qk_scores<HPW>(Kt, sb, qf, s, w);
+        if (!full) mask_scores<HPW>(s, kb, sb, w);
+        row_update<HPW>(s, acc, m_run, l_run, w);
+        bf16x8 pf[HPW][2];
+        probs<HPW>(s, m_run, l_run, pf, w);
+        pv_accum<HPW>(Vt, sb, pf, acc, w);
     }
 }
 
+// ---- per-wave setup shared by the kernels
+
+struct WaveSetup {
+    int b, kvh, h0, qpos0, wg_q0, wg_q1;
+    bool valid;
+};
+
+// Workgroup -> (position group, batch, kv head, head group).  The mapping is XCD-aware: the
+// hgroups workgroups that share one KV head and position group get ids that the hardware
+// dispatches to the same XCD one after another; position groups run heaviest first.
+template <int HPW>
+__device__ __forceinline__ WaveSetup wave_setup(const PrefillParams &p, int wave) {
+    WaveSetup ws;
+    const int C = p.hgroups;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int lam = (((slot / C) * 8 + xcd) * C) + slot % C;
+    ws.valid = lam < p.n_items;
+    int t = lam;
+    const int hg = t % C;
+    t /= C;
+    ws.kvh = t % p.Hkv;
+    t /= p.Hkv;
+    ws.b = t % p.B;
+    t /= p.B;
+    const int pbw = p.n_pbw - 1 - t;
+    const int wh = p.hw / HPW;  // waves along heads
+    ws.h0 = ws.kvh * p.G + hg * p.hw + (wave % wh) * HPW;
+    ws.qpos0 = (pbw * p.pw + wave / wh) * kBQ;
+    ws.wg_q0 = pbw * p.pw * kBQ;
+    ws.wg_q1 = min(p.L, ws.wg_q0 + p.pw * kBQ);
+    return ws;
+}
+
+// Q^T fragments (B operand): lane supplies q[h][qi][16kk + 8g .. +8]; rows past L are 0.
+template <int HPW>
+__device__ __forceinline__ void load_q(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
+                                       bf16x8 (&qf)[HPW][12]) {
+    const bool ok = w.qi < p.L;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const uint16_t *qrow = p.q + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.L) + (ok ? w.qi : 0)) * kDqk + 8 * w.g;
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0});
+    }
+}
+
+// The sink starts each row's running max and denominator: m = sink, l = exp(0) = 1 (counted
+// on one lane of the pair that shares the row).  No sink: m = -inf, l = 0.
+template <int HPW>
+__device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
+                                           f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
+                                           bool (&sink_inf)[HPW]) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const float sk = p.sink ? p.sink[ws.h0 + h] : -INFINITY;
+        const bool has_sink = sk != -INFINITY;
+        sink_inf[h] = sk == INFINITY;
+        m_run[h] = has_sink ? sk * kLog2e : -INFINITY;
+        l_run[h] = (has_sink && w.g == 0) ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[h][db] = f32x16{};
+    }
+}
+
+// O = acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi.
+template <int HPW>
+__device__ __forceinline__ void store_out(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w, bool live,
+                                          const f32x16 (&acc)[HPW][4], const float (&l_run)[HPW],
+                                          const bool (&sink_inf)[HPW]) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const float lt = sum_xor32(l_run[h]);
+        if (!live || w.qi >= p.L) continue;
+        const float inv = 1.f / lt;
+        uint16_t *orow = p.out + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.L) + w.qi) * kDv + 4 * w.g;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o0 = acc[h][db][4 * i] * inv, o1 = acc[h][db][4 * i + 1] * inv;
+                float o2 = acc[h][db][4 * i + 2] * inv, o3 = acc[h][db][4 * i + 3] * inv;
+                if (sink_inf[h]) o0 = o1 = o2 = o3 = 0.f;
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * i) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ WaveCtx make_ctx(const PrefillParams &p, const WaveSetup &ws, int lane) {
+    WaveCtx w;
+    w.L = p.L;
+    w.swa = p.swa;
+    w.window = p.window;
+    w.c = p.scale_log2;
+    w.qpos0 = ws.qpos0;
+    w.lane = lane;
+    w.g = lane >> 5;
+    w.lq = lane & 31;
+    w.qi = ws.qpos0 + w.lq;
+    return w;
+}
+
+// ---- general kernel (sliding window, odd group sizes): double-buffered tiles, each
+// sub-block computed start to finish.
 template <int HPW>
 __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) {
     __shared__ __attribute__((aligned(1024))) char KA[kKTileBytes];
@@ -216,75 +363,25 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
     __shared__ __attribute__((aligned(1024))) char VA[kVTileBytes];
     __shared__ __attribute__((aligned(1024))) char VB[kVTileBytes];
 
-    // ---- workgroup -> (position group, batch, kv head, head group), XCD-aware
-    const int C = p.hgroups;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int lam = (((slot / C) * 8 + xcd) * C) + slot % C;
-    if (lam >= p.n_items) return;  // padding workgroup (uniform: before any barrier)
-    int t = lam;
-    const int hg = t % C;
-    t /= C;
-    const int kvh = t % p.Hkv;
-    t /= p.Hkv;
-    const int b = t % p.B;
-    t /= p.B;
-    const int pbw = p.n_pbw - 1 - t;  // heaviest (latest) positions first
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+    const WaveSetup ws = wave_setup<HPW>(p, wave);
+    if (!ws.valid) return;  // padding workgroup (uniform: before any barrier)
+    const WaveCtx w = make_ctx(p, ws, lane);
+    const bool wave_live = ws.qpos0 < p.L;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wh = p.hw / HPW;  // waves along heads
-    const int h0 = kvh * p.G + hg * p.hw + (wave % wh) * HPW;
-    const int qpos0 = (pbw * p.pw + wave / wh) * kBQ;
-    const int wg_q0 = pbw * p.pw * kBQ;
-    const int wg_q1 = min(p.L, wg_q0 + p.pw * kBQ);
-
-    WaveCtx w;
-    w.L = p.L;
-    w.swa = p.swa;
-    w.window = p.window;
-    w.c = p.scale_log2;
-    w.qpos0 = qpos0;
-    w.lane = lane;
-    w.g = lane >> 5;
-    w.lq = lane & 31;
-    w.qi = qpos0 + w.lq;
-    const bool wave_live = qpos0 < p.L;
-
-    // ---- Q^T fragments (B operand): lane supplies q[h][qi][16kk + 8g .. +8]
     bf16x8 qf[HPW][12];
-    {
-        const bool ok = w.qi < p.L;
-#pragma unroll
-        for (int h = 0; h < HPW; ++h) {
-            const uint16_t *qrow = p.q + ((((size_t)b * p.Hq + h0 + h) * p.L) + (ok ? w.qi : 0)) * kDqk + 8 * w.g;
-#pragma unroll
-            for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0});
-        }
-    }
-
-    // ---- running state: the sink starts the max and the denominator
+    load_q<HPW>(p, ws, w, qf);
     float m_run[HPW], l_run[HPW];
     bool sink_inf[HPW];
     f32x16 acc[HPW][4];
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-        const float sk = p.sink ? p.sink[h0 + h] : -INFINITY;
-        const bool has_sink = sk != -INFINITY;
-        sink_inf[h] = sk == INFINITY;
-        m_run[h] = has_sink ? sk * kLog2e : -INFINITY;
-        l_run[h] = (has_sink && w.g == 0) ? 1.f : 0.f;  // exp2(sink - m) = 1, counted on one lane of the pair
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[h][db] = f32x16{};
-    }
+    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
 
-    const size_t kvbase = ((size_t)b * p.Hkv + kvh) * p.L;
-    const char *kbytes = reinterpret_cast<const char *>(p.k + kvbase * kDqk);
-    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)b * p.Hkv + kvh) * kDv * p.lpad);
+    const char *kbytes = reinterpret_cast<const char *>(p.k + ((size_t)ws.b * p.Hkv + ws.kvh) * p.L * kDqk);
+    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)ws.b * p.Hkv + ws.kvh) * kDv * p.lpad);
+    const int k_lo = p.swa ? max(0, ws.wg_q0 - p.window + 1) : 0;
+    const int t0 = k_lo / kBN, t1 = (ws.wg_q1 - 1) / kBN;
 
-    const int k_lo = p.swa ? max(0, wg_q0 - p.window + 1) : 0;
-    const int t0 = k_lo / kBN, t1 = (wg_q1 - 1) / kBN;
-
-    // prologue: tile t0 into buffers A
     issue_tile(KA, VA, kbytes, vtbytes, p.lpad, t0 * kBN, p.L, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -301,25 +398,123 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
         step(kt, KA, VA, KB, VB);
         if (kt + 1 <= t1) step(kt + 1, KB, VB, KA, VA);
     }
+    store_out<HPW>(p, ws, w, wave_live, acc, l_run, sink_inf);
+}
 
-    // ---- epilogue: O = acc / l; lane holds dv 32db + 8i + 4g + j of query qi
+// ---- causal kernel: two heads per wave, all four waves at the same 32 positions, and a
+// software pipeline over 32-key sub-blocks so that the softmax arithmetic of one sub-block
+// runs on the vector units while the matrix cores work on another:
+//
+//   phase A: S(t,1) = K(t)Q^T              with  P(t,0) = exp(S(t,0))
+//   phase B: O += V(t)^T P(t,0)            with  max of S(t,1), then the rare rescale
+//   barrier; tiles t+2 start streaming in
+//   phase C: S(t+1,0) = K(t+1)Q^T          with  P(t,1) = exp(S(t,1))
+//   phase D: O += V(t)^T P(t,1)            with  max of S(t+1,0), then the rare rescale
+//
+// K runs one tile ahead of V, so both are triple buffered (120 KB of LDS); loads issued
+// after the barrier of tile t land by the barrier of tile t+1.  The loop is unrolled by 3
+// so that every buffer is a distinct LDS object and the compiler can tell the loads in
+// flight from the reads.  Every rescale happens after the PV product that used the old
+// reference max, so the accumulator and the denominator always share one reference.
+__global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p) {
+    constexpr int HPW = 2;
+    __shared__ __attribute__((aligned(1024))) char K0[kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char K1[kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char K2[kKTileBytes];
+    __shared__ __attribute__((aligned(1024))) char V0[kVTileBytes];
+    __shared__ __attribute__((aligned(1024))) char V1[kVTileBytes];
+    __shared__ __attribute__((aligned(1024))) char V2[kVTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+    const WaveSetup ws = wave_setup<HPW>(p, wave);
+    if (!ws.valid) return;  // padding workgroup (uniform: before any barrier)
+    const WaveCtx w = make_ctx(p, ws, lane);
+
+    bf16x8 qf[HPW][12];
+    load_q<HPW>(p, ws, w, qf);
+    float m_run[HPW], l_run[HPW];
+    bool sink_inf[HPW];
+    f32x16 acc[HPW][4];
+    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
+
+    const char *kbytes = reinterpret_cast<const char *>(p.k + ((size_t)ws.b * p.Hkv + ws.kvh) * p.L * kDqk);
+    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)ws.b * p.Hkv + ws.kvh) * kDv * p.lpad);
+    const int t1 = (ws.wg_q1 - 1) / kBN;  // tiles 0..t1
+
+    // a sub-block needs masking when its last key lies past the first query row
+    auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
+
+    issue_tile(K0, V0, kbytes, vtbytes, p.lpad, 0, p.L, wave, lane);
+    if (t1 >= 1) issue_tile(K1, V1, kbytes, vtbytes, p.lpad, kBN, p.L, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    f32x16 s0[HPW], s1[HPW];
+    bf16x8 pf[HPW][2];
+    qk_scores<HPW>(K0, 0, qf, s0, w);
+    if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
+    row_update<HPW>(s0, acc, m_run, l_run, w);
+
+    // Interleaving inside a phase: LDS fragment reads run two steps ahead of the pair of
+    // MFMAs that use them, and the vector work of the other sub-block fills the gaps.
+    auto sched_qk_phase = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
 #pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-        const float lt = sum_xor32(l_run[h]);
-        if (!wave_live || w.qi >= p.L) continue;
-        const float inv = 1.f / lt;
-        uint16_t *orow = p.out + ((((size_t)b * p.Hq + h0 + h) * p.L) + w.qi) * kDv + 4 * w.g;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float o0 = acc[h][db][4 * i] * inv, o1 = acc[h][db][4 * i + 1] * inv;
-                float o2 = acc[h][db][4 * i + 2] * inv, o3 = acc[h][db][4 * i + 3] * inv;
-                if (sink_inf[h]) o0 = o1 = o2 = o3 = 0.f;
-                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * i) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-            }
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
         }
+    };
+    auto sched_pv_phase = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+        }
+    };
+
+    // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).
+    auto step = [&](int t, const char *Kc, const char *Kn, const char *Vc, char *Kf, char *Vf) {
+        const int kb = t * kBN;
+        float mnew[HPW];
+        bool grow;
+        // phase A: S(t,1) with P(t,0)
+        qk_scores<HPW>(Kc, 1, qf, s1, w);
+        probs<HPW>(s0, m_run, l_run, pf, w);
+        sched_qk_phase();
+        if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
+        // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
+        pv_accum<HPW>(Vc, 0, pf, acc, w);
+        grow = row_max<HPW>(s1, m_run, mnew, w);
+        sched_pv_phase();
+        rescale<HPW>(grow, mnew, acc, m_run, l_run);
+        // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        if (t + 2 <= t1) issue_tile(Kf, Vf, kbytes, vtbytes, p.lpad, kb + 2 * kBN, p.L, wave, lane);
+        // phase C: S(t+1,0) with P(t,1) (the scores of tile t+1 are unused after the last tile)
+        qk_scores<HPW>(Kn, 0, qf, s0, w);
+        probs<HPW>(s1, m_run, l_run, pf, w);
+        sched_qk_phase();
+        if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
+        // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0)
+        pv_accum<HPW>(Vc, 1, pf, acc, w);
+        grow = row_max<HPW>(s0, m_run, mnew, w);
+        sched_pv_phase();
+        if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
+    };
+    for (int t = 0; t <= t1; t += 3) {
+        step(t, K0, K1, V0, K2, V2);
+        if (t + 1 <= t1) step(t + 1, K1, K2, V1, K0, V0);
+        if (t + 2 <= t1) step(t + 2, K2, K0, V2, K1, V1);
     }
+    store_out<HPW>(p, ws, w, true, acc, l_run, sink_inf);
 }
 
 // V -> V^T with the keys of every 64-key tile in MFMA k-order (chunk 2*gam + g holds the
@@ -373,8 +568,11 @@ int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     }
     const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     void *args[] = {&p};
-    const void *fn = p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
-                                : reinterpret_cast<const void *>(&prefill_kernel<1>);
+    // the causal pipeline needs two heads per wave and all four waves on the same positions
+    const bool pipe = !p.swa && p.hpw == 2 && p.hw == 8;
+    const void *fn = pipe ? reinterpret_cast<const void *>(&prefill_causal_kernel)
+                          : p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
+                                       : reinterpret_cast<const void *>(&prefill_kernel<1>);
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) == hipSuccess ? 0 : -1;
 }
 

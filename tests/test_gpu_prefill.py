@@ -60,6 +60,17 @@ CASES = [
     (1, 64, 4, 130, oracle.GLOBAL, 0, True),
     (1, 32, 1, 64, oracle.SWA, 64, True),
     (1, 3, 1, 70, oracle.SWA, 33, True),
+    # global mode with 8 or 16 query heads per KV head (the pipelined causal kernel):
+    # 1, 2, 3 and 4+ key tiles, ragged ends, batches, with and without a sink
+    (2, 16, 2, 1, oracle.GLOBAL, 0, True),
+    (1, 16, 1, 33, oracle.GLOBAL, 0, False),
+    (1, 8, 1, 64, oracle.GLOBAL, 0, True),
+    (1, 8, 1, 65, oracle.GLOBAL, 0, True),
+    (1, 32, 2, 129, oracle.GLOBAL, 0, True),
+    (1, 16, 2, 191, oracle.GLOBAL, 0, True),
+    (1, 16, 2, 192, oracle.GLOBAL, 0, False),
+    (1, 16, 2, 193, oracle.GLOBAL, 0, True),
+    (2, 8, 1, 517, oracle.GLOBAL, 0, True),
 ]
 
 
@@ -87,6 +98,23 @@ def test_sink_extremes():
     a = run_prefill(oracle.SWA, 16, d2)
     b = run_prefill(oracle.SWA, 16, d2, sink=False)
     assert np.array_equal(a, b)
+
+
+def test_growing_max_rescales():
+    """Logits that keep growing along the sequence force the lazy rescale many times.  The
+    attention becomes nearly one-hot, so outputs approach single value rows; V is scaled by
+    1/4 to keep them inside the range where the absolute bound is not dominated by the bf16
+    rounding of the output itself (half an ulp is 0.016 for values in [4, 8))."""
+    B, Hq, Hkv, L = 1, 16, 2, 700
+    d = small_inputs(B, Hq, Hkv, L, seed=12)
+    k = inputs.bf16_to_f32(d["k"])
+    k *= (1.0 + np.arange(L, dtype=np.float32) / 40.0)[None, None, :, None]  # key norms grow ~18x
+    d["k"] = inputs.bf16_bits(k)
+    d["v"] = inputs.bf16_bits(inputs.bf16_to_f32(d["v"]) * 0.25)
+    for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 128)):
+        got = run_prefill(mode, W, d)
+        ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], mode, W, 192 ** -0.5)
+        assert_parity(got, ref, f"growing logits mode={mode}")
 
 
 def test_wide_window_equals_global_bitwise():
