@@ -8,7 +8,7 @@ namespace sinkattn {
 
 struct PrefillParams {
     const uint16_t *q, *k, *v;
-    uint16_t *vt;      // workspace: V^T [B][Hkv][kDv][lpad], keys of each 64-key tile in MFMA k-order
+    uint16_t *vt;      // workspace: V^T [B][Hkv][lpad/64][kDv][64], keys in MFMA k-order
     int lpad;          // L rounded up to a multiple of 64
     const float *sink;  // [Hq] or nullptr
     uint16_t *out;

@@ -21,8 +21,8 @@
 //     row statistics need only one exchange with the partner lane (lane ^ 32), and the
 //     probabilities P^T are already in the B-operand layout of the second product
 //     O^T = V^T P^T.
-//   * A first, HBM-bound kernel writes V^T into the caller's workspace with the keys of
-//     every 16-key group in MFMA k-order, so the A operand of V^T P^T is one 16-byte LDS
+//   * A first, HBM-bound kernel writes V^T into the caller's workspace, tile by tile
+//     (contiguous 16 KB blocks), with the keys of every 16-key group in MFMA k-order, so the A operand of V^T P^T is one 16-byte LDS
 //     read per lane.  K and V^T tiles then travel HBM -> LDS with 16-byte direct-to-LDS
 //     loads (no registers, no transposing in the hot loop) into blocks of 16 rows x 4
 //     chunks stored chunk-major: every 16-lane group of an MFMA operand read is one
@@ -91,22 +91,23 @@ __device__ __forceinline__ void dma_k_block(char *Kt, const char *kbytes, int kb
     __builtin_amdgcn_global_load_lds(kbytes + (uint32_t)(row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16),
                                      (lds_void *)(Kt + blk * 1024), 16, 0, 0);
 }
-// V^T tile (keys kb..kb+63 of every dv row of the transposed copy, whose rows are padded to
-// a whole number of tiles) -> LDS: block blk (0..15) = (rg, kg); lane l fetches dv row
-// 16rg + (l & 15), key chunk 4kg + (l >> 4).
-__device__ __forceinline__ void dma_vt_block(char *Vt, const char *vtbytes, int lpad, int kb, int blk, int lane) {
+// V^T tile (keys kb..kb+63) -> LDS.  The transposed copy is stored tile by tile, each tile a
+// contiguous 16 KB block [128 dv][64 keys], so a tile load touches one small address range.
+// Block blk (0..15) = (rg, kg); lane l fetches dv row 16rg + (l & 15), key chunk
+// 4kg + (l >> 4).
+__device__ __forceinline__ void dma_vt_block(char *Vt, const char *vtbytes, int kb, int blk, int lane) {
     const int rg = blk >> 1, kg = blk & 1;
     const int row = 16 * rg + (lane & 15);
-    __builtin_amdgcn_global_load_lds(vtbytes + (uint32_t)(row * lpad * 2 + (kb + 8 * (4 * kg + (lane >> 4))) * 2),
+    __builtin_amdgcn_global_load_lds(vtbytes + (uint32_t)(kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16),
                                      (lds_void *)(Vt + blk * 1024), 16, 0, 0);
 }
 // Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile (10 per wave).
-__device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const char *kbytes, const char *vtbytes, int lpad,
-                                           int kb, int L, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const char *kbytes, const char *vtbytes, int kb, int L,
+                                           int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 6; ++i) dma_k_block(Kt, kbytes, kb, L, wave + 4 * i, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_vt_block(Vt, vtbytes, lpad, kb, wave + 4 * i, lane);
+    for (int i = 0; i < 4; ++i) dma_vt_block(Vt, vtbytes, kb, wave + 4 * i, lane);
 }
 
 // ---- the four steps of a 32-key sub-block (keys kb + 32sb .. +31) for one wave
@@ -382,14 +383,14 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
     const int k_lo = p.swa ? max(0, ws.wg_q0 - p.window + 1) : 0;
     const int t0 = k_lo / kBN, t1 = (ws.wg_q1 - 1) / kBN;
 
-    issue_tile(KA, VA, kbytes, vtbytes, p.lpad, t0 * kBN, p.L, wave, lane);
+    issue_tile(KA, VA, kbytes, vtbytes, t0 * kBN, p.L, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     // Tile kt from (Kc, Vc) while tile kt+1 streams into (Kn, Vn).
     auto step = [&](int kt, const char *Kc, const char *Vc, char *Kn, char *Vn) {
         const bool more = kt < t1;
-        if (more) issue_tile(Kn, Vn, kbytes, vtbytes, p.lpad, (kt + 1) * kBN, p.L, wave, lane);
+        if (more) issue_tile(Kn, Vn, kbytes, vtbytes, (kt + 1) * kBN, p.L, wave, lane);
         if (wave_live) compute_tile<HPW>(Kc, Vc, kt * kBN, qf, acc, m_run, l_run, w);
         if (more) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 has landed
         __syncthreads();
@@ -445,8 +446,8 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
     // a sub-block needs masking when its last key lies past the first query row
     auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
 
-    issue_tile(K0, V0, kbytes, vtbytes, p.lpad, 0, p.L, wave, lane);
-    if (t1 >= 1) issue_tile(K1, V1, kbytes, vtbytes, p.lpad, kBN, p.L, wave, lane);
+    issue_tile(K0, V0, kbytes, vtbytes, 0, p.L, wave, lane);
+    if (t1 >= 1) issue_tile(K1, V1, kbytes, vtbytes, kBN, p.L, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
@@ -457,56 +458,67 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
     row_update<HPW>(s0, acc, m_run, l_run, w);
 
     // Interleaving inside a phase: LDS fragment reads run two steps ahead of the pair of
-    // MFMAs that use them, and the vector work of the other sub-block fills the gaps.
-    auto sched_qk_phase = [] {
+    // MFMAs that use them, the vector work of the other sub-block fills the gaps, and the
+    // loads of tile t+2 (6 K and 4 V^T direct-to-LDS loads per wave) are spread over phases
+    // C and D instead of queueing at the address unit all at once.
+    auto sched_qk_phase = [](bool dma) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
 #pragma unroll
         for (int i = 0; i < 12; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            if (dma && (i & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 load
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
         }
     };
-    auto sched_pv_phase = [] {
+    auto sched_pv_phase = [](bool dma) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            if (dma && (i & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 load
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
         }
     };
 
-    // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).
+    // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).  The loads of
+    // tile t+2 are issued unconditionally (past the last tile they re-read tile t1 into a
+    // buffer nobody reads any more), so that no branch splits phases C and D.
     auto step = [&](int t, const char *Kc, const char *Kn, const char *Vc, char *Kf, char *Vf) {
         const int kb = t * kBN;
+        const int kb_next = min(t + 2, t1) * kBN;
         float mnew[HPW];
         bool grow;
         // phase A: S(t,1) with P(t,0)
         qk_scores<HPW>(Kc, 1, qf, s1, w);
         probs<HPW>(s0, m_run, l_run, pf, w);
-        sched_qk_phase();
+        sched_qk_phase(false);
         if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
         // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
         pv_accum<HPW>(Vc, 0, pf, acc, w);
         grow = row_max<HPW>(s1, m_run, mnew, w);
-        sched_pv_phase();
+        sched_pv_phase(false);
         rescale<HPW>(grow, mnew, acc, m_run, l_run);
         // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        if (t + 2 <= t1) issue_tile(Kf, Vf, kbytes, vtbytes, p.lpad, kb + 2 * kBN, p.L, wave, lane);
-        // phase C: S(t+1,0) with P(t,1) (the scores of tile t+1 are unused after the last tile)
+        // phase C: S(t+1,0) with P(t,1) and the K loads of tile t+2 (the scores of tile t+1
+        // are unused after the last tile)
         qk_scores<HPW>(Kn, 0, qf, s0, w);
         probs<HPW>(s1, m_run, l_run, pf, w);
-        sched_qk_phase();
+#pragma unroll
+        for (int i = 0; i < 6; ++i) dma_k_block(Kf, kbytes, kb_next, p.L, wave + 4 * i, lane);
+        sched_qk_phase(true);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
-        // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0)
+        // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
         pv_accum<HPW>(Vc, 1, pf, acc, w);
         grow = row_max<HPW>(s0, m_run, mnew, w);
-        sched_pv_phase();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_vt_block(Vf, vtbytes, kb_next, wave + 4 * i, lane);
+        sched_pv_phase(true);
         if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
     };
     for (int t = 0; t <= t1; t += 3) {
@@ -514,12 +526,13 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
         if (t + 1 <= t1) step(t + 1, K1, K2, V1, K0, V0);
         if (t + 2 <= t1) step(t + 2, K2, K0, V2, K1, V1);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
     store_out<HPW>(p, ws, w, true, acc, l_run, sink_inf);
 }
 
-// V -> V^T with the keys of every 64-key tile in MFMA k-order (chunk 2*gam + g holds the
-// keys vkey(gam, g, 0..7)); rows padded with zeros to lpad keys.  One workgroup per
-// (batch x kv head, 64-key tile).
+// V -> V^T tile by tile: tile t of (batch, kv head) is a contiguous [128 dv][64 keys] block
+// with the keys of every 16-key group in MFMA k-order (chunk 2*gam + g holds the keys
+// vkey(gam, g, 0..7)); keys past L are zero.  One workgroup per (batch x kv head, tile).
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uint16_t *vt, int L, int lpad) {
     __shared__ uint16_t tile[kBN][kDv + 8];
     const int kb = blockIdx.x * kBN;
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uin
         *reinterpret_cast<u32x2 *>(&tile[key][8 * c + 4]) = u32x2{val.z, val.w};
     }
     __syncthreads();
-    uint16_t *dst = vt + bh * kDv * (size_t)lpad;
+    uint16_t *dst = vt + (bh * (size_t)lpad + kb) * kDv;  // this tile's block
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int idx = tid + 256 * e;
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uin
             const uint32_t hi = tile[vkey(kc >> 1, kc & 1, 2 * i + 1)][row];
             wv[i] = lo | (hi << 16);
         }
-        *reinterpret_cast<u32x4 *>(dst + (size_t)row * lpad + kb + 8 * kc) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        *reinterpret_cast<u32x4 *>(dst + row * kBN + 8 * kc) = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
 }
 
