@@ -33,6 +33,36 @@ MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "prefill attn TFLOP/s (SWA & GA+sink, 32K) + decode KV-read HBM GB/s at 256K"
 FLOP_PER_PAIR = 2 * (192 + 128)
+CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
+
+# HBM bytes per call read by rocprofv3 FETCH_SIZE and WRITE_SIZE (one pass each), scaled by
+# the same counters on a plain 1 GiB device copy (read x 2.0, written x 1.0).  Each entry
+# holds the hash of the kernel sources it was measured on; once they change the figure is
+# stale and `traffic` is reported as null until the counters are taken again.
+TRAFFIC = {
+    "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
+                          "sha256": "5ee3e6ed512b6f6adee29fdf834875499f9654b667039c041d323848f1db109b",
+                          "read_GB": 3.6043, "written_GB": 0.5705},
+    "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
+                                "sha256": "f812e0c037755bfcb19939bb48969eb30944e312e73ec77bee1ea76a937aac2f",
+                                "read_GB": 5.3880, "written_GB": 0.0179},
+}
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_gb(workload):
+    t = TRAFFIC.get(workload)
+    if not t or not t["sha256"] or sources_sha256(t["sources"]) != t["sha256"]:
+        return None
+    return round(t["read_GB"] + t["written_GB"], 4)
 
 
 def pairs_prefill(L, mode, W):
@@ -49,6 +79,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of workloads to run (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -62,6 +94,8 @@ def main() -> int:
     sa.lib()  # fails loudly when the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        return copy_calibration(torch, dev)
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -175,12 +209,15 @@ def main() -> int:
         c = comp["ga_prefill_L32768"]
         roofline = {"kernel": "prefill_kernel (ga_prefill_L32768)", "bound": "mfma", "achieved": c["tflops"],
                     "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(c["tflops"] / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None}
+                    "frac": round(c["tflops"] / MFMA_PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_gb("ga_prefill_L32768"), "traffic_unit": "GB per call (HBM read + written)"}
     roofline_decode = None
     if dec:
         roofline_decode = {"kernel": "decode_split_kernel+decode_merge_kernel (ga_decode_B8_256K_paged)",
                            "bound": "hbm", "achieved": dec["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+                           "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
+                           "traffic": traffic_gb("ga_decode_B8_256K_paged"),
+                           "traffic_unit": "GB per call (HBM read + written)"}
 
     cpu = None
     if not args.no_cpu_baseline and pre:
@@ -201,6 +238,25 @@ def main() -> int:
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of `nbytes`: it reads and writes exactly `nbytes` each,
+    so hardware byte counters read on it give the scale factor for the counters read on the
+    attention kernels."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
     return 0
 
 
