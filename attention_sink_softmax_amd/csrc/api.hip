@@ -110,17 +110,7 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
     p.swa = mode == SINKATTN_SWA;
     p.window = p.swa ? window : 0;
     p.scale_log2 = (float)((double)d->scale * kLog2eD);
-    p.hpw = (p.G % 2 == 0) ? 2 : 1;
-    p.hw = p.hpw;
-    while (p.hw * 2 <= 4 * p.hpw && p.G % (p.hw * 2) == 0) p.hw *= 2;
-    p.pw = 4 * p.hpw / p.hw;
-    const int64_t npb = (p.L + 31) / 32;
-    p.n_pbw = (int)((npb + p.pw - 1) / p.pw);
-    p.hgroups = p.G / p.hw;
-    const int64_t items = (int64_t)p.n_pbw * p.B * p.Hkv * p.hgroups;
-    const int64_t grid = ((items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
-    if (grid > INT32_MAX) return SINKATTN_E_SHAPE;
-    p.n_items = (int)items;
+    if (plan_prefill(p) > INT32_MAX) return SINKATTN_E_SHAPE;
     return launch_prefill(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 

@@ -15,9 +15,10 @@ struct PrefillParams {
     int B, L, Hq, Hkv, G;
     int swa, window;
     float scale_log2;  // logit scale * log2(e)
-    int hpw;           // query heads per wave (2 when G is even, else 1)
-    int hw;            // query heads per workgroup (a multiple of hpw dividing G, at most 4 * hpw)
-    int pw;            // 32-position blocks per workgroup (4 * hpw / hw)
+    // work layout, filled by plan_prefill
+    int hpw;           // query heads per wave
+    int hw;            // query heads per workgroup (a multiple of hpw dividing G)
+    int pw;            // 32-position blocks per workgroup
     int n_pbw;         // position groups per (batch, kv head)
     int hgroups;       // head groups per kv head (G / hw)
     int n_items;       // n_pbw * B * Hkv * hgroups
@@ -37,6 +38,9 @@ struct DecodeParams {
 };
 
 size_t prefill_workspace_bytes(int B, int Hkv, int L);
+// Fills the work layout of p from B, L, Hkv, G and swa; returns the number of workgroups to
+// launch (the caller rejects counts that do not fit a grid).
+int64_t plan_prefill(PrefillParams &p);
 int launch_prefill(const PrefillParams &p, hipStream_t stream);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 

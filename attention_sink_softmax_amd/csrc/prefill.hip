@@ -10,11 +10,13 @@
 // chunk), causal rows only the tiles at or below the diagonal.
 //
 // Layout of the work (gfx950, wave64):
-//   * A workgroup is 4 waves.  Each wave owns HPW query heads (2 when the GQA group size
-//     allows it) and 32 consecutive query positions; all waves of a workgroup share one KV
-//     head, so one key/value tile staged in LDS feeds all of them.  With two heads per wave
-//     every K and V fragment read from LDS feeds two MFMAs, which halves LDS read traffic
-//     per flop (LDS bandwidth, ~128 B/clk/CU, would otherwise cap the matrix cores).
+//   * Causal attention over a group of 8 or 16 query heads per KV head (the global layers):
+//     a workgroup of 8 waves, one query head each, all at the same 32 query positions, so
+//     one K / V^T tile staged in LDS feeds all eight; two waves share each SIMD and hide
+//     each other's LDS waits.
+//   * Everything else (sliding window, other group sizes): a workgroup of 4 waves, each
+//     owning HPW query heads (2 when the group size is even) and 32 positions; with two
+//     heads per wave every K and V fragment read from LDS feeds two MFMAs.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K comes
 //     from LDS as the A operand, Q^T stays in registers as the B operand for the whole
 //     kernel.  In the output layout a lane holds one query column and 16 key rows, so the
@@ -22,13 +24,14 @@
 //     probabilities P^T are already in the B-operand layout of the second product
 //     O^T = V^T P^T.
 //   * A first, HBM-bound kernel writes V^T into the caller's workspace, tile by tile
-//     (contiguous 16 KB blocks), with the keys of every 16-key group in MFMA k-order, so the A operand of V^T P^T is one 16-byte LDS
-//     read per lane.  K and V^T tiles then travel HBM -> LDS with 16-byte direct-to-LDS
-//     loads (no registers, no transposing in the hot loop) into blocks of 16 rows x 4
-//     chunks stored chunk-major: every 16-lane group of an MFMA operand read is one
-//     contiguous 256-byte run (no bank conflicts) and a lane's operand addresses differ
-//     only by compile-time offsets.  Tiles are double buffered in two distinct LDS objects,
-//     so the loads of tile t+1 overlap the math of tile t.
+//     (contiguous 16 KB blocks), with the keys of every 16-key group in MFMA k-order, so
+//     the A operand of V^T P^T is one 16-byte LDS read per lane.  K and V^T tiles then
+//     travel HBM -> LDS with 16-byte direct-to-LDS loads (no registers, no transposing in
+//     the hot loop) into blocks of 16 rows x 4 chunks stored chunk-major: every 16-lane
+//     group of an MFMA operand read is one contiguous 256-byte run (no bank conflicts) and
+//     a lane's operand addresses differ only by compile-time offsets.  Tiles are double
+//     (general kernel) or triple (causal kernel) buffered in distinct LDS objects, so the
+//     loads of the next tiles overlap the math of the current one.
 //   * Softmax: the logit scale is folded into one FMA per score (exp2 domain), the
 //     running max is taken on raw scores, and the output accumulator is rescaled only
 //     when a row's max grows by more than 2^8 (the result is exact for any reference
@@ -79,6 +82,7 @@ struct WaveCtx {
     int L, swa, window;
     float c;  // logit scale * log2(e)
     int qpos0, qi, g, lq, lane;
+    int klane, vlane;  // lane parts of the K and V^T operand offsets
 };
 
 // K tile rows kb..kb+63 -> LDS: block blk (0..23) = (rg, cg) is one wave instruction; lane l
@@ -120,7 +124,8 @@ __device__ __forceinline__ void qk_scores(const char *Kt, int sb, const bf16x8 (
     for (int h = 0; h < HPW; ++h) s[h] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Kt + k_off(32 * sb + w.lq, 2 * kk + w.g));
+        // = Kt + k_off(32 sb + lq, 2 kk + g): lane part plus a compile-time offset
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Kt + w.klane + (sb * 12288 + (kk >> 1) * 1024 + (kk & 1) * 512));
 #pragma unroll
         for (int h = 0; h < HPW; ++h) s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[h][kk], s[h], 0, 0, 0);
     }
@@ -222,7 +227,8 @@ __device__ __forceinline__ void pv_accum(const char *Vt, int sb, const bf16x8 (&
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + vt_off(32 * db + w.lq, 4 * sb + 2 * k2 + w.g));
+            // = Vt + vt_off(32 db + lq, 4 sb + 2 k2 + g)
+            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + w.vlane + (db * 4096 + sb * 1024 + k2 * 512));
 #pragma unroll
             for (int h = 0; h < HPW; ++h)
                 acc[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h][k2], acc[h][db], 0, 0, 0);
@@ -352,6 +358,10 @@ __device__ __forceinline__ WaveCtx make_ctx(const PrefillParams &p, const WaveSe
     w.g = lane >> 5;
     w.lq = lane & 31;
     w.qi = ws.qpos0 + w.lq;
+    // k_off and vt_off of the lane's operand reads split into a lane part (here) and a part
+    // known at compile time, which the LDS read instructions take as an immediate offset
+    w.klane = (w.lq >> 4) * 6144 + w.g * 256 + (w.lq & 15) * 16;
+    w.vlane = (w.lq >> 4) * 2048 + w.g * 256 + (w.lq & 15) * 16;
     return w;
 }
 
@@ -402,9 +412,11 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
     store_out<HPW>(p, ws, w, wave_live, acc, l_run, sink_inf);
 }
 
-// ---- causal kernel: two heads per wave, all four waves at the same 32 positions, and a
+// ---- causal kernel: eight waves, one head each, all at the same 32 positions (the eight
+// heads of one KV head's group share every K and V^T tile), two waves per SIMD so that one
+// wave's LDS waits and dependency stalls are filled by the other.  Each wave runs a
 // software pipeline over 32-key sub-blocks so that the softmax arithmetic of one sub-block
-// runs on the vector units while the matrix cores work on another:
+// overlaps the matrix products of another:
 //
 //   phase A: S(t,1) = K(t)Q^T              with  P(t,0) = exp(S(t,0))
 //   phase B: O += V(t)^T P(t,0)            with  max of S(t,1), then the rare rescale
@@ -417,8 +429,20 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 // so that every buffer is a distinct LDS object and the compiler can tell the loads in
 // flight from the reads.  Every rescale happens after the PV product that used the old
 // reference max, so the accumulator and the denominator always share one reference.
-__global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p) {
-    constexpr int HPW = 2;
+constexpr int kCausalWaves = 8;
+
+// Wave w of the causal kernel issues blocks w, w+8, ... of the 24 K and 16 V^T blocks.
+__device__ __forceinline__ void dma_k_part(char *Kt, const char *kbytes, int kb, int L, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma_k_block(Kt, kbytes, kb, L, wave + kCausalWaves * i, lane);
+}
+__device__ __forceinline__ void dma_vt_part(char *Vt, const char *vtbytes, int kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_vt_block(Vt, vtbytes, kb, wave + kCausalWaves * i, lane);
+}
+
+__global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(PrefillParams p) {
+    constexpr int HPW = 1;
     __shared__ __attribute__((aligned(1024))) char K0[kKTileBytes];
     __shared__ __attribute__((aligned(1024))) char K1[kKTileBytes];
     __shared__ __attribute__((aligned(1024))) char K2[kKTileBytes];
@@ -446,8 +470,12 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
     // a sub-block needs masking when its last key lies past the first query row
     auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
 
-    issue_tile(K0, V0, kbytes, vtbytes, 0, p.L, wave, lane);
-    if (t1 >= 1) issue_tile(K1, V1, kbytes, vtbytes, kBN, p.L, wave, lane);
+    dma_k_part(K0, kbytes, 0, p.L, wave, lane);
+    dma_vt_part(V0, vtbytes, 0, wave, lane);
+    if (t1 >= 1) {
+        dma_k_part(K1, kbytes, kBN, p.L, wave, lane);
+        dma_vt_part(V1, vtbytes, kBN, wave, lane);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
@@ -456,33 +484,6 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
     qk_scores<HPW>(K0, 0, qf, s0, w);
     if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
     row_update<HPW>(s0, acc, m_run, l_run, w);
-
-    // Interleaving inside a phase: LDS fragment reads run two steps ahead of the pair of
-    // MFMAs that use them, the vector work of the other sub-block fills the gaps, and the
-    // loads of tile t+2 (6 K and 4 V^T direct-to-LDS loads per wave) are spread over phases
-    // C and D instead of queueing at the address unit all at once.
-    auto sched_qk_phase = [](bool dma) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-#pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            if (dma && (i & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 load
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-        }
-    };
-    auto sched_pv_phase = [](bool dma) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            if (dma && (i & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 load
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-        }
-    };
 
     // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).  The loads of
     // tile t+2 are issued unconditionally (past the last tile they re-read tile t1 into a
@@ -495,12 +496,10 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
         // phase A: S(t,1) with P(t,0)
         qk_scores<HPW>(Kc, 1, qf, s1, w);
         probs<HPW>(s0, m_run, l_run, pf, w);
-        sched_qk_phase(false);
         if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
         // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
         pv_accum<HPW>(Vc, 0, pf, acc, w);
         grow = row_max<HPW>(s1, m_run, mnew, w);
-        sched_pv_phase(false);
         rescale<HPW>(grow, mnew, acc, m_run, l_run);
         // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -509,16 +508,12 @@ __global__ __launch_bounds__(256, 1) void prefill_causal_kernel(PrefillParams p)
         // are unused after the last tile)
         qk_scores<HPW>(Kn, 0, qf, s0, w);
         probs<HPW>(s1, m_run, l_run, pf, w);
-#pragma unroll
-        for (int i = 0; i < 6; ++i) dma_k_block(Kf, kbytes, kb_next, p.L, wave + 4 * i, lane);
-        sched_qk_phase(true);
+        dma_k_part(Kf, kbytes, kb_next, p.L, wave, lane);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
         // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
         pv_accum<HPW>(Vc, 1, pf, acc, w);
         grow = row_max<HPW>(s0, m_run, mnew, w);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dma_vt_block(Vf, vtbytes, kb_next, wave + 4 * i, lane);
-        sched_pv_phase(true);
+        dma_vt_part(Vf, vtbytes, kb_next, wave, lane);
         if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
     };
     for (int t = 0; t <= t1; t += 3) {
@@ -566,6 +561,32 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uin
 
 }  // namespace
 
+namespace {
+bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw == kCausalWaves; }
+}  // namespace
+
+// Causal mode with a group size divisible by 8: the eight-wave kernel, one head per wave.
+// Otherwise the general kernel: two heads per wave when the group size is even, and as many
+// waves along heads as divide the group (at most 4), the rest along positions.
+int64_t plan_prefill(PrefillParams &p) {
+    if (!p.swa && p.G % kCausalWaves == 0) {
+        p.hpw = 1;
+        p.hw = kCausalWaves;
+        p.pw = 1;
+    } else {
+        p.hpw = (p.G % 2 == 0) ? 2 : 1;
+        p.hw = p.hpw;
+        while (p.hw * 2 <= 4 * p.hpw && p.G % (p.hw * 2) == 0) p.hw *= 2;
+        p.pw = 4 * p.hpw / p.hw;
+    }
+    const int64_t npb = (p.L + 31) / 32;
+    p.n_pbw = (int)((npb + p.pw - 1) / p.pw);
+    p.hgroups = p.G / p.hw;
+    const int64_t items = (int64_t)p.n_pbw * p.B * p.Hkv * p.hgroups;
+    p.n_items = items > INT32_MAX ? INT32_MAX : (int)items;
+    return ((items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
+}
+
 size_t prefill_workspace_bytes(int B, int Hkv, int L) {
     const size_t lpad = ((size_t)L + kBN - 1) / kBN * kBN;
     return (size_t)B * Hkv * kDv * lpad * 2;
@@ -581,11 +602,12 @@ int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     }
     const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     void *args[] = {&p};
-    // the causal pipeline needs two heads per wave and all four waves on the same positions
-    const bool pipe = !p.swa && p.hpw == 2 && p.hw == 8;
-    const void *fn = pipe ? reinterpret_cast<const void *>(&prefill_causal_kernel)
-                          : p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
-                                       : reinterpret_cast<const void *>(&prefill_kernel<1>);
+    if (causal_layout(p)) {
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_causal_kernel), dim3(grid),
+                               dim3(64 * kCausalWaves), args, 0, stream) == hipSuccess ? 0 : -1;
+    }
+    const void *fn = p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
+                                : reinterpret_cast<const void *>(&prefill_kernel<1>);
     return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) == hipSuccess ? 0 : -1;
 }
 
