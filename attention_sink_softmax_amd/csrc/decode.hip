@@ -64,12 +64,14 @@ __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, 
     return base + (((size_t)page * p.Hkv + kvh) * p.page_size + (j % p.page_size)) * width;
 }
 
-template <bool kFast>
-__global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
-    // two buffer objects (even / odd slices) so that the compiler can tell the loads in
-    // flight into one from the reads of the other
+// kSingle: every wave holds at most one slice (a split of at most 4 x 32 keys, e.g. a
+// 128-slot ring); one buffer per wave, 80 KB of LDS, so two workgroups share a CU.
+template <bool kFast, bool kSingle>
+__global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(DecodeParams p) {
+    // slice buffers: even slices in bufA, odd ones in a second object (declared below, only
+    // when a wave has more than one slice) so that the compiler can tell the loads in flight
+    // into one from the reads of the other
     __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufBytes];
-    __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kBufBytes];
 
     const int split = blockIdx.x;
     const int kvh = blockIdx.y % p.Hkv, hc = blockIdx.y / p.Hkv;
@@ -247,9 +249,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeParams p) {
     };
 
     if (nmine > 0) issue(0, bufA[wave]);
-    for (int i = 0; i < nmine; i += 2) {
-        step(i, bufA[wave], bufB[wave]);
-        if (i + 1 < nmine) step(i + 1, bufB[wave], bufA[wave]);
+    if constexpr (kSingle) {
+        if (nmine > 0) step(0, bufA[wave], bufA[wave]);
+    } else {
+        __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kBufBytes];
+        for (int i = 0; i < nmine; i += 2) {
+            step(i, bufA[wave], bufB[wave]);
+            if (i + 1 < nmine) step(i + 1, bufB[wave], bufA[wave]);
+        }
     }
 
     // ---- merge the 4 waves' states through LDS (reusing the slice buffers)
@@ -403,8 +410,11 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     void *args[] = {&p};
     const dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B);
     const bool fast = !p.paged || (p.page_size % kSlice == 0);
-    const void *fn = fast ? reinterpret_cast<const void *>(&decode_split_kernel<true>)
-                          : reinterpret_cast<const void *>(&decode_split_kernel<false>);
+    // a ring of at most 128 visible slots in one split: one slice per wave
+    const bool single = !p.paged && p.nsplit == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
+    const void *fn = single ? reinterpret_cast<const void *>(&decode_split_kernel<true, true>)
+                     : fast ? reinterpret_cast<const void *>(&decode_split_kernel<true, false>)
+                            : reinterpret_cast<const void *>(&decode_split_kernel<false, false>);
     if (hipLaunchKernel(fn, grid, dim3(256), args, 0, stream) != hipSuccess) return -1;
     if (p.nsplit > 1) {
         if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_merge_kernel), dim3(p.B * p.Hq), dim3(128), args, 0,
