@@ -566,15 +566,17 @@ bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw
 }  // namespace
 
 // Causal mode with a group size divisible by 8: the eight-wave kernel, one head per wave.
-// Otherwise the general kernel: two heads per wave when the group size is even, and as many
-// waves along heads as divide the group (at most 4), the rest along positions.
+// Otherwise the general kernel, with as many waves along heads as divide the group (at most
+// 4) and the rest along positions: one head per wave in sliding-window mode (two workgroups
+// share a CU, so one's loads overlap the other's math on this short, memory-bound work), two
+// heads per wave for causal attention over an even group (half the LDS reads per MFMA).
 int64_t plan_prefill(PrefillParams &p) {
     if (!p.swa && p.G % kCausalWaves == 0) {
         p.hpw = 1;
         p.hw = kCausalWaves;
         p.pw = 1;
     } else {
-        p.hpw = (p.G % 2 == 0) ? 2 : 1;
+        p.hpw = (!p.swa && p.G % 2 == 0) ? 2 : 1;
         p.hw = p.hpw;
         while (p.hw * 2 <= 4 * p.hpw && p.G % (p.hw * 2) == 0) p.hw *= 2;
         p.pw = 4 * p.hpw / p.hw;
