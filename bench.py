@@ -41,11 +41,11 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "5ee3e6ed512b6f6adee29fdf834875499f9654b667039c041d323848f1db109b",
-                          "read_GB": 3.6043, "written_GB": 0.5705},
+                          "sha256": "f06857047928918216f4dad78a31e3393ed91c07616666bf31306a257fbb5296",
+                          "read_GB": 3.6197, "written_GB": 0.5872},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "f812e0c037755bfcb19939bb48969eb30944e312e73ec77bee1ea76a937aac2f",
-                                "read_GB": 5.3880, "written_GB": 0.0179},
+                                "sha256": "b613180c3bd310f07b43daaec1d2943d0218b686c5de03cbb000cc90a87e3c5d",
+                                "read_GB": 5.3880, "written_GB": 0.0180},
 }
 
 
@@ -207,7 +207,7 @@ def main() -> int:
     roofline = None
     if "ga_prefill_L32768" in comp:
         c = comp["ga_prefill_L32768"]
-        roofline = {"kernel": "prefill_kernel (ga_prefill_L32768)", "bound": "mfma", "achieved": c["tflops"],
+        roofline = {"kernel": "prefill_causal_kernel (ga_prefill_L32768)", "bound": "mfma", "achieved": c["tflops"],
                     "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(c["tflops"] / MFMA_PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_gb("ga_prefill_L32768"), "traffic_unit": "GB per call (HBM read + written)"}
@@ -262,14 +262,14 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
 
 def cpu_baseline():
     """The CPU oracle (fp64, OpenMP) on a fixed sample of both prefill workloads: all 64 heads
-    at 4096 seeded positions of the sliding workload and 160 seeded positions of the global
-    one (about 128 GFLOP of algorithmic work)."""
+    at 16384 seeded positions of the sliding workload and 1024 seeded positions of the global
+    one (about 0.75 TFLOP of algorithmic work, 10-20 s on 16 host cores)."""
     import oracle
     from attention_sink_softmax_amd import inputs
 
     total_flops, total_t = 0, 0.0
     parts = []
-    for w, npos in ((inputs.SWA_PREFILL, 4096), (inputs.GA_PREFILL, 160)):
+    for w, npos in ((inputs.SWA_PREFILL, 16384), (inputs.GA_PREFILL, 1024)):
         d = inputs.prefill_inputs(w)
         rng = np.random.default_rng([w.seed, 123])
         pos = np.sort(rng.choice(w.seqlen, size=npos, replace=False))
