@@ -135,10 +135,15 @@ __device__ __forceinline__ void qk_scores(const char *Kt, int sb, const bf16x8 (
 // Lane register r holds key row 8*(r/4) + 4g + r%4 of the sub-block.
 template <int HPW>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[HPW], int kb, int sb, const WaveCtx &w) {
+    // visible keys of row qi: [lo, hi]; register r holds key base + c_r, c_r known at compile
+    // time, so each test is two compares against lane constants (no branches)
+    const int base = kb + 32 * sb + 4 * w.g;
+    const int hi = min(w.qi, w.L - 1) - base;
+    const int lo = (w.swa ? w.qi - w.window + 1 : INT32_MIN / 2) - base;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int kj = kb + 32 * sb + 8 * (r >> 2) + 4 * w.g + (r & 3);
-        const bool ok = kj <= w.qi && kj < w.L && (!w.swa || kj > w.qi - w.window);
+        const int c = 8 * (r >> 2) + (r & 3);
+        const bool ok = (c >= lo) & (c <= hi);
 #pragma unroll
         for (int h = 0; h < HPW; ++h) s[h][r] = ok ? s[h][r] : -INFINITY;
     }
