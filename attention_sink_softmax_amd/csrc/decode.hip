@@ -65,13 +65,18 @@ __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, 
 }
 
 // kSingle: every wave holds at most one slice (a split of at most 4 x 32 keys, e.g. a
-// 128-slot ring); one buffer per wave, 80 KB of LDS, so two workgroups share a CU.
+// 128-slot ring).  Its K goes straight into registers (the direct-to-LDS layout below is
+// lane-private: lane l writes exactly the 16 bytes it later reads as its MFMA operand) and
+// only V passes through LDS, 33 KB per workgroup, so four workgroups share a CU and a whole
+// batch of rings is in flight at once.
 template <bool kFast, bool kSingle>
-__global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(DecodeParams p) {
     // slice buffers: even slices in bufA, odd ones in a second object (declared below, only
     // when a wave has more than one slice) so that the compiler can tell the loads in flight
-    // into one from the reads of the other
-    __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufBytes];
+    // into one from the reads of the other.  The single-slice buffer holds V only, plus room
+    // for the merge's row statistics.
+    constexpr int kBufA = kSingle ? kVBytes + 256 : kBufBytes;
+    __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufA];
 
     const int split = blockIdx.x;
     const int kvh = blockIdx.y % p.Hkv, hc = blockIdx.y / p.Hkv;
@@ -119,11 +124,13 @@ __global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(Deco
         page_reg = p.block_table[(size_t)b * p.max_pages + j0 / p.page_size];
     }
 
-    // Issue the 20 direct-to-LDS loads of slice i (of this wave) into `dst`.
+    bf16x8 kreg[2][6];  // single-slice path: this wave's K operands
+    // Issue the 20 loads of slice i (of this wave): K and V direct to LDS at `dst` (single-
+    // slice path: K into kreg, V to `dst`).
     auto issue = [&](int i, char *dst) {
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
         char *kb = dst;
-        char *vb = kb + kKBytes;
+        char *vb = kSingle ? dst : kb + kKBytes;
         const int r = lane >> 4, s = lane & 15;
         if (kFast) {
             // ring, or pages holding a multiple of 32 keys (one page per slice): rows
@@ -151,7 +158,13 @@ __global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(Deco
                 const int t = min(max(16 * sb + s, lo), hi);
                 const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
 #pragma unroll
-                for (int kk = 0; kk < 6; ++kk) dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                for (int kk = 0; kk < 6; ++kk) {
+                    if constexpr (kSingle) {
+                        kreg[sb][kk] = as_bf16x8(ldg16(kr + 32 * kk));
+                    } else {
+                        dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                    }
+                }
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(Deco
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         const char *kb = cur;
-        const char *vb = kb + kKBytes;
+        const char *vb = kSingle ? cur : kb + kKBytes;
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
 
         // ---- scores: S^T tiles of 16 keys x 16 heads
@@ -201,7 +214,8 @@ __global__ __launch_bounds__(256, kSingle ? 2 : 1) void decode_split_kernel(Deco
             s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
+                const bf16x8 kf =
+                    kSingle ? kreg[sb][kk] : *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
                 s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[sb], 0, 0, 0);
             }
         }
