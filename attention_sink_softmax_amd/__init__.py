@@ -53,7 +53,8 @@ class KVDesc(ctypes.Structure):
 
 
 EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_decode",
-           "sinkattn_decode_workspace_bytes", "sinkattn_status_string")
+           "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
+           "sinkattn_status_string")
 
 _lib = None
 
@@ -77,6 +78,11 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode.restype = I
     L.sinkattn_decode.argtypes = [I, I, ctypes.POINTER(Dims), P, ctypes.POINTER(KVDesc), P, ctypes.c_int32,
                                   P, P, P, ctypes.c_size_t, P]
+    L.sinkattn_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_decode_multi_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32]
+    L.sinkattn_decode_multi.restype = I
+    L.sinkattn_decode_multi.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), P,
+                                        ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
     L.sinkattn_status_string.restype = ctypes.c_char_p
     L.sinkattn_status_string.argtypes = [I]
     if path == LIB_PATH:
@@ -168,19 +174,24 @@ def sinkattn_decode_workspace_bytes(mode: int, window: int, batch: int, hq: int,
     return n
 
 
-def sinkattn_decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, max_seq_len: int,
-                    sink, out, workspace, block_table=None, scale: float | None = None, stream=None) -> None:
-    """q bf16 [B,Hq,192]; RING: k_cache [B,Hkv,W,192], v_cache [B,Hkv,W,128];
-    PAGED: k_cache [P,Hkv,page,192], v_cache [P,Hkv,page,128], block_table int32 [B,max_pages].
-    seq_lens int32 [B] (device), sink float32 [Hq] or None, out bf16 [B,Hq,128],
-    workspace uint8 tensor of at least sinkattn_decode_workspace_bytes(...) bytes or None."""
+def sinkattn_decode_multi_workspace_bytes(mode: int, window: int, batch: int, hq: int, hkv: int, q_len: int,
+                                          max_seq_len: int, d_qk: int = D_QK, d_v: int = D_V) -> int:
+    d = Dims(batch, 0, hq, hkv, d_qk, d_v, d_qk ** -0.5)
+    n = lib().sinkattn_decode_multi_workspace_bytes(mode, window, ctypes.byref(d), q_len, max_seq_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise SinkAttnError(2, "invalid sizes")
+    return n
+
+
+def _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out, workspace, block_table):
+    """Checks the decode tensors and builds the cache descriptor (q is [B,Hq,q_len,192] here)."""
     import torch
 
-    B, Hq, dqk = q.shape
+    B, Hq, _, dqk = q.shape
     Hkv = k_cache.shape[1]
     dv = v_cache.shape[3]
     _dev_tensor(q, "q", torch.bfloat16)
-    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, dv))
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, q_len, dv))
     _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
     if sink is not None:
         _dev_tensor(sink, "sink", torch.float32, (Hq,))
@@ -204,11 +215,43 @@ def sinkattn_decode(mode: int, window: int, q, layout: int, k_cache, v_cache, se
     for t in (k_cache, v_cache, out, seq_lens, sink, block_table, workspace):
         if t is not None and t.device != q.device:
             raise ValueError("all tensors must be on one device")
+    return B, Hq, Hkv, dqk, dv, desc, ws_ptr, ws_bytes
+
+
+def sinkattn_decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, max_seq_len: int,
+                    sink, out, workspace, block_table=None, scale: float | None = None, stream=None) -> None:
+    """q bf16 [B,Hq,192]; RING: k_cache [B,Hkv,W,192], v_cache [B,Hkv,W,128];
+    PAGED: k_cache [P,Hkv,page,192], v_cache [P,Hkv,page,128], block_table int32 [B,max_pages].
+    seq_lens int32 [B] (device), sink float32 [Hq] or None, out bf16 [B,Hq,128],
+    workspace uint8 tensor of at least sinkattn_decode_workspace_bytes(...) bytes or None."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, ws_ptr, ws_bytes = _decode_args(q.unsqueeze(2), 1, layout, window, k_cache, v_cache,
+                                                               seq_lens, sink, out.unsqueeze(2), workspace,
+                                                               block_table)
     d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
     with torch.cuda.device(q.device):
         rc = lib().sinkattn_decode(mode, window, ctypes.byref(d), _ptr(q), ctypes.byref(desc), _ptr(seq_lens),
                                    max_seq_len, _ptr(sink), _ptr(out), ws_ptr, ws_bytes,
                                    _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def sinkattn_decode_multi(mode: int, window: int, q_len: int, q, layout: int, k_cache, v_cache, seq_lens,
+                          max_seq_len: int, sink, out, workspace, block_table=None, scale: float | None = None,
+                          stream=None) -> None:
+    """q bf16 [B,Hq,q_len,192], out bf16 [B,Hq,q_len,128]; the q_len new tokens are the last
+    q_len positions of each sequence (seq_lens counts them).  Otherwise as sinkattn_decode;
+    workspace of at least sinkattn_decode_multi_workspace_bytes(...) bytes or None."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, ws_ptr, ws_bytes = _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens,
+                                                               sink, out, workspace, block_table)
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode_multi(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
+                                         _ptr(seq_lens), max_seq_len, _ptr(sink), _ptr(out), ws_ptr, ws_bytes,
+                                         _stream_ptr(stream, q.device))
     _raise(rc)
 
 
@@ -251,4 +294,27 @@ def decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, m
     out = torch.empty((B, Hq, v_cache.shape[3]), dtype=torch.bfloat16, device=q.device)
     sinkattn_decode(mode, window, q, layout, k_cache, v_cache, seq_lens, max_seq_len, sink, out, workspace,
                     block_table, scale, stream)
+    return out
+
+
+def decode_multi_workspace(mode: int, window: int, batch: int, hq: int, hkv: int, q_len: int, max_seq_len: int,
+                           device):
+    import torch
+
+    n = sinkattn_decode_multi_workspace_bytes(mode, window, batch, hq, hkv, q_len, max_seq_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def decode_multi(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, max_seq_len: int, sink=None,
+                 block_table=None, workspace=None, scale: float | None = None, stream=None):
+    """Allocate out (and the workspace if none is given) and run sinkattn_decode_multi on
+    q [B,Hq,q_len,192]."""
+    import torch
+
+    B, Hq, q_len, _ = q.shape
+    if workspace is None:
+        workspace = decode_multi_workspace(mode, window, B, Hq, k_cache.shape[1], q_len, max_seq_len, q.device)
+    out = torch.empty((B, Hq, q_len, v_cache.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_decode_multi(mode, window, q_len, q, layout, k_cache, v_cache, seq_lens, max_seq_len, sink, out,
+                          workspace, block_table, scale, stream)
     return out

@@ -31,19 +31,27 @@ int check_dims(int mode, int window, const sinkattn_dims *d) {
     return SINKATTN_OK;
 }
 
+constexpr int kMaxQLen = 256;  // new tokens per sequence at most (multi-token decode)
+
 struct DecodePlan {
-    int nsplit, chunk;
+    int nsplit, chunk, ncb, hchunks;
     size_t ws_bytes;
 };
 
-// Keys per split: enough splits that B * Hkv * head-chunks * splits reaches about
+// Columns: the G * q_len (query head, new token) pairs of a KV head, in blocks of 16; a
+// workgroup takes ncb blocks (up to 4), so one pass over a KV head's cache serves them all.
+// Keys per split: enough splits that B * Hkv * column-chunks * splits reaches about
 // kDecodeTargetWorkgroups, in whole 128-key blocks.  The kernel walks keys in 32-key
-// slices aligned to absolute positions, so a sliding window of W keys spans up to W + 31
-// aligned keys; short ranges (up to kDecodeSingleSplit keys) stay in one split.
-DecodePlan plan_decode(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
+// slices aligned to absolute positions, so a sliding window of W keys seen from q_len
+// consecutive positions spans up to W + q_len - 1 + 31 aligned keys; short ranges (up to
+// kDecodeSingleSplit keys) stay in one split.
+DecodePlan plan_decode(int mode, int window, const sinkattn_dims *d, int32_t q_len, int32_t max_seq_len) {
     const int64_t G = d->hq / d->hkv;
-    const int64_t hchunks = (G + 15) / 16;
-    const int64_t kmax = mode == SINKATTN_SWA ? (window < max_seq_len ? window : max_seq_len) + 31 : max_seq_len;
+    const int64_t rows = G * q_len;
+    const int64_t ncb = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+    const int64_t hchunks = (rows + 16 * ncb - 1) / (16 * ncb);
+    const int64_t span = (int64_t)window + q_len - 1;
+    const int64_t kmax = mode == SINKATTN_SWA ? (span < max_seq_len ? span : max_seq_len) + 31 : max_seq_len;
     const int64_t units = (int64_t)d->batch * d->hkv * hchunks;
     int64_t chunk = units > 0 ? (kmax * units + kDecodeTargetWorkgroups - 1) / kDecodeTargetWorkgroups : kmax;
     if (kmax <= kDecodeSingleSplit) chunk = kmax;
@@ -54,7 +62,10 @@ DecodePlan plan_decode(int mode, int window, const sinkattn_dims *d, int32_t max
     DecodePlan pl;
     pl.nsplit = (int)(nsplit < 1 ? 1 : nsplit);
     pl.chunk = (int)chunk;
-    pl.ws_bytes = pl.nsplit > 1 ? (size_t)d->batch * d->hq * pl.nsplit * (kDvSupported + 4) * sizeof(float) : 0;
+    pl.ncb = (int)ncb;
+    pl.hchunks = (int)hchunks;
+    pl.ws_bytes =
+        pl.nsplit > 1 ? (size_t)d->batch * d->hq * q_len * pl.nsplit * (kDvSupported + 4) * sizeof(float) : 0;
     return pl;
 }
 
@@ -116,17 +127,24 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
 
 size_t sinkattn_decode_workspace_bytes(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
     if (check_dims(mode, window, d) || max_seq_len < 1) return (size_t)-1;
-    return plan_decode(mode, window, d, max_seq_len).ws_bytes;
+    return plan_decode(mode, window, d, 1, max_seq_len).ws_bytes;
 }
 
-int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,
-                    const int32_t *seq_lens, int32_t max_seq_len, const float *sink, void *out, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+size_t sinkattn_decode_multi_workspace_bytes(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                                             int32_t max_seq_len) {
+    if (check_dims(mode, window, d) || max_seq_len < 1 || q_len < 1 || q_len > kMaxQLen) return (size_t)-1;
+    return plan_decode(mode, window, d, q_len, max_seq_len).ws_bytes;
+}
+
+int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                          const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_dims(mode, window, d);
     if (st) return st;
+    if (q_len < 1 || q_len > kMaxQLen) return SINKATTN_E_SHAPE;
     if (!kv) return SINKATTN_E_NULL;
     if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
-    if (kv->layout == SINKATTN_KV_RING && mode != SINKATTN_SWA) return SINKATTN_E_UNSUPPORTED;
+    if (kv->layout == SINKATTN_KV_RING && (mode != SINKATTN_SWA || q_len != 1)) return SINKATTN_E_UNSUPPORTED;
     if (max_seq_len < 1) return SINKATTN_E_SHAPE;
     if (kv->layout == SINKATTN_KV_PAGED) {
         if (kv->page_size <= 0 || kv->max_pages <= 0 || kv->num_pages <= 0) return SINKATTN_E_SHAPE;
@@ -138,7 +156,7 @@ int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q,
     if (misaligned(q) || misaligned(out) || misaligned(seq_lens) || misaligned(kv->k) || misaligned(kv->v) ||
         (sink && misaligned(sink)) || (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
         return SINKATTN_E_ALIGN;
-    const DecodePlan pl = plan_decode(mode, window, d, max_seq_len);
+    const DecodePlan pl = plan_decode(mode, window, d, q_len, max_seq_len);
     if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes) return SINKATTN_E_WORKSPACE;
         if (misaligned(workspace)) return SINKATTN_E_ALIGN;
@@ -157,7 +175,9 @@ int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q,
     p.Hq = d->hq;
     p.Hkv = d->hkv;
     p.G = d->hq / d->hkv;
-    p.hchunks = (p.G + 15) / 16;
+    p.q_len = q_len;
+    p.ncb = pl.ncb;
+    p.hchunks = pl.hchunks;
     p.swa = mode == SINKATTN_SWA;
     p.window = p.swa ? window : 0;
     p.paged = kv->layout == SINKATTN_KV_PAGED;
@@ -168,9 +188,16 @@ int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q,
     p.scale_log2 = (float)((double)d->scale * kLog2eD);
     p.nsplit = pl.nsplit;
     p.chunk = pl.chunk;
-    if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq > INT32_MAX)
+    if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq * p.q_len > INT32_MAX)
         return SINKATTN_E_SHAPE;
     return launch_decode(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,
+                    const int32_t *seq_lens, int32_t max_seq_len, const float *sink, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return sinkattn_decode_multi(mode, window, d, 1, q, kv, seq_lens, max_seq_len, sink, out, workspace,
+                                 workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -64,12 +64,33 @@ __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, 
     return base + (((size_t)page * p.Hkv + kvh) * p.page_size + (j % p.page_size)) * width;
 }
 
+// Keys that sequence b's queries can see, as the range the splits walk: [kbeg, kend).  The
+// new queries sit at positions n - q_len .. n - 1; a ring enumerates its slots [0, min(n, W))
+// (one query, every valid slot visible).
+__device__ __forceinline__ void key_range(const DecodeParams &p, int n, int &kbeg, int &kend) {
+    if (!p.paged) {
+        kbeg = 0;
+        kend = min(n, p.window);
+    } else {
+        kbeg = p.swa ? max(0, n - p.q_len - p.window + 1) : 0;
+        kend = n;
+    }
+}
+
+__device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
+    return n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
+}
+
+// Columns: the G * q_len (query head, new token) pairs of one KV head, column c = head-in-
+// group * q_len + token; a workgroup takes NCB blocks of 16 columns, and every K and V
+// fragment it reads from LDS feeds all NCB blocks (one pass over the cache per KV head).
+//
 // kSingle: every wave holds at most one slice (a split of at most 4 x 32 keys, e.g. a
 // 128-slot ring).  Its K goes straight into registers (the direct-to-LDS layout below is
 // lane-private: lane l writes exactly the 16 bytes it later reads as its MFMA operand) and
 // only V passes through LDS, 33 KB per workgroup, so four workgroups share a CU and a whole
 // batch of rings is in flight at once.
-template <bool kFast, bool kSingle>
+template <bool kFast, bool kSingle, int NCB>
 __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(DecodeParams p) {
     // slice buffers: even slices in bufA, odd ones in a second object (declared below, only
     // when a wave has more than one slice) so that the compiler can tell the loads in flight
@@ -82,35 +103,35 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     const int kvh = blockIdx.y % p.Hkv, hc = blockIdx.y / p.Hkv;
     const int b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int hl = lane & 15, q = lane >> 4;  // head column, k-group
-    const int hidx = hc * 16 + hl;            // head within the KV group
-    const bool head_ok = hidx < p.G;
-    const int h = kvh * p.G + hidx;
+    const int hl = lane & 15, q = lane >> 4;  // column within a block, k-group
+    const int rows = p.G * p.q_len;
 
     const int n = p.seq_lens[b];
-    // visible keys [kbeg, kend): positions [max(0, n-W), n) (sliding) or [0, n) (global);
-    // the ring enumerates them as slots [0, min(n, W)).  Slices are aligned to 32 keys.
     int kbeg, kend;
-    if (!p.paged) {
-        kbeg = 0;
-        kend = min(n, p.window);
-    } else {
-        kbeg = p.swa ? max(0, n - p.window) : 0;
-        kend = n;
-    }
-    const bool seq_ok = n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
+    key_range(p, n, kbeg, kend);
+    const bool seq_ok = seq_valid(p, n);
+    // slices are aligned to 32 keys
     const int kb0 = kbeg & ~(kSlice - 1);
     const int s_lo = kb0 + split * p.chunk;
     const int s_hi = seq_ok ? min(kend, s_lo + p.chunk) : s_lo;  // empty when the length is invalid
     const int nslices = s_hi > s_lo ? (s_hi - s_lo + kSlice - 1) / kSlice : 0;
     const int nmine = nslices > wave ? (nslices - wave + kWaves - 1) / kWaves : 0;
 
-    // Q^T fragments: lane supplies q[h][32kk + 8q .. +8]
-    bf16x8 qf[6];
-    {
-        const uint16_t *qrow = p.q + ((size_t)b * p.Hq + (head_ok ? h : 0)) * kDqk + 8 * q;
+    // this lane's columns: Q^T fragments (lane supplies q[32kk + 8q .. +8]) and the keys each
+    // one sees, [lo_c, hi_c] within this split
+    bf16x8 qf[NCB][6];
+    int lo_c[NCB], hi_c[NCB];
 #pragma unroll
-        for (int kk = 0; kk < 6; ++kk) qf[kk] = as_bf16x8(head_ok ? ldg16(qrow + 32 * kk) : u32x4{0, 0, 0, 0});
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int c = (hc * NCB + cb) * 16 + hl;
+        const bool ok = c < rows;
+        const int hq = kvh * p.G + (ok ? c / p.q_len : 0), tok = ok ? c % p.q_len : 0;
+        const int pos = n - p.q_len + tok;
+        lo_c[cb] = max(kbeg, (p.paged && p.swa) ? pos - p.window + 1 : 0);
+        hi_c[cb] = min(s_hi, p.paged ? pos + 1 : kend) - 1;
+        const uint16_t *qrow = p.q + (((size_t)b * p.Hq + hq) * p.q_len + tok) * kDqk + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) qf[cb][kk] = as_bf16x8(ok ? ldg16(qrow + 32 * kk) : u32x4{0, 0, 0, 0});
     }
 
     bool bad = false;
@@ -188,10 +209,15 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         }
     };
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[8];
+    float m_run[NCB], l_run[NCB];
+    f32x4 acc[NCB][8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Slice i: put slice i+1 in flight into `nxt`, wait for slice i, compute it from `cur`.
     auto step = [&](int i, const char *cur, char *nxt) {
@@ -207,45 +233,53 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         const char *vb = kSingle ? cur : kb + kKBytes;
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
 
-        // ---- scores: S^T tiles of 16 keys x 16 heads
-        f32x4 s[2];
+        // ---- scores: S^T tiles of 16 keys x 16 columns
+        f32x4 s[NCB][2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) s[cb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
                 const bf16x8 kf =
                     kSingle ? kreg[sb][kk] : *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
-                s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[sb], 0, 0, 0);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    s[cb][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][kk], s[cb][sb], 0, 0, 0);
             }
         }
-        // lane holds keys j0 + 16sb + 4q + e for head hl
-        float x[8];
-        float mx = m_run;
+        // lane holds keys j0 + 16sb + 4q + e for column hl of each block
+        bf16x8 pf[NCB];
+        float alpha[NCB];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        for (int cb = 0; cb < NCB; ++cb) {
+            float x[8];
+            float mx = m_run[cb];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + 16 * sb + 4 * q + e;
+                    const float v = (j >= lo_c[cb] && j <= hi_c[cb]) ? s[cb][sb][e] * p.scale_log2 : -INFINITY;
+                    x[4 * sb + e] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+            mx = max_xor32(max_xor16(mx));
+            const float mu = (mx == -INFINITY) ? 0.f : mx;
+            alpha[cb] = exp2f_fast(m_run[cb] - mu);
+            m_run[cb] = mx;
+            float ps = 0.f;
+            uint32_t pk[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 16 * sb + 4 * q + e;
-                const float v = (j >= kbeg && j < s_hi) ? s[sb][e] * p.scale_log2 : -INFINITY;
-                x[4 * sb + e] = v;
-                mx = fmaxf(mx, v);
+                const float p0 = exp2f_fast(x[2 * e] - mu), p1 = exp2f_fast(x[2 * e + 1] - mu);
+                ps += p0 + p1;
+                pk[e] = pack_bf16x2(p0, p1);
             }
+            l_run[cb] = l_run[cb] * alpha[cb] + ps;
+            pf[cb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
         }
-        mx = max_xor32(max_xor16(mx));
-        const float mu = (mx == -INFINITY) ? 0.f : mx;
-        const float alpha = exp2f_fast(m_run - mu);
-        m_run = mx;
-        float ps = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float p0 = exp2f_fast(x[2 * e] - mu), p1 = exp2f_fast(x[2 * e + 1] - mu);
-            ps += p0 + p1;
-            pk[e] = pack_bf16x2(p0, p1);
-        }
-        l_run = l_run * alpha + ps;
-        const bf16x8 pf = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
 
         // ---- O^T += V^T P^T; V^T through the transposing read: 16-lane group q, lane
         // 4r + c4 addresses row r (keys 4q + r, then 16 + 4q + r) at dv 16db + 4c4, and lane i
@@ -258,7 +292,9 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + q * 1024 + off));
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (4 + q) * 1024 + off));
             const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[db] * alpha, 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[cb], acc[cb][db] * alpha[cb], 0, 0, 0);
         }
     };
 
@@ -273,106 +309,107 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         }
     }
 
-    // ---- merge the 4 waves' states through LDS (reusing the slice buffers)
-    const float lsum = sum_xor32(sum_xor16(l_run));
+    // ---- merge the 4 waves' states through LDS (reusing the slice buffers), one block of
+    // 16 columns at a time
     const bool wave_bad = __any(bad);
-    __syncthreads();  // every wave is done with its slice buffers
-    float *ob = reinterpret_cast<float *>(&bufA[0][0]);  // [4 waves][16 heads][128 dv]
+    float *ob = reinterpret_cast<float *>(&bufA[0][0]);  // [4 waves][16 columns][128 dv]
     float *red_m = ob + kWaves * 16 * kDv, *red_l = red_m + kWaves * 16, *red_bad = red_l + kWaves * 16;
-    if (q == 0) {
-        red_m[wave * 16 + hl] = m_run;
-        red_l[wave * 16 + hl] = lsum;
-    }
-    if (lane == 0) red_bad[wave] = wave_bad ? 1.f : 0.f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ob[(wave * 16 + hl) * kDv + 16 * db + 4 * q + e] = acc[db][e];
-    __syncthreads();
-
-    const bool any_bad = (red_bad[0] + red_bad[1] + red_bad[2] + red_bad[3]) != 0.f;
-    // thread -> (head hh, 8 dv values)
-    const int hh = tid >> 4, d0 = (tid & 15) * 8;
-    const int hidx2 = hc * 16 + hh;
-    if (hidx2 >= p.G) return;
-    const int h2 = kvh * p.G + hidx2;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float sc = exp2f_fast(red_m[w * 16 + hh] - Mu);
-        L += sc * red_l[w * 16 + hh];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
-    }
-
-    if (p.nsplit == 1) {
-        // final output: add the sink term once, normalise, round to bf16
-        uint16_t *orow = p.out + ((size_t)b * p.Hq + h2) * kDv + d0;
-        float res[8];
-        if (n <= 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) res[e] = 0.f;
-        } else if (!seq_ok || any_bad) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) res[e] = __builtin_nanf("");
-        } else {
-            const float sk = p.sink ? p.sink[h2] : -INFINITY;
-            if (sk == INFINITY) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) res[e] = 0.f;
-            } else {
-                const float sl = sk * kLog2e;
-                const float M2 = fmaxf(M, sl);
-                const float sc = exp2f_fast(M - M2);
-                const float Lt = L * sc + (sk == -INFINITY ? 0.f : exp2f_fast(sl - M2));
-                const float inv = 1.f / Lt;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) res[e] = o[e] * sc * inv;
-            }
+    for (int cb = 0; cb < NCB; ++cb) {
+        const float lsum = sum_xor32(sum_xor16(l_run[cb]));
+        __syncthreads();  // the slice buffers (or the previous block's records) are free
+        if (q == 0) {
+            red_m[wave * 16 + hl] = m_run[cb];
+            red_l[wave * 16 + hl] = lsum;
         }
-        *reinterpret_cast<u32x4 *>(orow) = u32x4{pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]),
-                                                 pack_bf16x2(res[4], res[5]), pack_bf16x2(res[6], res[7])};
-    } else {
-        float *rec = p.ws + (((size_t)b * p.Hq + h2) * p.nsplit + split) * kPart;
-        *reinterpret_cast<f32x4 *>(rec + d0) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4 *>(rec + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        if ((tid & 15) == 0) {
-            rec[kDv] = M;
-            rec[kDv + 1] = any_bad ? __builtin_nanf("") : L;
+        if (lane == 0) red_bad[wave] = wave_bad ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[(wave * 16 + hl) * kDv + 16 * db + 4 * q + e] = acc[cb][db][e];
+        __syncthreads();
+
+        const bool any_bad = (red_bad[0] + red_bad[1] + red_bad[2] + red_bad[3]) != 0.f;
+        // thread -> (column hh, 8 dv values)
+        const int hh = tid >> 4, d0 = (tid & 15) * 8;
+        const int c = (hc * NCB + cb) * 16 + hh;
+        if (c < rows) {
+            const int h2 = kvh * p.G + c / p.q_len, tok = c % p.q_len;
+            const size_t row = ((size_t)b * p.Hq + h2) * p.q_len + tok;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
+            const float Mu = (M == -INFINITY) ? 0.f : M;
+            float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sc = exp2f_fast(red_m[w * 16 + hh] - Mu);
+                L += sc * red_l[w * 16 + hh];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
+            }
+            if (p.nsplit == 1) {
+                // final output: add the sink term once, normalise, round to bf16
+                uint16_t *orow = p.out + row * kDv + d0;
+                float res[8];
+                if (n - p.q_len + tok < 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) res[e] = 0.f;
+                } else if (!seq_ok || any_bad) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) res[e] = __builtin_nanf("");
+                } else {
+                    const float sk = p.sink ? p.sink[h2] : -INFINITY;
+                    if (sk == INFINITY) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) res[e] = 0.f;
+                    } else {
+                        const float sl = sk * kLog2e;
+                        const float M2 = fmaxf(M, sl);
+                        const float sc = exp2f_fast(M - M2);
+                        const float Lt = L * sc + (sk == -INFINITY ? 0.f : exp2f_fast(sl - M2));
+                        const float inv = 1.f / Lt;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) res[e] = o[e] * sc * inv;
+                    }
+                }
+                *reinterpret_cast<u32x4 *>(orow) = u32x4{pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]),
+                                                         pack_bf16x2(res[4], res[5]), pack_bf16x2(res[6], res[7])};
+            } else {
+                float *rec = p.ws + (row * p.nsplit + split) * kPart;
+                *reinterpret_cast<f32x4 *>(rec + d0) = f32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<f32x4 *>(rec + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+                if ((tid & 15) == 0) {
+                    rec[kDv] = M;
+                    rec[kDv + 1] = any_bad ? __builtin_nanf("") : L;
+                }
+            }
         }
     }
 }
 
-// One workgroup of 128 threads per (sequence, query head): thread t owns output dim t.
-// Merges the splits' partials and adds the sink term once.
+// One workgroup of 128 threads per (sequence, query head, new token): thread t owns output
+// dim t.  Merges the splits' partials and adds the sink term once.
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     __shared__ float red[128];
-    const int bh = blockIdx.x;
-    const int b = bh / p.Hq, h = bh % p.Hq;
+    const size_t row = blockIdx.x;  // (b * Hq + h) * q_len + token
+    const int tok = (int)(row % p.q_len);
+    const int h = (int)((row / p.q_len) % p.Hq), b = (int)(row / ((size_t)p.q_len * p.Hq));
     const int t = threadIdx.x;
     const int n = p.seq_lens[b];
-    uint16_t *out = p.out + (size_t)bh * kDv + t;
-    const bool seq_ok = n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
-    if (n <= 0 || !seq_ok) {
-        const float z = n <= 0 ? 0.f : __builtin_nanf("");
+    uint16_t *out = p.out + row * kDv + t;
+    const bool seq_ok = seq_valid(p, n);
+    if (n - p.q_len + tok < 0 || !seq_ok) {
+        const float z = n - p.q_len + tok < 0 ? 0.f : __builtin_nanf("");
         *out = __builtin_bit_cast(uint16_t, (__bf16)z);
         return;
     }
     int kbeg, kend;
-    if (!p.paged) {
-        kbeg = 0;
-        kend = min(n, p.window);
-    } else {
-        kbeg = p.swa ? max(0, n - p.window) : 0;
-        kend = n;
-    }
+    key_range(p, n, kbeg, kend);
     const int kb0 = kbeg & ~(kSlice - 1);
     const int used = (kend - kb0 + p.chunk - 1) / p.chunk;  // splits that saw keys
-    const float *base = p.ws + (size_t)bh * p.nsplit * kPart;
+    const float *base = p.ws + row * p.nsplit * kPart;
+
 
     const float sk = p.sink ? p.sink[h] : -INFINITY;
     const bool sink_inf = sk == INFINITY;
@@ -425,14 +462,23 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     const dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B);
     const bool fast = !p.paged || (p.page_size % kSlice == 0);
     // a ring of at most 128 visible slots in one split: one slice per wave
-    const bool single = !p.paged && p.nsplit == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
-    const void *fn = single ? reinterpret_cast<const void *>(&decode_split_kernel<true, true>)
-                     : fast ? reinterpret_cast<const void *>(&decode_split_kernel<true, false>)
-                            : reinterpret_cast<const void *>(&decode_split_kernel<false, false>);
+    const bool single = !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
+    const void *fn;
+    if (single) {
+        fn = reinterpret_cast<const void *>(&decode_split_kernel<true, true, 1>);
+    } else if (fast) {
+        fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 4>)
+             : p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 2>)
+                          : reinterpret_cast<const void *>(&decode_split_kernel<true, false, 1>);
+    } else {
+        fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<false, false, 4>)
+             : p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<false, false, 2>)
+                          : reinterpret_cast<const void *>(&decode_split_kernel<false, false, 1>);
+    }
     if (hipLaunchKernel(fn, grid, dim3(256), args, 0, stream) != hipSuccess) return -1;
     if (p.nsplit > 1) {
-        if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_merge_kernel), dim3(p.B * p.Hq), dim3(128), args, 0,
-                            stream) != hipSuccess)
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&decode_merge_kernel), dim3(p.B * p.Hq * p.q_len), dim3(128),
+                            args, 0, stream) != hipSuccess)
             return -1;
     }
     return 0;

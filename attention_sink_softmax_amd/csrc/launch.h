@@ -30,8 +30,10 @@ struct DecodeParams {
     const int32_t *seq_lens;
     const float *sink;  // [Hq] or nullptr
     uint16_t *out;
-    float *ws;  // partials [B][Hq][nsplit][kDv + 4] when nsplit > 1
-    int B, Hq, Hkv, G, hchunks;
+    float *ws;  // partials [B][Hq][q_len][nsplit][kDv + 4] when nsplit > 1
+    int B, Hq, Hkv, G;
+    int q_len;         // new tokens per sequence (positions seq_len - q_len .. seq_len - 1)
+    int ncb, hchunks;  // 16-column blocks per workgroup; workgroups per KV head
     int swa, window, paged, page_size, max_pages, num_pages, max_seq_len;
     float scale_log2;
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)

@@ -104,6 +104,7 @@ class Workload:
     ctx_lo: int = 0
     ctx_hi: int = 0
     page_size: int = 64
+    q_len: int = 1       # new tokens per sequence (q_len > 1: drafted tokens verified together)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -121,8 +122,11 @@ SWA_DECODE = Workload("swa_decode_B128_ring", "decode", MODE_SWA, 128, 64, 8, wi
                       layout="ring", ctx_lo=4096, ctx_hi=65536)
 GA_DECODE = Workload("ga_decode_B8_256K_paged", "decode", MODE_GLOBAL, 8, 64, 4, window=0, seed=4,
                      layout="paged", ctx_lo=262144, ctx_hi=262144, page_size=64)
+# verification of 4 drafted tokens per sequence (the multi-token-prediction step) at 256K
+GA_VERIFY = Workload("ga_verify_B8_256K_q4_paged", "decode", MODE_GLOBAL, 8, 64, 4, window=0, seed=5,
+                     layout="paged", ctx_lo=262144, ctx_hi=262144, page_size=64, q_len=4)
 
-WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE)}
+WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE, GA_VERIFY)}
 
 
 # --------------------------------------------------------------------------- prefill
@@ -189,7 +193,8 @@ def page_table(batch: int, pages_per_seq: int, num_pages: int, seed: int, permut
 def decode_paged_inputs(w: Workload, seed: int | None = None, batch: int | None = None,
                         ctx: int | None = None, num_pages: int | None = None,
                         permute: bool = True) -> dict:
-    """Paged caches: pool k [P,Hkv,page,dqk], v [P,Hkv,page,dv], block_table [B,max_pages]."""
+    """Paged caches: pool k [P,Hkv,page,dqk], v [P,Hkv,page,dv], block_table [B,max_pages];
+    q [B,Hq,dqk], or [B,Hq,q_len,dqk] when the workload has q_len > 1."""
     s = w.seed if seed is None else seed
     B = w.batch if batch is None else batch
     n = w.ctx_hi if ctx is None else ctx
@@ -197,7 +202,7 @@ def decode_paged_inputs(w: Workload, seed: int | None = None, batch: int | None 
     max_pages = (n + ps - 1) // ps
     P = B * max_pages if num_pages is None else num_pages
     return {
-        "q": normal((B, w.hq, w.d_qk), s, 0),
+        "q": normal((B, w.hq, w.d_qk) if w.q_len == 1 else (B, w.hq, w.q_len, w.d_qk), s, 0),
         "k": normal((P, w.hkv, ps, w.d_qk), s, 1),
         "v": normal((P, w.hkv, ps, w.d_v), s, 2),
         "block_table": page_table(B, max_pages, P, s, permute),

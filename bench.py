@@ -5,6 +5,7 @@ One step runs every kernel of the path once, each on its benchmark workload:
   ga_prefill_L32768    global causal prefill with sink, L=32768, 64 query / 4 KV heads
   swa_decode_B128_ring sliding-window decode, 128 sequences, 128-slot ring caches
   ga_decode_B8_256K    global decode, 8 sequences x 262144 tokens, 64-token permuted pages
+  ga_verify_B8_256K_q4 the same caches with 4 new (drafted) tokens per sequence at once
 All inputs are synthetic (seeded N(0,1) bf16, sink ~ U[0,6]) and resident in HBM before
 timing starts.  Each call is timed with HIP events recorded on the stream the library
 launches on.
@@ -165,6 +166,27 @@ def main() -> int:
 
         runs[w.name] = (call, flops, nbytes)
 
+    # --- verification of 4 drafted tokens per sequence at 256K (same cache shape as above)
+    w = inputs.GA_VERIFY
+    if not only or w.name in only:
+        d = inputs.decode_paged_inputs(w)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        bt = torch.from_numpy(d["block_table"]).to(dev)
+        lens = torch.from_numpy(d["seq_lens"]).to(dev)
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        del d
+        out = torch.empty((w.batch, w.hq, w.q_len, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_multi_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, w.q_len, w.ctx_hi, dev)
+        # token t of q_len sees ctx - q_len + t + 1 keys; the cache is read once for all of them
+        flops = sum(w.ctx_hi - w.q_len + t + 1 for t in range(w.q_len)) * w.batch * w.hq * FLOP_PER_PAIR
+        nbytes = w.batch * w.ctx_hi * w.hkv * (w.d_qk + w.d_v) * 2
+
+        def call(w=w, q=q, k=k, v=v, bt=bt, lens=lens, sink=sink, out=out, ws=ws):
+            sa.sinkattn_decode_multi(w.mode, w.window, w.q_len, q, sa.KV_PAGED, k, v, lens, w.ctx_hi, sink, out, ws,
+                                     bt)
+
+        runs[w.name] = (call, flops, nbytes)
+
     names = list(runs)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -233,7 +255,8 @@ def main() -> int:
                    "swa_prefill": "B=1 L=32768 Hq=64 Hkv=8 W=128 d_qk=192 d_v=128",
                    "ga_prefill": "B=1 L=32768 Hq=64 Hkv=4 causal+sink d_qk=192 d_v=128",
                    "swa_decode": "B=128 ctx~U[4096,65536] 128-slot ring Hq=64 Hkv=8",
-                   "ga_decode": "B=8 ctx=262144 64-token pages, permuted table, Hq=64 Hkv=4"},
+                   "ga_decode": "B=8 ctx=262144 64-token pages, permuted table, Hq=64 Hkv=4",
+                   "ga_verify": "as ga_decode with q_len=4 new tokens per sequence"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode, "cpu_baseline": cpu,
     }

@@ -150,6 +150,38 @@ int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q,
                     const float *sink, void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * Bytes of device workspace sinkattn_decode_multi needs (0 when none); (size_t)-1 for
+ * invalid arguments.  Pass the same max_seq_len to sinkattn_decode_multi.
+ */
+size_t sinkattn_decode_multi_workspace_bytes(int mode, int window, const sinkattn_dims *d,
+                                             int32_t q_len, int32_t max_seq_len);
+
+/*
+ * Multi-token decode: q_len new queries per sequence, at positions seq_lens[b] - q_len ..
+ * seq_lens[b] - 1, as when the model checks several draft tokens in one forward pass
+ * (deep-dive page CH 4.4: the main model verifies the MTP drafts in parallel; paper-notes
+ * page §6.4 walks through one such step with four tokens).  The new tokens' keys and values
+ * must already be in the cache.  Query i attends to the keys j <= its own position p_i
+ * (causal among the new tokens) and, in SWA mode, only to j > p_i - window; each gets the
+ * sink term of its head.  q_len = 1 is sinkattn_decode.
+ *   q_len        1 .. 256
+ *   q            bf16 [batch][hq][q_len][d_qk]
+ *   kv           PAGED (either mode).  A RING cache holds only the last `window` tokens,
+ *                too few for the earlier new tokens' windows: RING needs q_len = 1
+ *                (SINKATTN_E_UNSUPPORTED otherwise).
+ *   seq_lens     device int32 [batch]: tokens in each sequence INCLUDING the q_len new
+ *                ones.  A query whose position is negative (seq_lens[b] < q_len) gets a zero
+ *                row; seq_lens[b] above max_seq_len makes the sequence's rows NaN.
+ *   out          bf16 [batch][hq][q_len][d_v]
+ *   everything else as sinkattn_decode.  All q_len * (hq / hkv) queries of a KV head read
+ * its cache once.
+ */
+int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                          const void *q, const sinkattn_kv *kv, const int32_t *seq_lens,
+                          int32_t max_seq_len, const float *sink, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(int status);
 

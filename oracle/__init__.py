@@ -53,7 +53,7 @@ def load(path: str = LIB):
     lib.oracle_prefill.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P,
                                    ctypes.c_int64, P, P]
     lib.oracle_decode.restype = I
-    lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
+    lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
                                   P, P, P]
     lib.oracle_threads.restype = I
     lib.oracle_threads.argtypes = []
@@ -105,13 +105,16 @@ def prefill(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=
 
 def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout: int,
            block_table=None, lib=None) -> np.ndarray:
-    """q [B,Hq,dqk]; RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv]; PAGED: k [P,Hkv,page,dqk],
-    v [P,Hkv,page,dv] with block_table [B,max_pages].  Returns float64 [B,Hq,dv]."""
+    """q [B,Hq,dqk] (one new token per sequence) or [B,Hq,q_len,dqk] (q_len new tokens at
+    positions seq_lens-q_len .. seq_lens-1); RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv];
+    PAGED: k [P,Hkv,page,dqk], v [P,Hkv,page,dv] with block_table [B,max_pages].
+    Returns float64 [B,Hq,dv] or [B,Hq,q_len,dv], matching q."""
     lib = lib or load()
     qa, dt = _arr(q, None)
     ka, _ = _arr(k, None)
     va, _ = _arr(v, None)
-    B, Hq, dqk = qa.shape
+    B, Hq, dqk = qa.shape[0], qa.shape[1], qa.shape[-1]
+    q_len = qa.shape[2] if qa.ndim == 4 else 1
     Hkv, dv = ka.shape[1], va.shape[3]
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
@@ -120,8 +123,8 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
         ps, mp, npg = ka.shape[2], bt.shape[1], ka.shape[0]
     else:
         bt, ps, mp, npg = None, 0, 0, 0
-    out = np.empty((B, Hq, dv), np.float64)
-    rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka),
+    out = np.empty(qa.shape[:-1] + (dv,), np.float64)
+    rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
                            _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")

@@ -118,23 +118,30 @@ int oracle_prefill(int mode, int window, int B, int L, int Hq, int Hkv, int dqk,
 }
 
 /*
- * Decode: one new query per sequence at position n_b - 1, where n_b = seq_lens[b] counts
- * the new token (its key and value are already in the cache).
- * q [B][Hq][dqk]; sink [Hq] or NULL; out [B][Hq][dv].
- * RING  (sliding mode only): k [B][Hkv][window][dqk], v [B][Hkv][window][dv]; position p
- *       lives in slot p mod window.
+ * Decode: q_len new queries per sequence at positions n_b - q_len .. n_b - 1, where
+ * n_b = seq_lens[b] counts the new tokens (their keys and values are already in the cache).
+ * q_len = 1 is ordinary one-token decoding; q_len > 1 is the parallel verification of
+ * drafted tokens ("MiMo-V2-Flash 模型架构深度拆解", CH 4.4; paper notes §6.4): each new
+ * token is a causal query that sees the cache up to and including its own position, so
+ * the result equals the last q_len rows of a prefill over the whole sequence.
+ * A position below 0 (n_b < q_len) has an empty visible set: its output row is 0.
+ * q [B][Hq][q_len][dqk]; sink [Hq] or NULL; out [B][Hq][q_len][dv].
+ * RING  (sliding mode and q_len = 1 only): k [B][Hkv][window][dqk], v [B][Hkv][window][dv];
+ *       position p lives in slot p mod window.  (With q_len > 1 the earlier queries would
+ *       need keys the ring has already overwritten.)
  * PAGED (either mode): k [num_pages][Hkv][page_size][dqk], v [num_pages][Hkv][page_size][dv];
  *       position p of sequence b lives in page block_table[b*max_pages + p/page_size] at
  *       offset p mod page_size.
  * Returns 0, or -1 on bad arguments (including a page id outside the pool).
  */
 int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
-                  double scale, int dtype, const void *q, const void *k, const void *v,
+                  int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
                   const int32_t *block_table, int page_size, int max_pages, int num_pages,
                   const int32_t *seq_lens, const double *sink, double *out) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
-    if (layout == ORACLE_RING && mode != ORACLE_SWA) return -1;
+    if (q_len <= 0) return -1;
+    if (layout == ORACLE_RING && (mode != ORACLE_SWA || q_len != 1)) return -1;
     if (layout == ORACLE_PAGED && (!block_table || page_size <= 0 || max_pages < 0)) return -1;
     const int G = Hq / Hkv;
     int bad = 0;
@@ -150,10 +157,10 @@ int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int 
         size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
         size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
-            const int64_t b = r / Hq, h = r % Hq, g = h / G;
+        for (int64_t r = 0; r < (int64_t)B * Hq * q_len; ++r) {
+            const int64_t b = r / ((int64_t)Hq * q_len), h = (r / q_len) % Hq, g = h / G;
             const int64_t nb = seq_lens[b];
-            const int64_t i = nb - 1;
+            const int64_t i = nb - q_len + r % q_len; /* this query's position */
             const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
             int n = 0;
             int local_bad = 0;
@@ -175,7 +182,7 @@ int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int 
                 bad = 1;
                 continue;
             }
-            attend_row(dtype, q, (size_t)((b * Hq + h) * dqk), k, v, ki, vi, n, dqk, dv, scale,
+            attend_row(dtype, q, (size_t)r * dqk, k, v, ki, vi, n, dqk, dv, scale,
                        sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
         }
         free(a);

@@ -286,8 +286,40 @@ def pin_decode_mixed_lengths(lib):
         _close(got[b], pre[b, :, lens[b] - 1], 1e-12, 1e-14, f"mixed b={b}")
 
 
+def pin_decode_multi_matches_prefill(lib):
+    """q_len new tokens per sequence (the parallel verification of drafted tokens, deep-dive
+    CH 4.4) equal the last q_len rows of the prefill over the same sequence; positions below
+    0 (n < q_len) give zero rows; q_len = 1 with a 4-D query equals the 3-D decode."""
+    from attention_sink_softmax_amd import inputs
+
+    B, Hq, Hkv, dqk, dv, L = 3, 4, 2, 16, 8, 70
+    q = _rand((B, Hq, L, dqk), 700)
+    k = _rand((B, Hkv, L, dqk), 701)
+    v = _rand((B, Hkv, L, dv), 702)
+    sink = np.array([3.0, 0.5, 1.5, 6.0])
+    for mode, W in ((oracle.SWA, 5), (oracle.GLOBAL, 0)):
+        pre = oracle.prefill(q, k, v, sink, mode, W, 0.3, lib=lib)
+        for q_len in (1, 2, 4, 7):
+            lens = np.array([70, 3, 41], np.int32)
+            kp, vp, bt = inputs.pages_from_sequence(k, v, L, 8, 40, 9, True)
+            qm = np.zeros((B, Hq, q_len, dqk), np.float32)
+            want = np.zeros((B, Hq, q_len, dv))
+            for b in range(B):
+                for t in range(q_len):
+                    i = int(lens[b]) - q_len + t
+                    if i >= 0:
+                        qm[b, :, t] = q[b, :, i]
+                        want[b, :, t] = pre[b, :, i]
+            got = oracle.decode(qm, kp, vp, lens, sink, mode, W, 0.3, oracle.PAGED, bt, lib=lib)
+            _close(got, want, 1e-12, 1e-14, f"multi mode={mode} q_len={q_len}")
+            if q_len == 1:
+                got3 = oracle.decode(qm[:, :, 0], kp, vp, lens, sink, mode, W, 0.3, oracle.PAGED, bt, lib=lib)
+                assert np.array_equal(got3, got[:, :, 0]), "q_len = 1 differs from one-token decode"
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
+    pin_decode_multi_matches_prefill,
 ]

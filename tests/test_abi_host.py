@@ -116,6 +116,45 @@ def test_decode_argument_errors(L):
     assert decode(L, d=dims(B=0, hq=64, hkv=4), q=None, out=None) == OK
 
 
+def decode_multi(L, q_len=4, mode=0, window=0, d=None, q=A, desc=None, lens=A, maxlen=262144, sink=None, out=A,
+                 ws=A, wsb=1 << 30):
+    d = d or dims(B=8, hq=64, hkv=4)
+    desc = desc if desc is not None else kv()
+    return L.sinkattn_decode_multi(mode, window, ctypes.byref(d), q_len, q, ctypes.byref(desc), lens, maxlen, sink,
+                                   out, ws, wsb, None)
+
+
+def test_decode_multi_argument_errors(L):
+    assert decode_multi(L, q_len=0) == E_SHAPE
+    assert decode_multi(L, q_len=-3) == E_SHAPE
+    assert decode_multi(L, q_len=257) == E_SHAPE
+    # a ring keeps only the last W keys, which the earlier drafted tokens would need to go past
+    assert decode_multi(L, q_len=2, mode=1, window=128, desc=kv(layout=0)) == E_UNSUP
+    assert decode_multi(L, q_len=1, mode=0, desc=kv(layout=0)) == E_UNSUP
+    assert decode_multi(L, maxlen=262145) == E_SHAPE
+    assert decode_multi(L, q=None) == E_NULL
+    assert decode_multi(L, out=A + 2) == E_ALIGN
+    assert decode_multi(L, ws=None) == E_WS
+    assert decode_multi(L, wsb=100) == E_WS
+    assert L.sinkattn_decode_multi(0, 0, ctypes.byref(dims()), 4, A, None, A, 1, None, A, A, 0, None) == E_NULL
+    assert decode_multi(L, d=dims(B=0, hq=64, hkv=4), q=None, out=None) == OK
+
+
+def test_decode_multi_workspace_plan(L):
+    # q_len = 1 plans exactly as one-token decode
+    for args in ((0, 0, 8, 64, 4, 262144), (1, 128, 128, 64, 8, 65536), (0, 0, 1, 64, 4, 5000)):
+        assert sa.sinkattn_decode_multi_workspace_bytes(*args[:5], 1, args[5]) == \
+            sa.sinkattn_decode_workspace_bytes(*args)
+    # 256K global, four drafted tokens: one workgroup covers all 16 heads x 4 tokens of a KV
+    # head, so the split is the same 64 x 4096 keys and the partials grow by q_len
+    assert sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 4, 262144) == 8 * 64 * 4 * 64 * 132 * 4
+    assert sa.sinkattn_decode_multi_workspace_bytes(1, 128, 128, 64, 8, 4, 65536) == 0
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 0, 262144)
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 257, 262144)
+
+
 def test_prefill_workspace_size(L):
     # a transposed copy of V, rows padded to 64 keys
     assert sa.sinkattn_prefill_workspace_bytes(1, 32768, 64, 8) == 8 * 128 * 32768 * 2

@@ -26,7 +26,12 @@ MUTATIONS = {
     "max without the row logits": ("if (a[t] > m) m = a[t];", ""),
     "ring slot off by one": ("const int64_t slot = j % window;", "const int64_t slot = (j + 1) % window;"),
     "page offset from the wrong end": ("const int64_t off = j % page_size;", "const int64_t off = page_size - 1 - j % page_size;"),
-    "decode query position off by one": ("const int64_t i = nb - 1;", "const int64_t i = nb - 2;"),
+    "decode query position off by one": ("const int64_t i = nb - q_len + r % q_len;",
+                                         "const int64_t i = nb - q_len + r % q_len - 1;"),
+    "drafted tokens all at the last position": ("const int64_t i = nb - q_len + r % q_len;",
+                                                "const int64_t i = nb - 1 + 0 * (r % q_len);"),
+    "drafted tokens in reverse order": ("const int64_t i = nb - q_len + r % q_len;",
+                                       "const int64_t i = nb - 1 - r % q_len;"),
     "value row from the query position": ("vi[n] = (size_t)(((b * Hkv + g) * L + j) * dv);",
                                           "vi[n] = (size_t)(((b * Hkv + g) * L + i) * dv);"),
 }
