@@ -89,29 +89,44 @@ struct WaveCtx {
 // fetches row 16rg + (l & 15), chunk 4cg + (l >> 4) (four lanes read 64 contiguous bytes of
 // each of 16 rows).  Rows past the sequence end are clamped to the last row (their scores
 // are masked).
-__device__ __forceinline__ void dma_k_block(char *Kt, const char *kbytes, int kb, int L, int blk, int lane) {
+// The loads go through buffer resources (one per K or V^T region of a (batch, KV head)):
+// a buffer load into LDS counts only towards vmcnt, so the LDS operand reads that overlap
+// it can wait for each other one at a time (lgkmcnt(n)); a global load into LDS would make
+// every such wait a wait for all of them.  An offset past the region reads zeros.
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t k, vt;
+};
+__device__ __forceinline__ TileSrc tile_src(const PrefillParams &p, int b, int kvh) {
+    constexpr int kRawDword3 = 0x00020000;  // untyped 32-bit data, no swizzle
+    TileSrc t;
+    t.k = __builtin_amdgcn_make_buffer_rsrc((void *)(p.k + ((size_t)b * p.Hkv + kvh) * p.L * kDqk), 0,
+                                            p.L * (kDqk * 2), kRawDword3);
+    t.vt = __builtin_amdgcn_make_buffer_rsrc((void *)(p.vt + ((size_t)b * p.Hkv + kvh) * kDv * p.lpad), 0,
+                                             p.lpad * (kDv * 2), kRawDword3);
+    return t;
+}
+__device__ __forceinline__ void dma_k_block(char *Kt, const TileSrc &src, int kb, int L, int blk, int lane) {
     const int rg = blk / 6, cg = blk % 6;
     const int row = min(kb + 16 * rg + (lane & 15), L - 1);
-    __builtin_amdgcn_global_load_lds(kbytes + (uint32_t)(row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16),
-                                     (lds_void *)(Kt + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(Kt + blk * 1024), 16,
+                                             row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16, 0, 0, 0);
 }
 // V^T tile (keys kb..kb+63) -> LDS.  The transposed copy is stored tile by tile, each tile a
 // contiguous 16 KB block [128 dv][64 keys], so a tile load touches one small address range.
 // Block blk (0..15) = (rg, kg); lane l fetches dv row 16rg + (l & 15), key chunk
 // 4kg + (l >> 4).
-__device__ __forceinline__ void dma_vt_block(char *Vt, const char *vtbytes, int kb, int blk, int lane) {
+__device__ __forceinline__ void dma_vt_block(char *Vt, const TileSrc &src, int kb, int blk, int lane) {
     const int rg = blk >> 1, kg = blk & 1;
     const int row = 16 * rg + (lane & 15);
-    __builtin_amdgcn_global_load_lds(vtbytes + (uint32_t)(kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16),
-                                     (lds_void *)(Vt + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.vt, (lds_void *)(Vt + blk * 1024), 16,
+                                             kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16, 0, 0, 0);
 }
 // Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile (10 per wave).
-__device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const char *kbytes, const char *vtbytes, int kb, int L,
-                                           int wave, int lane) {
+__device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const TileSrc &src, int kb, int L, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) dma_k_block(Kt, kbytes, kb, L, wave + 4 * i, lane);
+    for (int i = 0; i < 6; ++i) dma_k_block(Kt, src, kb, L, wave + 4 * i, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_vt_block(Vt, vtbytes, kb, wave + 4 * i, lane);
+    for (int i = 0; i < 4; ++i) dma_vt_block(Vt, src, kb, wave + 4 * i, lane);
 }
 
 // ---- the four steps of a 32-key sub-block (keys kb + 32sb .. +31) for one wave
@@ -393,19 +408,18 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
     f32x16 acc[HPW][4];
     init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
 
-    const char *kbytes = reinterpret_cast<const char *>(p.k + ((size_t)ws.b * p.Hkv + ws.kvh) * p.L * kDqk);
-    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)ws.b * p.Hkv + ws.kvh) * kDv * p.lpad);
+    const TileSrc src = tile_src(p, ws.b, ws.kvh);
     const int k_lo = p.swa ? max(0, ws.wg_q0 - p.window + 1) : 0;
     const int t0 = k_lo / kBN, t1 = (ws.wg_q1 - 1) / kBN;
 
-    issue_tile(KA, VA, kbytes, vtbytes, t0 * kBN, p.L, wave, lane);
+    issue_tile(KA, VA, src, t0 * kBN, p.L, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     // Tile kt from (Kc, Vc) while tile kt+1 streams into (Kn, Vn).
     auto step = [&](int kt, const char *Kc, const char *Vc, char *Kn, char *Vn) {
         const bool more = kt < t1;
-        if (more) issue_tile(Kn, Vn, kbytes, vtbytes, (kt + 1) * kBN, p.L, wave, lane);
+        if (more) issue_tile(Kn, Vn, src, (kt + 1) * kBN, p.L, wave, lane);
         if (wave_live) compute_tile<HPW>(Kc, Vc, kt * kBN, qf, acc, m_run, l_run, w);
         if (more) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 has landed
         __syncthreads();
@@ -437,13 +451,13 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 constexpr int kCausalWaves = 8;
 
 // Wave w of the causal kernel issues blocks w, w+8, ... of the 24 K and 16 V^T blocks.
-__device__ __forceinline__ void dma_k_part(char *Kt, const char *kbytes, int kb, int L, int wave, int lane) {
+__device__ __forceinline__ void dma_k_part(char *Kt, const TileSrc &src, int kb, int L, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) dma_k_block(Kt, kbytes, kb, L, wave + kCausalWaves * i, lane);
+    for (int i = 0; i < 3; ++i) dma_k_block(Kt, src, kb, L, wave + kCausalWaves * i, lane);
 }
-__device__ __forceinline__ void dma_vt_part(char *Vt, const char *vtbytes, int kb, int wave, int lane) {
+__device__ __forceinline__ void dma_vt_part(char *Vt, const TileSrc &src, int kb, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma_vt_block(Vt, vtbytes, kb, wave + kCausalWaves * i, lane);
+    for (int i = 0; i < 2; ++i) dma_vt_block(Vt, src, kb, wave + kCausalWaves * i, lane);
 }
 
 __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(PrefillParams p) {
@@ -468,18 +482,17 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     f32x16 acc[HPW][4];
     init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
 
-    const char *kbytes = reinterpret_cast<const char *>(p.k + ((size_t)ws.b * p.Hkv + ws.kvh) * p.L * kDqk);
-    const char *vtbytes = reinterpret_cast<const char *>(p.vt + ((size_t)ws.b * p.Hkv + ws.kvh) * kDv * p.lpad);
+    const TileSrc src = tile_src(p, ws.b, ws.kvh);
     const int t1 = (ws.wg_q1 - 1) / kBN;  // tiles 0..t1
 
     // a sub-block needs masking when its last key lies past the first query row
     auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
 
-    dma_k_part(K0, kbytes, 0, p.L, wave, lane);
-    dma_vt_part(V0, vtbytes, 0, wave, lane);
+    dma_k_part(K0, src, 0, p.L, wave, lane);
+    dma_vt_part(V0, src, 0, wave, lane);
     if (t1 >= 1) {
-        dma_k_part(K1, kbytes, kBN, p.L, wave, lane);
-        dma_vt_part(V1, vtbytes, kBN, wave, lane);
+        dma_k_part(K1, src, kBN, p.L, wave, lane);
+        dma_vt_part(V1, src, kBN, wave, lane);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -513,12 +526,12 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
         // are unused after the last tile)
         qk_scores<HPW>(Kn, 0, qf, s0, w);
         probs<HPW>(s1, m_run, l_run, pf, w);
-        dma_k_part(Kf, kbytes, kb_next, p.L, wave, lane);
+        dma_k_part(Kf, src, kb_next, p.L, wave, lane);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
         // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
         pv_accum<HPW>(Vc, 1, pf, acc, w);
         grow = row_max<HPW>(s0, m_run, mnew, w);
-        dma_vt_part(Vf, vtbytes, kb_next, wave, lane);
+        dma_vt_part(Vf, src, kb_next, wave, lane);
         if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
     };
     for (int t = 0; t <= t1; t += 3) {
