@@ -52,7 +52,8 @@ class KVDesc(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
-EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_decode",
+EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_prefill_chunk",
+           "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
            "sinkattn_status_string")
 
@@ -73,6 +74,11 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_prefill.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P, ctypes.c_size_t, P]
     L.sinkattn_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.sinkattn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+    L.sinkattn_prefill_chunk.restype = I
+    L.sinkattn_prefill_chunk.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    L.sinkattn_prefill_chunk_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_prefill_chunk_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
     L.sinkattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.sinkattn_decode_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
     L.sinkattn_decode.restype = I
@@ -162,6 +168,44 @@ def sinkattn_prefill(mode: int, window: int, q, k, v, sink, out, workspace, scal
     with torch.cuda.device(q.device):
         rc = lib().sinkattn_prefill(mode, window, ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out),
                                     ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def sinkattn_prefill_chunk_workspace_bytes(batch: int, seqlen: int, hq: int, hkv: int, kv_len: int,
+                                           d_qk: int = D_QK, d_v: int = D_V) -> int:
+    d = Dims(batch, seqlen, hq, hkv, d_qk, d_v, d_qk ** -0.5)
+    n = lib().sinkattn_prefill_chunk_workspace_bytes(ctypes.byref(d), kv_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise SinkAttnError(2, "invalid sizes")
+    return n
+
+
+def sinkattn_prefill_chunk(mode: int, window: int, q, k, v, sink, out, workspace, scale: float | None = None,
+                           stream=None) -> None:
+    """Chunked prefill: q bf16 [B,Hq,Lq,192] holds positions kv_len-Lq .. kv_len-1; k bf16
+    [B,Hkv,kv_len,192] and v bf16 [B,Hkv,kv_len,128] hold the prefix and the chunk; out bf16
+    [B,Hq,Lq,128]; workspace of at least sinkattn_prefill_chunk_workspace_bytes(...) bytes."""
+    import torch
+
+    B, Hq, Lq, dqk = q.shape
+    Hkv, kv_len = k.shape[1], k.shape[2]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(k, "k", torch.bfloat16, (B, Hkv, kv_len, dqk))
+    _dev_tensor(v, "v", torch.bfloat16, (B, Hkv, kv_len, v.shape[3]))
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, Lq, v.shape[3]))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    for t in (k, v, out, sink, workspace):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    d = Dims(B, Lq, Hq, Hkv, dqk, v.shape[3], dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_prefill_chunk(mode, window, ctypes.byref(d), kv_len, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(sink), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
     _raise(rc)
 
 
@@ -273,6 +317,19 @@ def prefill(mode: int, window: int, q, k, v, sink=None, scale: float | None = No
     if workspace is None:
         workspace = prefill_workspace(q, k)
     sinkattn_prefill(mode, window, q, k, v, sink, out, workspace, scale, stream)
+    return out
+
+
+def prefill_chunk(mode: int, window: int, q, k, v, sink=None, scale: float | None = None, stream=None,
+                  workspace=None):
+    """Allocate out (and the workspace if none is given) and run sinkattn_prefill_chunk."""
+    import torch
+
+    out = torch.empty((*q.shape[:3], v.shape[3]), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        n = sinkattn_prefill_chunk_workspace_bytes(q.shape[0], q.shape[2], q.shape[1], k.shape[1], k.shape[2])
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    sinkattn_prefill_chunk(mode, window, q, k, v, sink, out, workspace, scale, stream)
     return out
 
 

@@ -91,17 +91,29 @@ size_t sinkattn_prefill_workspace_bytes(const sinkattn_dims *d) {
     return prefill_workspace_bytes(d->batch, d->hkv, d->seqlen);
 }
 
+size_t sinkattn_prefill_chunk_workspace_bytes(const sinkattn_dims *d, int32_t kv_len) {
+    if (!d || d->batch < 0 || d->seqlen < 0 || d->hkv <= 0 || kv_len < d->seqlen) return (size_t)-1;
+    return prefill_workspace_bytes(d->batch, d->hkv, kv_len);
+}
+
 int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q, const void *k, const void *v,
                      const float *sink, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return sinkattn_prefill_chunk(mode, window, d, d ? d->seqlen : 0, q, k, v, sink, out, workspace,
+                                  workspace_bytes, stream);
+}
+
+int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t kv_len, const void *q,
+                           const void *k, const void *v, const float *sink, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     int st = check_dims(mode, window, d);
     if (st) return st;
-    if (d->seqlen < 0) return SINKATTN_E_SHAPE;
-    if ((int64_t)d->seqlen * kDqkSupported * 2 > INT32_MAX) return SINKATTN_E_SHAPE;  // 32-bit row offsets
+    if (d->seqlen < 0 || kv_len < d->seqlen) return SINKATTN_E_SHAPE;
+    if ((int64_t)kv_len * kDqkSupported * 2 > INT32_MAX) return SINKATTN_E_SHAPE;  // 32-bit row offsets
     if (d->batch == 0 || d->seqlen == 0) return SINKATTN_OK;
     if (!q || !k || !v || !out) return SINKATTN_E_NULL;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (sink && misaligned(sink)))
         return SINKATTN_E_ALIGN;
-    const size_t need = prefill_workspace_bytes(d->batch, d->hkv, d->seqlen);
+    const size_t need = prefill_workspace_bytes(d->batch, d->hkv, kv_len);
     if (!workspace || workspace_bytes < need) return SINKATTN_E_WORKSPACE;
     if (misaligned(workspace)) return SINKATTN_E_ALIGN;
 
@@ -112,9 +124,11 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
     p.sink = sink;
     p.out = static_cast<uint16_t *>(out);
     p.vt = static_cast<uint16_t *>(workspace);
-    p.lpad = (d->seqlen + 63) / 64 * 64;
+    p.lpad = (kv_len + 63) / 64 * 64;
     p.B = d->batch;
-    p.L = d->seqlen;
+    p.L = kv_len;
+    p.Lq = d->seqlen;
+    p.q0 = kv_len - d->seqlen;
     p.Hq = d->hq;
     p.Hkv = d->hkv;
     p.G = d->hq / d->hkv;

@@ -12,7 +12,8 @@ struct PrefillParams {
     int lpad;          // L rounded up to a multiple of 64
     const float *sink;  // [Hq] or nullptr
     uint16_t *out;
-    int B, L, Hq, Hkv, G;
+    int B, L, Hq, Hkv, G;  // L: keys per sequence (positions 0..L-1)
+    int Lq, q0;            // query rows in q and out, at positions q0 .. q0 + Lq - 1 (q0 = L - Lq)
     int swa, window;
     float scale_log2;  // logit scale * log2(e)
     // work layout, filled by plan_prefill

@@ -306,20 +306,21 @@ __device__ __forceinline__ WaveSetup wave_setup(const PrefillParams &p, int wave
     const int pbw = p.n_pbw - 1 - t;
     const int wh = p.hw / HPW;  // waves along heads
     ws.h0 = ws.kvh * p.G + hg * p.hw + (wave % wh) * HPW;
-    ws.qpos0 = (pbw * p.pw + wave / wh) * kBQ;
-    ws.wg_q0 = pbw * p.pw * kBQ;
+    ws.qpos0 = p.q0 + (pbw * p.pw + wave / wh) * kBQ;
+    ws.wg_q0 = p.q0 + pbw * p.pw * kBQ;
     ws.wg_q1 = min(p.L, ws.wg_q0 + p.pw * kBQ);
     return ws;
 }
 
-// Q^T fragments (B operand): lane supplies q[h][qi][16kk + 8g .. +8]; rows past L are 0.
+// Q^T fragments (B operand): lane supplies row qi - q0 of q[h], elements 16kk + 8g .. +8;
+// positions past L give zeros.
 template <int HPW>
 __device__ __forceinline__ void load_q(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
                                        bf16x8 (&qf)[HPW][12]) {
     const bool ok = w.qi < p.L;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-        const uint16_t *qrow = p.q + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.L) + (ok ? w.qi : 0)) * kDqk + 8 * w.g;
+        const uint16_t *qrow = p.q + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq) + (ok ? w.qi - p.q0 : 0)) * kDqk + 8 * w.g;
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0});
     }
@@ -343,7 +344,7 @@ __device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSet
     }
 }
 
-// O = acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi.
+// O = acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi (row qi - q0).
 template <int HPW>
 __device__ __forceinline__ void store_out(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w, bool live,
                                           const f32x16 (&acc)[HPW][4], const float (&l_run)[HPW],
@@ -353,7 +354,7 @@ __device__ __forceinline__ void store_out(const PrefillParams &p, const WaveSetu
         const float lt = sum_xor32(l_run[h]);
         if (!live || w.qi >= p.L) continue;
         const float inv = 1.f / lt;
-        uint16_t *orow = p.out + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.L) + w.qi) * kDv + 4 * w.g;
+        uint16_t *orow = p.out + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq) + (w.qi - p.q0)) * kDv + 4 * w.g;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -599,7 +600,7 @@ int64_t plan_prefill(PrefillParams &p) {
         while (p.hw * 2 <= 4 * p.hpw && p.G % (p.hw * 2) == 0) p.hw *= 2;
         p.pw = 4 * p.hpw / p.hw;
     }
-    const int64_t npb = (p.L + 31) / 32;
+    const int64_t npb = (p.Lq + 31) / 32;
     p.n_pbw = (int)((npb + p.pw - 1) / p.pw);
     p.hgroups = p.G / p.hw;
     const int64_t items = (int64_t)p.n_pbw * p.B * p.Hkv * p.hgroups;

@@ -121,6 +121,34 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
                      size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace sinkattn_prefill_chunk needs: the transposed copy of V over all
+ * kv_len keys, 2 * batch * hkv * 128 * roundup(kv_len, 64) bytes (batch, seqlen, hkv are
+ * read; seqlen <= kv_len).  Returns (size_t)-1 for invalid sizes.
+ */
+size_t sinkattn_prefill_chunk_workspace_bytes(const sinkattn_dims *d, int32_t kv_len);
+
+/*
+ * Chunked prefill over a cached prefix: the last d->seqlen positions of sequences that are
+ * kv_len tokens long.  The serving set-up on the model card ("MiMo-V2-Flash-Base", SGLang
+ * quick start) prefills long prompts in chunks of 16384 tokens; each chunk's queries attend
+ * to the keys of the earlier chunks and causally within the chunk, which is the prefill
+ * definition above restricted to rows kv_len - seqlen .. kv_len - 1.
+ *   d         sizes as for sinkattn_prefill; d->seqlen = Lq, the new tokens (0 <= Lq <= kv_len)
+ *   kv_len    keys per sequence, the prefix and the chunk together; kv_len * 384 < 2^31
+ *   q         bf16 [batch][hq][Lq][d_qk]: query row r is position kv_len - Lq + r
+ *   k         bf16 [batch][hkv][kv_len][d_qk]
+ *   v         bf16 [batch][hkv][kv_len][d_v]
+ *   sink      float32 [hq], or NULL
+ *   out       bf16 [batch][hq][Lq][d_v]
+ *   workspace at least sinkattn_prefill_chunk_workspace_bytes(d, kv_len) bytes
+ * With kv_len == d->seqlen this is sinkattn_prefill.  Errors as sinkattn_prefill; kv_len <
+ * d->seqlen is SINKATTN_E_SHAPE.
+ */
+int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t kv_len,
+                           const void *q, const void *k, const void *v, const float *sink,
+                           void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace sinkattn_decode needs for these arguments (0 when none).
  * max_seq_len is the host-side upper bound on seq_lens used to plan the key splits; pass
  * the same value to sinkattn_decode.  Returns (size_t)-1 for invalid sizes.

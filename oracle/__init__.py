@@ -52,6 +52,9 @@ def load(path: str = LIB):
     lib.oracle_prefill.restype = I
     lib.oracle_prefill.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P,
                                    ctypes.c_int64, P, P]
+    lib.oracle_prefill_chunk.restype = I
+    lib.oracle_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, ctypes.c_int64, P,
+                                         P]
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
                                   P, P, P]
@@ -100,6 +103,31 @@ def prefill(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=
                             _ptr(va), _ptr(s), n, _ptr(rp), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments")
+    return out
+
+
+def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=None) -> np.ndarray:
+    """Chunked prefill: q [B,Hq,Lq,dqk] holds positions Lk-Lq .. Lk-1 of sequences whose keys
+    and values k [B,Hkv,Lk,dqk], v [B,Hkv,Lk,dv] cover positions 0 .. Lk-1.  rows: optional
+    (b, h, r) triplets (r = chunk row).  Returns float64 [B,Hq,Lq,dv] or [nrows,dv]."""
+    lib = lib or load()
+    qa, dt = _arr(q, None)
+    ka, _ = _arr(k, None)
+    va, _ = _arr(v, None)
+    B, Hq, Lq, dqk = qa.shape
+    Hkv, Lk, dv = ka.shape[1], ka.shape[2], va.shape[3]
+    s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    if rows is None:
+        rp, n = None, 0
+        out = np.empty((B, Hq, Lq, dv), np.float64)
+    else:
+        rp = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rp.shape[0]
+        out = np.empty((n, dv), np.float64)
+    rc = lib.oracle_prefill_chunk(mode, window, B, Lq, Lk, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka), _ptr(va),
+                                  _ptr(s), n, _ptr(rp), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prefill_chunk rejected its arguments")
     return out
 
 

@@ -75,40 +75,60 @@ static void attend_row(int dtype, const void *q, size_t qrow, const void *k, con
  * rows == NULL: out [B][Hq][L][dv].  Otherwise rows holds nrows triplets (b, h, i) and
  * out is [nrows][dv].  Returns 0, or -1 on bad arguments.
  */
+int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, int Hkv, int dqk, int dv,
+                         double scale, int dtype, const void *q, const void *k, const void *v,
+                         const double *sink, int64_t nrows, const int64_t *rows, double *out);
+
 int oracle_prefill(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv,
                    double scale, int dtype, const void *q, const void *k, const void *v,
                    const double *sink, int64_t nrows, const int64_t *rows, double *out) {
-    if (B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
+    /* every position is a query: the chunk that is the whole sequence */
+    return oracle_prefill_chunk(mode, window, B, L, L, Hq, Hkv, dqk, dv, scale, dtype, q, k, v, sink, nrows, rows,
+                                out);
+}
+
+/*
+ * Chunked prefill over a cached prefix: the rows of the prefill definition at positions
+ * Lk - Lq .. Lk - 1 of sequences of Lk tokens (the model card's serving set-up prefills long
+ * prompts in chunks).  q [B][Hq][Lq][dqk] (row r is position Lk - Lq + r), k [B][Hkv][Lk][dqk],
+ * v [B][Hkv][Lk][dv].  rows == NULL: out [B][Hq][Lq][dv]; else nrows triplets (b, h, r) and
+ * out [nrows][dv].  Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, int Hkv, int dqk, int dv,
+                         double scale, int dtype, const void *q, const void *k, const void *v,
+                         const double *sink, int64_t nrows, const int64_t *rows, double *out) {
+    if (B < 0 || Lq < 0 || Lk < Lq || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
     if (mode != ORACLE_SWA && mode != ORACLE_GLOBAL) return -1;
     const int G = Hq / Hkv;
-    const int64_t total = rows ? nrows : (int64_t)B * Hq * L;
+    const int64_t total = rows ? nrows : (int64_t)B * Hq * Lq;
 #pragma omp parallel
     {
-        double *a = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-        size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)(L > 0 ? L : 1));
-        size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)(L > 0 ? L : 1));
+        double *a = (double *)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+        size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)(Lk > 0 ? Lk : 1));
+        size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)(Lk > 0 ? Lk : 1));
 #pragma omp for schedule(dynamic, 16)
-        for (int64_t r = 0; r < total; ++r) {
-            int64_t b, h, i;
+        for (int64_t n = 0; n < total; ++n) {
+            int64_t b, h, r;
             if (rows) {
-                b = rows[3 * r];
-                h = rows[3 * r + 1];
-                i = rows[3 * r + 2];
+                b = rows[3 * n];
+                h = rows[3 * n + 1];
+                r = rows[3 * n + 2];
             } else {
-                b = r / ((int64_t)Hq * L);
-                h = (r / L) % Hq;
-                i = r % L;
+                b = n / ((int64_t)Hq * Lq);
+                h = (n / Lq) % Hq;
+                r = n % Lq;
             }
+            const int64_t i = (int64_t)Lk - Lq + r; /* position of this query */
             const int64_t g = h / G;
             const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
-            int n = 0;
-            for (int64_t j = jlo; j <= i; ++j, ++n) {
-                ki[n] = (size_t)(((b * Hkv + g) * L + j) * dqk);
-                vi[n] = (size_t)(((b * Hkv + g) * L + j) * dv);
+            int cnt = 0;
+            for (int64_t j = jlo; j <= i; ++j, ++cnt) {
+                ki[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dqk);
+                vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);
             }
-            attend_row(dtype, q, (size_t)(((b * Hq + h) * L + i) * dqk), k, v, ki, vi, n, dqk, dv,
-                       scale, sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+            attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), k, v, ki, vi, cnt, dqk, dv, scale,
+                       sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)n * dv);
         }
         free(a);
         free(ki);

@@ -317,9 +317,27 @@ def pin_decode_multi_matches_prefill(lib):
                 assert np.array_equal(got3, got[:, :, 0]), "q_len = 1 differs from one-token decode"
 
 
+def pin_prefill_chunk_is_prefill_rows(lib):
+    """A chunk of Lq new tokens after a prefix of Lk - Lq tokens gives exactly the prefill rows
+    Lk - Lq .. Lk - 1 of the whole sequence (model card serving set-up: chunked prefill)."""
+    B, Hq, Hkv, dqk, dv, Lk = 2, 4, 2, 16, 8, 90
+    q = _rand((B, Hq, Lk, dqk), 800)
+    k = _rand((B, Hkv, Lk, dqk), 801)
+    v = _rand((B, Hkv, Lk, dv), 802)
+    sink = np.array([2.0, 0.0, 4.0, 1.0])
+    for mode, W in ((oracle.SWA, 7), (oracle.GLOBAL, 0)):
+        pre = oracle.prefill(q, k, v, sink, mode, W, 0.3, lib=lib)
+        for Lq in (1, 13, 64, 90):
+            qc = np.ascontiguousarray(q[:, :, Lk - Lq:])
+            got = oracle.prefill_chunk(qc, k, v, sink, mode, W, 0.3, lib=lib)
+            assert np.array_equal(got, pre[:, :, Lk - Lq:]), f"chunk mode={mode} Lq={Lq}"
+        got = oracle.prefill_chunk(np.ascontiguousarray(q[:, :, :0]), k, v, sink, mode, W, 0.3, lib=lib)
+        assert got.shape == (B, Hq, 0, dv)
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
-    pin_decode_multi_matches_prefill,
+    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows,
 ]

@@ -155,6 +155,26 @@ def test_decode_multi_workspace_plan(L):
         sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 257, 262144)
 
 
+def test_prefill_chunk_argument_errors(L):
+    def chunk(kv_len, d=None, ws=A, wsb=1 << 40, q=A):
+        d = d or dims(Lq=64)
+        return L.sinkattn_prefill_chunk(1, 128, ctypes.byref(d), kv_len, q, A, A, None, A, ws, wsb, None)
+    assert chunk(63) == E_SHAPE                   # fewer keys than new tokens
+    assert chunk(6_000_000) == E_SHAPE            # 32-bit row offsets over the keys
+    assert chunk(100_000, wsb=1000) == E_WS       # the V^T copy covers every key
+    assert chunk(100_000, q=None) == E_NULL
+    assert chunk(100_000, d=dims(Lq=0), q=None) == OK
+    assert L.sinkattn_prefill_chunk(1, 128, None, 10, A, A, A, None, A, A, 1 << 40, None) == E_NULL
+
+
+def test_prefill_chunk_workspace_size(L):
+    assert sa.sinkattn_prefill_chunk_workspace_bytes(1, 16384, 64, 4, 32768) == 4 * 128 * 32768 * 2
+    assert sa.sinkattn_prefill_chunk_workspace_bytes(2, 1, 4, 1, 65) == 2 * 128 * 128 * 2
+    assert sa.sinkattn_prefill_chunk_workspace_bytes(1, 100, 4, 1, 100) == sa.sinkattn_prefill_workspace_bytes(1, 100, 4, 1)
+    with pytest.raises(sa.SinkAttnError):
+        sa.sinkattn_prefill_chunk_workspace_bytes(1, 101, 4, 1, 100)
+
+
 def test_prefill_workspace_size(L):
     # a transposed copy of V, rows padded to 64 keys
     assert sa.sinkattn_prefill_workspace_bytes(1, 32768, 64, 8) == 8 * 128 * 32768 * 2

@@ -16,10 +16,10 @@ MUTATIONS = {
                                            "sink *= scale; double m = has_sink ? sink : -INFINITY;"),
     "sink given a unit value": ("if (n == 0 || isinf(m)) return;",
                                 "if (n == 0 || isinf(m)) return; if (has_sink) out[0] += 0.0 + exp(sink - m) / (exp(sink - m) + 1.0) * 0.5;"),
-    "window one key too wide": ("(i - window + 1 > 0 ? i - window + 1 : 0) : 0;\n            int n = 0;\n            for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv",
-                                "(i - window > 0 ? i - window : 0) : 0;\n            int n = 0;\n            for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv"),
-    "causal mask excludes self": ("for (int64_t j = jlo; j <= i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv",
-                                  "for (int64_t j = jlo; j < i; ++j, ++n) {\n                ki[n] = (size_t)(((b * Hkv"),
+    "window one key too wide": ("(i - window + 1 > 0 ? i - window + 1 : 0) : 0;\n            int cnt = 0;",
+                                "(i - window > 0 ? i - window : 0) : 0;\n            int cnt = 0;"),
+    "causal mask excludes self": ("for (int64_t j = jlo; j <= i; ++j, ++cnt) {",
+                                  "for (int64_t j = jlo; j < i; ++j, ++cnt) {"),
     "GQA head interleaved": ("const int64_t g = h / G;\n            const int64_t jlo", "const int64_t g = h % Hkv;\n            const int64_t jlo"),
     "wrong exponent sign": ("double s = exp(a[t] - m) / z;", "double s = exp(m - a[t]) / z;"),
     "logit scale dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
@@ -32,8 +32,10 @@ MUTATIONS = {
                                                 "const int64_t i = nb - 1 + 0 * (r % q_len);"),
     "drafted tokens in reverse order": ("const int64_t i = nb - q_len + r % q_len;",
                                        "const int64_t i = nb - 1 - r % q_len;"),
-    "value row from the query position": ("vi[n] = (size_t)(((b * Hkv + g) * L + j) * dv);",
-                                          "vi[n] = (size_t)(((b * Hkv + g) * L + i) * dv);"),
+    "chunk rows placed at the sequence start": ("const int64_t i = (int64_t)Lk - Lq + r; /* position of this query */",
+                                                "const int64_t i = r;"),
+    "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
+                                          "vi[cnt] = (size_t)(((b * Hkv + g) * Lk + i) * dv);"),
 }
 
 
