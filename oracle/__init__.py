@@ -55,6 +55,11 @@ def load(path: str = LIB):
     lib.oracle_prefill_chunk.restype = I
     lib.oracle_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, ctypes.c_int64, P,
                                          P]
+    lib.oracle_decode_fp8.restype = I
+    lib.oracle_decode_fp8.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, ctypes.c_double,
+                                      ctypes.c_double, P, I, I, I, P, P, P]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
                                   P, P, P]
@@ -132,15 +137,22 @@ def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None
 
 
 def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout: int,
-           block_table=None, lib=None) -> np.ndarray:
+           block_table=None, lib=None, kv_scales=None) -> np.ndarray:
     """q [B,Hq,dqk] (one new token per sequence) or [B,Hq,q_len,dqk] (q_len new tokens at
     positions seq_lens-q_len .. seq_lens-1); RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv];
     PAGED: k [P,Hkv,page,dqk], v [P,Hkv,page,dv] with block_table [B,max_pages].
-    Returns float64 [B,Hq,dv] or [B,Hq,q_len,dv], matching q."""
+    Returns float64 [B,Hq,dv] or [B,Hq,q_len,dv], matching q.
+    uint8 k and v are E4M3 codes of an 8-bit cache; kv_scales = (k_scale, v_scale) then
+    gives the per-tensor scales (element = scale * code value)."""
     lib = lib or load()
     qa, dt = _arr(q, None)
-    ka, _ = _arr(k, None)
-    va, _ = _arr(v, None)
+    fp8 = np.asarray(k).dtype == np.uint8
+    if fp8:
+        ka = np.ascontiguousarray(k, dtype=np.uint8)
+        va = np.ascontiguousarray(v, dtype=np.uint8)
+    else:
+        ka, _ = _arr(k, None)
+        va, _ = _arr(v, None)
     B, Hq, dqk = qa.shape[0], qa.shape[1], qa.shape[-1]
     q_len = qa.shape[2] if qa.ndim == 4 else 1
     Hkv, dv = ka.shape[1], va.shape[3]
@@ -152,11 +164,20 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
     else:
         bt, ps, mp, npg = None, 0, 0, 0
     out = np.empty(qa.shape[:-1] + (dv,), np.float64)
-    rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
-                           _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
+    if fp8:
+        ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
+        rc = lib.oracle_decode_fp8(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
+                                   _ptr(va), ks, vs, _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
+    else:
+        rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
+                               _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return out
+
+
+def e4m3_value(code: int, lib=None) -> float:
+    return (lib or load()).oracle_e4m3_value(code)
 
 
 def threads() -> int:

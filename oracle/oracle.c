@@ -33,11 +33,25 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
 enum { ORACLE_GLOBAL = 0, ORACLE_SWA = 1 };
 enum { ORACLE_RING = 0, ORACLE_PAGED = 1 };
 
+/* OCP 8-bit floating point E4M3 (the "FN" variant: no infinities): sign bit 7, exponent
+ * bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 holds the subnormals m * 2^-9; the
+ * all-ones exponent with mantissa 7 is NaN, every other code is (1 + m/8) * 2^(e - 7).
+ * Largest finite value 448. */
+static double e4m3_value(uint8_t code) {
+    const int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double x;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) x = ldexp((double)m, -9);
+    else x = ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -x : x;
+}
+
 static double load(const void *p, size_t idx, int dtype) {
+    if (dtype == ORACLE_FP8_E4M3) return e4m3_value(((const uint8_t *)p)[idx]);
     if (dtype == ORACLE_BF16) {
         uint32_t u = ((uint32_t)((const uint16_t *)p)[idx]) << 16;
         float f;
@@ -49,15 +63,15 @@ static double load(const void *p, size_t idx, int dtype) {
 
 /* One output row.  qrow: index of q[0] of the row; key j of the visible list lives at
  * kidx[t]*dqk in k and vidx[t]*dv in v.  n keys.  Writes dv doubles to out. */
-static void attend_row(int dtype, const void *q, size_t qrow, const void *k, const void *v,
-                       const size_t *kidx, const size_t *vidx, int n, int dqk, int dv,
-                       double scale, int has_sink, double sink, double *a, double *out) {
+static void attend_row(int dtype, const void *q, size_t qrow, int kvdtype, double kscale, double vscale,
+                       const void *k, const void *v, const size_t *kidx, const size_t *vidx, int n, int dqk,
+                       int dv, double scale, int has_sink, double sink, double *a, double *out) {
     for (int e = 0; e < dv; ++e) out[e] = 0.0;
     if (has_sink && isinf(sink) && sink > 0) return; /* all mass on the sink */
     double m = has_sink ? sink : -INFINITY;
     for (int t = 0; t < n; ++t) {
         double dot = 0.0;
-        for (int d = 0; d < dqk; ++d) dot += load(q, qrow + d, dtype) * load(k, kidx[t] + d, dtype);
+        for (int d = 0; d < dqk; ++d) dot += load(q, qrow + d, dtype) * (kscale * load(k, kidx[t] + d, kvdtype));
         a[t] = scale * dot;
         if (a[t] > m) m = a[t];
     }
@@ -66,7 +80,7 @@ static void attend_row(int dtype, const void *q, size_t qrow, const void *k, con
     for (int t = 0; t < n; ++t) z += exp(a[t] - m);
     for (int t = 0; t < n; ++t) {
         double s = exp(a[t] - m) / z;
-        for (int e = 0; e < dv; ++e) out[e] += s * load(v, vidx[t] + e, dtype);
+        for (int e = 0; e < dv; ++e) out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));
     }
 }
 
@@ -127,7 +141,7 @@ int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, in
                 ki[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dqk);
                 vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);
             }
-            attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), k, v, ki, vi, cnt, dqk, dv, scale,
+            attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), dtype, 1.0, 1.0, k, v, ki, vi, cnt, dqk, dv, scale,
                        sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)n * dv);
         }
         free(a);
@@ -154,10 +168,11 @@ int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, in
  *       offset p mod page_size.
  * Returns 0, or -1 on bad arguments (including a page id outside the pool).
  */
-int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
-                  int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
-                  const int32_t *block_table, int page_size, int max_pages, int num_pages,
-                  const int32_t *seq_lens, const double *sink, double *out) {
+static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
+                       int q_len, double scale, int dtype, const void *q, int kvdtype, double kscale,
+                       double vscale, const void *k, const void *v, const int32_t *block_table,
+                       int page_size, int max_pages, int num_pages, const int32_t *seq_lens,
+                       const double *sink, double *out) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
     if (q_len <= 0) return -1;
@@ -202,7 +217,7 @@ int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int 
                 bad = 1;
                 continue;
             }
-            attend_row(dtype, q, (size_t)r * dqk, k, v, ki, vi, n, dqk, dv, scale,
+            attend_row(dtype, q, (size_t)r * dqk, kvdtype, kscale, vscale, k, v, ki, vi, n, dqk, dv, scale,
                        sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
         }
         free(a);
@@ -211,6 +226,33 @@ int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int 
     }
     return bad ? -1 : 0;
 }
+
+int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
+                  int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
+                  const int32_t *block_table, int page_size, int max_pages, int num_pages,
+                  const int32_t *seq_lens, const double *sink, double *out) {
+    return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, dtype, 1.0, 1.0, k, v,
+                       block_table, page_size, max_pages, num_pages, seq_lens, sink, out);
+}
+
+/*
+ * Decode from a KV cache held in 8-bit floating point (the pages size the cache with one
+ * byte per element: paper notes §3.2): k and v hold E4M3 codes, element values are
+ * kscale * e4m3(code) and vscale * e4m3(code).  Everything else as oracle_decode (q in
+ * `dtype`).  kscale, vscale > 0.
+ */
+int oracle_decode_fp8(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
+                      int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
+                      double kscale, double vscale, const int32_t *block_table, int page_size,
+                      int max_pages, int num_pages, const int32_t *seq_lens, const double *sink,
+                      double *out) {
+    if (!(kscale > 0) || !(vscale > 0)) return -1;
+    return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, ORACLE_FP8_E4M3, kscale,
+                       vscale, k, v, block_table, page_size, max_pages, num_pages, seq_lens, sink, out);
+}
+
+/* The value of one E4M3 code (exported for the tests). */
+double oracle_e4m3_value(int code) { return e4m3_value((uint8_t)code); }
 
 /* Number of OpenMP threads a parallel region would use (reported next to timings). */
 int oracle_threads(void) {

@@ -335,9 +335,50 @@ def pin_prefill_chunk_is_prefill_rows(lib):
         assert got.shape == (B, Hq, 0, dv)
 
 
+def pin_e4m3_codes(lib):
+    """The 8-bit cache format: all 256 E4M3 codes against torch's float8_e4m3fn decoding (a
+    library routine), plus the format's landmarks (largest finite 448, smallest subnormal 2^-9,
+    smallest normal 2^-6, 1.0 and its negative, the two NaN codes)."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        got = oracle.e4m3_value(c, lib=lib)
+        assert (math.isnan(got) and math.isnan(ref[c])) or got == ref[c], f"code {c}: {got} vs {ref[c]}"
+    assert oracle.e4m3_value(0x7E, lib=lib) == 448.0 and oracle.e4m3_value(0xFE, lib=lib) == -448.0
+    assert oracle.e4m3_value(0x01, lib=lib) == 2.0 ** -9 and oracle.e4m3_value(0x08, lib=lib) == 2.0 ** -6
+    assert oracle.e4m3_value(0x38, lib=lib) == 1.0 and oracle.e4m3_value(0xB8, lib=lib) == -1.0
+    assert math.isnan(oracle.e4m3_value(0x7F, lib=lib)) and math.isnan(oracle.e4m3_value(0xFF, lib=lib))
+
+
+def pin_fp8_decode_is_decode_of_values(lib):
+    """Decode from an 8-bit cache equals decode from a float32 cache holding the values the
+    codes stand for (scale * code value, exact in float32 for these scales), both layouts."""
+    from attention_sink_softmax_amd import inputs
+
+    B, Hq, Hkv, dqk, dv, L = 2, 4, 2, 16, 8, 100
+    rng = np.random.default_rng(900)
+    k8 = rng.integers(0, 256, size=(B, Hkv, L, dqk), dtype=np.uint8)
+    v8 = rng.integers(0, 256, size=(B, Hkv, L, dv), dtype=np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    v8[(v8 & 0x7F) == 0x7F] = 0x30
+    dec = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    ks, vs = 0.125, 2.0
+    kf = (dec[k8] * ks).astype(np.float32)
+    vf = (dec[v8] * vs).astype(np.float32)
+    q = _rand((B, Hq, 3, dqk), 901)
+    sink = np.array([1.0, 0.0, 3.0, 2.0])
+    lens = np.array([100, 41], np.int32)
+    for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 9)):
+        kp8, vp8, bt = inputs.pages_from_sequence(k8, v8, L, 16, 20, 5, True)
+        kpf, vpf, _ = inputs.pages_from_sequence(kf, vf, L, 16, 20, 5, True)
+        got = oracle.decode(q, kp8, vp8, lens, sink, mode, W, 0.3, oracle.PAGED, bt, lib=lib, kv_scales=(ks, vs))
+        want = oracle.decode(q, kpf, vpf, lens, sink, mode, W, 0.3, oracle.PAGED, bt, lib=lib)
+        _close(got, want, 1e-12, 1e-14, f"fp8 decode mode={mode}")
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
-    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows,
+    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes,
+    pin_fp8_decode_is_decode_of_values,
 ]

@@ -34,6 +34,10 @@ MUTATIONS = {
                                        "const int64_t i = nb - 1 - r % q_len;"),
     "chunk rows placed at the sequence start": ("const int64_t i = (int64_t)Lk - Lq + r; /* position of this query */",
                                                 "const int64_t i = r;"),
+    "E4M3 exponent bias off by one": ("else x = ldexp(1.0 + m / 8.0, e - 7);", "else x = ldexp(1.0 + m / 8.0, e - 8);"),
+    "E4M3 subnormals without the 2^-9 scale": ("if (e == 0) x = ldexp((double)m, -9);", "if (e == 0) x = ldexp((double)m, -6);"),
+    "cache scale applied to the value twice": ("out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));",
+                                               "out[e] += s * (vscale * vscale * load(v, vidx[t] + e, kvdtype));"),
     "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
                                           "vi[cnt] = (size_t)(((b * Hkv + g) * Lk + i) * dv);"),
 }
