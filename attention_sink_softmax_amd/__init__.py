@@ -54,7 +54,7 @@ class KVDesc(ctypes.Structure):
 
 EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_prefill_chunk",
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_decode",
-           "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
+           "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes", "sinkattn_decode_fp8",
            "sinkattn_status_string")
 
 _lib = None
@@ -89,6 +89,9 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_multi.restype = I
     L.sinkattn_decode_multi.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), P,
                                         ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+    L.sinkattn_decode_fp8.restype = I
+    L.sinkattn_decode_fp8.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), P,
+                                      ctypes.c_int32, P, ctypes.c_float, ctypes.c_float, P, P, ctypes.c_size_t, P]
     L.sinkattn_status_string.restype = ctypes.c_char_p
     L.sinkattn_status_string.argtypes = [I]
     if path == LIB_PATH:
@@ -352,6 +355,59 @@ def decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, m
     sinkattn_decode(mode, window, q, layout, k_cache, v_cache, seq_lens, max_seq_len, sink, out, workspace,
                     block_table, scale, stream)
     return out
+
+
+def sinkattn_decode_fp8(mode: int, window: int, q_len: int, q, k_cache, v_cache, seq_lens, max_seq_len: int, sink,
+                        k_scale: float, v_scale: float, out, workspace, block_table,
+                        scale: float | None = None, stream=None) -> None:
+    """8-bit paged cache: k_cache uint8 [P,Hkv,page,192], v_cache uint8 [P,Hkv,page,128] of
+    E4M3 codes (element = scale * code value), block_table int32 [B,max_pages]; q bf16
+    [B,Hq,q_len,192], out bf16 [B,Hq,q_len,128]; workspace of at least
+    sinkattn_decode_multi_workspace_bytes(...) bytes or None."""
+    import torch
+
+    B, Hq, _, dqk = q.shape
+    P, Hkv, ps, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, q_len, dv))
+    _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    _dev_tensor(k_cache, "k_cache", torch.uint8, (P, Hkv, ps, dqk))
+    _dev_tensor(v_cache, "v_cache", torch.uint8, (P, Hkv, ps, dv))
+    _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
+    desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps, block_table.shape[1], P)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    for t in (k_cache, v_cache, out, seq_lens, sink, block_table, workspace):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode_fp8(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
+                                       _ptr(seq_lens), max_seq_len, _ptr(sink), k_scale, v_scale, _ptr(out), ws_ptr,
+                                       ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def decode_fp8(mode: int, window: int, q, k_cache, v_cache, seq_lens, max_seq_len: int, k_scale: float,
+               v_scale: float, block_table, sink=None, workspace=None, scale: float | None = None, stream=None):
+    """Allocate out (and the workspace) and run sinkattn_decode_fp8; q is [B,Hq,192] (one new
+    token) or [B,Hq,q_len,192]."""
+    import torch
+
+    one = q.dim() == 3
+    q4 = q.unsqueeze(2) if one else q
+    B, Hq, q_len, _ = q4.shape
+    if workspace is None:
+        workspace = decode_multi_workspace(mode, window, B, Hq, k_cache.shape[1], q_len, max_seq_len, q.device)
+    out = torch.empty((B, Hq, q_len, v_cache.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_decode_fp8(mode, window, q_len, q4, k_cache, v_cache, seq_lens, max_seq_len, sink, k_scale, v_scale,
+                        out, workspace, block_table, scale, stream)
+    return out[:, :, 0] if one else out
 
 
 def decode_multi_workspace(mode: int, window: int, batch: int, hq: int, hkv: int, q_len: int, max_seq_len: int,

@@ -150,9 +150,13 @@ size_t sinkattn_decode_multi_workspace_bytes(int mode, int window, const sinkatt
     return plan_decode(mode, window, d, q_len, max_seq_len).ws_bytes;
 }
 
-int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
-                          const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
-                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Decode from a bf16 cache (fp8 = 0) or an E4M3 cache with per-tensor scales (fp8 = 1).
+int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q, const sinkattn_kv *kv,
+                  const int32_t *seq_lens, int32_t max_seq_len, const float *sink, int fp8, float k_scale,
+                  float v_scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_dims(mode, window, d);
     if (st) return st;
     if (q_len < 1 || q_len > kMaxQLen) return SINKATTN_E_SHAPE;
@@ -199,12 +203,36 @@ int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t 
     p.max_pages = p.paged ? kv->max_pages : 0;
     p.num_pages = p.paged ? kv->num_pages : 0;
     p.max_seq_len = max_seq_len;
-    p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    p.scale_log2 = (float)((double)d->scale * kLog2eD * (fp8 ? (double)k_scale : 1.0));
+    p.fp8 = fp8;
+    p.v_scale = fp8 ? v_scale : 1.f;
     p.nsplit = pl.nsplit;
     p.chunk = pl.chunk;
     if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq * p.q_len > INT32_MAX)
         return SINKATTN_E_SHAPE;
     return launch_decode(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                          const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 0, 1.f, 1.f, out, workspace,
+                         workspace_bytes, stream);
+}
+
+int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                        const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
+                        float k_scale, float v_scale, void *out, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    if (!kv) return SINKATTN_E_NULL;
+    if (kv->layout != SINKATTN_KV_PAGED || kv->page_size <= 0 || kv->page_size % 32) return SINKATTN_E_UNSUPPORTED;
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return SINKATTN_E_SHAPE;
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 1, k_scale, v_scale, out,
+                         workspace, workspace_bytes, stream);
 }
 
 int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,

@@ -36,10 +36,18 @@ constexpr int kVBytes = kSlice * kDv * 2;            // 8 KB: 8 blocks of 1 KB
 constexpr int kBufBytes = kKBytes + kVBytes;         // one slice
 constexpr int kPart = kDv + 4;                       // partial record: o[128], m, l, 2 pad
 constexpr int kDmaPerSlice = (kKBytes + kVBytes) / 1024;  // 20 wave-wide 1 KB loads
+// 8-bit (E4M3) cache: the same slice in half the bytes
+constexpr int kKBytes8 = kSlice * kDqk;                  // 6 KB
+constexpr int kVBytes8 = kSlice * kDv;                   // 4 KB
+constexpr int kBufBytes8 = kKBytes8 + kVBytes8;
+constexpr int kDmaPerSlice8 = kBufBytes8 / 1024;         // 10
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform).
 __device__ __forceinline__ void dma16(const uint16_t *src, char *dst) {
@@ -51,6 +59,25 @@ __device__ __forceinline__ void dma16(const uint16_t *src, char *dst) {
 //      K[16sb + key][32kk + 8q .. +8], so the A operand of S^T is the 1 KB block itself.
 //   V: block m = keys 4m .. 4m+3, 256 bytes each; row r keeps its 16-byte chunk c in slot
 //      c ^ 2r, so the transposing reads of 4 rows x 32 bytes hit distinct banks.
+
+// 8-bit cache layout of one slice (per wave, per buffer):
+//   K: for each 16-key half sb (3 KB), 16-byte chunk c (d = 16c .. 16c+15) of key k sits in
+//      slot 16c + k, so an operand read (8 bytes: d = 32kk + 8q .. +8) of 16 keys x 2 halves
+//      of one chunk covers 256 contiguous bytes.
+//   V: key k (0..31) keeps 128 bytes, its 16-byte chunk c in slot c ^ vswz(k); the
+//      transposing byte read gathers 8 keys x 16 dv per 16-lane group, and vswz spreads the
+//      keys a group (and a pair of groups) reads over distinct banks.
+__device__ __forceinline__ int vswz(int k) { return ((k >> 1) & 3) | ((k >> 2) & 4); }
+
+// Eight E4M3 codes (two dwords, code i in byte i % 4 of dword i / 4) -> eight bf16, exactly
+// (every E4M3 value is a bf16 value).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(v2i32 c) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c[0], 1.f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c[0], 1.f, true);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c[1], 1.f, false);
+    const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c[1], 1.f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+}
 
 // Row of key j (general path): ring slot j, or page block_table[b][j / page_size].
 __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, int kvh, int j, const uint16_t *base,
@@ -90,13 +117,20 @@ __device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
 // lane-private: lane l writes exactly the 16 bytes it later reads as its MFMA operand) and
 // only V passes through LDS, 33 KB per workgroup, so four workgroups share a CU and a whole
 // batch of rings is in flight at once.
-template <bool kFast, bool kSingle, int NCB>
+//
+// kFp8: K and V are E4M3 codes (8-bit cache, fast paged layout only); they are converted to
+// bf16 after the LDS read, the K scale is part of the logit scale and the V scale multiplies
+// the unnormalised output.
+template <bool kFast, bool kSingle, int NCB, bool kFp8 = false>
 __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(DecodeParams p) {
+    static_assert(!kFp8 || (kFast && !kSingle), "8-bit caches use the double-buffered fast path");
+    constexpr int kSliceBytes = kFp8 ? kBufBytes8 : kBufBytes;
+    constexpr int kDma = kFp8 ? kDmaPerSlice8 : kDmaPerSlice;
     // slice buffers: even slices in bufA, odd ones in a second object (declared below, only
     // when a wave has more than one slice) so that the compiler can tell the loads in flight
     // into one from the reads of the other.  The single-slice buffer holds V only, plus room
     // for the merge's row statistics.
-    constexpr int kBufA = kSingle ? kVBytes + 256 : kBufBytes;
+    constexpr int kBufA = kSingle ? kVBytes + 256 : kSliceBytes;
     __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufA];
 
     const int split = blockIdx.x;
@@ -157,23 +191,41 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             // ring, or pages holding a multiple of 32 keys (one page per slice): rows
             // j0..j0+31 are contiguous; keys outside [kbeg, kend) read a clamped valid row
             // (their scores are masked)
-            const uint16_t *kbase, *vbase;
+            size_t row0;  // cache row of key offset 0 of this slice's page (or ring)
             int off0;
             if (p.paged) {
                 const int page = __builtin_amdgcn_readlane(page_reg, i);
                 const bool ok = page >= 0 && page < p.num_pages;
                 bad |= !ok;
-                const size_t row0 = ((size_t)(ok ? page : 0) * p.Hkv + kvh) * p.page_size;
-                kbase = p.k + row0 * kDqk;
-                vbase = p.v + row0 * kDv;
+                row0 = ((size_t)(ok ? page : 0) * p.Hkv + kvh) * p.page_size;
                 off0 = j0 % p.page_size;
             } else {
-                const size_t row0 = ((size_t)b * p.Hkv + kvh) * p.window;
-                kbase = p.k + row0 * kDqk;
-                vbase = p.v + row0 * kDv;
+                row0 = ((size_t)b * p.Hkv + kvh) * p.window;
                 off0 = j0;
             }
+            const uint16_t *kbase = p.k + row0 * kDqk, *vbase = p.v + row0 * kDv;
             const int lo = max(kbeg, j0) - j0, hi = min(kend, j0 + kSlice) - 1 - j0;  // valid key offsets
+            if constexpr (kFp8) {
+                // one byte per element: rows of kDqk and kDv bytes
+                const uint8_t *kbase8 = reinterpret_cast<const uint8_t *>(p.k) + row0 * kDqk;
+                const uint8_t *vbase8 = reinterpret_cast<const uint8_t *>(p.v) + row0 * kDv;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int t = min(max(16 * sb + s, lo), hi);
+#pragma unroll
+                    for (int i2 = 0; i2 < 3; ++i2)
+                        __builtin_amdgcn_global_load_lds(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
+                                                         (lds_void *)(kb + sb * 3072 + i2 * 1024), 16, 0, 0);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int key = 8 * m + (lane >> 3);
+                    const int t = min(max(key, lo), hi);
+                    __builtin_amdgcn_global_load_lds(vbase8 + (size_t)(off0 + t) * kDv + ((lane & 7) ^ vswz(key)) * 16,
+                                                     (lds_void *)(kb + kKBytes8 + m * 1024), 16, 0, 0);
+                }
+                return;
+            }
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
                 const int t = min(max(16 * sb + s, lo), hi);
@@ -224,13 +276,13 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         if (i + 1 < nmine) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of `nxt` are done
             issue(i + 1, nxt);
-            // vmcnt(20): the 20 loads just issued may stay in flight; slice i has landed
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerSlice & 15) | ((kDmaPerSlice >> 4) << 14));
+            // vmcnt(kDma): the loads just issued may stay in flight; slice i has landed
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kDma & 15) | ((kDma >> 4) << 14));
         } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         const char *kb = cur;
-        const char *vb = kSingle ? cur : kb + kKBytes;
+        const char *vb = kSingle ? cur : kb + (kFp8 ? kKBytes8 : kKBytes);
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
 
         // ---- scores: S^T tiles of 16 keys x 16 columns
@@ -241,8 +293,12 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             for (int cb = 0; cb < NCB; ++cb) s[cb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
-                const bf16x8 kf =
-                    kSingle ? kreg[sb][kk] : *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
+                bf16x8 kf;
+                if constexpr (kFp8)
+                    kf = e4m3x8_to_bf16(*reinterpret_cast<const v2i32 *>(
+                        kb + sb * 3072 + ((2 * kk + (q >> 1)) * 16 + hl) * 16 + (q & 1) * 8));
+                else
+                    kf = kSingle ? kreg[sb][kk] : *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     s[cb][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][kk], s[cb][sb], 0, 0, 0);
@@ -285,13 +341,24 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         // 4r + c4 addresses row r (keys 4q + r, then 16 + 4q + r) at dv 16db + 4c4, and lane i
         // of the group receives dv 16db + i of the 4 rows
         const int r = hl >> 2, c4 = lane & 3;
+        // 8-bit V: lane 2r8 + c2 of group q addresses key kr8 (rows r8 < 4: keys 4q + r8, then
+        // 16 + 4q + r8 - 4) at dv 16db + 8c2, and lane i receives dv 16db + i of the 8 keys
+        const int r8 = hl >> 1, c2 = hl & 1;
+        const int kr8 = (r8 < 4) ? 4 * q + r8 : 12 + 4 * q + r8;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const int c = 2 * db + (c4 >> 1);
-            const int off = r * 256 + ((c ^ (2 * r)) * 16) + (c4 & 1) * 8;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + q * 1024 + off));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (4 + q) * 1024 + off));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            bf16x8 vf;
+            if constexpr (kFp8) {
+                const v2i32 codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_v2i32 *)(vb + kr8 * 128 + (db ^ vswz(kr8)) * 16 + c2 * 8));
+                vf = e4m3x8_to_bf16(codes);
+            } else {
+                const int c = 2 * db + (c4 >> 1);
+                const int off = r * 256 + ((c ^ (2 * r)) * 16) + (c4 & 1) * 8;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + q * 1024 + off));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (4 + q) * 1024 + off));
+                vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
                 acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[cb], acc[cb][db] * alpha[cb], 0, 0, 0);
@@ -302,7 +369,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     if constexpr (kSingle) {
         if (nmine > 0) step(0, bufA[wave], bufA[wave]);
     } else {
-        __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kBufBytes];
+        __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kSliceBytes];
         for (int i = 0; i < nmine; i += 2) {
             step(i, bufA[wave], bufB[wave]);
             if (i + 1 < nmine) step(i + 1, bufB[wave], bufA[wave]);
@@ -347,6 +414,10 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 L += sc * red_l[w * 16 + hh];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
+            }
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] *= p.v_scale;
             }
             if (p.nsplit == 1) {
                 // final output: add the sink term once, normalise, round to bf16
@@ -464,7 +535,12 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     // a ring of at most 128 visible slots in one split: one slice per wave
     const bool single = !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
     const void *fn;
-    if (single) {
+    if (p.fp8) {
+        if (!p.paged || !fast) return -1;
+        fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 4, true>)
+             : p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 2, true>)
+                          : reinterpret_cast<const void *>(&decode_split_kernel<true, false, 1, true>);
+    } else if (single) {
         fn = reinterpret_cast<const void *>(&decode_split_kernel<true, true, 1>);
     } else if (fast) {
         fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 4>)

@@ -36,7 +36,9 @@ struct DecodeParams {
     int q_len;         // new tokens per sequence (positions seq_len - q_len .. seq_len - 1)
     int ncb, hchunks;  // 16-column blocks per workgroup; workgroups per KV head
     int swa, window, paged, page_size, max_pages, num_pages, max_seq_len;
-    float scale_log2;
+    float scale_log2;  // logit scale * log2(e) (8-bit cache: times the K scale)
+    int fp8;           // K and V are E4M3 codes (paged, page_size a multiple of 32)
+    float v_scale;     // 8-bit cache: V element = v_scale * code value
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
 };
 

@@ -72,6 +72,32 @@ def _fill_normal(n: int, seed: int, stream: int, bf16: bool) -> np.ndarray:
     return out
 
 
+def e4m3_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of x / scale in the OCP 8-bit E4M3 format (round to nearest even, clamped to the
+    largest finite value 448), as uint8, by torch's float8_e4m3fn conversion."""
+    import torch
+
+    y = np.clip(np.asarray(x, np.float32) / np.float32(scale), -448.0, 448.0)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def normal_e4m3(shape, seed: int, stream: int, scale: float) -> np.ndarray:
+    """Seeded N(0,1) draws stored as E4M3 codes of value / scale (uint8), chunk by chunk."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def work(c: int) -> None:
+        lo = c * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        g = np.random.default_rng([seed, stream, c])
+        out[lo:hi] = e4m3_codes(g.standard_normal(hi - lo, dtype=np.float32), scale)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(nchunks)))
+    return out.reshape(shape)
+
+
 def normal(shape, seed: int, stream: int, bf16: bool = True) -> np.ndarray:
     """Seeded N(0,1) tensor: uint16 bf16 bits when bf16, else float32."""
     n = int(np.prod(shape))
@@ -105,6 +131,7 @@ class Workload:
     ctx_hi: int = 0
     page_size: int = 64
     q_len: int = 1       # new tokens per sequence (q_len > 1: drafted tokens verified together)
+    kv_fp8: bool = False  # 8-bit E4M3 cache with per-tensor scales (decode only)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -126,7 +153,13 @@ GA_DECODE = Workload("ga_decode_B8_256K_paged", "decode", MODE_GLOBAL, 8, 64, 4,
 GA_VERIFY = Workload("ga_verify_B8_256K_q4_paged", "decode", MODE_GLOBAL, 8, 64, 4, window=0, seed=5,
                      layout="paged", ctx_lo=262144, ctx_hi=262144, page_size=64, q_len=4)
 
-WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE, GA_VERIFY)}
+# the global decode workload with the cache in 8-bit floating point (one byte per element, as
+# the pages size it), K and V stored as codes of value / 2^-6
+GA_DECODE_FP8 = Workload("ga_decode_B8_256K_paged_fp8", "decode", MODE_GLOBAL, 8, 64, 4, window=0, seed=6,
+                         layout="paged", ctx_lo=262144, ctx_hi=262144, page_size=64, kv_fp8=True)
+FP8_KV_SCALE = 2.0 ** -6
+
+WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE, GA_VERIFY, GA_DECODE_FP8)}
 
 
 # --------------------------------------------------------------------------- prefill
@@ -203,8 +236,9 @@ def decode_paged_inputs(w: Workload, seed: int | None = None, batch: int | None 
     P = B * max_pages if num_pages is None else num_pages
     return {
         "q": normal((B, w.hq, w.d_qk) if w.q_len == 1 else (B, w.hq, w.q_len, w.d_qk), s, 0),
-        "k": normal((P, w.hkv, ps, w.d_qk), s, 1),
-        "v": normal((P, w.hkv, ps, w.d_v), s, 2),
+        "k": normal_e4m3((P, w.hkv, ps, w.d_qk), s, 1, FP8_KV_SCALE) if w.kv_fp8 else normal((P, w.hkv, ps, w.d_qk), s, 1),
+        "v": normal_e4m3((P, w.hkv, ps, w.d_v), s, 2, FP8_KV_SCALE) if w.kv_fp8 else normal((P, w.hkv, ps, w.d_v), s, 2),
+        "kv_scales": (FP8_KV_SCALE, FP8_KV_SCALE) if w.kv_fp8 else None,
         "block_table": page_table(B, max_pages, P, s, permute),
         "seq_lens": np.full(B, n, dtype=np.int32),
         "sink": sink_values(w.hq, s),

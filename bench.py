@@ -6,6 +6,7 @@ One step runs every kernel of the path once, each on its benchmark workload:
   swa_decode_B128_ring sliding-window decode, 128 sequences, 128-slot ring caches
   ga_decode_B8_256K    global decode, 8 sequences x 262144 tokens, 64-token permuted pages
   ga_verify_B8_256K_q4 the same caches with 4 new (drafted) tokens per sequence at once
+  ga_decode_..._fp8    the 256K global decode from an 8-bit E4M3 cache (half the bytes)
 All inputs are synthetic (seeded N(0,1) bf16, sink ~ U[0,6]) and resident in HBM before
 timing starts.  Each call is timed with HIP events recorded on the stream the library
 launches on.
@@ -187,6 +188,29 @@ def main() -> int:
 
         runs[w.name] = (call, flops, nbytes)
 
+    # --- global decode at 256K from an 8-bit (E4M3) cache: half the bytes of the bf16 cache
+    w = inputs.GA_DECODE_FP8
+    if not only or w.name in only:
+        d = inputs.decode_paged_inputs(w)
+        q = up(d["q"])
+        k = torch.from_numpy(d["k"]).to(dev)
+        v = torch.from_numpy(d["v"]).to(dev)
+        bt = torch.from_numpy(d["block_table"]).to(dev)
+        lens = torch.from_numpy(d["seq_lens"]).to(dev)
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        ks, vs = d["kv_scales"]
+        del d
+        out = torch.empty((w.batch, w.hq, 1, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_multi_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, 1, w.ctx_hi, dev)
+        visible = w.batch * w.ctx_hi
+        flops = visible * w.hq * FLOP_PER_PAIR
+        nbytes = visible * w.hkv * (w.d_qk + w.d_v)  # one byte per element
+
+        def call(w=w, q=q.unsqueeze(2), k=k, v=v, bt=bt, lens=lens, sink=sink, out=out, ws=ws, ks=ks, vs=vs):
+            sa.sinkattn_decode_fp8(w.mode, w.window, 1, q, k, v, lens, w.ctx_hi, sink, ks, vs, out, ws, bt)
+
+        runs[w.name] = (call, flops, nbytes)
+
     names = list(runs)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -256,7 +280,8 @@ def main() -> int:
                    "ga_prefill": "B=1 L=32768 Hq=64 Hkv=4 causal+sink d_qk=192 d_v=128",
                    "swa_decode": "B=128 ctx~U[4096,65536] 128-slot ring Hq=64 Hkv=8",
                    "ga_decode": "B=8 ctx=262144 64-token pages, permuted table, Hq=64 Hkv=4",
-                   "ga_verify": "as ga_decode with q_len=4 new tokens per sequence"},
+                   "ga_verify": "as ga_decode with q_len=4 new tokens per sequence",
+                   "ga_decode_fp8": "as ga_decode with an E4M3 cache, per-tensor scales 2^-6"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode, "cpu_baseline": cpu,
     }

@@ -210,6 +210,28 @@ int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t 
                           int32_t max_seq_len, const float *sink, void *out, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * Decode (q_len >= 1 new tokens, as sinkattn_decode_multi) from a KV cache held in 8-bit
+ * floating point: the pages size the cache with one byte per element (paper notes "MiMo-
+ * V2-Flash Technical Report", §3.2), which halves the bytes that bound decode.
+ *   kv         PAGED only, page_size a multiple of 32 (else SINKATTN_E_UNSUPPORTED);
+ *              kv->k: uint8 [num_pages][hkv][page_size][d_qk], kv->v: uint8 [num_pages][hkv]
+ *              [page_size][d_v], each byte an OCP E4M3 code (sign, 4 exponent bits with bias
+ *              7, 3 mantissa bits; no infinities, code 0x7F / 0xFF is NaN)
+ *   k_scale    K element = k_scale * value(code); v_scale likewise for V; both finite and
+ *              > 0 (else SINKATTN_E_SHAPE)
+ *   q, out, seq_lens, sink, workspace, stream: as sinkattn_decode_multi (q and out bf16); the
+ *              workspace size is sinkattn_decode_multi_workspace_bytes(mode, window, d, q_len,
+ *              max_seq_len).
+ * The codes are widened to bf16 exactly after they reach LDS; k_scale joins the logit
+ * scale and v_scale multiplies the output, so the result is attention over the scaled
+ * values.
+ */
+int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                        const void *q, const sinkattn_kv *kv, const int32_t *seq_lens,
+                        int32_t max_seq_len, const float *sink, float k_scale, float v_scale,
+                        void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(int status);
 

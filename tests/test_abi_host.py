@@ -175,6 +175,22 @@ def test_prefill_chunk_workspace_size(L):
         sa.sinkattn_prefill_chunk_workspace_bytes(1, 101, 4, 1, 100)
 
 
+def test_decode_fp8_argument_errors(L):
+    def fp8(desc=None, ks=0.5, vs=0.5, q=A):
+        d = dims(B=8, hq=64, hkv=4)
+        desc = desc if desc is not None else kv()
+        return L.sinkattn_decode_fp8(0, 0, ctypes.byref(d), 1, q, ctypes.byref(desc), A, 262144, None, ks, vs, A, A,
+                                     1 << 30, None)
+    assert fp8(desc=kv(layout=0)) == E_UNSUP               # paged caches only
+    assert fp8(desc=kv(ps=48, mp=6000)) == E_UNSUP        # pages of a multiple of 32 keys
+    assert fp8(ks=0.0) == E_SHAPE
+    assert fp8(vs=-1.0) == E_SHAPE
+    assert fp8(ks=float("nan")) == E_SHAPE
+    assert fp8(ks=float("inf")) == E_SHAPE
+    assert fp8(q=None) == E_NULL
+    assert L.sinkattn_decode_fp8(0, 0, ctypes.byref(dims()), 1, A, None, A, 1, None, 1.0, 1.0, A, A, 0, None) == E_NULL
+
+
 def test_prefill_workspace_size(L):
     # a transposed copy of V, rows padded to 64 keys
     assert sa.sinkattn_prefill_workspace_bytes(1, 32768, 64, 8) == 8 * 128 * 32768 * 2
