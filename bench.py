@@ -43,11 +43,14 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "f06857047928918216f4dad78a31e3393ed91c07616666bf31306a257fbb5296",
-                          "read_GB": 3.6197, "written_GB": 0.5872},
+                          "sha256": "d12e9276964b7df6251fe96840020508fbda34c971803822fa7cc61457a20db6",
+                          "read_GB": 3.5704, "written_GB": 0.5373},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "b613180c3bd310f07b43daaec1d2943d0218b686c5de03cbb000cc90a87e3c5d",
-                                "read_GB": 5.3880, "written_GB": 0.0180},
+                                "sha256": "e4fe2a3a89c9f99e3baa31966c7f50c3a2d6fd99158172d687c080a50d971f30",
+                                "read_GB": 5.3880, "written_GB": 0.0179},
+    "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
+                                    "sha256": "e4fe2a3a89c9f99e3baa31966c7f50c3a2d6fd99158172d687c080a50d971f30",
+                                    "read_GB": 2.7037, "written_GB": 0.0179},
 }
 
 
@@ -265,6 +268,15 @@ def main() -> int:
                            "traffic": traffic_gb("ga_decode_B8_256K_paged"),
                            "traffic_unit": "GB per call (HBM read + written)"}
 
+    dec8 = comp.get("ga_decode_B8_256K_paged_fp8")
+    roofline_decode_fp8 = None
+    if dec8:
+        roofline_decode_fp8 = {"kernel": "decode_split_kernel<fp8>+decode_merge_kernel (ga_decode_B8_256K_paged_fp8)",
+                               "bound": "hbm", "achieved": dec8["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(dec8["gbps"] / HBM_PEAK_GBPS, 4),
+                               "traffic": traffic_gb("ga_decode_B8_256K_paged_fp8"),
+                               "traffic_unit": "GB per call (HBM read + written)"}
+
     cpu = None
     if not args.no_cpu_baseline and pre:
         cpu = cpu_baseline()
@@ -283,7 +295,8 @@ def main() -> int:
                    "ga_verify": "as ga_decode with q_len=4 new tokens per sequence",
                    "ga_decode_fp8": "as ga_decode with an E4M3 cache, per-tensor scales 2^-6"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
-        "components": comp, "roofline": roofline, "roofline_decode": roofline_decode, "cpu_baseline": cpu,
+        "components": comp, "roofline": roofline, "roofline_decode": roofline_decode,
+        "roofline_decode_fp8": roofline_decode_fp8, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
