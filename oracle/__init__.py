@@ -54,15 +54,17 @@ def load(path: str = LIB):
                                    ctypes.c_int64, P, P]
     lib.oracle_prefill_chunk.restype = I
     lib.oracle_prefill_chunk.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, ctypes.c_int64, P,
-                                         P]
+                                         P, P]
     lib.oracle_decode_fp8.restype = I
     lib.oracle_decode_fp8.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, ctypes.c_double,
-                                      ctypes.c_double, P, I, I, I, P, P, P]
+                                      ctypes.c_double, P, I, I, I, P, P, P, P]
+    lib.oracle_rope.restype = I
+    lib.oracle_rope.argtypes = [ctypes.c_int64, I, I, ctypes.c_double, I, P, P, P]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
-                                  P, P, P]
+                                  P, P, P, P]
     lib.oracle_threads.restype = I
     lib.oracle_threads.argtypes = []
     if path == LIB:
@@ -111,10 +113,11 @@ def prefill(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=
     return out
 
 
-def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=None) -> np.ndarray:
+def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None, lib=None, return_lse=False):
     """Chunked prefill: q [B,Hq,Lq,dqk] holds positions Lk-Lq .. Lk-1 of sequences whose keys
     and values k [B,Hkv,Lk,dqk], v [B,Hkv,Lk,dv] cover positions 0 .. Lk-1.  rows: optional
-    (b, h, r) triplets (r = chunk row).  Returns float64 [B,Hq,Lq,dv] or [nrows,dv]."""
+    (b, h, r) triplets (r = chunk row).  Returns float64 [B,Hq,Lq,dv] or [nrows,dv], and with
+    return_lse also each row's log-sum-exp ([B,Hq,Lq] or [nrows])."""
     lib = lib or load()
     qa, dt = _arr(q, None)
     ka, _ = _arr(k, None)
@@ -129,21 +132,23 @@ def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None
         rp = np.ascontiguousarray(rows, dtype=np.int64)
         n = rp.shape[0]
         out = np.empty((n, dv), np.float64)
+    lse = np.empty(out.shape[:-1], np.float64)
     rc = lib.oracle_prefill_chunk(mode, window, B, Lq, Lk, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka), _ptr(va),
-                                  _ptr(s), n, _ptr(rp), _ptr(out))
+                                  _ptr(s), n, _ptr(rp), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_prefill_chunk rejected its arguments")
-    return out
+    return (out, lse) if return_lse else out
 
 
 def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout: int,
-           block_table=None, lib=None, kv_scales=None) -> np.ndarray:
+           block_table=None, lib=None, kv_scales=None, return_lse=False):
     """q [B,Hq,dqk] (one new token per sequence) or [B,Hq,q_len,dqk] (q_len new tokens at
     positions seq_lens-q_len .. seq_lens-1); RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv];
     PAGED: k [P,Hkv,page,dqk], v [P,Hkv,page,dv] with block_table [B,max_pages].
     Returns float64 [B,Hq,dv] or [B,Hq,q_len,dv], matching q.
     uint8 k and v are E4M3 codes of an 8-bit cache; kv_scales = (k_scale, v_scale) then
-    gives the per-tensor scales (element = scale * code value)."""
+    gives the per-tensor scales (element = scale * code value).  With return_lse also each
+    row's log-sum-exp, shaped like the output without its last axis."""
     lib = lib or load()
     qa, dt = _arr(q, None)
     fp8 = np.asarray(k).dtype == np.uint8
@@ -164,16 +169,62 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
     else:
         bt, ps, mp, npg = None, 0, 0, 0
     out = np.empty(qa.shape[:-1] + (dv,), np.float64)
+    lse = np.empty(out.shape[:-1], np.float64)
     if fp8:
         ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
         rc = lib.oracle_decode_fp8(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
-                                   _ptr(va), ks, vs, _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
+                                   _ptr(va), ks, vs, _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out),
+                                   _ptr(lse))
     else:
         rc = lib.oracle_decode(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
-                               _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out))
+                               _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return (out, lse) if return_lse else out
+
+
+SWA_ROPE_THETA = 10000.0     # sliding-window layers (deep-dive CH 3.5)
+GA_ROPE_THETA = 5000000.0    # global layers
+ROPE_DIMS = 64               # rotated leading dimensions of the 192 (partial_rotary_factor 0.334)
+
+
+def rope(x, positions, theta: float, rot: int = ROPE_DIMS, lib=None) -> np.ndarray:
+    """Partial RoPE of x [..., dim] (uint16 bf16 bits or float) at integer positions shaped like
+    x without its last axis.  Returns float64 like x."""
+    lib = lib or load()
+    xa, dt = _arr(x, None)
+    pa = np.ascontiguousarray(np.broadcast_to(np.asarray(positions, np.int64), xa.shape[:-1]))
+    out = np.empty(xa.shape, np.float64)
+    rows = int(np.prod(xa.shape[:-1]))
+    if lib.oracle_rope(rows, xa.shape[-1], rot, theta, dt, _ptr(xa), _ptr(pa), _ptr(out)) != 0:
+        raise ValueError("oracle_rope rejected its arguments")
     return out
+
+
+def kv_append(k_cache, v_cache, layout: int, k_new, v_new, seq_lens, window: int = 0, block_table=None):
+    """Write n new tokens per sequence into a cache (in place): token t of sequence b, at
+    position seq_lens[b] - n + t, goes to ring slot pos mod window (the last `window`
+    positions only) or to page block_table[b][pos // page] at offset pos mod page.
+    k_new [B,Hkv,n,dqk], v_new [B,Hkv,n,dv]; positions below 0 and page ids outside the pool
+    are skipped.  Plain indexing, no arithmetic."""
+    B, Hkv, n = k_new.shape[:3]
+    for b in range(B):
+        for t in range(n):
+            pos = int(seq_lens[b]) - n + t
+            if pos < 0:
+                continue
+            if layout == RING:
+                if pos < int(seq_lens[b]) - window:
+                    continue
+                k_cache[b, :, pos % window] = k_new[b, :, t]
+                v_cache[b, :, pos % window] = v_new[b, :, t]
+            else:
+                ps = k_cache.shape[2]
+                page = int(block_table[b, pos // ps])
+                if not 0 <= page < k_cache.shape[0]:
+                    continue
+                k_cache[page, :, pos % ps] = k_new[b, :, t]
+                v_cache[page, :, pos % ps] = v_new[b, :, t]
 
 
 def e4m3_value(code: int, lib=None) -> float:

@@ -62,12 +62,14 @@ static double load(const void *p, size_t idx, int dtype) {
 }
 
 /* One output row.  qrow: index of q[0] of the row; key j of the visible list lives at
- * kidx[t]*dqk in k and vidx[t]*dv in v.  n keys.  Writes dv doubles to out. */
-static void attend_row(int dtype, const void *q, size_t qrow, int kvdtype, double kscale, double vscale,
+ * kidx[t]*dqk in k and vidx[t]*dv in v.  n keys.  Writes dv doubles to out and returns the
+ * row's log-sum-exp over the sink and the visible logits, log(exp(sink) + sum_j exp(a_j))
+ * (natural log; -inf when both are empty, +inf for a sink of +inf). */
+static double attend_row(int dtype, const void *q, size_t qrow, int kvdtype, double kscale, double vscale,
                        const void *k, const void *v, const size_t *kidx, const size_t *vidx, int n, int dqk,
                        int dv, double scale, int has_sink, double sink, double *a, double *out) {
     for (int e = 0; e < dv; ++e) out[e] = 0.0;
-    if (has_sink && isinf(sink) && sink > 0) return; /* all mass on the sink */
+    if (has_sink && isinf(sink) && sink > 0) return INFINITY; /* all mass on the sink */
     double m = has_sink ? sink : -INFINITY;
     for (int t = 0; t < n; ++t) {
         double dot = 0.0;
@@ -75,13 +77,14 @@ static void attend_row(int dtype, const void *q, size_t qrow, int kvdtype, doubl
         a[t] = scale * dot;
         if (a[t] > m) m = a[t];
     }
-    if (n == 0 || isinf(m)) return; /* empty visible set (or only a -inf sink) */
+    if (n == 0 || isinf(m)) return m; /* empty visible set: the sink alone (or nothing) */
     double z = has_sink ? exp(sink - m) : 0.0;
     for (int t = 0; t < n; ++t) z += exp(a[t] - m);
     for (int t = 0; t < n; ++t) {
         double s = exp(a[t] - m) / z;
         for (int e = 0; e < dv; ++e) out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));
     }
+    return m + log(z);
 }
 
 /*
@@ -91,14 +94,14 @@ static void attend_row(int dtype, const void *q, size_t qrow, int kvdtype, doubl
  */
 int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, int Hkv, int dqk, int dv,
                          double scale, int dtype, const void *q, const void *k, const void *v,
-                         const double *sink, int64_t nrows, const int64_t *rows, double *out);
+                         const double *sink, int64_t nrows, const int64_t *rows, double *out, double *lse);
 
 int oracle_prefill(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv,
                    double scale, int dtype, const void *q, const void *k, const void *v,
                    const double *sink, int64_t nrows, const int64_t *rows, double *out) {
     /* every position is a query: the chunk that is the whole sequence */
     return oracle_prefill_chunk(mode, window, B, L, L, Hq, Hkv, dqk, dv, scale, dtype, q, k, v, sink, nrows, rows,
-                                out);
+                                out, NULL);
 }
 
 /*
@@ -106,11 +109,12 @@ int oracle_prefill(int mode, int window, int B, int L, int Hq, int Hkv, int dqk,
  * Lk - Lq .. Lk - 1 of sequences of Lk tokens (the model card's serving set-up prefills long
  * prompts in chunks).  q [B][Hq][Lq][dqk] (row r is position Lk - Lq + r), k [B][Hkv][Lk][dqk],
  * v [B][Hkv][Lk][dv].  rows == NULL: out [B][Hq][Lq][dv]; else nrows triplets (b, h, r) and
- * out [nrows][dv].  Returns 0, or -1 on bad arguments.
+ * out [nrows][dv].  lse (optional, NULL for none): each row's log-sum-exp, [B][Hq][Lq] or
+ * [nrows].  Returns 0, or -1 on bad arguments.
  */
 int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, int Hkv, int dqk, int dv,
                          double scale, int dtype, const void *q, const void *k, const void *v,
-                         const double *sink, int64_t nrows, const int64_t *rows, double *out) {
+                         const double *sink, int64_t nrows, const int64_t *rows, double *out, double *lse) {
     if (B < 0 || Lq < 0 || Lk < Lq || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
     if (mode != ORACLE_SWA && mode != ORACLE_GLOBAL) return -1;
@@ -141,8 +145,10 @@ int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, in
                 ki[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dqk);
                 vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);
             }
-            attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), dtype, 1.0, 1.0, k, v, ki, vi, cnt, dqk, dv, scale,
-                       sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)n * dv);
+            const double l = attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), dtype, 1.0, 1.0, k, v, ki,
+                                        vi, cnt, dqk, dv, scale, sink != NULL, sink ? sink[h] : 0.0, a,
+                                        out + (size_t)n * dv);
+            if (lse) lse[n] = l;
         }
         free(a);
         free(ki);
@@ -172,7 +178,7 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
                        int q_len, double scale, int dtype, const void *q, int kvdtype, double kscale,
                        double vscale, const void *k, const void *v, const int32_t *block_table,
                        int page_size, int max_pages, int num_pages, const int32_t *seq_lens,
-                       const double *sink, double *out) {
+                       const double *sink, double *out, double *lse) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
     if (q_len <= 0) return -1;
@@ -217,8 +223,9 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
                 bad = 1;
                 continue;
             }
-            attend_row(dtype, q, (size_t)r * dqk, kvdtype, kscale, vscale, k, v, ki, vi, n, dqk, dv, scale,
-                       sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+            const double l = attend_row(dtype, q, (size_t)r * dqk, kvdtype, kscale, vscale, k, v, ki, vi, n, dqk,
+                                        dv, scale, sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+            if (lse) lse[r] = l;
         }
         free(a);
         free(ki);
@@ -230,9 +237,9 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
 int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
                   int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
                   const int32_t *block_table, int page_size, int max_pages, int num_pages,
-                  const int32_t *seq_lens, const double *sink, double *out) {
+                  const int32_t *seq_lens, const double *sink, double *out, double *lse) {
     return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, dtype, 1.0, 1.0, k, v,
-                       block_table, page_size, max_pages, num_pages, seq_lens, sink, out);
+                       block_table, page_size, max_pages, num_pages, seq_lens, sink, out, lse);
 }
 
 /*
@@ -245,10 +252,37 @@ int oracle_decode_fp8(int mode, int window, int layout, int B, int Hq, int Hkv, 
                       int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
                       double kscale, double vscale, const int32_t *block_table, int page_size,
                       int max_pages, int num_pages, const int32_t *seq_lens, const double *sink,
-                      double *out) {
+                      double *out, double *lse) {
     if (!(kscale > 0) || !(vscale > 0)) return -1;
     return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, ORACLE_FP8_E4M3, kscale,
-                       vscale, k, v, block_table, page_size, max_pages, num_pages, seq_lens, sink, out);
+                       vscale, k, v, block_table, page_size, max_pages, num_pages, seq_lens, sink, out, lse);
+}
+
+/*
+ * Partial rotary position embedding ("MiMo-V2-Flash 模型架构深度拆解", CH 3.5 and CH 10.5;
+ * "MiMo-V2-Flash 架构 QA", Q2.7): only the first `rot` of the `dim` q/k dimensions are
+ * rotated (64 of 192); pair i (i < rot/2) turns by the angle pos * theta^(-2i/rot), theta
+ * 10 000 in sliding-window layers and 5 000 000 in global ones.  Pair i is made of
+ * dimensions i and i + rot/2 (the rotate-half pairing).  x [rows][dim] in `dtype`, pos
+ * [rows]; out [rows][dim] doubles.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_rope(int64_t rows, int dim, int rot, double theta, int dtype, const void *x, const int64_t *pos,
+                double *out) {
+    if (rows < 0 || dim <= 0 || rot < 0 || rot > dim || rot % 2 || !(theta > 0)) return -1;
+    const int half = rot / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const size_t base = (size_t)r * dim;
+        for (int d = rot; d < dim; ++d) out[base + d] = load(x, base + d, dtype);
+        for (int i = 0; i < half; ++i) {
+            const double ang = (double)pos[r] * pow(theta, -2.0 * i / rot);
+            const double c = cos(ang), sn = sin(ang);
+            const double a = load(x, base + i, dtype), b = load(x, base + i + half, dtype);
+            out[base + i] = a * c - b * sn;
+            out[base + i + half] = b * c + a * sn;
+        }
+    }
+    return 0;
 }
 
 /* The value of one E4M3 code (exported for the tests). */

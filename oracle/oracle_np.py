@@ -25,9 +25,10 @@ def mask_matrix(L: int, mode: int, window: int) -> np.ndarray:
     return keep
 
 
-def prefill(q, k, v, sink, mode: int, window: int, scale: float) -> np.ndarray:
+def prefill(q, k, v, sink, mode: int, window: int, scale: float, return_lse: bool = False):
     """q [B,Hq,L,dqk], k [B,Hkv,L,dqk], v [B,Hkv,L,dv] (any float dtype), sink [Hq] or None.
-    Returns float64 [B,Hq,L,dv]."""
+    Returns float64 [B,Hq,L,dv]; with return_lse also scipy's logsumexp over each row's
+    S+1 columns (the log of the softmax denominator), [B,Hq,L]."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -41,6 +42,10 @@ def prefill(q, k, v, sink, mode: int, window: int, scale: float) -> np.ndarray:
     if sink is not None:
         col = np.broadcast_to(np.asarray(sink, np.float64)[None, :, None, None], (B, Hq, L, 1))
         scores = np.concatenate([scores, col], axis=-1)
+    if return_lse:
+        from scipy.special import logsumexp
+
+        lse = logsumexp(scores, axis=-1)
     mx = scores.max(axis=-1, keepdims=True)
     with np.errstate(invalid="ignore"):
         e = np.exp(scores - mx)
@@ -48,4 +53,4 @@ def prefill(q, k, v, sink, mode: int, window: int, scale: float) -> np.ndarray:
     if sink is not None:
         probs = probs[..., :-1]
         probs = np.where(np.isposinf(np.asarray(sink, np.float64))[None, :, None, None], 0.0, probs)
-    return probs @ vx
+    return (probs @ vx, lse) if return_lse else probs @ vx

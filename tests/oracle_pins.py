@@ -375,10 +375,100 @@ def pin_fp8_decode_is_decode_of_values(lib):
         _close(got, want, 1e-12, 1e-14, f"fp8 decode mode={mode}")
 
 
+def pin_lse(lib):
+    """Each row's log-sum-exp (the log of the sink softmax denominator) against scipy's
+    logsumexp over the eager form's S+1 columns; with a sink of -inf (no sink) it is the
+    plain softmax's; LSE(sink) = logaddexp(LSE(no sink), sink); an empty row (a decode
+    position before the sequence) has LSE = sink."""
+    B, Hq, Hkv, L, dqk, dv = 1, 4, 2, 40, 16, 8
+    q = _rand((B, Hq, L, dqk), 1000)
+    k = _rand((B, Hkv, L, dqk), 1001)
+    v = _rand((B, Hkv, L, dv), 1002)
+    sink = np.array([0.5, 3.0, -1.0, 6.0])
+    for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 5)):
+        out, lse = oracle.prefill_chunk(q, k, v, sink, mode, W, 0.4, lib=lib, return_lse=True)
+        _, ref = oracle_np.prefill(q, k, v, sink, mode, W, 0.4, return_lse=True)
+        _close(lse, ref, 1e-12, 1e-13, f"lse mode={mode}")
+        _, lse0 = oracle.prefill_chunk(q, k, v, None, mode, W, 0.4, lib=lib, return_lse=True)
+        _, ref0 = oracle_np.prefill(q, k, v, None, mode, W, 0.4, return_lse=True)
+        _close(lse0, ref0, 1e-12, 1e-13, f"lse no sink mode={mode}")
+        _close(lse, np.logaddexp(lse0, sink[None, :, None]), 1e-12, 1e-13, f"lse sink relation mode={mode}")
+    # decode rows before the sequence start: empty visible set
+    from attention_sink_softmax_amd import inputs
+    kp, vp, bt = inputs.pages_from_sequence(k, v, L, 8, 6, 3, True)
+    qd = np.ascontiguousarray(q[:, :, :3])
+    lens = np.array([1], np.int32)
+    _, lsed = oracle.decode(qd, kp, vp, lens, sink, oracle.GLOBAL, 0, 0.4, oracle.PAGED, bt, lib=lib, return_lse=True)
+    assert np.array_equal(lsed[0, :, 0], sink) and np.array_equal(lsed[0, :, 1], sink)
+    _, lsen = oracle.decode(qd, kp, vp, lens, None, oracle.GLOBAL, 0, 0.4, oracle.PAGED, bt, lib=lib, return_lse=True)
+    assert np.all(np.isneginf(lsen[0, :, :2]))
+
+
+def pin_rope(lib):
+    """Partial RoPE: the pages' angle pos * theta^(-2i/64) for pair i, seen on unit vectors
+    (dimension i turns towards i + 32); position 0 is the identity; the 128 trailing
+    dimensions are untouched; every pair keeps its length; the rotated dot product depends on
+    the position difference only (q at m, k at n equals q at m - n, k at 0)."""
+    rng = np.random.default_rng(1100)
+    for theta in (oracle.SWA_ROPE_THETA, oracle.GA_ROPE_THETA):
+        eye = np.eye(192, dtype=np.float32)[:64]
+        for pos in (0, 1, 7, 131071, 262143):
+            out = oracle.rope(eye, np.full(64, pos), theta, lib=lib)
+            for i in (0, 1, 13, 31):
+                ang = pos * theta ** (-2.0 * i / 64)
+                want = np.zeros(192)
+                want[i], want[i + 32] = math.cos(ang), math.sin(ang)
+                assert np.allclose(out[i], want, rtol=0, atol=1e-12), (theta, pos, i)
+                want2 = np.zeros(192)
+                want2[i + 32], want2[i] = math.cos(ang), -math.sin(ang)
+                assert np.allclose(out[i + 32], want2, rtol=0, atol=1e-12), (theta, pos, i, "partner")
+        x = rng.standard_normal((50, 192)).astype(np.float32)
+        assert np.array_equal(oracle.rope(x, np.zeros(50), theta, lib=lib), x.astype(np.float64))
+        pos = rng.integers(0, 262144, 50)
+        out = oracle.rope(x, pos, theta, lib=lib)
+        assert np.array_equal(out[:, 64:], x[:, 64:].astype(np.float64))
+        n_in = x[:, :32].astype(np.float64) ** 2 + x[:, 32:64].astype(np.float64) ** 2
+        assert np.allclose(out[:, :32] ** 2 + out[:, 32:64] ** 2, n_in, rtol=1e-12, atol=0)
+        qv, kv = x[:25], x[25:]
+        m, n = pos[:25], rng.integers(0, 262144, 25)
+        lhs = np.sum(oracle.rope(qv, m, theta, lib=lib)[:, :64] * oracle.rope(kv, n, theta, lib=lib)[:, :64], axis=1)
+        rhs = np.sum(oracle.rope(qv, m - n, theta, lib=lib)[:, :64] * kv[:, :64].astype(np.float64), axis=1)
+        assert np.allclose(lhs, rhs, rtol=1e-9, atol=1e-9), "relative-position property"
+
+
+def pin_append_then_decode_is_prefill(lib):
+    """Tokens appended one step at a time into a ring and into pages, then decoded, give the
+    prefill rows of the whole sequence (both modes for pages; the ring in sliding mode)."""
+    B, Hq, Hkv, dqk, dv, L, W, ps = 2, 4, 2, 16, 8, 45, 6, 8
+    q = _rand((B, Hq, L, dqk), 1200)
+    k = _rand((B, Hkv, L, dqk), 1201)
+    v = _rand((B, Hkv, L, dv), 1202)
+    sink = np.array([1.0, 2.0, 0.5, 4.0])
+    kr = np.zeros((B, Hkv, W, dqk), np.float32)
+    vr = np.zeros((B, Hkv, W, dv), np.float32)
+    bt = np.random.default_rng(1203).permutation(B * 6 + 2)[:B * 6].reshape(B, 6).astype(np.int32)
+    kp = np.zeros((B * 6 + 2, Hkv, ps, dqk), np.float32)
+    vp = np.zeros((B * 6 + 2, Hkv, ps, dv), np.float32)
+    pre_swa = oracle.prefill(q, k, v, sink, oracle.SWA, W, 0.3, lib=lib)
+    pre_ga = oracle.prefill(q, k, v, sink, oracle.GLOBAL, 0, 0.3, lib=lib)
+    n = 0
+    for step in (3, 1, 1, 7, 1, 20, 12):  # new tokens per step; the first steps act as prefill
+        lens = np.full(B, n + step, np.int32)
+        oracle.kv_append(kr, vr, oracle.RING, k[:, :, n:n + step], v[:, :, n:n + step], lens, window=W)
+        oracle.kv_append(kp, vp, oracle.PAGED, k[:, :, n:n + step], v[:, :, n:n + step], lens, block_table=bt)
+        n += step
+        qn = np.ascontiguousarray(q[:, :, n - 1])
+        got = oracle.decode(qn, kr, vr, lens, sink, oracle.SWA, W, 0.3, oracle.RING, lib=lib)
+        _close(got, pre_swa[:, :, n - 1], 1e-12, 1e-14, f"ring after append n={n}")
+        for mode, Wm, pre in ((oracle.SWA, W, pre_swa), (oracle.GLOBAL, 0, pre_ga)):
+            got = oracle.decode(qn, kp, vp, lens, sink, mode, Wm, 0.3, oracle.PAGED, bt, lib=lib)
+            _close(got, pre[:, :, n - 1], 1e-12, 1e-14, f"pages after append n={n} mode={mode}")
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
     pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes,
-    pin_fp8_decode_is_decode_of_values,
+    pin_fp8_decode_is_decode_of_values, pin_lse, pin_rope, pin_append_then_decode_is_prefill,
 ]

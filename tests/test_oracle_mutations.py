@@ -14,8 +14,8 @@ MUTATIONS = {
     "sink dropped from the denominator": ("double z = has_sink ? exp(sink - m) : 0.0;", "double z = 0.0;"),
     "sink multiplied by the logit scale": ("double m = has_sink ? sink : -INFINITY;",
                                            "sink *= scale; double m = has_sink ? sink : -INFINITY;"),
-    "sink given a unit value": ("if (n == 0 || isinf(m)) return;",
-                                "if (n == 0 || isinf(m)) return; if (has_sink) out[0] += 0.0 + exp(sink - m) / (exp(sink - m) + 1.0) * 0.5;"),
+    "sink given a unit value": ("if (n == 0 || isinf(m)) return m;",
+                                "if (n == 0 || isinf(m)) return m; if (has_sink) out[0] += 0.0 + exp(sink - m) / (exp(sink - m) + 1.0) * 0.5;"),
     "window one key too wide": ("(i - window + 1 > 0 ? i - window + 1 : 0) : 0;\n            int cnt = 0;",
                                 "(i - window > 0 ? i - window : 0) : 0;\n            int cnt = 0;"),
     "causal mask excludes self": ("for (int64_t j = jlo; j <= i; ++j, ++cnt) {",
@@ -38,6 +38,11 @@ MUTATIONS = {
     "E4M3 subnormals without the 2^-9 scale": ("if (e == 0) x = ldexp((double)m, -9);", "if (e == 0) x = ldexp((double)m, -6);"),
     "cache scale applied to the value twice": ("out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));",
                                                "out[e] += s * (vscale * vscale * load(v, vidx[t] + e, kvdtype));"),
+    "log-sum-exp without the row max": ("    return m + log(z);", "    return log(z);"),
+    "rotary sine with the wrong sign": ("out[base + i] = a * c - b * sn;", "out[base + i] = a * c + b * sn;"),
+    "rotary frequencies over all 192 dimensions": ("pow(theta, -2.0 * i / rot)", "pow(theta, -2.0 * i / dim)"),
+    "rotary pairs interleaved": ("const double a = load(x, base + i, dtype), b = load(x, base + i + half, dtype);",
+                                 "const double a = load(x, base + 2 * (i % (half / 2)) + (i >= half / 2) * half, dtype), b = load(x, base + 2 * (i % (half / 2)) + 1 + (i >= half / 2) * half, dtype);"),
     "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
                                           "vi[cnt] = (size_t)(((b * Hkv + g) * Lk + i) * dv);"),
 }
