@@ -52,9 +52,14 @@ class KVDesc(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
+class Epilogue(ctypes.Structure):
+    _fields_ = [("out_scale", ctypes.c_float), ("lse", ctypes.c_void_p)]
+
+
 EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_prefill_chunk",
-           "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_decode",
-           "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes", "sinkattn_decode_fp8",
+           "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
+           "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
+           "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_rope", "sinkattn_kv_append",
            "sinkattn_status_string")
 
 _lib = None
@@ -92,6 +97,19 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_fp8.restype = I
     L.sinkattn_decode_fp8.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), P,
                                       ctypes.c_int32, P, ctypes.c_float, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    L.sinkattn_prefill_ex.restype = I
+    L.sinkattn_prefill_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, P, P, P, ctypes.POINTER(Epilogue),
+                                      P, P, ctypes.c_size_t, P]
+    L.sinkattn_decode_ex.restype = I
+    L.sinkattn_decode_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
+                                     ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P,
+                                     P, ctypes.c_size_t, P]
+    L.sinkattn_rope.restype = I
+    L.sinkattn_rope.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
+                                P]
+    L.sinkattn_kv_append.restype = I
+    L.sinkattn_kv_append.argtypes = [ctypes.POINTER(KVDesc), I, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                     P, I, ctypes.c_float, ctypes.c_float, P]
     L.sinkattn_status_string.restype = ctypes.c_char_p
     L.sinkattn_status_string.argtypes = [I]
     if path == LIB_PATH:
@@ -230,10 +248,12 @@ def sinkattn_decode_multi_workspace_bytes(mode: int, window: int, batch: int, hq
     return n
 
 
-def _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out, workspace, block_table):
+def _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out, workspace, block_table,
+                 kv_fp8=False):
     """Checks the decode tensors and builds the cache descriptor (q is [B,Hq,q_len,192] here)."""
     import torch
 
+    cdt = torch.uint8 if kv_fp8 else torch.bfloat16
     B, Hq, _, dqk = q.shape
     Hkv = k_cache.shape[1]
     dv = v_cache.shape[3]
@@ -243,13 +263,13 @@ def _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out
     if sink is not None:
         _dev_tensor(sink, "sink", torch.float32, (Hq,))
     if layout == KV_RING:
-        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (B, Hkv, window, dqk))
-        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (B, Hkv, window, dv))
+        _dev_tensor(k_cache, "k_cache", cdt, (B, Hkv, window, dqk))
+        _dev_tensor(v_cache, "v_cache", cdt, (B, Hkv, window, dv))
         desc = KVDesc(KV_RING, k_cache.data_ptr(), v_cache.data_ptr(), None, 0, 0, 0)
     elif layout == KV_PAGED:
         P, _, ps, _ = k_cache.shape
-        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (P, Hkv, ps, dqk))
-        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (P, Hkv, ps, dv))
+        _dev_tensor(k_cache, "k_cache", cdt, (P, Hkv, ps, dqk))
+        _dev_tensor(v_cache, "v_cache", cdt, (P, Hkv, ps, dv))
         _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
         desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps,
                       block_table.shape[1], P)
@@ -355,6 +375,112 @@ def decode(mode: int, window: int, q, layout: int, k_cache, v_cache, seq_lens, m
     sinkattn_decode(mode, window, q, layout, k_cache, v_cache, seq_lens, max_seq_len, sink, out, workspace,
                     block_table, scale, stream)
     return out
+
+
+def _epilogue(out_scale, lse, shape, device):
+    import torch
+
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, shape)
+        if lse.device != device:
+            raise ValueError("all tensors must be on one device")
+    return Epilogue(out_scale, None if lse is None else lse.data_ptr())
+
+
+def sinkattn_prefill_ex(mode: int, window: int, q, k, v, sink, out, workspace, out_scale: float = 1.0, lse=None,
+                        scale: float | None = None, stream=None) -> None:
+    """sinkattn_prefill_chunk (q [B,Hq,Lq,192] after a prefix: k, v hold kv_len = k.shape[2]
+    keys) with an epilogue: out = out_scale * attention, lse float32 [B,Hq,Lq] or None."""
+    import torch
+
+    B, Hq, Lq, dqk = q.shape
+    Hkv, kv_len = k.shape[1], k.shape[2]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(k, "k", torch.bfloat16, (B, Hkv, kv_len, dqk))
+    _dev_tensor(v, "v", torch.bfloat16, (B, Hkv, kv_len, v.shape[3]))
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, Lq, v.shape[3]))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    for t in (k, v, out, sink, workspace):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    ep = _epilogue(out_scale, lse, (B, Hq, Lq), q.device)
+    d = Dims(B, Lq, Hq, Hkv, dqk, v.shape[3], dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_prefill_ex(mode, window, ctypes.byref(d), kv_len, _ptr(q), _ptr(k), _ptr(v), _ptr(sink),
+                                       ctypes.byref(ep), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def sinkattn_decode_ex(mode: int, window: int, q_len: int, q, layout: int, k_cache, v_cache, seq_lens,
+                       max_seq_len: int, sink, out, workspace, block_table=None, kv_fp8: bool = False,
+                       k_scale: float = 1.0, v_scale: float = 1.0, out_scale: float = 1.0, lse=None,
+                       scale: float | None = None, stream=None) -> None:
+    """Decode with every option: q bf16 [B,Hq,q_len,192], out bf16 [B,Hq,q_len,128]; caches
+    bf16 (kv_fp8 False) or uint8 E4M3 codes (kv_fp8 True, paged); lse float32 [B,Hq,q_len]."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, ws_ptr, ws_bytes = _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens,
+                                                               sink, out, workspace, block_table, kv_fp8)
+    ep = _epilogue(out_scale, lse, (B, Hq, q_len), q.device)
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode_ex(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
+                                      1 if kv_fp8 else 0, k_scale, v_scale, _ptr(seq_lens), max_seq_len, _ptr(sink),
+                                      ctypes.byref(ep), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+SWA_ROPE_THETA = 10000.0
+GA_ROPE_THETA = 5000000.0
+
+
+def sinkattn_rope(theta: float, x, seq_lens=None, pos0: int = 0, stream=None) -> None:
+    """Rotate the first 64 of the 192 dimensions of x bf16 [B,H,rows,192] in place; row r of
+    sequence b at position seq_lens[b] - rows + r (seq_lens int32 [B] on the device) or
+    pos0 + r."""
+    import torch
+
+    B, H, rows, d = x.shape
+    _dev_tensor(x, "x", torch.bfloat16, (B, H, rows, 192))
+    if seq_lens is not None:
+        _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    with torch.cuda.device(x.device):
+        rc = lib().sinkattn_rope(theta, B, H, rows, _ptr(x), _ptr(seq_lens), pos0, _stream_ptr(stream, x.device))
+    _raise(rc)
+
+
+def sinkattn_kv_append(layout: int, k_cache, v_cache, k_new, v_new, seq_lens, window: int = 0, block_table=None,
+                       kv_fp8: bool = False, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Write k_new bf16 [B,Hkv,n,192] and v_new bf16 [B,Hkv,n,128] at positions
+    seq_lens[b] - n .. seq_lens[b] - 1 into a ring ([B,Hkv,window,d]) or paged
+    ([P,Hkv,page,d]) cache, bf16 or uint8 E4M3 codes (kv_fp8)."""
+    import torch
+
+    B, Hkv, n, dqk = k_new.shape
+    cdt = torch.uint8 if kv_fp8 else torch.bfloat16
+    _dev_tensor(k_new, "k_new", torch.bfloat16, (B, Hkv, n, 192))
+    _dev_tensor(v_new, "v_new", torch.bfloat16, (B, Hkv, n, 128))
+    _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    if layout == KV_RING:
+        _dev_tensor(k_cache, "k_cache", cdt, (B, Hkv, window, 192))
+        _dev_tensor(v_cache, "v_cache", cdt, (B, Hkv, window, 128))
+        desc = KVDesc(KV_RING, k_cache.data_ptr(), v_cache.data_ptr(), None, 0, 0, 0)
+    else:
+        P, _, ps, _ = k_cache.shape
+        _dev_tensor(k_cache, "k_cache", cdt, (P, Hkv, ps, 192))
+        _dev_tensor(v_cache, "v_cache", cdt, (P, Hkv, ps, 128))
+        _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
+        desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps,
+                      block_table.shape[1], P)
+    with torch.cuda.device(k_new.device):
+        rc = lib().sinkattn_kv_append(ctypes.byref(desc), window, B, Hkv, n, _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                                      1 if kv_fp8 else 0, k_scale, v_scale, _stream_ptr(stream, k_new.device))
+    _raise(rc)
 
 
 def sinkattn_decode_fp8(mode: int, window: int, q_len: int, q, k_cache, v_cache, seq_lens, max_seq_len: int, sink,

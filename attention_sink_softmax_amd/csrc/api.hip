@@ -21,6 +21,14 @@ constexpr double kLog2eD = 1.4426950408889634;
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Optional epilogue: a finite output scale and a 4-byte aligned LSE buffer.
+int check_epilogue(const sinkattn_epilogue *ep) {
+    if (!ep) return SINKATTN_OK;
+    if (!isfinite(ep->out_scale)) return SINKATTN_E_SHAPE;
+    if (ep->lse && (reinterpret_cast<uintptr_t>(ep->lse) & 3u)) return SINKATTN_E_ALIGN;
+    return SINKATTN_OK;
+}
+
 int check_dims(int mode, int window, const sinkattn_dims *d) {
     if (!d) return SINKATTN_E_NULL;
     if (mode != SINKATTN_GLOBAL && mode != SINKATTN_SWA) return SINKATTN_E_UNSUPPORTED;
@@ -105,7 +113,16 @@ int sinkattn_prefill(int mode, int window, const sinkattn_dims *d, const void *q
 int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t kv_len, const void *q,
                            const void *k, const void *v, const float *sink, void *out, void *workspace,
                            size_t workspace_bytes, void *stream) {
+    return sinkattn_prefill_ex(mode, window, d, kv_len, q, k, v, sink, nullptr, out, workspace, workspace_bytes,
+                               stream);
+}
+
+int sinkattn_prefill_ex(int mode, int window, const sinkattn_dims *d, int32_t kv_len, const void *q, const void *k,
+                        const void *v, const float *sink, const sinkattn_epilogue *ep, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     int st = check_dims(mode, window, d);
+    if (st) return st;
+    st = check_epilogue(ep);
     if (st) return st;
     if (d->seqlen < 0 || kv_len < d->seqlen) return SINKATTN_E_SHAPE;
     if ((int64_t)kv_len * kDqkSupported * 2 > INT32_MAX) return SINKATTN_E_SHAPE;  // 32-bit row offsets
@@ -135,6 +152,8 @@ int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t
     p.swa = mode == SINKATTN_SWA;
     p.window = p.swa ? window : 0;
     p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    p.out_scale = ep ? ep->out_scale : 1.f;
+    p.lse = ep ? ep->lse : nullptr;
     if (plan_prefill(p) > INT32_MAX) return SINKATTN_E_SHAPE;
     return launch_prefill(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
@@ -156,9 +175,17 @@ namespace {
 // Decode from a bf16 cache (fp8 = 0) or an E4M3 cache with per-tensor scales (fp8 = 1).
 int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q, const sinkattn_kv *kv,
                   const int32_t *seq_lens, int32_t max_seq_len, const float *sink, int fp8, float k_scale,
-                  float v_scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+                  float v_scale, const sinkattn_epilogue *ep, void *out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
     int st = check_dims(mode, window, d);
     if (st) return st;
+    st = check_epilogue(ep);
+    if (st) return st;
+    if (fp8) {
+        if (!kv) return SINKATTN_E_NULL;
+        if (kv->layout != SINKATTN_KV_PAGED || kv->page_size <= 0 || kv->page_size % 32) return SINKATTN_E_UNSUPPORTED;
+        if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)) return SINKATTN_E_SHAPE;
+    }
     if (q_len < 1 || q_len > kMaxQLen) return SINKATTN_E_SHAPE;
     if (!kv) return SINKATTN_E_NULL;
     if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
@@ -205,7 +232,8 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
     p.max_seq_len = max_seq_len;
     p.scale_log2 = (float)((double)d->scale * kLog2eD * (fp8 ? (double)k_scale : 1.0));
     p.fp8 = fp8;
-    p.v_scale = fp8 ? v_scale : 1.f;
+    p.out_scale = (fp8 ? v_scale : 1.f) * (ep ? ep->out_scale : 1.f);
+    p.lse = ep ? ep->lse : nullptr;
     p.nsplit = pl.nsplit;
     p.chunk = pl.chunk;
     if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq * p.q_len > INT32_MAX)
@@ -219,20 +247,83 @@ extern "C" {
 int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                           const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
                           void *out, void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 0, 1.f, 1.f, out, workspace,
-                         workspace_bytes, stream);
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 0, 1.f, 1.f, nullptr, out,
+                         workspace, workspace_bytes, stream);
+}
+
+int sinkattn_decode_ex(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                       const sinkattn_kv *kv, int kv_fp8, float k_scale, float v_scale, const int32_t *seq_lens,
+                       int32_t max_seq_len, const float *sink, const sinkattn_epilogue *ep, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0, k_scale,
+                         v_scale, ep, out, workspace, workspace_bytes, stream);
 }
 
 int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                         const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
                         float k_scale, float v_scale, void *out, void *workspace, size_t workspace_bytes,
                         void *stream) {
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 1, k_scale, v_scale, nullptr,
+                         out, workspace, workspace_bytes, stream);
+}
+
+int sinkattn_rope(double theta, int32_t batch, int32_t heads, int32_t rows, void *x, const int32_t *seq_lens,
+                  int32_t pos0, void *stream) {
+    if (!(theta > 0.0) || !isfinite(theta)) return SINKATTN_E_SHAPE;
+    if (batch < 0 || heads < 0 || rows < 0 || batch > 65535) return SINKATTN_E_SHAPE;
+    if (batch == 0 || heads == 0 || rows == 0) return SINKATTN_OK;
+    if (!x) return SINKATTN_E_NULL;
+    if (misaligned(x) || (seq_lens && misaligned(seq_lens))) return SINKATTN_E_ALIGN;
+    RopeParams p{};
+    p.x = static_cast<uint16_t *>(x);
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.heads = heads;
+    p.rows = rows;
+    p.pos0 = pos0;
+    for (int i = 0; i < 32; ++i) p.inv_freq[i] = pow(theta, -2.0 * i / 64.0);
+    return launch_rope(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t hkv, int32_t n_new,
+                       const void *k_new, const void *v_new, const int32_t *seq_lens, int kv_fp8, float k_scale,
+                       float v_scale, void *stream) {
     if (!kv) return SINKATTN_E_NULL;
-    if (kv->layout != SINKATTN_KV_PAGED || kv->page_size <= 0 || kv->page_size % 32) return SINKATTN_E_UNSUPPORTED;
-    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale))
+    if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
+    if (batch < 0 || hkv < 1 || n_new < 0 || batch > 65535) return SINKATTN_E_SHAPE;
+    if (kv->layout == SINKATTN_KV_RING && window < 1) return SINKATTN_E_SHAPE;
+    if (kv->layout == SINKATTN_KV_PAGED && (kv->page_size <= 0 || kv->max_pages <= 0 || kv->num_pages <= 0))
         return SINKATTN_E_SHAPE;
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 1, k_scale, v_scale, out,
-                         workspace, workspace_bytes, stream);
+    if (kv_fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)))
+        return SINKATTN_E_SHAPE;
+    if (batch == 0 || n_new == 0) return SINKATTN_OK;
+    if (!kv->k || !kv->v || !k_new || !v_new || !seq_lens) return SINKATTN_E_NULL;
+    if (kv->layout == SINKATTN_KV_PAGED && !kv->block_table) return SINKATTN_E_NULL;
+    if (misaligned(kv->k) || misaligned(kv->v) || misaligned(k_new) || misaligned(v_new) || misaligned(seq_lens) ||
+        (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
+        return SINKATTN_E_ALIGN;
+    AppendParams p{};
+    p.k_new = static_cast<const uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
+    // the descriptor is shared with decode, which only reads; appending writes the cache
+    p.k_cache = static_cast<uint16_t *>(const_cast<void *>(kv->k));
+    p.v_cache = static_cast<uint16_t *>(const_cast<void *>(kv->v));
+    p.k_cache8 = static_cast<uint8_t *>(const_cast<void *>(kv->k));
+    p.v_cache8 = static_cast<uint8_t *>(const_cast<void *>(kv->v));
+    p.paged = kv->layout == SINKATTN_KV_PAGED;
+    p.block_table = p.paged ? kv->block_table : nullptr;
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.hkv = hkv;
+    p.n_new = n_new;
+    p.window = p.paged ? 0 : window;
+    p.page_size = p.paged ? kv->page_size : 0;
+    p.max_pages = p.paged ? kv->max_pages : 0;
+    p.num_pages = p.paged ? kv->num_pages : 0;
+    p.fp8 = kv_fp8 ? 1 : 0;
+    p.k_scale = kv_fp8 ? k_scale : 1.f;
+    p.v_scale = kv_fp8 ? v_scale : 1.f;
+    return launch_kv_append(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 
 int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,

@@ -9,6 +9,7 @@ namespace sinkattn {
 constexpr int kDqk = 192;  // q/k head size
 constexpr int kDv = 128;   // v head size
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

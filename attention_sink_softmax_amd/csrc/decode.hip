@@ -415,35 +415,36 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
             }
-            if constexpr (kFp8) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] *= p.v_scale;
-            }
             if (p.nsplit == 1) {
-                // final output: add the sink term once, normalise, round to bf16
+                // final output: add the sink term once, normalise, scale, round to bf16; the
+                // row's log-sum-exp (natural log) on request
                 uint16_t *orow = p.out + row * kDv + d0;
                 float res[8];
-                if (n - p.q_len + tok < 0) {
+                const float sk = p.sink ? p.sink[h2] : -INFINITY;
+                float lse;
+                if (n - p.q_len + tok < 0) {  // no visible key: the sink alone
 #pragma unroll
                     for (int e = 0; e < 8; ++e) res[e] = 0.f;
+                    lse = sk;
                 } else if (!seq_ok || any_bad) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) res[e] = __builtin_nanf("");
+                    lse = __builtin_nanf("");
+                } else if (sk == INFINITY) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) res[e] = 0.f;
+                    lse = INFINITY;
                 } else {
-                    const float sk = p.sink ? p.sink[h2] : -INFINITY;
-                    if (sk == INFINITY) {
+                    const float sl = sk * kLog2e;
+                    const float M2 = fmaxf(M, sl);
+                    const float sc = exp2f_fast(M - M2);
+                    const float Lt = L * sc + (sk == -INFINITY ? 0.f : exp2f_fast(sl - M2));
+                    const float inv = p.out_scale / Lt;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) res[e] = 0.f;
-                    } else {
-                        const float sl = sk * kLog2e;
-                        const float M2 = fmaxf(M, sl);
-                        const float sc = exp2f_fast(M - M2);
-                        const float Lt = L * sc + (sk == -INFINITY ? 0.f : exp2f_fast(sl - M2));
-                        const float inv = 1.f / Lt;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) res[e] = o[e] * sc * inv;
-                    }
+                    for (int e = 0; e < 8; ++e) res[e] = o[e] * sc * inv;
+                    lse = (M2 + __builtin_amdgcn_logf(Lt)) * kLn2;
                 }
+                if (p.lse && (tid & 15) == 0) p.lse[row] = lse;
                 *reinterpret_cast<u32x4 *>(orow) = u32x4{pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]),
                                                          pack_bf16x2(res[4], res[5]), pack_bf16x2(res[6], res[7])};
             } else {
@@ -470,9 +471,11 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     const int n = p.seq_lens[b];
     uint16_t *out = p.out + row * kDv + t;
     const bool seq_ok = seq_valid(p, n);
+    const float sk = p.sink ? p.sink[h] : -INFINITY;
     if (n - p.q_len + tok < 0 || !seq_ok) {
-        const float z = n - p.q_len + tok < 0 ? 0.f : __builtin_nanf("");
-        *out = __builtin_bit_cast(uint16_t, (__bf16)z);
+        const bool before = n - p.q_len + tok < 0;  // no visible key: the sink alone
+        *out = __builtin_bit_cast(uint16_t, (__bf16)(before ? 0.f : __builtin_nanf("")));
+        if (p.lse && t == 0) p.lse[row] = before ? sk : __builtin_nanf("");
         return;
     }
     int kbeg, kend;
@@ -482,7 +485,6 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     const float *base = p.ws + row * p.nsplit * kPart;
 
 
-    const float sk = p.sink ? p.sink[h] : -INFINITY;
     const bool sink_inf = sk == INFINITY;
     const float sl = (sink_inf ? -INFINITY : sk) * kLog2e;  // an infinite sink is applied at the end
     float M = sl;
@@ -520,9 +522,10 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
         L += e * rec[kDv + 1];
         o += e * rec[t];
     }
-    float r = o / L;
+    float r = o * (p.out_scale / L);
     if (sink_inf && !__builtin_isnan(L)) r = 0.f;
     *out = __builtin_bit_cast(uint16_t, (__bf16)r);
+    if (p.lse && t == 0) p.lse[row] = sink_inf && !__builtin_isnan(L) ? INFINITY : (Mu + __builtin_amdgcn_logf(L)) * kLn2;
 }
 
 }  // namespace

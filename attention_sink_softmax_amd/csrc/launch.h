@@ -14,6 +14,8 @@ struct PrefillParams {
     uint16_t *out;
     int B, L, Hq, Hkv, G;  // L: keys per sequence (positions 0..L-1)
     int Lq, q0;            // query rows in q and out, at positions q0 .. q0 + Lq - 1 (q0 = L - Lq)
+    float out_scale;       // multiplies the output
+    float *lse;            // optional: natural-log log-sum-exp per row [B][Hq][Lq], or nullptr
     int swa, window;
     float scale_log2;  // logit scale * log2(e)
     // work layout, filled by plan_prefill
@@ -38,8 +40,28 @@ struct DecodeParams {
     int swa, window, paged, page_size, max_pages, num_pages, max_seq_len;
     float scale_log2;  // logit scale * log2(e) (8-bit cache: times the K scale)
     int fp8;           // K and V are E4M3 codes (paged, page_size a multiple of 32)
-    float v_scale;     // 8-bit cache: V element = v_scale * code value
+    float out_scale;   // multiplies the output (8-bit cache: times the V scale)
+    float *lse;        // optional: natural-log log-sum-exp per row [B][Hq][q_len], or nullptr
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
+};
+
+// Partial rotary embedding of x [batch][heads][rows][kDqk] in place; row r of sequence b sits
+// at position (seq_lens ? seq_lens[b] - rows : pos0) + r.
+struct RopeParams {
+    uint16_t *x;
+    const int32_t *seq_lens;
+    int batch, heads, rows, pos0;
+    double inv_freq[32];  // theta^(-2i/64)
+};
+
+// New tokens -> KV cache: token t of sequence b (position seq_lens[b] - n_new + t).
+struct AppendParams {
+    const uint16_t *k_new, *v_new;  // [batch][hkv][n_new][kDqk or kDv]
+    uint16_t *k_cache, *v_cache;    // bf16 caches
+    uint8_t *k_cache8, *v_cache8;   // E4M3 caches (fp8)
+    const int32_t *block_table, *seq_lens;
+    int batch, hkv, n_new, paged, window, page_size, max_pages, num_pages, fp8;
+    float k_scale, v_scale;  // fp8: codes of value / scale
 };
 
 size_t prefill_workspace_bytes(int B, int Hkv, int L);
@@ -48,5 +70,7 @@ size_t prefill_workspace_bytes(int B, int Hkv, int L);
 int64_t plan_prefill(PrefillParams &p);
 int launch_prefill(const PrefillParams &p, hipStream_t stream);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
+int launch_rope(const RopeParams &p, hipStream_t stream);
+int launch_kv_append(const AppendParams &p, hipStream_t stream);
 
 }  // namespace sinkattn

@@ -344,17 +344,21 @@ __device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSet
     }
 }
 
-// O = acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi (row qi - q0).
+// O = out_scale * acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi (row
+// qi - q0).  On request the row's log-sum-exp in natural log, (m + log2 l) ln 2: m is the
+// reference the sums are kept against (log2 units of the scaled logits, the sink included).
 template <int HPW>
 __device__ __forceinline__ void store_out(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w, bool live,
-                                          const f32x16 (&acc)[HPW][4], const float (&l_run)[HPW],
-                                          const bool (&sink_inf)[HPW]) {
+                                          const f32x16 (&acc)[HPW][4], const float (&m_run)[HPW],
+                                          const float (&l_run)[HPW], const bool (&sink_inf)[HPW]) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
         const float lt = sum_xor32(l_run[h]);
         if (!live || w.qi >= p.L) continue;
-        const float inv = 1.f / lt;
-        uint16_t *orow = p.out + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq) + (w.qi - p.q0)) * kDv + 4 * w.g;
+        const float inv = p.out_scale / lt;
+        const size_t row = (((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq) + (w.qi - p.q0);
+        if (p.lse && w.g == 0) p.lse[row] = (m_run[h] + __builtin_amdgcn_logf(lt)) * kLn2;
+        uint16_t *orow = p.out + row * kDv + 4 * w.g;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
         step(kt, KA, VA, KB, VB);
         if (kt + 1 <= t1) step(kt + 1, KB, VB, KA, VA);
     }
-    store_out<HPW>(p, ws, w, wave_live, acc, l_run, sink_inf);
+    store_out<HPW>(p, ws, w, wave_live, acc, m_run, l_run, sink_inf);
 }
 
 // ---- causal kernel: eight waves, one head each, all at the same 32 positions (the eight
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
         if (t + 2 <= t1) step(t + 2, K2, K0, V2, K1, V1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
-    store_out<HPW>(p, ws, w, true, acc, l_run, sink_inf);
+    store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
 }
 
 // V -> V^T tile by tile: tile t of (batch, kv head) is a contiguous [128 dv][64 keys] block

@@ -91,6 +91,26 @@ typedef struct {
 } sinkattn_kv;
 
 /*
+ * Optional work at the end of the attention (the *_ex entry points; a NULL pointer means
+ * out_scale = 1 and no lse).
+ *   out_scale  multiplies every output element; must be finite.  The attention layer scales
+ *              the values by 0.707 before attention ("MiMo-V2-Flash 模型架构深度拆解", CH 10.3
+ *              forward step 2; "MiMo-V2-Flash 架构 QA", Q2.10); the output is linear in the
+ *              values, so passing that factor here gives the same result without a pass
+ *              over V.
+ *   lse        device float32, 4-byte aligned, one value per output row laid out like the
+ *              output without its last axis, or NULL: the row's log-sum-exp in natural
+ *              log, log(exp(sink) + sum over the visible keys of exp(scale * q.k)), the
+ *              log of the sink softmax denominator ("MiMo-V2-Flash 架构 QA", Q3.8).  No
+ *              sink and no visible key: -inf; a row before its sequence (decode): the
+ *              sink; sink +inf: +inf; a row whose output is NaN: NaN.
+ */
+typedef struct {
+    float out_scale;
+    float *lse;
+} sinkattn_epilogue;
+
+/*
  * Bytes of device workspace sinkattn_prefill needs for these sizes (batch, seqlen, hkv are
  * read): a transposed copy of V, 2 * batch * hkv * 128 * roundup(seqlen, 64) bytes.
  * Returns (size_t)-1 for invalid sizes.
@@ -147,6 +167,16 @@ size_t sinkattn_prefill_chunk_workspace_bytes(const sinkattn_dims *d, int32_t kv
 int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t kv_len,
                            const void *q, const void *k, const void *v, const float *sink,
                            void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sinkattn_prefill_chunk with an epilogue (lse: float32 [batch][hq][seqlen]).  Errors as
+ * sinkattn_prefill_chunk; a non-finite out_scale is SINKATTN_E_SHAPE, a misaligned lse
+ * SINKATTN_E_ALIGN.
+ */
+int sinkattn_prefill_ex(int mode, int window, const sinkattn_dims *d, int32_t kv_len,
+                        const void *q, const void *k, const void *v, const float *sink,
+                        const sinkattn_epilogue *ep, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of device workspace sinkattn_decode needs for these arguments (0 when none).
@@ -231,6 +261,56 @@ int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_
                         const void *q, const sinkattn_kv *kv, const int32_t *seq_lens,
                         int32_t max_seq_len, const float *sink, float k_scale, float v_scale,
                         void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Partial rotary position embedding, in place ("MiMo-V2-Flash 模型架构深度拆解", CH 3.5 and
+ * CH 10.5; "MiMo-V2-Flash 架构 QA", Q2.7): of each row's 192 q or k dimensions only the first
+ * 64 turn, pair i (dimensions i and i + 32) by the angle pos * theta^(-2i/64); the other 128
+ * carry content only.  theta is 10 000 in sliding-window layers and 5 000 000 in global
+ * ones.  Apply it to q and to the new keys before attention and before sinkattn_kv_append.
+ *   theta     > 0, finite (else SINKATTN_E_SHAPE)
+ *   x         bf16 [batch][heads][rows][192], rotated in place
+ *   seq_lens  device int32 [batch] or NULL: with it, row r of sequence b is at position
+ *             seq_lens[b] - rows + r (the new tokens of a decode step); without it at
+ *             pos0 + r (a prefill chunk starting at pos0)
+ * The angle is formed in double precision and reduced before its sine and cosine are taken
+ * in float, so positions up to 256K keep their accuracy.  Zero sizes are a no-op.
+ */
+int sinkattn_rope(double theta, int32_t batch, int32_t heads, int32_t rows, void *x,
+                  const int32_t *seq_lens, int32_t pos0, void *stream);
+
+/*
+ * Write new tokens' keys and values into a KV cache (the cache update that precedes
+ * attention, deep-dive CH 10.3 forward step 6).
+ *   kv        descriptor of the cache to write (RING or PAGED, as for decode; the library
+ *             writes through its k and v pointers)
+ *   window    ring slots (RING)
+ *   batch, hkv, n_new  sizes; n_new tokens per sequence
+ *   k_new     bf16 [batch][hkv][n_new][192] (already rotated), v_new bf16 [batch][hkv][n_new][128]
+ *   seq_lens  device int32 [batch]: tokens per sequence INCLUDING the new ones; token t
+ *             goes to position seq_lens[b] - n_new + t
+ *   kv_fp8    0: bf16 cache; 1: E4M3 cache, codes of value / k_scale (or v_scale), rounded
+ *             to nearest even and clamped to +-448
+ * Positions below 0, ring positions older than the last `window` of the sequence, and page
+ * ids outside [0, num_pages) are skipped.  Errors: SINKATTN_E_NULL, _SHAPE, _ALIGN,
+ * _UNSUPPORTED as for decode.
+ */
+int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t hkv, int32_t n_new,
+                       const void *k_new, const void *v_new, const int32_t *seq_lens, int kv_fp8,
+                       float k_scale, float v_scale, void *stream);
+
+/*
+ * Decode with every option: q_len new tokens (as sinkattn_decode_multi), a bf16 cache
+ * (kv_fp8 = 0; k_scale and v_scale ignored) or an E4M3 cache (kv_fp8 = 1, as
+ * sinkattn_decode_fp8), and an epilogue (lse: float32 [batch][hq][q_len]).  Errors as those
+ * entry points; a non-finite out_scale is SINKATTN_E_SHAPE, a misaligned lse
+ * SINKATTN_E_ALIGN.
+ */
+int sinkattn_decode_ex(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                       const void *q, const sinkattn_kv *kv, int kv_fp8, float k_scale,
+                       float v_scale, const int32_t *seq_lens, int32_t max_seq_len,
+                       const float *sink, const sinkattn_epilogue *ep, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(int status);

@@ -201,12 +201,28 @@ def rope(x, positions, theta: float, rot: int = ROPE_DIMS, lib=None) -> np.ndarr
     return out
 
 
-def kv_append(k_cache, v_cache, layout: int, k_new, v_new, seq_lens, window: int = 0, block_table=None):
+def e4m3_encode(x, scale: float) -> np.ndarray:
+    """E4M3 codes (uint8) of x / scale: x as float32 (uint16 input = bf16 bits), divided in
+    float32, clamped to +-448, rounded to nearest even by torch's float8_e4m3fn conversion."""
+    import torch
+
+    xa = np.asarray(x)
+    if xa.dtype == np.uint16:
+        xa = (xa.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    y = np.clip(xa.astype(np.float32) / np.float32(scale), np.float32(-448), np.float32(448))
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def kv_append(k_cache, v_cache, layout: int, k_new, v_new, seq_lens, window: int = 0, block_table=None,
+              fp8_scales=None):
     """Write n new tokens per sequence into a cache (in place): token t of sequence b, at
     position seq_lens[b] - n + t, goes to ring slot pos mod window (the last `window`
     positions only) or to page block_table[b][pos // page] at offset pos mod page.
     k_new [B,Hkv,n,dqk], v_new [B,Hkv,n,dv]; positions below 0 and page ids outside the pool
-    are skipped.  Plain indexing, no arithmetic."""
+    are skipped.  Plain indexing; with fp8_scales = (k_scale, v_scale) the caches hold E4M3
+    codes and the new rows are encoded by e4m3_encode first."""
+    if fp8_scales is not None:
+        k_new, v_new = e4m3_encode(k_new, fp8_scales[0]), e4m3_encode(v_new, fp8_scales[1])
     B, Hkv, n = k_new.shape[:3]
     for b in range(B):
         for t in range(n):

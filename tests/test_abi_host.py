@@ -191,6 +191,51 @@ def test_decode_fp8_argument_errors(L):
     assert L.sinkattn_decode_fp8(0, 0, ctypes.byref(dims()), 1, A, None, A, 1, None, 1.0, 1.0, A, A, 0, None) == E_NULL
 
 
+def test_rope_argument_errors(L):
+    assert L.sinkattn_rope(0.0, 1, 64, 10, A, None, 0, None) == E_SHAPE
+    assert L.sinkattn_rope(float("inf"), 1, 64, 10, A, None, 0, None) == E_SHAPE
+    assert L.sinkattn_rope(1e4, -1, 64, 10, A, None, 0, None) == E_SHAPE
+    assert L.sinkattn_rope(1e4, 1, 64, 10, None, None, 0, None) == E_NULL
+    assert L.sinkattn_rope(1e4, 1, 64, 10, A + 2, None, 0, None) == E_ALIGN
+    assert L.sinkattn_rope(1e4, 1, 64, 0, None, None, 0, None) == OK
+
+
+def test_kv_append_argument_errors(L):
+    def app(desc=None, window=128, n=1, fp8=0, ks=1.0, vs=1.0, kn=A, lens=A):
+        desc = desc if desc is not None else kv()
+        return L.sinkattn_kv_append(ctypes.byref(desc), window, 2, 4, n, kn, A, lens, fp8, ks, vs, None)
+    assert L.sinkattn_kv_append(None, 128, 1, 4, 1, A, A, A, 0, 1.0, 1.0, None) == E_NULL
+    assert app(desc=kv(layout=7)) == E_UNSUP
+    assert app(desc=kv(layout=0), window=0) == E_SHAPE
+    assert app(desc=kv(ps=0)) == E_SHAPE
+    assert app(fp8=1, ks=0.0) == E_SHAPE
+    assert app(kn=None) == E_NULL
+    assert app(lens=None) == E_NULL
+    assert app(desc=kv(bt=None)) == E_NULL
+    assert app(kn=A + 8) == E_ALIGN
+    assert app(n=0, kn=None) == OK
+
+
+def test_epilogue_argument_errors(L):
+    ep = sa.Epilogue(float("nan"), None)
+    d = dims(Lq=64)
+    assert L.sinkattn_prefill_ex(1, 128, ctypes.byref(d), 64, A, A, A, None, ctypes.byref(ep), A, A, 1 << 40,
+                                 None) == E_SHAPE
+    ep = sa.Epilogue(0.7, A + 2)
+    assert L.sinkattn_prefill_ex(1, 128, ctypes.byref(d), 64, A, A, A, None, ctypes.byref(ep), A, A, 1 << 40,
+                                 None) == E_ALIGN
+    d2 = dims(B=8, hq=64, hkv=4)
+    desc = kv()
+    ep = sa.Epilogue(float("inf"), None)
+    assert L.sinkattn_decode_ex(0, 0, ctypes.byref(d2), 1, A, ctypes.byref(desc), 0, 1.0, 1.0, A, 262144, None,
+                                ctypes.byref(ep), A, A, 1 << 30, None) == E_SHAPE
+    ep = sa.Epilogue(0.707, A + 4)  # 4-byte aligned lse is fine; the null q is reported next
+    assert L.sinkattn_decode_ex(0, 0, ctypes.byref(d2), 1, None, ctypes.byref(desc), 0, 1.0, 1.0, A, 262144, None,
+                                ctypes.byref(ep), A, A, 1 << 30, None) == E_NULL
+    assert L.sinkattn_decode_ex(0, 0, ctypes.byref(d2), 1, A, ctypes.byref(desc), 1, 0.0, 1.0, A, 262144, None,
+                                None, A, A, 1 << 30, None) == E_SHAPE
+
+
 def test_prefill_workspace_size(L):
     # a transposed copy of V, rows padded to 64 keys
     assert sa.sinkattn_prefill_workspace_bytes(1, 32768, 64, 8) == 8 * 128 * 32768 * 2
