@@ -58,6 +58,8 @@ def load(path: str = LIB):
     lib.oracle_decode_fp8.restype = I
     lib.oracle_decode_fp8.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, ctypes.c_double,
                                       ctypes.c_double, P, I, I, I, P, P, P, P]
+    lib.oracle_prefill_backward.restype = I
+    lib.oracle_prefill_backward.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, P, P, P, P, P]
     lib.oracle_rope.restype = I
     lib.oracle_rope.argtypes = [ctypes.c_int64, I, I, ctypes.c_double, I, P, P, P]
     lib.oracle_e4m3_value.restype = ctypes.c_double
@@ -181,6 +183,28 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return (out, lse) if return_lse else out
+
+
+def prefill_backward(q, k, v, sink, dout, mode: int, window: int, scale: float, lib=None):
+    """Gradients of prefill attention: q [B,Hq,L,dqk], k, v [B,Hkv,L,.], sink [Hq] or None,
+    dout [B,Hq,L,dv] (same dtype as q).  Returns float64 (dq, dk, dv, dsink or None)."""
+    lib = lib or load()
+    qa, dt = _arr(q, None)
+    ka, _ = _arr(k, None)
+    va, _ = _arr(v, None)
+    da, _ = _arr(dout, None)
+    B, Hq, L, dqk = qa.shape
+    Hkv, dv = ka.shape[1], va.shape[3]
+    s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    dq = np.empty(qa.shape, np.float64)
+    dk = np.empty(ka.shape, np.float64)
+    dvv = np.empty(va.shape, np.float64)
+    ds = None if sink is None else np.empty(Hq, np.float64)
+    rc = lib.oracle_prefill_backward(mode, window, B, L, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka), _ptr(va),
+                                     _ptr(s), _ptr(da), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(ds))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments")
+    return dq, dk, dvv, ds
 
 
 SWA_ROPE_THETA = 10000.0     # sliding-window layers (deep-dive CH 3.5)

@@ -259,6 +259,99 @@ int oracle_decode_fp8(int mode, int window, int layout, int B, int Hq, int Hkv, 
 }
 
 /*
+ * Backward of prefill attention with a sink (the sink is a learnable per-head scalar: deep-dive
+ * CH 10.1 declares it a parameter; its gradient is below).  For each row i of head h, with the
+ * forward weights P_ij = exp(a_ij - LSE_i) over the visible keys and P_i,sink = exp(sink_h -
+ * LSE_i) (the sink has no value vector), and dO_i the gradient of the output row:
+ *   dP_ij = dO_i . v_j          D_i = sum_j P_ij dP_ij          dS_ij = P_ij (dP_ij - D_i)
+ *   dq_i  = scale sum_j dS_ij k_j      dk_j += scale dS_ij q_i      dv_j += P_ij dO_i
+ *   dsink_h += dL/dsink through P_i,sink only = -P_i,sink D_i  (the sink enters the outputs
+ *   only through the shared denominator).
+ * A NULL sink has no gradient (dsink untouched).  q, k, v, dout in `dtype`; outputs doubles:
+ * dq [B][Hq][L][dqk], dk [B][Hkv][L][dqk], dv [B][Hkv][L][dv] (overwritten), dsink [Hq]
+ * (overwritten when sink is given).  Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill_backward(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv, double scale,
+                            int dtype, const void *q, const void *k, const void *v, const double *sink,
+                            const void *dout, double *dq, double *dk, double *dvo, double *dsink) {
+    if (B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
+    if (mode == ORACLE_SWA && window <= 0) return -1;
+    if (mode != ORACLE_SWA && mode != ORACLE_GLOBAL) return -1;
+    const int G = Hq / Hkv;
+    double *dsink_part = (double *)calloc((size_t)(B > 0 ? B : 1) * Hq, sizeof(double));
+    if (!dsink_part) return -1;
+    /* one (sequence, KV head) per thread: it owns the dk and dv rows of that KV head */
+#pragma omp parallel
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *pr = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+            const int64_t b = bg / Hkv, g = bg % Hkv;
+            const size_t kvbase = (size_t)(b * Hkv + g) * L;
+            for (size_t e = 0; e < (size_t)L * dqk; ++e) dk[kvbase * dqk + e] = 0.0;
+            for (size_t e = 0; e < (size_t)L * dv; ++e) dvo[kvbase * dv + e] = 0.0;
+            for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                const int has_sink = sink != NULL;
+                const double sk = has_sink ? sink[h] : 0.0;
+                for (int64_t i = 0; i < L; ++i) {
+                    const size_t qrow = (size_t)((b * Hq + h) * L + i);
+                    double *dqi = dq + qrow * dqk;
+                    for (int d = 0; d < dqk; ++d) dqi[d] = 0.0;
+                    if (has_sink && isinf(sk) && sk > 0) continue; /* every weight is 0 */
+                    const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
+                    const int n = (int)(i - jlo + 1);
+                    /* forward weights of this row */
+                    double m = has_sink ? sk : -INFINITY;
+                    for (int t = 0; t < n; ++t) {
+                        const size_t krow = (kvbase + (size_t)(jlo + t)) * dqk;
+                        double dot = 0.0;
+                        for (int d = 0; d < dqk; ++d) dot += load(q, qrow * dqk + d, dtype) * load(k, krow + d, dtype);
+                        a[t] = scale * dot;
+                        if (a[t] > m) m = a[t];
+                    }
+                    double z = has_sink ? exp(sk - m) : 0.0;
+                    for (int t = 0; t < n; ++t) z += exp(a[t] - m);
+                    for (int t = 0; t < n; ++t) pr[t] = exp(a[t] - m) / z;
+                    const double psink = has_sink ? exp(sk - m) / z : 0.0;
+                    /* dP, D */
+                    double Dsum = 0.0;
+                    for (int t = 0; t < n; ++t) {
+                        const size_t vrow = (kvbase + (size_t)(jlo + t)) * dv;
+                        double dot = 0.0;
+                        for (int e = 0; e < dv; ++e) dot += load(dout, qrow * dv + e, dtype) * load(v, vrow + e, dtype);
+                        dp[t] = dot;
+                        Dsum += pr[t] * dot;
+                    }
+                    if (has_sink) dsink_part[b * Hq + h] += -psink * Dsum;
+                    for (int t = 0; t < n; ++t) {
+                        const double ds = pr[t] * (dp[t] - Dsum);
+                        const size_t j = kvbase + (size_t)(jlo + t);
+                        for (int d = 0; d < dqk; ++d) {
+                            dqi[d] += scale * ds * load(k, j * dqk + d, dtype);
+                            dk[j * dqk + d] += scale * ds * load(q, qrow * dqk + d, dtype);
+                        }
+                        for (int e = 0; e < dv; ++e) dvo[j * dv + e] += pr[t] * load(dout, qrow * dv + e, dtype);
+                    }
+                }
+            }
+        }
+        free(a);
+        free(pr);
+        free(dp);
+    }
+    if (sink)
+        for (int h = 0; h < Hq; ++h) {
+            double acc = 0.0;
+            for (int b = 0; b < B; ++b) acc += dsink_part[b * Hq + h];
+            dsink[h] = acc;
+        }
+    free(dsink_part);
+    return 0;
+}
+
+/*
  * Partial rotary position embedding ("MiMo-V2-Flash 模型架构深度拆解", CH 3.5 and CH 10.5;
  * "MiMo-V2-Flash 架构 QA", Q2.7): only the first `rot` of the `dim` q/k dimensions are
  * rotated (64 of 192); pair i (i < rot/2) turns by the angle pos * theta^(-2i/rot), theta

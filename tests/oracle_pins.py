@@ -465,10 +465,83 @@ def pin_append_then_decode_is_prefill(lib):
             _close(got, pre[:, :, n - 1], 1e-12, 1e-14, f"pages after append n={n} mode={mode}")
 
 
+def pin_backward_autograd(lib):
+    """Gradients of sum(dO * O) against torch autograd through the eager form (concat the sink
+    column -> softmax -> drop -> times V), fp64 on the CPU, with and without a sink, both
+    modes, grouped heads."""
+    B, Hq, Hkv, L, dqk, dv = 2, 4, 2, 37, 16, 8
+    q = _rand((B, Hq, L, dqk), 1300)
+    k = _rand((B, Hkv, L, dqk), 1301)
+    v = _rand((B, Hkv, L, dv), 1302)
+    do = _rand((B, Hq, L, dv), 1303)
+    for sink_val in (np.array([0.5, 3.0, -1.0, 2.0]), None):
+        for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 6)):
+            got = oracle.prefill_backward(q, k, v, sink_val, do, mode, W, 0.35, lib=lib)
+            tq = torch.from_numpy(q.astype(np.float64)).requires_grad_()
+            tk = torch.from_numpy(k.astype(np.float64)).requires_grad_()
+            tv = torch.from_numpy(v.astype(np.float64)).requires_grad_()
+            ts = None if sink_val is None else torch.from_numpy(sink_val).requires_grad_()
+            G = Hq // Hkv
+            kx, vx = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+            sc = (tq @ kx.transpose(-1, -2)) * 0.35
+            keep = torch.from_numpy(oracle_np.mask_matrix(L, mode, W))
+            sc = sc.masked_fill(~keep, float("-inf"))
+            if ts is not None:
+                sc = torch.cat([sc, ts.view(1, Hq, 1, 1).expand(B, Hq, L, 1)], dim=-1)
+            pr = torch.softmax(sc, dim=-1)
+            if ts is not None:
+                pr = pr[..., :-1]
+            out = pr @ vx
+            (out * torch.from_numpy(do.astype(np.float64))).sum().backward()
+            _close(got[0], tq.grad.numpy(), 1e-10, 1e-12, f"dq sink={sink_val is not None} mode={mode}")
+            _close(got[1], tk.grad.numpy(), 1e-10, 1e-12, f"dk sink={sink_val is not None} mode={mode}")
+            _close(got[2], tv.grad.numpy(), 1e-10, 1e-12, f"dv sink={sink_val is not None} mode={mode}")
+            if ts is not None:
+                _close(got[3], ts.grad.numpy(), 1e-10, 1e-12, f"dsink mode={mode}")
+            else:
+                assert got[3] is None
+
+
+def pin_backward_finite_differences(lib):
+    """dL/dsink and a few dq, dk, dv entries against central differences of the forward oracle
+    (L = sum(dO * O), step 1e-5, fp64)."""
+    B, Hq, Hkv, L, dqk, dv = 1, 2, 1, 12, 8, 4
+    q = _rand((B, Hq, L, dqk), 1400).astype(np.float64)
+    k = _rand((B, Hkv, L, dqk), 1401).astype(np.float64)
+    v = _rand((B, Hkv, L, dv), 1402).astype(np.float64)
+    do = _rand((B, Hq, L, dv), 1403).astype(np.float64)
+    sink = np.array([1.5, -0.5])
+
+    def loss(q_, k_, v_, s_):
+        return float(np.sum(oracle_np.prefill(q_, k_, v_, s_, oracle.SWA, 5, 0.3) * do))
+
+    dq, dk, dvv, ds = oracle.prefill_backward(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32), sink,
+                                              do.astype(np.float32), oracle.SWA, 5, 0.3, lib=lib)
+    h = 1e-5
+    for hh in range(Hq):
+        sp, sm = sink.copy(), sink.copy()
+        sp[hh] += h
+        sm[hh] -= h
+        num = (loss(q, k, v, sp) - loss(q, k, v, sm)) / (2 * h)
+        assert abs(num - ds[hh]) < 1e-6 * max(1.0, abs(num)), f"dsink[{hh}] {ds[hh]} vs {num}"
+    q32, k32, v32 = (x.astype(np.float32).astype(np.float64) for x in (q, k, v))
+    for arr, grad, idx in ((q32, dq, (0, 1, 7, 3)), (k32, dk, (0, 0, 4, 5)), (v32, dvv, (0, 0, 9, 2))):
+        xp, xm = arr.copy(), arr.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        args_p = [q32, k32, v32]
+        args_m = [q32, k32, v32]
+        which = 0 if arr is q32 else 1 if arr is k32 else 2
+        args_p[which], args_m[which] = xp, xm
+        num = (loss(*args_p, sink) - loss(*args_m, sink)) / (2 * h)
+        assert abs(num - grad[idx]) < 1e-6 * max(1.0, abs(num)), f"grad {which} {idx}: {grad[idx]} vs {num}"
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
     pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes,
     pin_fp8_decode_is_decode_of_values, pin_lse, pin_rope, pin_append_then_decode_is_prefill,
+    pin_backward_autograd, pin_backward_finite_differences,
 ]

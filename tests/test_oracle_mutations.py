@@ -22,8 +22,9 @@ MUTATIONS = {
                                   "for (int64_t j = jlo; j < i; ++j, ++cnt) {"),
     "GQA head interleaved": ("const int64_t g = h / G;\n            const int64_t jlo", "const int64_t g = h % Hkv;\n            const int64_t jlo"),
     "wrong exponent sign": ("double s = exp(a[t] - m) / z;", "double s = exp(m - a[t]) / z;"),
-    "logit scale dropped": ("a[t] = scale * dot;", "a[t] = dot;"),
-    "max without the row logits": ("if (a[t] > m) m = a[t];", ""),
+    "logit scale dropped": ("a[t] = scale * dot;\n        if (a[t] > m) m = a[t];\n    }\n    if (n == 0",
+                            "a[t] = dot;\n        if (a[t] > m) m = a[t];\n    }\n    if (n == 0"),
+    "max without the row logits": ("if (a[t] > m) m = a[t];\n    }\n    if (n == 0", "\n    }\n    if (n == 0"),
     "ring slot off by one": ("const int64_t slot = j % window;", "const int64_t slot = (j + 1) % window;"),
     "page offset from the wrong end": ("const int64_t off = j % page_size;", "const int64_t off = page_size - 1 - j % page_size;"),
     "decode query position off by one": ("const int64_t i = nb - q_len + r % q_len;",
@@ -43,6 +44,10 @@ MUTATIONS = {
     "rotary frequencies over all 192 dimensions": ("pow(theta, -2.0 * i / rot)", "pow(theta, -2.0 * i / dim)"),
     "rotary pairs interleaved": ("const double a = load(x, base + i, dtype), b = load(x, base + i + half, dtype);",
                                  "const double a = load(x, base + 2 * (i % (half / 2)) + (i >= half / 2) * half, dtype), b = load(x, base + 2 * (i % (half / 2)) + 1 + (i >= half / 2) * half, dtype);"),
+    "sink gradient with the wrong sign": ("dsink_part[b * Hq + h] += -psink * Dsum;", "dsink_part[b * Hq + h] += psink * Dsum;"),
+    "score gradient without the row term D": ("const double ds = pr[t] * (dp[t] - Dsum);", "const double ds = pr[t] * dp[t];"),
+    "key gradient without the logit scale": ("dk[j * dqk + d] += scale * ds * load(q, qrow * dqk + d, dtype);",
+                                             "dk[j * dqk + d] += ds * load(q, qrow * dqk + d, dtype);"),
     "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
                                           "vi[cnt] = (size_t)(((b * Hkv + g) * Lk + i) * dv);"),
 }
