@@ -60,6 +60,7 @@ EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_pre
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
            "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_rope", "sinkattn_kv_append",
+           "sinkattn_prefill_backward", "sinkattn_prefill_backward_workspace_bytes",
            "sinkattn_status_string")
 
 _lib = None
@@ -104,6 +105,11 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
                                      ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P,
                                      P, ctypes.c_size_t, P]
+    L.sinkattn_prefill_backward.restype = I
+    L.sinkattn_prefill_backward.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P, P, P, P, P, P, P,
+                                            ctypes.c_size_t, P]
+    L.sinkattn_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.sinkattn_rope.restype = I
     L.sinkattn_rope.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
                                 P]
@@ -437,6 +443,51 @@ def sinkattn_decode_ex(mode: int, window: int, q_len: int, q, layout: int, k_cac
 
 SWA_ROPE_THETA = 10000.0
 GA_ROPE_THETA = 5000000.0
+
+
+def sinkattn_prefill_backward(mode: int, window: int, q, k, v, sink, out, dout, lse, dq, dk, dv, dsink, workspace,
+                              scale: float | None = None, stream=None) -> None:
+    """Gradients of prefill: q, k, v, out, dout bf16 (shapes as sinkattn_prefill), lse float32
+    [B,Hq,L] from sinkattn_prefill_ex; writes dq, dk, dv (float32, shaped like q, k, v) and dsink
+    (float32 [Hq], when sink is given)."""
+    import torch
+
+    B, Hq, L, dqk = q.shape
+    Hkv = k.shape[1]
+    for t, name, dt, shp in ((q, "q", torch.bfloat16, None), (k, "k", torch.bfloat16, (B, Hkv, L, dqk)),
+                             (v, "v", torch.bfloat16, (B, Hkv, L, 128)), (out, "out", torch.bfloat16, (B, Hq, L, 128)),
+                             (dout, "dout", torch.bfloat16, (B, Hq, L, 128)), (lse, "lse", torch.float32, (B, Hq, L)),
+                             (dq, "dq", torch.float32, (B, Hq, L, dqk)), (dk, "dk", torch.float32, (B, Hkv, L, dqk)),
+                             (dv, "dv", torch.float32, (B, Hkv, L, 128))):
+        _dev_tensor(t, name, dt, shp)
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+        _dev_tensor(dsink, "dsink", torch.float32, (Hq,))
+    _dev_tensor(workspace, "workspace", workspace.dtype)
+    d = Dims(B, L, Hq, Hkv, dqk, 128, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_prefill_backward(mode, window, ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(sink),
+                                             _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                             _ptr(dsink) if sink is not None else None, _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def prefill_backward(mode: int, window: int, q, k, v, sink, out, dout, lse, scale: float | None = None, stream=None):
+    """Allocate the gradients and the workspace and run sinkattn_prefill_backward; returns
+    (dq, dk, dv, dsink or None)."""
+    import torch
+
+    B, Hq, L, _ = q.shape
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    dsink = torch.empty(Hq, dtype=torch.float32, device=q.device) if sink is not None else None
+    dd = Dims(B, L, Hq, k.shape[1], 192, 128, 192 ** -0.5)
+    n = lib().sinkattn_prefill_backward_workspace_bytes(ctypes.byref(dd))
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    sinkattn_prefill_backward(mode, window, q, k, v, sink, out, dout, lse, dq, dk, dv, dsink, ws, scale, stream)
+    return dq, dk, dv, dsink
 
 
 def sinkattn_rope(theta: float, x, seq_lens=None, pos0: int = 0, stream=None) -> None:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ("api.hip", "prefill.hip", "decode.hip", "prologue.hip")
+SOURCES = ("api.hip", "prefill.hip", "decode.hip", "prologue.hip", "backward.hip")
 # Per-source flags.  The prefill kernels never test for NaN (masked scores are -inf), so
 # max/min need no NaN canonicalisation of the MFMA results.
 EXTRA = {"prefill.hip": ["-fno-honor-nans"]}

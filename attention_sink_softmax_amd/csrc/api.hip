@@ -267,6 +267,55 @@ int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_
                          out, workspace, workspace_bytes, stream);
 }
 
+size_t sinkattn_prefill_backward_workspace_bytes(const sinkattn_dims *d) {
+    if (!d || d->batch < 0 || d->seqlen < 0 || d->hq <= 0) return (size_t)-1;
+    return backward_workspace_bytes(d->batch, d->hq, d->seqlen);
+}
+
+int sinkattn_prefill_backward(int mode, int window, const sinkattn_dims *d, const void *q, const void *k,
+                              const void *v, const float *sink, const void *out, const void *dout, const float *lse,
+                              float *dq, float *dk, float *dv, float *dsink, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    int st = check_dims(mode, window, d);
+    if (st) return st;
+    if (d->seqlen < 0) return SINKATTN_E_SHAPE;
+    if ((d->hq / d->hkv) % 4) return SINKATTN_E_UNSUPPORTED;
+    if (d->batch > 65535 || d->hq / 4 > 65535 || (int64_t)d->seqlen * kDqkSupported * 2 > INT32_MAX)
+        return SINKATTN_E_SHAPE;
+    if (d->batch == 0 || d->seqlen == 0) return SINKATTN_OK;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || (sink && !dsink)) return SINKATTN_E_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(dout) || misaligned(lse) ||
+        misaligned(dq) || misaligned(dk) || misaligned(dv) || (sink && (misaligned(sink) || misaligned(dsink))))
+        return SINKATTN_E_ALIGN;
+    const size_t need = backward_workspace_bytes(d->batch, d->hq, d->seqlen);
+    if (!workspace || workspace_bytes < need) return SINKATTN_E_WORKSPACE;
+    if (misaligned(workspace)) return SINKATTN_E_ALIGN;
+    BwdParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.out = static_cast<const uint16_t *>(out);
+    p.dout = static_cast<const uint16_t *>(dout);
+    p.lse = lse;
+    p.sink = sink;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dsink = dsink;
+    p.delta = static_cast<float *>(workspace);
+    p.dsink_part = p.delta + (size_t)d->batch * d->hq * d->seqlen;
+    p.B = d->batch;
+    p.L = d->seqlen;
+    p.Hq = d->hq;
+    p.Hkv = d->hkv;
+    p.G = d->hq / d->hkv;
+    p.swa = mode == SINKATTN_SWA;
+    p.window = p.swa ? window : 0;
+    p.scale = d->scale;
+    p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    return launch_backward(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
 int sinkattn_rope(double theta, int32_t batch, int32_t heads, int32_t rows, void *x, const int32_t *seq_lens,
                   int32_t pos0, void *stream) {
     if (!(theta > 0.0) || !isfinite(theta)) return SINKATTN_E_SHAPE;

@@ -1,0 +1,401 @@
+// Backward of prefill attention with a per-head sink, for gfx950.
+//
+// With the forward weights recomputed from the saved log-sum-exp, P_ij = exp(a_ij - LSE_i), the
+// sink's weight exp(sink - LSE_i), and dO the gradient of the output:
+//   D_i = dO_i . O_i   dS_ij = P_ij (dO_i . v_j - D_i)   dq = scale dS k   dk = scale dS^T q
+//   dv = P^T dO        dsink_h = -sum_i exp(sink_h - LSE_i) D_i
+// (the sink enters the outputs only through the shared softmax denominator and has no value
+// vector: "MiMo-V2-Flash 架构 QA", Q3.8; it is a learnable per-head scalar: "MiMo-V2-Flash 模型
+// 架构深度拆解", CH 10.1).
+//
+// Four kernels on one stream:
+//   bwd_pre     D_i and the per-block partial sums of the sink gradient;
+//   bwd_dkdv    one workgroup per 128 keys of a (sequence, KV head): each wave keeps its 32 keys'
+//               K and V operands and its dK, dV accumulators in registers and walks every query
+//               head of the group and every 32-row query tile that sees its keys:
+//                 S = Q K^T, dP = dO V^T (query rows x keys), dS = P (dP - D),
+//                 dV += P^T dO, dK += dS^T Q       (P and dS feed the A operand as they are;
+//                                                    dO and Q arrive through transposing reads);
+//   bwd_dq      one workgroup per 32 query rows of four query heads of one KV head: each wave
+//               keeps its head's Q and dO operands and dQ^T in registers and walks the key tiles:
+//                 S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
+//   bwd_dsink   sums the sink gradient partials in a fixed order (deterministic).
+// All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P and dS enter them as
+// bf16.  Tiles pass through LDS with their 16-byte chunks XOR-swizzled by row so that both the
+// row reads and the transposing reads spread over the banks.
+#include "common.h"
+#include "launch.h"
+
+namespace sinkattn {
+
+namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int kQT = 32;                    // query rows per tile
+constexpr int kKeysPerWave = 32;
+constexpr int kKeysPerWg = 4 * kKeysPerWave;  // bwd_dkdv
+constexpr int kKT = 64;                    // keys per tile in bwd_dq
+constexpr int kPreRows = 16;               // rows per bwd_pre workgroup
+
+// Byte offset of 16-byte chunk c of row r: rows of 192 (384 B) and of 128 (256 B) elements.
+__device__ __forceinline__ int off192(int r, int c) { return r * 384 + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int off128(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+template <int W>
+__device__ __forceinline__ int tile_off(int r, int c) {
+    if constexpr (W == 192) return off192(r, c);
+    else return off128(r, c);
+}
+
+// Row m of a 32x32 MFMA result held in register e by lane group g.
+__device__ __forceinline__ int mrow(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
+
+// 8 elements of column `col0 + (lane & 31)` of a swizzled row-major tile, from rows
+// rbase + {4g .. 4g+3} and rbase + 8 + {4g .. 4g+3} (g = lane >> 5): the operand, in the k
+// order of a score tile's registers, of a product that contracts over those rows.
+template <int W>
+__device__ __forceinline__ bf16x8 col_operand(const char *tile, int rbase, int col0, int lane) {
+    const int g = lane >> 5, gl = (lane >> 4) & 1, i = lane & 15;
+    const int r = i >> 2, c4 = i & 3;
+    const int col = col0 + 16 * gl + 4 * c4;
+    const int chunk = col >> 3, half = (col >> 2) & 1;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + tile_off<W>(rbase + 4 * g + r, chunk) + 8 * half));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + tile_off<W>(rbase + 8 + 4 * g + r, chunk) + 8 * half));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 8 elements of row rbase + (lane & 31), chunk 2kk + g, of a swizzled row-major tile.
+template <int W>
+__device__ __forceinline__ bf16x8 row_operand(const char *tile, int rbase, int kk, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(tile + tile_off<W>(rbase + (lane & 31), 2 * kk + (lane >> 5)));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+
+// Pack registers e0 .. e0+7 of a score tile to the bf16 operand of one 16-wide k-step.
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int e0) {
+    return as_bf16x8(u32x4{pack_bf16x2(x[e0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
+                           pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])});
+}
+
+__device__ __forceinline__ bool visible(const BwdParams &p, int qpos, int key) {
+    return qpos < p.L && key <= qpos && (!p.swa || key > qpos - p.window);
+}
+
+// ---- D_i = dO_i . O_i and the sink gradient's partial sums
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+    __shared__ float part[256 / 16];
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
+    const int i = blockIdx.x * kPreRows + r;
+    float dsum = 0.f;
+    if (i < p.L) {
+        const size_t row = ((size_t)b * p.Hq + h) * p.L + i;
+        const u32x4 o = ldg16(p.out + row * kDv + 8 * c), d = ldg16(p.dout + row * kDv + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dsum += bf16_to_f32(o[e] & 0xffffu) * bf16_to_f32(d[e] & 0xffffu);
+            dsum += bf16_to_f32(o[e] >> 16) * bf16_to_f32(d[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 16);
+    float contrib = 0.f;
+    if (i < p.L && c == 0) {
+        const size_t row = ((size_t)b * p.Hq + h) * p.L + i;
+        p.delta[row] = dsum;
+        if (p.sink) {
+            const float sk = p.sink[h];
+            // the sink's weight exp(sink - LSE); with a sink of +inf every output is 0 (D = 0)
+            if (sk != INFINITY && sk != -INFINITY) contrib = -exp2f_fast((sk - p.lse[row]) * kLog2e) * dsum;
+        }
+    }
+    if (c == 0) part[r] = contrib;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int k = 0; k < 256 / 16; ++k) s += part[k];
+        p.dsink_part[((size_t)b * p.Hq + h) * gridDim.x + blockIdx.x] = s;
+    }
+}
+
+__global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdParams p, int nblk) {
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= p.Hq) return;
+    float s = 0.f;
+    for (int b = 0; b < p.B; ++b)
+        for (int k = 0; k < nblk; ++k) s += p.dsink_part[((size_t)b * p.Hq + h) * nblk + k];
+    p.dsink[h] = s;
+}
+
+// ---- dK and dV
+// LDS tile of one query tile: Q [32][192] (12 KB), dO [32][128] (8 KB), LSE and D [32] each.
+constexpr int kDkQBytes = kQT * kDqk * 2, kDkOBytes = kQT * kDv * 2;
+constexpr int kQChunks = kQT * kDqk / 8, kOChunks = kQT * kDv / 8;  // 768 + 512 16-byte chunks
+constexpr int kDkLoads = (kQChunks + kOChunks) / 256;               // 5 per thread
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char qt_lds[kDkQBytes];
+    __shared__ __attribute__((aligned(1024))) char ot_lds[kDkOBytes];
+    __shared__ float lse_lds[kQT], d_lds[kQT];
+
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int kb0 = blockIdx.x * kKeysPerWg;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, g = lane >> 5;
+    const int key = kb0 + kKeysPerWave * wave + n;  // this lane's key (B-operand column)
+
+    // this wave's K and V rows as the B operands of S = Q K^T and dP = dO V^T
+    bf16x8 kB[12], vB[8];
+    {
+        const bool ok = key < p.L;
+        const size_t kr = ((size_t)b * p.Hkv + kvh) * p.L + (ok ? key : 0);
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk)
+            kB[kk] = as_bf16x8(ok ? ldg16(p.k + kr * kDqk + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            vB[kk] = as_bf16x8(ok ? ldg16(p.v + kr * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+    }
+    f32x16 dK[6], dV[4];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
+
+    // query tiles that can see keys kb0 .. kb0 + 127
+    const int qt_lo = kb0 / kQT;
+    const int q_last = p.swa ? min(p.L - 1, kb0 + kKeysPerWg - 1 + p.window - 1) : p.L - 1;
+    const int qt_hi = kb0 < p.L ? q_last / kQT : qt_lo - 1;
+    const int ntile = qt_hi - qt_lo + 1;
+    const int total = ntile > 0 ? ntile * p.G : 0;
+
+    // global -> registers for item `it` (head it / ntile, tile it % ntile)
+    u32x4 stage[kDkLoads];
+    float lse_st = 0.f, d_st = 0.f;
+    auto fetch = [&](int it) {
+        const int hq = kvh * p.G + it / ntile, q0 = (qt_lo + it % ntile) * kQT;
+        const size_t rbase = ((size_t)b * p.Hq + hq) * p.L;
+#pragma unroll
+        for (int j = 0; j < kDkLoads; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < kQChunks) {
+                const int r = ch / 24, c = ch % 24;
+                stage[j] = q0 + r < p.L ? ldg16(p.q + (rbase + q0 + r) * kDqk + 8 * c) : u32x4{0, 0, 0, 0};
+            } else {
+                const int c2 = ch - kQChunks, r = c2 >> 4, c = c2 & 15;
+                stage[j] = q0 + r < p.L ? ldg16(p.dout + (rbase + q0 + r) * kDv + 8 * c) : u32x4{0, 0, 0, 0};
+            }
+        }
+        if (tid < kQT) lse_st = q0 + tid < p.L ? p.lse[rbase + q0 + tid] : 0.f;
+        else if (tid < 2 * kQT) d_st = q0 + tid - kQT < p.L ? p.delta[rbase + q0 + tid - kQT] : 0.f;
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int j = 0; j < kDkLoads; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < kQChunks) {
+                const int r = ch / 24, c = ch % 24;
+                *reinterpret_cast<u32x4 *>(qt_lds + off192(r, c)) = stage[j];
+            } else {
+                const int c2 = ch - kQChunks, r = c2 >> 4, c = c2 & 15;
+                *reinterpret_cast<u32x4 *>(ot_lds + off128(r, c)) = stage[j];
+            }
+        }
+        if (tid < kQT) lse_lds[tid] = lse_st;
+        else if (tid < 2 * kQT) d_lds[tid - kQT] = d_st;
+    };
+
+    if (total > 0) fetch(0);
+    for (int it = 0; it < total; ++it) {
+        __syncthreads();  // the previous tile's reads are done
+        store();
+        __syncthreads();
+        if (it + 1 < total) fetch(it + 1);  // in flight while this tile is computed
+        const int q0 = (qt_lo + it % ntile) * kQT;
+
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(qt_lds, 0, kk, lane), kB[kk], s, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(ot_lds, 0, kk, lane), vB[kk], dp, 0, 0, 0);
+        // lane: key column n, query rows mrow(e, g)
+        f32x16 pr, ds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = mrow(e, g);
+            const bool ok = key < p.L && visible(p, q0 + m, key);
+            const float pv = ok ? exp2f_fast(s[e] * p.scale_log2 - lse_lds[m] * kLog2e) : 0.f;
+            pr[e] = pv;
+            ds[e] = pv * (dp[e] - d_lds[m]);
+        }
+        const bf16x8 pa0 = pack8(pr, 0), pa1 = pack8(pr, 8), da0 = pack8(ds, 0), da1 = pack8(ds, 8);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(ot_lds, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
+            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(ot_lds, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 6; ++nb) {
+            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(qt_lds, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
+            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(qt_lds, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
+        }
+    }
+
+    // rows: this wave's keys mrow(e, g); columns: dims 32 nb + n
+    const float scale = p.scale;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int kr = kb0 + kKeysPerWave * wave + mrow(e, g);
+        if (kr >= p.L) continue;
+        const size_t row = ((size_t)b * p.Hkv + kvh) * p.L + kr;
+#pragma unroll
+        for (int nb = 0; nb < 6; ++nb) p.dk[row * kDqk + 32 * nb + n] = dK[nb][e] * scale;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) p.dv[row * kDv + 32 * nb + n] = dV[nb][e];
+    }
+}
+
+// ---- dQ
+constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;       // 24 + 16 KB
+constexpr int kKChunks = kKT * kDqk / 8, kVChunks = kKT * kDv / 8;         // 1536 + 1024
+constexpr int kDqLoads = (kKChunks + kVChunks) / 256;                      // 10 per thread
+
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char kt_lds[kDqKBytes];
+    __shared__ __attribute__((aligned(1024))) char vt_lds[kDqVBytes];
+
+    const int q0 = blockIdx.x * kQT, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, g = lane >> 5;
+    const int hq = blockIdx.y * 4 + wave, kvh = (blockIdx.y * 4) / p.G;
+    const int qpos = q0 + n;  // this lane's query (B-operand column)
+    const size_t qrow = ((size_t)b * p.Hq + hq) * p.L + (qpos < p.L ? qpos : 0);
+    const bool qok = qpos < p.L;
+
+    bf16x8 qB[12], oB[8];
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) qB[kk] = as_bf16x8(qok ? ldg16(p.q + qrow * kDqk + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) oB[kk] = as_bf16x8(qok ? ldg16(p.dout + qrow * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+    const float lse_q = qok ? p.lse[qrow] : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
+    f32x16 dQ[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) dQ[i] = f32x16{};
+
+    // key tiles that rows q0 .. q0 + 31 see
+    const int q_hi = min(p.L, q0 + kQT) - 1;
+    const int k_lo = p.swa ? max(0, q0 - p.window + 1) : 0;
+    const int t0 = k_lo / kKT, t1 = q_hi / kKT;
+    const size_t kvbase = ((size_t)b * p.Hkv + kvh) * p.L;
+
+    u32x4 stage[kDqLoads];
+    auto fetch = [&](int t) {
+        const int kbase = t * kKT;
+#pragma unroll
+        for (int j = 0; j < kDqLoads; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < kKChunks) {
+                const int r = ch / 24, c = ch % 24;
+                stage[j] = kbase + r < p.L ? ldg16(p.k + (kvbase + kbase + r) * kDqk + 8 * c) : u32x4{0, 0, 0, 0};
+            } else {
+                const int c2 = ch - kKChunks, r = c2 >> 4, c = c2 & 15;
+                stage[j] = kbase + r < p.L ? ldg16(p.v + (kvbase + kbase + r) * kDv + 8 * c) : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int j = 0; j < kDqLoads; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < kKChunks) {
+                const int r = ch / 24, c = ch % 24;
+                *reinterpret_cast<u32x4 *>(kt_lds + off192(r, c)) = stage[j];
+            } else {
+                const int c2 = ch - kKChunks, r = c2 >> 4, c = c2 & 15;
+                *reinterpret_cast<u32x4 *>(vt_lds + off128(r, c)) = stage[j];
+            }
+        }
+    };
+
+    if (q0 < p.L) fetch(t0);
+    for (int t = t0; t <= t1 && q0 < p.L; ++t) {
+        __syncthreads();
+        store();
+        __syncthreads();
+        if (t + 1 <= t1) fetch(t + 1);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kbase = t * kKT + 32 * sb;
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 12; ++kk)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt_lds, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt_lds, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
+            // lane: query column n, key rows mrow(e, g)
+            f32x16 ds;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kr = kbase + mrow(e, g);
+                const bool ok = kr < p.L && visible(p, qpos, kr);
+                const float pv = ok ? exp2f_fast(s[e] * p.scale_log2 - lse_q * kLog2e) : 0.f;
+                ds[e] = pv * (dp[e] - d_q);
+            }
+            const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
+#pragma unroll
+            for (int db = 0; db < 6; ++db) {
+                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt_lds, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
+                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt_lds, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
+            }
+        }
+    }
+    if (!qok) return;
+    // dQ^T: lane holds query qpos, dims 32 db + mrow(e, g): four consecutive dims per group of 4
+    float *dst = p.dq + qrow * kDqk;
+#pragma unroll
+    for (int db = 0; db < 6; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * j + 4 * g) =
+                f32x4{dQ[db][4 * j] * p.scale, dQ[db][4 * j + 1] * p.scale, dQ[db][4 * j + 2] * p.scale,
+                      dQ[db][4 * j + 3] * p.scale};
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int Hq, int L) {
+    const size_t nblk = ((size_t)L + kPreRows - 1) / kPreRows;
+    return ((size_t)B * Hq * L + (size_t)B * Hq * nblk) * sizeof(float);
+}
+
+int launch_backward(const BwdParams &prm, hipStream_t stream) {
+    BwdParams p = prm;
+    const int nblk = (p.L + kPreRows - 1) / kPreRows;
+    void *args[] = {&p};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel), dim3(nblk, p.Hq, p.B), dim3(256), args, 0,
+                        stream) != hipSuccess)
+        return -1;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dkdv_kernel),
+                        dim3((p.L + kKeysPerWg - 1) / kKeysPerWg, p.Hkv, p.B), dim3(256), args, 0, stream) != hipSuccess)
+        return -1;
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel), dim3((p.L + kQT - 1) / kQT, p.Hq / 4, p.B),
+                        dim3(256), args, 0, stream) != hipSuccess)
+        return -1;
+    if (p.sink) {
+        void *args2[] = {&p, (void *)&nblk};
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dsink_kernel), dim3((p.Hq + 63) / 64), dim3(64), args2,
+                            0, stream) != hipSuccess)
+            return -1;
+    }
+    return 0;
+}
+
+}  // namespace sinkattn

@@ -64,6 +64,21 @@ struct AppendParams {
     float k_scale, v_scale;  // fp8: codes of value / scale
 };
 
+// Backward of prefill (q, k, v, out, dout bf16; lse, delta, gradients float32).
+struct BwdParams {
+    const uint16_t *q, *k, *v, *out, *dout;
+    const float *lse;   // [B][Hq][L] from the forward (natural log)
+    const float *sink;  // [Hq] or nullptr
+    float *dq, *dk, *dv;  // [B][Hq][L][kDqk], [B][Hkv][L][kDqk], [B][Hkv][L][kDv]
+    float *dsink;         // [Hq] (sink given)
+    float *delta;         // workspace [B][Hq][L]: dO . O
+    float *dsink_part;    // workspace [B][Hq][ceil(L / 16)]
+    int B, L, Hq, Hkv, G, swa, window;
+    float scale, scale_log2;
+};
+size_t backward_workspace_bytes(int B, int Hq, int L);
+int launch_backward(const BwdParams &p, hipStream_t stream);
+
 size_t prefill_workspace_bytes(int B, int Hkv, int L);
 // Fills the work layout of p from B, L, Hkv, G and swa; returns the number of workgroups to
 // launch (the caller rejects counts that do not fit a grid).

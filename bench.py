@@ -191,6 +191,33 @@ def main() -> int:
 
         runs[w.name] = (call, flops, nbytes)
 
+    # --- backward of the 32K global prefill (q, k, v, sink gradients), from the forward's
+    # output and log-sum-exp; dO seeded N(0,1)
+    name = "ga_prefill_backward_L32768"
+    if only and name in only:
+        w = inputs.GA_PREFILL
+        d = inputs.prefill_inputs(w)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        del d
+        out = torch.empty((w.batch, w.hq, w.seqlen, w.d_v), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=dev)
+        sa.sinkattn_prefill_ex(w.mode, w.window, q, k, v, sink, out, sa.prefill_workspace(q, k), lse=lse)
+        dout = up(inputs.normal((w.batch, w.hq, w.seqlen, w.d_v), w.seed, 5))
+        grads = [torch.empty(q.shape, dtype=torch.float32, device=dev), torch.empty(k.shape, dtype=torch.float32, device=dev),
+                 torch.empty(v.shape, dtype=torch.float32, device=dev), torch.empty(w.hq, dtype=torch.float32, device=dev)]
+        dd = sa.Dims(w.batch, w.seqlen, w.hq, w.hkv, 192, 128, w.scale)
+        wsb = torch.empty(sa.lib().sinkattn_prefill_backward_workspace_bytes(sa.ctypes.byref(dd)), dtype=torch.uint8,
+                          device=dev)
+        # algorithmic work: S, dP, dV, dK, dQ once each per visible pair
+        flops = pairs_prefill(w.seqlen, w.mode, w.window) * w.hq * w.batch * 2 * (3 * 192 + 2 * 128)
+        nbytes = (q.numel() + k.numel() + v.numel() + out.numel() + dout.numel()) * 2 + sum(g.numel() * 4 for g in grads)
+
+        def call(w=w, q=q, k=k, v=v, sink=sink, out=out, dout=dout, lse=lse, g=grads, ws=wsb):
+            sa.sinkattn_prefill_backward(w.mode, w.window, q, k, v, sink, out, dout, lse, g[0], g[1], g[2], g[3], ws)
+
+        runs[name] = (call, flops, nbytes)
+
     # --- global decode at 256K from an 8-bit (E4M3) cache: half the bytes of the bf16 cache
     w = inputs.GA_DECODE_FP8
     if not only or w.name in only:

@@ -263,6 +263,37 @@ int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_
                         void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace sinkattn_prefill_backward needs: 4 * batch * hq * (seqlen +
+ * ceil(seqlen / 16)).  Returns (size_t)-1 for invalid sizes.
+ */
+size_t sinkattn_prefill_backward_workspace_bytes(const sinkattn_dims *d);
+
+/*
+ * Backward of prefill attention, including the gradient of the sink.  The sink is a
+ * learnable per-head scalar ("MiMo-V2-Flash 模型架构深度拆解", CH 10.1) that enters the
+ * outputs only through the softmax denominator ("MiMo-V2-Flash 架构 QA", Q3.8); with P the
+ * forward weights, D_i = dO_i . O_i and dS = P (dO v^T - D):
+ *   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dO,  dsink_h = -sum_i exp(sink_h - LSE_i) D_i
+ * (dsink summed over the batch).
+ *   mode, window, d   as for sinkattn_prefill; hq / hkv must be a multiple of 4 (else
+ *                     SINKATTN_E_UNSUPPORTED)
+ *   q, k, v, sink     the forward's inputs
+ *   out, lse          the forward's output (bf16 [batch][hq][seqlen][d_v]) and its per-row
+ *                     log-sum-exp (float32 [batch][hq][seqlen], from sinkattn_prefill_ex)
+ *   dout              bf16 [batch][hq][seqlen][d_v], the gradient of out
+ *   dq, dk, dv        float32 [batch][hq][seqlen][d_qk], [batch][hkv][seqlen][d_qk],
+ *                     [batch][hkv][seqlen][d_v]: written (not accumulated into)
+ *   dsink             float32 [hq], written; required when sink is given, ignored otherwise
+ *   workspace         at least sinkattn_prefill_backward_workspace_bytes(d) bytes
+ * The products run on bf16 matrix cores with float32 accumulation (the weights and dS enter
+ * them rounded to bf16); the sink gradient is summed in a fixed order (deterministic).
+ */
+int sinkattn_prefill_backward(int mode, int window, const sinkattn_dims *d, const void *q,
+                              const void *k, const void *v, const float *sink, const void *out,
+                              const void *dout, const float *lse, float *dq, float *dk, float *dv,
+                              float *dsink, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Partial rotary position embedding, in place ("MiMo-V2-Flash 模型架构深度拆解", CH 3.5 and
  * CH 10.5; "MiMo-V2-Flash 架构 QA", Q2.7): of each row's 192 q or k dimensions only the first
  * 64 turn, pair i (dimensions i and i + 32) by the angle pos * theta^(-2i/64); the other 128

@@ -1,0 +1,99 @@
+"""Backward of prefill attention (gradients of q, k, v and of the sink) against the oracle.
+
+Tolerance: the products run in bf16 with float32 accumulation, and the weights P and the
+score gradients dS enter them rounded to bf16 (relative error 2^-9 each).  Gradients sum
+many such terms (dk and dv over every query row and head of the group), so their size grows
+with the sequence; the bar is relative: rel-L2 <= 5e-3 and every element within
+2e-2 * max(1, max |reference|).  The sink gradient, a float32 sum over all rows of a head,
+is bounded by the scale of its summands (see run())."""
+import numpy as np
+import pytest
+import torch
+
+import attention_sink_softmax_amd as sa
+from attention_sink_softmax_amd import inputs
+import oracle
+from gpu_util import dev_bf16, dev_f32, errors
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 192 ** -0.5
+
+
+def assert_grad(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    max_abs, rel = errors(got, ref)
+    bound = 2e-2 * max(1.0, float(np.max(np.abs(ref))))
+    print(f"[grad] {what}: max_abs={max_abs:.3e} (bound {bound:.3e}) rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= bound and rel <= 5e-3, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+
+
+def run(mode, W, Hq, Hkv, L, B=1, sink_kind="sink", seed=0):
+    w = inputs.Workload("t", "prefill", 0, B, Hq, Hkv, seqlen=L, seed=seed)
+    d = inputs.prefill_inputs(w)
+    dout = inputs.normal((B, Hq, L, 128), seed, 5)
+    sink = None
+    if sink_kind != "none":
+        sink = d["sink"].copy()
+        if sink_kind == "extremes":
+            sink[0] = np.inf
+            sink[1] = -np.inf
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    s = dev_f32(sink)
+    out = torch.empty((B, Hq, L, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sa.sinkattn_prefill_chunk_workspace_bytes(B, L, Hq, Hkv, L), dtype=torch.uint8, device="cuda")
+    sa.sinkattn_prefill_ex(mode, W, q, k, v, s, out, ws, lse=lse)
+    dq, dk, dv, ds = sa.prefill_backward(mode, W, q, k, v, s, out, dev_bf16(dout), lse)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_backward(d["q"], d["k"], d["v"], sink, dout, mode, W, SCALE)
+    got = (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy(), None if ds is None else ds.cpu().numpy())
+    bound = None
+    if sink is not None:
+        # The sink gradient sums -exp(sink - LSE_i) (dO_i . O_i) over rows, with O the stored
+        # bf16 output (each element within 2^-9 relative of the exact one, before and after the
+        # bf16 weights of the forward's value product): its error is bounded by a small multiple
+        # of sum_i exp(sink - LSE_i) |dO_i| |O_i|, a scale of the summands rather than of their
+        # (cancelling) sum.  The bar is 2^-6 of that.
+        o_ref, lse_ref = oracle.prefill_chunk(d["q"], d["k"], d["v"], sink, mode, W, SCALE, return_lse=True)
+        dof = inputs.bf16_to_f32(dout).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            ps = np.where(np.isinf(sink)[None, :, None], 0.0, np.exp(sink[None, :, None] - lse_ref))
+        mag = ps * np.linalg.norm(dof, axis=-1) * np.linalg.norm(o_ref, axis=-1)
+        bound = 2.0 ** -6 * mag.sum(axis=(0, 2))
+    return got, ref, sink, bound
+
+
+def assert_dsink(g, r, bound):
+    err = np.abs(np.asarray(g, np.float64) - r)
+    print(f"[grad] dsink: max_abs={err.max():.3e} max(err / bound)={np.max(err / np.maximum(bound, 1e-30)):.3f}",
+          flush=True)
+    assert np.all(err <= np.maximum(bound, 1e-6)), (err, bound)
+
+
+@pytest.mark.parametrize("mode,W,Hq,Hkv,L,B,sink_kind", [
+    (oracle.GLOBAL, 0, 64, 4, 300, 1, "sink"),
+    (oracle.GLOBAL, 0, 16, 4, 129, 2, "extremes"),   # group of 4; sinks of +inf and -inf
+    (oracle.GLOBAL, 0, 16, 4, 200, 1, "none"),
+    (oracle.SWA, 128, 64, 8, 500, 1, "sink"),
+    (oracle.SWA, 100, 16, 2, 257, 1, "sink"),        # window not a multiple of 32; group of 8
+    (oracle.SWA, 1, 8, 2, 70, 1, "sink"),            # each row sees only itself
+])
+def test_backward(mode, W, Hq, Hkv, L, B, sink_kind):
+    print(f"[case] backward mode={mode} W={W} Hq={Hq} Hkv={Hkv} L={L} B={B} sink={sink_kind}", flush=True)
+    got, ref, sink, bound = run(mode, W, Hq, Hkv, L, B, sink_kind, seed=L + Hq)
+    for name, i in (("dq", 0), ("dk", 1), ("dv", 2)):
+        assert_grad(got[i], ref[i], name)
+    if sink is None:
+        assert got[3] is None
+    else:
+        assert_dsink(got[3], ref[3], bound)
+
+
+def test_backward_ga_2k_all_heads():
+    """64 query / 4 KV heads over 2048 positions (64 tiles of queries and 16 key blocks)."""
+    got, ref, sink, bound = run(oracle.GLOBAL, 0, 64, 4, 2048, 1, "sink", seed=3)
+    for name, i in (("dq", 0), ("dk", 1), ("dv", 2)):
+        assert_grad(got[i], ref[i], f"2K {name}")
+    assert_dsink(got[3], ref[3], bound)
