@@ -21,8 +21,10 @@
 //                 S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
 //   bwd_dsink   sums the sink gradient partials in a fixed order (deterministic).
 // All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P and dS enter them as
-// bf16.  Tiles pass through LDS with their 16-byte chunks XOR-swizzled by row so that both the
-// row reads and the transposing reads spread over the banks.
+// bf16.  Tiles pass through double-buffered LDS (one barrier per tile) with their 16-byte
+// chunks XOR-swizzled by row so that both the row reads and the transposing reads spread over
+// the banks.  Masking is branch-free and only runs on tiles that cross the causal diagonal, the
+// window's edge or the sequence end.
 #include "common.h"
 #include "launch.h"
 
@@ -32,6 +34,24 @@ namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Tiles travel HBM -> LDS with 16-byte (4-byte for row statistics) buffer loads that write
+// LDS directly: lane l of one instruction fills bytes 16 l .. 16 l + 15 of a 1 KB block, so
+// each lane fetches the global chunk that the swizzled layout puts there.  A buffer region
+// covers one (sequence, head) matrix; offsets past its end read zeros, which pads the last
+// tile of a sequence.
+constexpr int kRawDword3 = 0x00020000;  // untyped 32-bit data, no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void *base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRawDword3);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 constexpr int kQT = 32;                    // query rows per tile
 constexpr int kKeysPerWave = 32;
@@ -40,13 +60,27 @@ constexpr int kKT = 64;                    // keys per tile in bwd_dq
 constexpr int kPreRows = 16;               // rows per bwd_pre workgroup
 
 // Byte offset of 16-byte chunk c of row r: rows of 192 (384 B) and of 128 (256 B) elements.
-__device__ __forceinline__ int off192(int r, int c) { return r * 384 + ((c ^ ((r >> 1) & 7)) << 4); }
-__device__ __forceinline__ int off128(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+// Both row lengths are multiples of 128 B (the 32 banks), so chunk c of every row starts on the
+// same bank; the chunk index is XORed with swz(r), which takes the 8 values 0..7 over any 8
+// aligned rows (the 8 lanes of one 128-byte phase of a row read) and 4 values with distinct
+// bits 1-2 over any 4 aligned rows (the 4 rows x 2 adjacent chunks of one 16-lane phase of a
+// transposing read).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int off192(int r, int c) { return r * 384 + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int off128(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
 
 template <int W>
 __device__ __forceinline__ int tile_off(int r, int c) {
     if constexpr (W == 192) return off192(r, c);
     else return off128(r, c);
+}
+// Source offset (bytes, from the tile's first row) of the chunk that lands in 16-byte slot
+// `slot` of a swizzled tile of W-element rows.
+template <int W>
+__device__ __forceinline__ int src_of_slot(int slot) {
+    constexpr int kChunks = W / 8;
+    const int r = slot / kChunks, c = (slot % kChunks) ^ swz(r);
+    return r * (W * 2) + c * 16;
 }
 
 // Row m of a 32x32 MFMA result held in register e by lane group g.
@@ -84,6 +118,11 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int e0) {
 
 __device__ __forceinline__ bool visible(const BwdParams &p, int qpos, int key) {
     return qpos < p.L && key <= qpos && (!p.swa || key > qpos - p.window);
+}
+
+// True when every (query, key) pair of queries q0 .. q0+31 and keys k0 .. k0+31 is visible.
+__device__ __forceinline__ bool all_visible(const BwdParams &p, int q0, int k0) {
+    return k0 + 31 <= q0 && q0 + 31 < p.L && (!p.swa || k0 > q0 + 31 - p.window);
 }
 
 // ---- D_i = dO_i . O_i and the sink gradient's partial sums
@@ -133,21 +172,27 @@ __global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdParams p, int nblk) {
 }
 
 // ---- dK and dV
-// LDS tile of one query tile: Q [32][192] (12 KB), dO [32][128] (8 KB), LSE and D [32] each.
+// LDS tile of one query tile: Q [32][192] (12 KB = 12 blocks of 1 KB), dO [32][128] (8 blocks),
+// and the LSE and D of its rows (64 floats each: the 32 rows of the tile and 32 unused).
 constexpr int kDkQBytes = kQT * kDqk * 2, kDkOBytes = kQT * kDv * 2;
-constexpr int kQChunks = kQT * kDqk / 8, kOChunks = kQT * kDv / 8;  // 768 + 512 16-byte chunks
-constexpr int kDkLoads = (kQChunks + kOChunks) / 256;               // 5 per thread
+
+struct DkTile {
+    char *q, *o;
+    float *lse, *d;
+};
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char qt_lds[kDkQBytes];
-    __shared__ __attribute__((aligned(1024))) char ot_lds[kDkOBytes];
-    __shared__ float lse_lds[kQT], d_lds[kQT];
+    __shared__ __attribute__((aligned(1024))) char qa[kDkQBytes], qb[kDkQBytes];
+    __shared__ __attribute__((aligned(1024))) char oa[kDkOBytes], ob[kDkOBytes];
+    __shared__ __attribute__((aligned(256))) float la[64], lb[64], da[64], db_[64];
 
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int kb0 = blockIdx.x * kKeysPerWg;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
-    const int key = kb0 + kKeysPerWave * wave + n;  // this lane's key (B-operand column)
+    const int kw0 = kb0 + kKeysPerWave * wave;  // this wave's first key
+    const int key = kw0 + n;                    // this lane's key (B-operand column)
 
     // this wave's K and V rows as the B operands of S = Q K^T and dP = dO V^T
     bf16x8 kB[12], vB[8];
@@ -160,6 +205,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
             vB[kk] = as_bf16x8(ok ? ldg16(p.v + kr * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+        // parked in AGPRs (the matrix unit reads them there), leaving the VGPRs to the
+        // operands streamed from LDS
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) asm volatile("" : "+a"(kB[kk]));
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(vB[kk]));
     }
     f32x16 dK[6], dV[4];
 #pragma unroll
@@ -174,85 +225,88 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int ntile = qt_hi - qt_lo + 1;
     const int total = ntile > 0 ? ntile * p.G : 0;
 
-    // global -> registers for item `it` (head it / ntile, tile it % ntile)
-    u32x4 stage[kDkLoads];
-    float lse_st = 0.f, d_st = 0.f;
-    auto fetch = [&](int it) {
+    // Item it = (head it / ntile, query tile it % ntile).  Wave w loads blocks w, w + 4, w + 8
+    // of Q and w, w + 4 of dO; waves 0 and 1 also load the LSE and D rows.
+    const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (wave + 4) + lane),
+              qsrc2 = src_of_slot<192>(64 * (wave + 8) + lane);
+    const int osrc0 = src_of_slot<128>(64 * wave + lane), osrc1 = src_of_slot<128>(64 * (wave + 4) + lane);
+    auto issue = [&](int it, const DkTile &t) {
         const int hq = kvh * p.G + it / ntile, q0 = (qt_lo + it % ntile) * kQT;
         const size_t rbase = ((size_t)b * p.Hq + hq) * p.L;
-#pragma unroll
-        for (int j = 0; j < kDkLoads; ++j) {
-            const int ch = tid + 256 * j;
-            if (ch < kQChunks) {
-                const int r = ch / 24, c = ch % 24;
-                stage[j] = q0 + r < p.L ? ldg16(p.q + (rbase + q0 + r) * kDqk + 8 * c) : u32x4{0, 0, 0, 0};
-            } else {
-                const int c2 = ch - kQChunks, r = c2 >> 4, c = c2 & 15;
-                stage[j] = q0 + r < p.L ? ldg16(p.dout + (rbase + q0 + r) * kDv + 8 * c) : u32x4{0, 0, 0, 0};
-            }
-        }
-        if (tid < kQT) lse_st = q0 + tid < p.L ? p.lse[rbase + q0 + tid] : 0.f;
-        else if (tid < 2 * kQT) d_st = q0 + tid - kQT < p.L ? p.delta[rbase + q0 + tid - kQT] : 0.f;
+        const auto rq = region(p.q + rbase * kDqk, (size_t)p.L * kDqk * 2);
+        const auto ro = region(p.dout + rbase * kDv, (size_t)p.L * kDv * 2);
+        dma16(rq, t.q + 1024 * wave, qsrc0, q0 * (kDqk * 2));
+        dma16(rq, t.q + 1024 * (wave + 4), qsrc1, q0 * (kDqk * 2));
+        dma16(rq, t.q + 1024 * (wave + 8), qsrc2, q0 * (kDqk * 2));
+        dma16(ro, t.o + 1024 * wave, osrc0, q0 * (kDv * 2));
+        dma16(ro, t.o + 1024 * (wave + 4), osrc1, q0 * (kDv * 2));
+        if (wave == 0) dma4(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
+        if (wave == 1) dma4(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
     };
-    auto store = [&]() {
-#pragma unroll
-        for (int j = 0; j < kDkLoads; ++j) {
-            const int ch = tid + 256 * j;
-            if (ch < kQChunks) {
-                const int r = ch / 24, c = ch % 24;
-                *reinterpret_cast<u32x4 *>(qt_lds + off192(r, c)) = stage[j];
-            } else {
-                const int c2 = ch - kQChunks, r = c2 >> 4, c = c2 & 15;
-                *reinterpret_cast<u32x4 *>(ot_lds + off128(r, c)) = stage[j];
-            }
-        }
-        if (tid < kQT) lse_lds[tid] = lse_st;
-        else if (tid < 2 * kQT) d_lds[tid - kQT] = d_st;
-    };
-
-    if (total > 0) fetch(0);
-    for (int it = 0; it < total; ++it) {
-        __syncthreads();  // the previous tile's reads are done
-        store();
-        __syncthreads();
-        if (it + 1 < total) fetch(it + 1);  // in flight while this tile is computed
+    auto compute = [&](const DkTile &t, int it) {
         const int q0 = (qt_lo + it % ntile) * kQT;
-
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(qt_lds, 0, kk, lane), kB[kk], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(t.q, 0, kk, lane), kB[kk], s, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(ot_lds, 0, kk, lane), vB[kk], dp, 0, 0, 0);
-        // lane: key column n, query rows mrow(e, g)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(t.o, 0, kk, lane), vB[kk], dp, 0, 0, 0);
+        // lane: key column n, query rows mrow(e, g) = 8 (e / 4) + 4 g + e % 4
+        if (!all_visible(p, q0, kw0)) {  // wave-uniform
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (!visible(p, q0 + mrow(e, g), key)) s[e] = -INFINITY;
+        }
         f32x16 pr, ds;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = mrow(e, g);
-            const bool ok = key < p.L && visible(p, q0 + m, key);
-            const float pv = ok ? exp2f_fast(s[e] * p.scale_log2 - lse_lds[m] * kLog2e) : 0.f;
-            pr[e] = pv;
-            ds[e] = pv * (dp[e] - d_lds[m]);
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(t.lse + 8 * j + 4 * g);
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(t.d + 8 * j + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * j + i;
+                const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, -l4[i] * kLog2e));
+                pr[e] = pv;
+                ds[e] = pv * (dp[e] - d4[i]);
+            }
         }
         const bf16x8 pa0 = pack8(pr, 0), pa1 = pack8(pr, 8), da0 = pack8(ds, 0), da1 = pack8(ds, 8);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(ot_lds, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
-            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(ot_lds, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
+            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(t.o, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
+            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(t.o, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
         }
 #pragma unroll
         for (int nb = 0; nb < 6; ++nb) {
-            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(qt_lds, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
-            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(qt_lds, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
+            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(t.q, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
+            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
         }
+    };
+    // Item it uses buffer it % 2.  The loads of item it + 1 are issued after the barrier of
+    // item it, when every wave has finished item it - 1, the last reader of that buffer; each
+    // wave waits for its own loads before the next barrier.
+    const DkTile ta{qa, oa, la, da}, tb{qb, ob, lb, db_};
+    auto step = [&](int it, const DkTile &cur, const DkTile &nxt) {
+        wait_dma();
+        __syncthreads();
+        if (it + 1 < total) issue(it + 1, nxt);
+        compute(cur, it);
+    };
+    if (total > 0) issue(0, ta);
+    int it = 0;
+    for (; it + 1 < total; it += 2) {
+        step(it, ta, tb);
+        step(it + 1, tb, ta);
     }
+    if (it < total) step(it, ta, tb);
+    wait_dma();  // no load into LDS outlives the workgroup
 
     // rows: this wave's keys mrow(e, g); columns: dims 32 nb + n
     const float scale = p.scale;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const int kr = kb0 + kKeysPerWave * wave + mrow(e, g);
+        const int kr = kw0 + mrow(e, g);
         if (kr >= p.L) continue;
         const size_t row = ((size_t)b * p.Hkv + kvh) * p.L + kr;
 #pragma unroll
@@ -263,28 +317,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---- dQ
-constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;       // 24 + 16 KB
-constexpr int kKChunks = kKT * kDqk / 8, kVChunks = kKT * kDv / 8;         // 1536 + 1024
-constexpr int kDqLoads = (kKChunks + kVChunks) / 256;                      // 10 per thread
+// LDS tile of 64 keys: K [64][192] (24 blocks of 1 KB) and V [64][128] (16 blocks).
+constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;
 
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char kt_lds[kDqKBytes];
-    __shared__ __attribute__((aligned(1024))) char vt_lds[kDqVBytes];
+    __shared__ __attribute__((aligned(1024))) char ka[kDqKBytes], kb_[kDqKBytes];
+    __shared__ __attribute__((aligned(1024))) char va[kDqVBytes], vb[kDqVBytes];
 
     const int q0 = blockIdx.x * kQT, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
     const int hq = blockIdx.y * 4 + wave, kvh = (blockIdx.y * 4) / p.G;
     const int qpos = q0 + n;  // this lane's query (B-operand column)
     const size_t qrow = ((size_t)b * p.Hq + hq) * p.L + (qpos < p.L ? qpos : 0);
     const bool qok = qpos < p.L;
+    if (q0 >= p.L) return;  // uniform over the workgroup
 
     bf16x8 qB[12], oB[8];
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) qB[kk] = as_bf16x8(qok ? ldg16(p.q + qrow * kDqk + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) oB[kk] = as_bf16x8(qok ? ldg16(p.dout + qrow * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
-    const float lse_q = qok ? p.lse[qrow] : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
+    // a row past the sequence end has every pair masked; its LSE only has to be finite
+    const float nlse2 = qok ? -p.lse[qrow] * kLog2e : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
     f32x16 dQ[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) dQ[i] = f32x16{};
@@ -294,69 +350,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     const int k_lo = p.swa ? max(0, q0 - p.window + 1) : 0;
     const int t0 = k_lo / kKT, t1 = q_hi / kKT;
     const size_t kvbase = ((size_t)b * p.Hkv + kvh) * p.L;
+    const auto rk = region(p.k + kvbase * kDqk, (size_t)p.L * kDqk * 2);
+    const auto rv = region(p.v + kvbase * kDv, (size_t)p.L * kDv * 2);
 
-    u32x4 stage[kDqLoads];
-    auto fetch = [&](int t) {
+    // wave w loads blocks w + 4 i of K (i < 6) and of V (i < 4)
+    int ksrc[6], vsrc[4];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 4 * i) + lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vsrc[i] = src_of_slot<128>(64 * (wave + 4 * i) + lane);
+    auto issue = [&](int t, char *kt, char *vt) {
         const int kbase = t * kKT;
 #pragma unroll
-        for (int j = 0; j < kDqLoads; ++j) {
-            const int ch = tid + 256 * j;
-            if (ch < kKChunks) {
-                const int r = ch / 24, c = ch % 24;
-                stage[j] = kbase + r < p.L ? ldg16(p.k + (kvbase + kbase + r) * kDqk + 8 * c) : u32x4{0, 0, 0, 0};
-            } else {
-                const int c2 = ch - kKChunks, r = c2 >> 4, c = c2 & 15;
-                stage[j] = kbase + r < p.L ? ldg16(p.v + (kvbase + kbase + r) * kDv + 8 * c) : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store = [&]() {
+        for (int i = 0; i < 6; ++i) dma16(rk, kt + 1024 * (wave + 4 * i), ksrc[i], kbase * (kDqk * 2));
 #pragma unroll
-        for (int j = 0; j < kDqLoads; ++j) {
-            const int ch = tid + 256 * j;
-            if (ch < kKChunks) {
-                const int r = ch / 24, c = ch % 24;
-                *reinterpret_cast<u32x4 *>(kt_lds + off192(r, c)) = stage[j];
-            } else {
-                const int c2 = ch - kKChunks, r = c2 >> 4, c = c2 & 15;
-                *reinterpret_cast<u32x4 *>(vt_lds + off128(r, c)) = stage[j];
-            }
-        }
+        for (int i = 0; i < 4; ++i) dma16(rv, vt + 1024 * (wave + 4 * i), vsrc[i], kbase * (kDv * 2));
     };
-
-    if (q0 < p.L) fetch(t0);
-    for (int t = t0; t <= t1 && q0 < p.L; ++t) {
-        __syncthreads();
-        store();
-        __syncthreads();
-        if (t + 1 <= t1) fetch(t + 1);
+    auto compute = [&](const char *kt, const char *vt, int t) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int kbase = t * kKT + 32 * sb;
+            if (kbase > q_hi) break;  // uniform: keys past the last row of the tile
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 12; ++kk)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt_lds, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt_lds, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
             // lane: query column n, key rows mrow(e, g)
+            if (!all_visible(p, q0, kbase)) {  // uniform
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (!visible(p, qpos, kbase + mrow(e, g))) s[e] = -INFINITY;
+            }
             f32x16 ds;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int kr = kbase + mrow(e, g);
-                const bool ok = kr < p.L && visible(p, qpos, kr);
-                const float pv = ok ? exp2f_fast(s[e] * p.scale_log2 - lse_q * kLog2e) : 0.f;
+                const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, nlse2));
                 ds[e] = pv * (dp[e] - d_q);
             }
             const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
 #pragma unroll
             for (int db = 0; db < 6; ++db) {
-                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt_lds, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
-                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt_lds, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
+                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
+                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
             }
         }
+    };
+    // Tile t uses buffer (t - t0) % 2; its successor's loads are issued after the barrier of
+    // tile t, when every wave has finished tile t - 1, the last reader of that buffer.
+    auto step = [&](int t, char *kc, char *vc, char *kn, char *vn) {
+        wait_dma();
+        __syncthreads();
+        if (t + 1 <= t1) issue(t + 1, kn, vn);
+        compute(kc, vc, t);
+    };
+    issue(t0, ka, va);
+    for (int t = t0; t <= t1; t += 2) {
+        step(t, ka, va, kb_, vb);
+        if (t + 1 <= t1) step(t + 1, kb_, vb, ka, va);
     }
+    wait_dma();  // no load into LDS outlives the workgroup
     if (!qok) return;
     // dQ^T: lane holds query qpos, dims 32 db + mrow(e, g): four consecutive dims per group of 4
     float *dst = p.dq + qrow * kDqk;
