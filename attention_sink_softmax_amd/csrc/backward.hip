@@ -162,13 +162,22 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     }
 }
 
-__global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdParams p, int nblk) {
-    const int h = blockIdx.x * 64 + threadIdx.x;
-    if (h >= p.Hq) return;
+// One workgroup per head: thread t sums the partials t, t + 256, ... of every sequence in a
+// fixed order, then a fixed tree adds the 256 sums (the result does not depend on timing).
+__global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int nblk) {
+    __shared__ float part[256];
+    const int h = blockIdx.x, tid = threadIdx.x;
     float s = 0.f;
     for (int b = 0; b < p.B; ++b)
-        for (int k = 0; k < nblk; ++k) s += p.dsink_part[((size_t)b * p.Hq + h) * nblk + k];
-    p.dsink[h] = s;
+        for (int k = tid; k < nblk; k += 256) s += p.dsink_part[((size_t)b * p.Hq + h) * nblk + k];
+    part[tid] = s;
+    __syncthreads();
+#pragma unroll
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (tid < w) part[tid] += part[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) p.dsink[h] = part[0];
 }
 
 // ---- dK and dV
@@ -186,8 +195,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char oa[kDkOBytes], ob[kDkOBytes];
     __shared__ __attribute__((aligned(256))) float la[64], lb[64], da[64], db_[64];
 
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int kb0 = blockIdx.x * kKeysPerWg;
+    // workgroup -> (key block, sequence, KV head): KV heads vary fastest, so that the
+    // workgroups that the hardware places on one XCD (ids equal mod 8) share a KV head, and
+    // the key blocks with the most query tiles come first
+    int bid = blockIdx.x;
+    const int kvh = bid % p.Hkv;
+    bid /= p.Hkv;
+    const int b = bid % p.B;
+    const int kb0 = (bid / p.B) * kKeysPerWg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
@@ -225,13 +240,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int ntile = qt_hi - qt_lo + 1;
     const int total = ntile > 0 ? ntile * p.G : 0;
 
-    // Item it = (head it / ntile, query tile it % ntile).  Wave w loads blocks w, w + 4, w + 8
-    // of Q and w, w + 4 of dO; waves 0 and 1 also load the LSE and D rows.
+    // Item it = (query tile qt_hi - it / G, head it % G): every workgroup walks the query
+    // tiles from the last one down, so the workgroups of one KV head that run together read
+    // the same tiles at about the same time (shared in L2).  Wave w loads blocks w, w + 4,
+    // w + 8 of Q and w, w + 4 of dO; waves 0 and 1 also load the LSE and D rows.
     const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (wave + 4) + lane),
               qsrc2 = src_of_slot<192>(64 * (wave + 8) + lane);
     const int osrc0 = src_of_slot<128>(64 * wave + lane), osrc1 = src_of_slot<128>(64 * (wave + 4) + lane);
     auto issue = [&](int it, const DkTile &t) {
-        const int hq = kvh * p.G + it / ntile, q0 = (qt_lo + it % ntile) * kQT;
+        const int hq = kvh * p.G + it % p.G, q0 = (qt_hi - it / p.G) * kQT;
         const size_t rbase = ((size_t)b * p.Hq + hq) * p.L;
         const auto rq = region(p.q + rbase * kDqk, (size_t)p.L * kDqk * 2);
         const auto ro = region(p.dout + rbase * kDv, (size_t)p.L * kDv * 2);
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         if (wave == 1) dma4(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
     };
     auto compute = [&](const DkTile &t, int it) {
-        const int q0 = (qt_lo + it % ntile) * kQT;
+        const int q0 = (qt_hi - it / p.G) * kQT;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk)
@@ -324,11 +341,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char ka[kDqKBytes], kb_[kDqKBytes];
     __shared__ __attribute__((aligned(1024))) char va[kDqVBytes], vb[kDqVBytes];
 
-    const int q0 = blockIdx.x * kQT, b = blockIdx.z;
+    // workgroup -> (query tile, sequence, group of four heads): head groups vary fastest and
+    // the query tiles with the most key tiles come first
+    int bid = blockIdx.x;
+    const int hgroup = bid % (p.Hq / 4);
+    bid /= p.Hq / 4;
+    const int b = bid % p.B;
+    const int q0 = ((p.L + kQT - 1) / kQT - 1 - bid / p.B) * kQT;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
-    const int hq = blockIdx.y * 4 + wave, kvh = (blockIdx.y * 4) / p.G;
+    const int hq = hgroup * 4 + wave, kvh = (hgroup * 4) / p.G;
     const int qpos = q0 + n;  // this lane's query (B-operand column)
     const size_t qrow = ((size_t)b * p.Hq + hq) * p.L + (qpos < p.L ? qpos : 0);
     const bool qok = qpos < p.L;
@@ -439,14 +462,14 @@ int launch_backward(const BwdParams &prm, hipStream_t stream) {
                         stream) != hipSuccess)
         return -1;
     if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dkdv_kernel),
-                        dim3((p.L + kKeysPerWg - 1) / kKeysPerWg, p.Hkv, p.B), dim3(256), args, 0, stream) != hipSuccess)
+                        dim3(((p.L + kKeysPerWg - 1) / kKeysPerWg) * p.Hkv * p.B), dim3(256), args, 0, stream) != hipSuccess)
         return -1;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel), dim3((p.L + kQT - 1) / kQT, p.Hq / 4, p.B),
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel), dim3(((p.L + kQT - 1) / kQT) * (p.Hq / 4) * p.B),
                         dim3(256), args, 0, stream) != hipSuccess)
         return -1;
     if (p.sink) {
         void *args2[] = {&p, (void *)&nblk};
-        if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dsink_kernel), dim3((p.Hq + 63) / 64), dim3(64), args2,
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dsink_kernel), dim3(p.Hq), dim3(256), args2,
                             0, stream) != hipSuccess)
             return -1;
     }
