@@ -334,12 +334,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---- dQ
-// LDS tile of 64 keys: K [64][192] (24 blocks of 1 KB) and V [64][128] (16 blocks).
+// LDS tile of 64 keys: K [64][192] (24 blocks of 1 KB) and V [64][128] (16 blocks), triple
+// buffered (120 KB).  Each wave runs a software pipeline over 32-key sub-blocks so that the
+// softmax arithmetic of one sub-block overlaps the products of the next:
+//   phase A: S^T, dP^T of (t, 1)       with  dS^T of (t, 0)
+//   phase B: dQ^T += K(t, 0)^T dS^T(t, 0)
+//   barrier: tile t + 1 has landed, the buffer of tile t - 1 is free; tile t + 2 starts
+//   phase C: S^T, dP^T of (t + 1, 0)   with  dS^T of (t, 1)
+//   phase D: dQ^T += K(t, 1)^T dS^T(t, 1)
+// Sub-blocks past the last row or before the window are computed and masked to zero, and
+// past the last tile the loads and scores repeat the last tile unused, so that no branch
+// splits a phase.
 constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;
 
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char ka[kDqKBytes], kb_[kDqKBytes];
-    __shared__ __attribute__((aligned(1024))) char va[kDqVBytes], vb[kDqVBytes];
+    __shared__ __attribute__((aligned(1024))) char K0[kDqKBytes], K1[kDqKBytes], K2[kDqKBytes];
+    __shared__ __attribute__((aligned(1024))) char V0[kDqVBytes], V1[kDqVBytes], V2[kDqVBytes];
 
     // workgroup -> (query tile, sequence, group of four heads): head groups vary fastest and
     // the query tiles with the most key tiles come first
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     const auto rk = region(p.k + kvbase * kDqk, (size_t)p.L * kDqk * 2);
     const auto rv = region(p.v + kvbase * kDv, (size_t)p.L * kDv * 2);
 
-    // wave w loads blocks w + 4 i of K (i < 6) and of V (i < 4)
+    // wave w loads blocks w + 4 i of K (24 blocks) and of V (16 blocks)
     int ksrc[6], vsrc[4];
 #pragma unroll
     for (int i = 0; i < 6; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 4 * i) + lane);
@@ -389,62 +399,77 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(rv, vt + 1024 * (wave + 4 * i), vsrc[i], kbase * (kDv * 2));
     };
-    auto compute = [&](const char *kt, const char *vt, int t) {
+    // S^T = K Q^T and dP^T = V dO^T of sub-block sb of a tile
+    auto scores = [&](const char *kt, const char *vt, int sb, f32x16 &s, f32x16 &dp) {
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int kbase = t * kKT + 32 * sb;
-            if (kbase > q_hi) break;  // uniform: keys past the last row of the tile
-            f32x16 s = f32x16{}, dp = f32x16{};
+        for (int kk = 0; kk < 12; ++kk)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
 #pragma unroll
-            for (int kk = 0; kk < 12; ++kk)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
+        for (int kk = 0; kk < 8; ++kk)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
+    };
+    // dS^T = P^T (dP^T - D) of the sub-block whose first key is kbase, as two bf16 k-steps;
+    // lane: query column n, key rows mrow(e, g)
+    auto dscores = [&](f32x16 s, const f32x16 &dp, int kbase, bf16x8 &d0, bf16x8 &d1) {
+        if (!all_visible(p, q0, kbase)) {  // uniform
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
-            // lane: query column n, key rows mrow(e, g)
-            if (!all_visible(p, q0, kbase)) {  // uniform
+            for (int e = 0; e < 16; ++e)
+                if (!visible(p, qpos, kbase + mrow(e, g))) s[e] = -INFINITY;
+        }
+        f32x16 ds;
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (!visible(p, qpos, kbase + mrow(e, g))) s[e] = -INFINITY;
-            }
-            f32x16 ds;
+        for (int e = 0; e < 16; ++e) {
+            const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, nlse2));
+            ds[e] = pv * (dp[e] - d_q);
+        }
+        d0 = pack8(ds, 0);
+        d1 = pack8(ds, 8);
+    };
+    auto dq_acc = [&](const char *kt, int sb, const bf16x8 &d0, const bf16x8 &d1) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, nlse2));
-                ds[e] = pv * (dp[e] - d_q);
-            }
-            const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
-#pragma unroll
-            for (int db = 0; db < 6; ++db) {
-                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
-                dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
-            }
+        for (int db = 0; db < 6; ++db) {
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
         }
     };
-    // Tile t uses buffer (t - t0) % 2; its successor's loads are issued after the barrier of
-    // tile t, when every wave has finished tile t - 1, the last reader of that buffer.
-    auto step = [&](int t, char *kc, char *vc, char *kn, char *vn) {
+
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 da, db;
+    auto step = [&](int t, const char *Kc, const char *Vc, const char *Kn, const char *Vn, char *Kf, char *Vf) {
+        const int kb = t * kKT;
+        scores(Kc, Vc, 1, s1, dp1);        // phase A
+        dscores(s0, dp0, kb, da, db);
+        dq_acc(Kc, 0, da, db);             // phase B
         wait_dma();
         __syncthreads();
-        if (t + 1 <= t1) issue(t + 1, kn, vn);
-        compute(kc, vc, t);
+        issue(min(t + 2, t1), Kf, Vf);
+        scores(Kn, Vn, 0, s0, dp0);        // phase C (unused after the last tile)
+        dscores(s1, dp1, kb + 32, da, db);
+        dq_acc(Kc, 1, da, db);             // phase D
     };
-    issue(t0, ka, va);
-    for (int t = t0; t <= t1; t += 2) {
-        step(t, ka, va, kb_, vb);
-        if (t + 1 <= t1) step(t + 1, kb_, vb, ka, va);
+    issue(t0, K0, V0);
+    issue(min(t0 + 1, t1), K1, V1);
+    wait_dma();
+    __syncthreads();
+    scores(K0, V0, 0, s0, dp0);
+    for (int t = t0; t <= t1; t += 3) {
+        step(t, K0, V0, K1, V1, K2, V2);
+        if (t + 1 <= t1) step(t + 1, K1, V1, K2, V2, K0, V0);
+        if (t + 2 <= t1) step(t + 2, K2, V2, K0, V0, K1, V1);
     }
     wait_dma();  // no load into LDS outlives the workgroup
     if (!qok) return;
     // dQ^T: lane holds query qpos, dims 32 db + mrow(e, g): four consecutive dims per group of 4
     float *dst = p.dq + qrow * kDqk;
 #pragma unroll
-    for (int db = 0; db < 6; ++db)
+    for (int i = 0; i < 6; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * j + 4 * g) =
-                f32x4{dQ[db][4 * j] * p.scale, dQ[db][4 * j + 1] * p.scale, dQ[db][4 * j + 2] * p.scale,
-                      dQ[db][4 * j + 3] * p.scale};
+            *reinterpret_cast<f32x4 *>(dst + 32 * i + 8 * j + 4 * g) =
+                f32x4{dQ[i][4 * j] * p.scale, dQ[i][4 * j + 1] * p.scale, dQ[i][4 * j + 2] * p.scale,
+                      dQ[i][4 * j + 3] * p.scale};
 }
 
 }  // namespace
