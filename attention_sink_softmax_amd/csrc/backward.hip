@@ -191,9 +191,9 @@ struct DkTile {
 };
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char qa[kDkQBytes], qb[kDkQBytes];
-    __shared__ __attribute__((aligned(1024))) char oa[kDkOBytes], ob[kDkOBytes];
-    __shared__ __attribute__((aligned(256))) float la[64], lb[64], da[64], db_[64];
+    __shared__ __attribute__((aligned(1024))) char qa[kDkQBytes], qb[kDkQBytes], qc[kDkQBytes];
+    __shared__ __attribute__((aligned(1024))) char oa[kDkOBytes], ob[kDkOBytes], oc[kDkOBytes];
+    __shared__ __attribute__((aligned(256))) float la[64], lb[64], lc[64], da[64], db_[64], dc[64];
 
     // workgroup -> (key block, sequence, KV head): KV heads vary fastest, so that the
     // workgroups that the hardware places on one XCD (ids equal mod 8) share a KV head, and
@@ -300,23 +300,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
         }
     };
-    // Item it uses buffer it % 2.  The loads of item it + 1 are issued after the barrier of
-    // item it, when every wave has finished item it - 1, the last reader of that buffer; each
-    // wave waits for its own loads before the next barrier.
-    const DkTile ta{qa, oa, la, da}, tb{qb, ob, lb, db_};
-    auto step = [&](int it, const DkTile &cur, const DkTile &nxt) {
-        wait_dma();
+    // Item it uses buffer it % 3 and its loads are issued two items ahead: after the barrier
+    // of item it - 2, when every wave has finished item it - 3, the last reader of that
+    // buffer.  Before the barrier of item it each wave waits for all but its newest loads
+    // (those of item it + 1: six instructions on waves 0 and 1, five on the others); past
+    // the last item the loads repeat the last item, so that the count never changes.
+    const DkTile ta{qa, oa, la, da}, tb{qb, ob, lb, db_}, tc{qc, oc, lc, dc};
+    auto step = [&](int it, const DkTile &cur, const DkTile &fut) {
+        if (wave < 2) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+        else __builtin_amdgcn_s_waitcnt(0x0F75);           // vmcnt(5)
         __syncthreads();
-        if (it + 1 < total) issue(it + 1, nxt);
+        issue(min(it + 2, total - 1), fut);
         compute(cur, it);
     };
-    if (total > 0) issue(0, ta);
-    int it = 0;
-    for (; it + 1 < total; it += 2) {
-        step(it, ta, tb);
-        step(it + 1, tb, ta);
+    if (total > 0) {
+        issue(0, ta);
+        issue(min(1, total - 1), tb);
     }
-    if (it < total) step(it, ta, tb);
+    int it = 0;
+    for (; it + 2 < total; it += 3) {
+        step(it, ta, tc);
+        step(it + 1, tb, ta);
+        step(it + 2, tc, tb);
+    }
+    if (it < total) step(it, ta, tc);
+    if (it + 1 < total) step(it + 1, tb, ta);
     wait_dma();  // no load into LDS outlives the workgroup
 
     // rows: this wave's keys mrow(e, g); columns: dims 32 nb + n
