@@ -43,13 +43,13 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "d12e9276964b7df6251fe96840020508fbda34c971803822fa7cc61457a20db6",
-                          "read_GB": 3.5704, "written_GB": 0.5373},
+                          "sha256": "eebd41a6daa410953173992f9367b133b50ab0c97caa6a1bb7314a9d898f371d",
+                          "read_GB": 3.5705, "written_GB": 0.5372},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "e4fe2a3a89c9f99e3baa31966c7f50c3a2d6fd99158172d687c080a50d971f30",
+                                "sha256": "4abae72239412941c0457187832f56caa0799fbffb95080e33aaeb8b8718b27d",
                                 "read_GB": 5.3880, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "e4fe2a3a89c9f99e3baa31966c7f50c3a2d6fd99158172d687c080a50d971f30",
+                                    "sha256": "4abae72239412941c0457187832f56caa0799fbffb95080e33aaeb8b8718b27d",
                                     "read_GB": 2.7037, "written_GB": 0.0179},
 }
 
