@@ -20,8 +20,10 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
 SOURCES = ("api.hip", "prefill.hip", "decode.hip", "prologue.hip", "backward.hip")
 # Per-source flags.  The prefill kernels never test for NaN (masked scores are -inf), so
-# max/min need no NaN canonicalisation of the MFMA results.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# max/min need no NaN canonicalisation of the MFMA results; their matrix products write
+# ordinary VGPRs (the softmax reads the scores with no copy out of accumulator registers,
+# and the sliding-window ring kernel fits two waves per SIMD without spilling).
+EXTRA = {"prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -25,6 +25,8 @@ struct PrefillParams {
     int n_pbw;         // position groups per (batch, kv head)
     int hgroups;       // head groups per kv head (G / hw)
     int n_items;       // n_pbw * B * Hkv * hgroups
+    int ring;          // 1: the sliding-window ring kernel (then n_items = workgroups)
+    int chunk;         // ring kernel: 32-position blocks per workgroup
 };
 
 struct DecodeParams {

@@ -187,11 +187,6 @@ __device__ __forceinline__ bool row_max(const f32x16 (&s)[HPW], const float (&m_
 template <int HPW>
 __device__ __forceinline__ void rescale(bool grow, const float (&mnew)[HPW], f32x16 (&acc)[HPW][4],
                                         float (&m_run)[HPW], float (&l_run)[HPW]) {
-    // keep the accumulators in AGPRs on the common path (the rare rescale moves them)
-#pragma unroll
-    for (int h = 0; h < HPW; ++h)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) asm volatile("" : "+a"(acc[h][db]));
     if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
@@ -548,6 +543,150 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
 }
 
+// ---- sliding-window ring kernel (window <= 128, group size a multiple of 8, whole-sequence
+// prefill).  A workgroup of 8 waves, one query head each, owns a run of consecutive 32-position
+// blocks of one (sequence, KV head, 8 heads).  The keys a block sees, [32j - W + 1, 32j + 31],
+// lie in the five 32-key sub-blocks j - 4 .. j, so K and V^T stay in LDS as a ring of six
+// sub-blocks: each step computes block j from five of them while sub-block j + 1 and the next
+// block's queries load, and every K/V row is read from HBM once per run.  The queries and
+// outputs, which are most of the traffic, stream with a step of latency to hide behind.
+// Two waves per SIMD overlap each other's softmax with their products.
+constexpr int kSwaWaves = 8;
+constexpr int kRingSlots = 6;
+constexpr int kSubKBytes = 32 * kDqk * 2;  // 12 KB: rows of a K tile's first 32 keys
+constexpr int kSubVBytes = kDv * 32 * 2;   // 8 KB: V^T [128 dv][32 keys]
+constexpr int kSlotBytes = kSubKBytes + kSubVBytes;
+
+// One 32-key sub-block, global -> registers: K chunk idx lands at byte 16 idx of the K part in
+// the K tile layout (rows 0..31), V^T chunk idx at byte 16 idx of the V part: block rg holds
+// dv rows 16rg .. 16rg + 15 and the sub-block's 4 key chunks (chunk c of row r in slot 16c + r).
+// Thread t moves K chunks t and 512 + t (t < 256) and V^T chunk t.
+struct SubStage {
+    u32x4 k0, k1, v;
+};
+__device__ __forceinline__ void sub_load(SubStage &st, const PrefillParams &p, int b, int kvh, int sub, int tid) {
+    const uint16_t *kbase = p.k + ((size_t)b * p.Hkv + kvh) * p.L * kDqk;
+    auto kchunk = [&](int idx) {
+        const int blk = idx >> 6, l = idx & 63;
+        const int row = min(32 * sub + 16 * (blk / 6) + (l & 15), p.L - 1);
+        return ldg16(kbase + (size_t)row * kDqk + (4 * (blk % 6) + (l >> 4)) * 8);
+    };
+    st.k0 = kchunk(tid);
+    if (tid < 256) st.k1 = kchunk(512 + tid);
+    const uint16_t *vtile = p.vt + (((size_t)b * p.Hkv + kvh) * (p.lpad / kBN) + (sub >> 1)) * (kDv * kBN);
+    const int rg = tid >> 6, l = tid & 63;
+    st.v = ldg16(vtile + (16 * rg + (l & 15)) * kBN + (4 * (sub & 1) + (l >> 4)) * 8);
+}
+__device__ __forceinline__ void sub_store(const SubStage &st, char *slot, int tid) {
+    *reinterpret_cast<u32x4 *>(slot + 16 * tid) = st.k0;
+    if (tid < 256) *reinterpret_cast<u32x4 *>(slot + 16 * (512 + tid)) = st.k1;
+    *reinterpret_cast<u32x4 *>(slot + kSubKBytes + 16 * tid) = st.v;
+}
+
+// O^T += V^T P^T from a V^T sub-block (layout of sub_store).
+__device__ __forceinline__ void pv_sub(const char *Vs, const bf16x8 (&pf)[1][2], f32x16 (&acc)[1][4], const WaveCtx &w) {
+    const int vl = (w.lq >> 4) * 1024 + w.g * 256 + (w.lq & 15) * 16;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vs + vl + db * 2048 + k2 * 512);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][k2], acc[0][db], 0, 0, 0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillParams p) {
+    constexpr int HPW = 1;
+    __shared__ __attribute__((aligned(1024))) char ring[kRingSlots * kSlotBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // workgroup -> (chunk of blocks, batch, KV head, group of 8 heads)
+    const int nqb = (p.L + kBQ - 1) / kBQ;
+    const int nchunk = (nqb + p.chunk - 1) / p.chunk;
+    int u = blockIdx.x;
+    const int hg = u % p.hgroups;
+    u /= p.hgroups;
+    const int kvh = u % p.Hkv;
+    u /= p.Hkv;
+    const int b = u % p.B;
+    const int c = u / p.B;
+    if (c >= nchunk) return;  // uniform: before any barrier
+    const int j_lo = c * p.chunk, j_hi = min(nqb, j_lo + p.chunk);
+
+    WaveSetup ws;
+    ws.b = b;
+    ws.kvh = kvh;
+    ws.h0 = kvh * p.G + hg * kSwaWaves + wave;
+    ws.valid = true;
+    auto setup_block = [&](int j) {
+        ws.qpos0 = kBQ * j;
+        ws.wg_q0 = ws.qpos0;
+        ws.wg_q1 = min(p.L, ws.qpos0 + kBQ);
+        return make_ctx(p, ws, lane);
+    };
+
+    // the sub-blocks of the first block's band
+    {
+        SubStage st[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int sub = j_lo - 4 + i;
+            if (sub >= 0) sub_load(st[i], p, b, kvh, sub, tid);
+        }
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int sub = j_lo - 4 + i;
+            if (sub >= 0) sub_store(st[i], ring + (sub % kRingSlots) * kSlotBytes, tid);
+        }
+    }
+    bf16x8 qa[HPW][12], qb[HPW][12];
+    {
+        const WaveCtx w0 = setup_block(j_lo);
+        load_q<HPW>(p, ws, w0, qa);
+    }
+    __syncthreads();
+
+    auto step = [&](int j, const bf16x8 (&qc)[HPW][12], bf16x8 (&qn)[HPW][12]) {
+        const bool nxt = j + 1 < j_hi;
+        SubStage st;
+        if (nxt) {
+            sub_load(st, p, b, kvh, j + 1, tid);
+            const WaveCtx wn = setup_block(j + 1);
+            load_q<HPW>(p, ws, wn, qn);
+        }
+        const WaveCtx w = setup_block(j);
+        float m_run[HPW], l_run[HPW];
+        bool sink_inf[HPW];
+        f32x16 acc[HPW][4];
+        init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int sub = j - 4 + i, k0 = kBQ * sub;
+            const bool dead = sub < 0 || k0 >= p.L || k0 + 31 < w.qpos0 - p.window + 1;
+            if (dead) continue;
+            const bool full = k0 + 31 <= w.qpos0 && k0 + 32 <= p.L && k0 >= w.qpos0 + kBQ - p.window;
+            const char *slot = ring + (sub % kRingSlots) * kSlotBytes;
+            f32x16 sc[HPW];
+            qk_scores<HPW>(slot, 0, qc, sc, w);
+            if (!full) mask_scores<HPW>(sc, k0, 0, w);
+            row_update<HPW>(sc, acc, m_run, l_run, w);
+            bf16x8 pf[HPW][2];
+            probs<HPW>(sc, m_run, l_run, pf, w);
+            pv_sub(slot + kSubKBytes, pf, acc, w);
+        }
+        // slot (j + 1) % 6 held sub-block j - 5, outside this block's band
+        if (nxt) sub_store(st, ring + ((j + 1) % kRingSlots) * kSlotBytes, tid);
+        store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
+        __syncthreads();
+    };
+    for (int j = j_lo; j < j_hi; j += 2) {
+        step(j, qa, qb);
+        if (j + 1 < j_hi) step(j + 1, qb, qa);
+    }
+}
+
 // V -> V^T tile by tile: tile t of (batch, kv head) is a contiguous [128 dv][64 keys] block
 // with the keys of every 16-key group in MFMA k-order (chunk 2*gam + g holds the keys
 // vkey(gam, g, 0..7)); keys past L are zero.  One workgroup per (batch x kv head, tile).
@@ -586,6 +725,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uin
 
 namespace {
 bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw == kCausalWaves; }
+constexpr int kComputeUnits = 256;  // MI355X; only the size of the ring kernel's runs depends on it
 }  // namespace
 
 // Causal mode with a group size divisible by 8: the eight-wave kernel, one head per wave.
@@ -594,6 +734,24 @@ bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw
 // share a CU, so one's loads overlap the other's math on this short, memory-bound work), two
 // heads per wave for causal attention over an even group (half the LDS reads per MFMA).
 int64_t plan_prefill(PrefillParams &p) {
+    p.ring = 0;
+    p.chunk = 0;
+    if (p.swa && p.window <= 128 && p.G % kSwaWaves == 0 && p.q0 == 0 && p.Lq == p.L) {
+        // ring kernel: runs of consecutive blocks, about one workgroup per compute unit
+        p.ring = 1;
+        p.hpw = 1;
+        p.hw = kSwaWaves;
+        p.pw = 1;
+        p.hgroups = p.G / kSwaWaves;
+        const int64_t units = (int64_t)p.B * p.Hkv * p.hgroups;
+        const int64_t nqb = (p.L + 31) / 32;
+        const int64_t split = std::max<int64_t>(1, std::min<int64_t>(nqb, (kComputeUnits + units - 1) / units));
+        p.chunk = (int)((nqb + split - 1) / split);
+        p.n_pbw = (int)((nqb + p.chunk - 1) / p.chunk);
+        const int64_t items = units * p.n_pbw;
+        p.n_items = items > INT32_MAX ? INT32_MAX : (int)items;
+        return items;
+    }
     if (!p.swa && p.G % kCausalWaves == 0) {
         p.hpw = 1;
         p.hw = kCausalWaves;
@@ -625,8 +783,11 @@ int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
                             dim3(256), targs, 0, stream) != hipSuccess)
             return -1;
     }
-    const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     void *args[] = {&p};
+    if (p.ring)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_swa_kernel), dim3(p.n_items),
+                               dim3(64 * kSwaWaves), args, 0, stream) == hipSuccess ? 0 : -1;
+    const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     if (causal_layout(p)) {
         return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_causal_kernel), dim3(grid),
                                dim3(64 * kCausalWaves), args, 0, stream) == hipSuccess ? 0 : -1;

@@ -71,6 +71,14 @@ CASES = [
     (1, 16, 2, 192, oracle.GLOBAL, 0, False),
     (1, 16, 2, 193, oracle.GLOBAL, 0, True),
     (2, 8, 1, 517, oracle.GLOBAL, 0, True),
+    # sliding window with a group of 8 or 16 and W <= 128 (the ring kernel): workgroups that
+    # walk runs of 3 and 4 blocks with a short last run, sub-block 1 of the ring's first
+    # band, single-block runs, windows 1 and 100
+    (8, 64, 8, 300, oracle.SWA, 128, True),
+    (4, 64, 8, 1000, oracle.SWA, 100, True),
+    (1, 8, 1, 20, oracle.SWA, 128, True),
+    (2, 16, 1, 97, oracle.SWA, 1, True),
+    (1, 8, 1, 200, oracle.SWA, 16, False),
 ]
 
 
