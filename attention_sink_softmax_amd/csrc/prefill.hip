@@ -307,8 +307,10 @@ __device__ __forceinline__ WaveSetup wave_setup(const PrefillParams &p, int wave
     return ws;
 }
 
-// Q^T fragments (B operand): lane supplies row qi - q0 of q[h], elements 16kk + 8g .. +8;
-// positions past L give zeros.
+// Q^T fragments (B operand): lane supplies row qi - q0 of q[h], elements 16kk + 8g .. +8.
+// A lane past the sequence end reads row 0 instead: its scores are finite, it never shares
+// statistics with a valid row, and its output is never stored.  The loads are unconditional
+// and their values used as they are, so the compiler waits for them only at their first use.
 template <int HPW>
 __device__ __forceinline__ void load_q(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
                                        bf16x8 (&qf)[HPW][12]) {
@@ -317,19 +319,18 @@ __device__ __forceinline__ void load_q(const PrefillParams &p, const WaveSetup &
     for (int h = 0; h < HPW; ++h) {
         const uint16_t *qrow = p.q + ((((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq) + (ok ? w.qi - p.q0 : 0)) * kDqk + 8 * w.g;
 #pragma unroll
-        for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ok ? ldg16(qrow + 16 * kk) : u32x4{0, 0, 0, 0});
+        for (int kk = 0; kk < 12; ++kk) qf[h][kk] = as_bf16x8(ldg16(qrow + 16 * kk));
     }
 }
 
 // The sink starts each row's running max and denominator: m = sink, l = exp(0) = 1 (counted
 // on one lane of the pair that shares the row).  No sink: m = -inf, l = 0.
 template <int HPW>
-__device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
-                                           f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
-                                           bool (&sink_inf)[HPW]) {
+__device__ __forceinline__ void init_state_from(const float (&sink)[HPW], const WaveCtx &w, f32x16 (&acc)[HPW][4],
+                                                float (&m_run)[HPW], float (&l_run)[HPW], bool (&sink_inf)[HPW]) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-        const float sk = p.sink ? p.sink[ws.h0 + h] : -INFINITY;
+        const float sk = sink[h];
         const bool has_sink = sk != -INFINITY;
         sink_inf[h] = sk == INFINITY;
         m_run[h] = has_sink ? sk * kLog2e : -INFINITY;
@@ -337,6 +338,19 @@ __device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSet
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[h][db] = f32x16{};
     }
+}
+template <int HPW>
+__device__ __forceinline__ void load_sink(const PrefillParams &p, const WaveSetup &ws, float (&sink)[HPW]) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) sink[h] = p.sink ? p.sink[ws.h0 + h] : -INFINITY;
+}
+template <int HPW>
+__device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
+                                           f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
+                                           bool (&sink_inf)[HPW]) {
+    float sink[HPW];
+    load_sink<HPW>(p, ws, sink);
+    init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf);
 }
 
 // O = out_scale * acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi (row
@@ -560,7 +574,9 @@ constexpr int kSlotBytes = kSubKBytes + kSubVBytes;
 // One 32-key sub-block, global -> registers: K chunk idx lands at byte 16 idx of the K part in
 // the K tile layout (rows 0..31), V^T chunk idx at byte 16 idx of the V part: block rg holds
 // dv rows 16rg .. 16rg + 15 and the sub-block's 4 key chunks (chunk c of row r in slot 16c + r).
-// Thread t moves K chunks t and 512 + t (t < 256) and V^T chunk t.
+// Thread t moves K chunks t and 512 + t (t < 256) and V^T chunk t; every thread issues the
+// same three loads (the second K load of threads 256 .. 511 is not stored), so the number in
+// flight is the same on every path.
 struct SubStage {
     u32x4 k0, k1, v;
 };
@@ -572,7 +588,7 @@ __device__ __forceinline__ void sub_load(SubStage &st, const PrefillParams &p, i
         return ldg16(kbase + (size_t)row * kDqk + (4 * (blk % 6) + (l >> 4)) * 8);
     };
     st.k0 = kchunk(tid);
-    if (tid < 256) st.k1 = kchunk(512 + tid);
+    st.k1 = kchunk(512 + (tid & 255));
     const uint16_t *vtile = p.vt + (((size_t)b * p.Hkv + kvh) * (p.lpad / kBN) + (sub >> 1)) * (kDv * kBN);
     const int rg = tid >> 6, l = tid & 63;
     st.v = ldg16(vtile + (16 * rg + (l & 15)) * kBN + (4 * (sub & 1) + (l >> 4)) * 8);
@@ -642,25 +658,33 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
         }
     }
     bf16x8 qa[HPW][12], qb[HPW][12];
+    float sink[HPW];  // loaded once: a load inside the loop would wait for the prefetches
+    load_sink<HPW>(p, ws, sink);
     {
         const WaveCtx w0 = setup_block(j_lo);
         load_q<HPW>(p, ws, w0, qa);
     }
+    // Nothing may stay in flight into the loop: the compiler's wait analysis merges the
+    // conditional prologue loads into every later use and would wait for all loads (the
+    // prefetches included) in each step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
+    // The loads for the next step are unconditional (the last step of a run reloads its own
+    // block and the last sub-block of the sequence into places nobody reads again), so the
+    // compiler can count them exactly and wait for nothing but what each use needs.
     auto step = [&](int j, const bf16x8 (&qc)[HPW][12], bf16x8 (&qn)[HPW][12]) {
-        const bool nxt = j + 1 < j_hi;
         SubStage st;
-        if (nxt) {
-            sub_load(st, p, b, kvh, j + 1, tid);
-            const WaveCtx wn = setup_block(j + 1);
+        sub_load(st, p, b, kvh, min(j + 1, nqb - 1), tid);
+        {
+            const WaveCtx wn = setup_block(min(j + 1, j_hi - 1));
             load_q<HPW>(p, ws, wn, qn);
         }
         const WaveCtx w = setup_block(j);
         float m_run[HPW], l_run[HPW];
         bool sink_inf[HPW];
         f32x16 acc[HPW][4];
-        init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
+        init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int sub = j - 4 + i, k0 = kBQ * sub;
@@ -677,7 +701,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
             pv_sub(slot + kSubKBytes, pf, acc, w);
         }
         // slot (j + 1) % 6 held sub-block j - 5, outside this block's band
-        if (nxt) sub_store(st, ring + ((j + 1) % kRingSlots) * kSlotBytes, tid);
+        sub_store(st, ring + ((j + 1) % kRingSlots) * kSlotBytes, tid);
         store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
         __syncthreads();
     };
