@@ -121,6 +121,37 @@ __device__ __forceinline__ void dma_vt_block(char *Vt, const TileSrc &src, int k
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.vt, (lds_void *)(Vt + blk * 1024), 16,
                                              kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16, 0, 0, 0);
 }
+// The same 16-byte loads into LDS, written as instructions the compiler does not interpret.
+// In the causal kernel's loop the compiler cannot tell that the LDS reads after such a load
+// read other buffers. With the builtin it waits for the load before them, which makes the
+// load synchronous. Here it inserts no wait; the kernel waits itself (vmcnt(0)) before each
+// barrier, and the data is read only after the barrier.
+__device__ __forceinline__ void dma16_opaque(__amdgpu_buffer_rsrc_t r, char *lds, int voff) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds;
+    uint32_t saved;
+    // m0 carries the LDS address; one wait state between writing it and the load; m0 is
+    // restored for the compiler's own use
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r)
+        : "memory");
+}
+__device__ __forceinline__ void dma_k_block_opaque(char *Kt, const TileSrc &src, int kb, int L, int blk, int lane) {
+    const int rg = blk / 6, cg = blk % 6;
+    const int row = min(kb + 16 * rg + (lane & 15), L - 1);
+    dma16_opaque(src.k, Kt + blk * 1024, row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16);
+}
+__device__ __forceinline__ void dma_vt_block_opaque(char *Vt, const TileSrc &src, int kb, int blk, int lane) {
+    const int rg = blk >> 1, kg = blk & 1;
+    const int row = 16 * rg + (lane & 15);
+    dma16_opaque(src.vt, Vt + blk * 1024, kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16);
+}
+
 // Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile (10 per wave).
 __device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const TileSrc &src, int kb, int L, int wave, int lane) {
 #pragma unroll
@@ -540,12 +571,14 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
         // are unused after the last tile)
         qk_scores<HPW>(Kn, 0, qf, s0, w);
         probs<HPW>(s1, m_run, l_run, pf, w);
-        dma_k_part(Kf, src, kb_next, p.L, wave, lane);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) dma_k_block_opaque(Kf, src, kb_next, p.L, wave + kCausalWaves * i, lane);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
         // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
         pv_accum<HPW>(Vc, 1, pf, acc, w);
         grow = row_max<HPW>(s0, m_run, mnew, w);
-        dma_vt_part(Vf, src, kb_next, wave, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma_vt_block_opaque(Vf, src, kb_next, wave + kCausalWaves * i, lane);
         if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
     };
     for (int t = 0; t <= t1; t += 3) {
