@@ -60,6 +60,9 @@ def load(path: str = LIB):
                                       ctypes.c_double, P, I, I, I, P, P, P, P]
     lib.oracle_prefill_backward.restype = I
     lib.oracle_prefill_backward.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, P, P, P, P, P]
+    lib.oracle_prefill_backward_sampled.restype = I
+    lib.oracle_prefill_backward_sampled.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, P, I, P, P,
+                                                    I, P, P, P]
     lib.oracle_rope.restype = I
     lib.oracle_rope.argtypes = [ctypes.c_int64, I, I, ctypes.c_double, I, P, P, P]
     lib.oracle_e4m3_value.restype = ctypes.c_double
@@ -205,6 +208,31 @@ def prefill_backward(q, k, v, sink, dout, mode: int, window: int, scale: float, 
     if rc != 0:
         raise ValueError("oracle_prefill_backward rejected its arguments")
     return dq, dk, dvv, ds
+
+
+def prefill_backward_sampled(q, k, v, sink, dout, mode: int, window: int, scale: float, qrows, krows, lib=None):
+    """Entries of the prefill gradients of a large problem, by the same definitions as
+    prefill_backward: dq of the rows qrows [(b, h, i), ...] and dk, dv of the keys
+    krows [(b, KV head, j), ...].  Returns float64 (dq [nq, dqk], dk [nk, dqk], dv [nk, dv])."""
+    lib = lib or load()
+    qa, dt = _arr(q, None)
+    ka, _ = _arr(k, None)
+    va, _ = _arr(v, None)
+    da, _ = _arr(dout, None)
+    B, Hq, L, dqk = qa.shape
+    Hkv, dv = ka.shape[1], va.shape[3]
+    s = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    qr = np.ascontiguousarray(np.asarray(qrows, np.int64).reshape(-1, 3))
+    kr = np.ascontiguousarray(np.asarray(krows, np.int64).reshape(-1, 3))
+    dq = np.empty((qr.shape[0], dqk), np.float64)
+    dk = np.empty((kr.shape[0], dqk), np.float64)
+    dvv = np.empty((kr.shape[0], dv), np.float64)
+    rc = lib.oracle_prefill_backward_sampled(mode, window, B, L, Hq, Hkv, dqk, dv, scale, dt, _ptr(qa), _ptr(ka),
+                                             _ptr(va), _ptr(s), _ptr(da), qr.shape[0], _ptr(qr), _ptr(dq),
+                                             kr.shape[0], _ptr(kr), _ptr(dk), _ptr(dvv))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward_sampled rejected its arguments")
+    return dq, dk, dvv
 
 
 SWA_ROPE_THETA = 10000.0     # sliding-window layers (deep-dive CH 3.5)

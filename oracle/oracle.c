@@ -271,6 +271,52 @@ int oracle_decode_fp8(int mode, int window, int layout, int B, int Hq, int Hkv, 
  * dq [B][Hq][L][dqk], dk [B][Hkv][L][dqk], dv [B][Hkv][L][dv] (overwritten), dsink [Hq]
  * (overwritten when sink is given).  Returns 0, or -1 on bad arguments.
  */
+/* dS_ij = P_ij (dP_ij - D_i): the gradient of the loss with respect to the logit a_ij. */
+static double score_grad(double p, double dp, double D) { return p * (dp - D); }
+
+/* The quantities of one row (b, h, i) that every gradient above is built from: the visible
+ * keys jlo .. jlo + n - 1, their weights pr[t] = P_i,jlo+t and dP values dp[t], D_i and the
+ * sink's weight.  Returns 0 when the row has no gradient (a sink of +inf makes every weight 0). */
+static int backward_row(int mode, int window, int L, int Hq, int Hkv, int dqk, int dv, double scale, int dtype,
+                        const void *q, const void *k, const void *v, const double *sink, const void *dout,
+                        int64_t b, int64_t h, int64_t i, double *a, double *pr, double *dp, int64_t *jlo_out,
+                        int *n_out, double *D_out, double *psink_out) {
+    const int64_t g = h / (Hq / Hkv);
+    const size_t kvbase = (size_t)(b * Hkv + g) * L;
+    const size_t qrow = (size_t)((b * Hq + h) * L + i);
+    const int has_sink = sink != NULL;
+    const double sk = has_sink ? sink[h] : 0.0;
+    if (has_sink && isinf(sk) && sk > 0) return 0; /* every weight is 0 */
+    const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
+    const int n = (int)(i - jlo + 1);
+    /* forward weights of this row */
+    double m = has_sink ? sk : -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        const size_t krow = (kvbase + (size_t)(jlo + t)) * dqk;
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += load(q, qrow * dqk + d, dtype) * load(k, krow + d, dtype);
+        a[t] = scale * dot;
+        if (a[t] > m) m = a[t];
+    }
+    double z = has_sink ? exp(sk - m) : 0.0;
+    for (int t = 0; t < n; ++t) z += exp(a[t] - m);
+    for (int t = 0; t < n; ++t) pr[t] = exp(a[t] - m) / z;
+    /* dP, D */
+    double Dsum = 0.0;
+    for (int t = 0; t < n; ++t) {
+        const size_t vrow = (kvbase + (size_t)(jlo + t)) * dv;
+        double dot = 0.0;
+        for (int e = 0; e < dv; ++e) dot += load(dout, qrow * dv + e, dtype) * load(v, vrow + e, dtype);
+        dp[t] = dot;
+        Dsum += pr[t] * dot;
+    }
+    *jlo_out = jlo;
+    *n_out = n;
+    *D_out = Dsum;
+    *psink_out = has_sink ? exp(sk - m) / z : 0.0;
+    return 1;
+}
+
 int oracle_prefill_backward(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv, double scale,
                             int dtype, const void *q, const void *k, const void *v, const double *sink,
                             const void *dout, double *dq, double *dk, double *dvo, double *dsink) {
@@ -293,40 +339,19 @@ int oracle_prefill_backward(int mode, int window, int B, int L, int Hq, int Hkv,
             for (size_t e = 0; e < (size_t)L * dqk; ++e) dk[kvbase * dqk + e] = 0.0;
             for (size_t e = 0; e < (size_t)L * dv; ++e) dvo[kvbase * dv + e] = 0.0;
             for (int64_t h = g * G; h < (g + 1) * G; ++h) {
-                const int has_sink = sink != NULL;
-                const double sk = has_sink ? sink[h] : 0.0;
                 for (int64_t i = 0; i < L; ++i) {
                     const size_t qrow = (size_t)((b * Hq + h) * L + i);
                     double *dqi = dq + qrow * dqk;
                     for (int d = 0; d < dqk; ++d) dqi[d] = 0.0;
-                    if (has_sink && isinf(sk) && sk > 0) continue; /* every weight is 0 */
-                    const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
-                    const int n = (int)(i - jlo + 1);
-                    /* forward weights of this row */
-                    double m = has_sink ? sk : -INFINITY;
+                    int64_t jlo;
+                    int n;
+                    double Dsum, psink;
+                    if (!backward_row(mode, window, L, Hq, Hkv, dqk, dv, scale, dtype, q, k, v, sink, dout, b, h, i, a,
+                                      pr, dp, &jlo, &n, &Dsum, &psink))
+                        continue;
+                    if (sink) dsink_part[b * Hq + h] += -psink * Dsum;
                     for (int t = 0; t < n; ++t) {
-                        const size_t krow = (kvbase + (size_t)(jlo + t)) * dqk;
-                        double dot = 0.0;
-                        for (int d = 0; d < dqk; ++d) dot += load(q, qrow * dqk + d, dtype) * load(k, krow + d, dtype);
-                        a[t] = scale * dot;
-                        if (a[t] > m) m = a[t];
-                    }
-                    double z = has_sink ? exp(sk - m) : 0.0;
-                    for (int t = 0; t < n; ++t) z += exp(a[t] - m);
-                    for (int t = 0; t < n; ++t) pr[t] = exp(a[t] - m) / z;
-                    const double psink = has_sink ? exp(sk - m) / z : 0.0;
-                    /* dP, D */
-                    double Dsum = 0.0;
-                    for (int t = 0; t < n; ++t) {
-                        const size_t vrow = (kvbase + (size_t)(jlo + t)) * dv;
-                        double dot = 0.0;
-                        for (int e = 0; e < dv; ++e) dot += load(dout, qrow * dv + e, dtype) * load(v, vrow + e, dtype);
-                        dp[t] = dot;
-                        Dsum += pr[t] * dot;
-                    }
-                    if (has_sink) dsink_part[b * Hq + h] += -psink * Dsum;
-                    for (int t = 0; t < n; ++t) {
-                        const double ds = pr[t] * (dp[t] - Dsum);
+                        const double ds = score_grad(pr[t], dp[t], Dsum);
                         const size_t j = kvbase + (size_t)(jlo + t);
                         for (int d = 0; d < dqk; ++d) {
                             dqi[d] += scale * ds * load(k, j * dqk + d, dtype);
@@ -348,6 +373,94 @@ int oracle_prefill_backward(int mode, int window, int B, int L, int Hq, int Hkv,
             dsink[h] = acc;
         }
     free(dsink_part);
+    return 0;
+}
+
+/*
+ * Sampled gradients, the same definitions as oracle_prefill_backward for a few entries of a
+ * large problem: dq of the rows qrows[r] = (b, h, i), r < nq, into dq_out [nq][dqk]; dk and dv
+ * of the keys krows[r] = (b, KV head g, j), r < nk, into dk_out [nk][dqk] and dv_out [nk][dv]
+ * (the sums over every row of every head of the group that sees key j).  Returns 0, or -1 on
+ * bad arguments.
+ */
+int oracle_prefill_backward_sampled(int mode, int window, int B, int L, int Hq, int Hkv, int dqk, int dv,
+                                    double scale, int dtype, const void *q, const void *k, const void *v,
+                                    const double *sink, const void *dout, int nq, const int64_t *qrows,
+                                    double *dq_out, int nk, const int64_t *krows, double *dk_out, double *dv_out) {
+    if (B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0 || nq < 0 || nk < 0) return -1;
+    if (mode == ORACLE_SWA && window <= 0) return -1;
+    if (mode != ORACLE_SWA && mode != ORACLE_GLOBAL) return -1;
+    const int G = Hq / Hkv;
+    for (int r = 0; r < nq; ++r)
+        if (qrows[3 * r] < 0 || qrows[3 * r] >= B || qrows[3 * r + 1] < 0 || qrows[3 * r + 1] >= Hq ||
+            qrows[3 * r + 2] < 0 || qrows[3 * r + 2] >= L)
+            return -1;
+    for (int r = 0; r < nk; ++r)
+        if (krows[3 * r] < 0 || krows[3 * r] >= B || krows[3 * r + 1] < 0 || krows[3 * r + 1] >= Hkv ||
+            krows[3 * r + 2] < 0 || krows[3 * r + 2] >= L)
+            return -1;
+    /* per (key, head of its group) partial sums, added in head order afterwards */
+    double *part = (double *)calloc((size_t)(nk > 0 ? nk : 1) * G * (dqk + dv), sizeof(double));
+    if (!part) return -1;
+#pragma omp parallel
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *pr = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nq; ++r) {
+            const int64_t b = qrows[3 * r], h = qrows[3 * r + 1], i = qrows[3 * r + 2];
+            const size_t kvbase = (size_t)(b * Hkv + h / G) * L;
+            double *dqi = dq_out + (size_t)r * dqk;
+            for (int d = 0; d < dqk; ++d) dqi[d] = 0.0;
+            int64_t jlo;
+            int n;
+            double Dsum, psink;
+            if (!backward_row(mode, window, L, Hq, Hkv, dqk, dv, scale, dtype, q, k, v, sink, dout, b, h, i, a, pr, dp,
+                              &jlo, &n, &Dsum, &psink))
+                continue;
+            for (int t = 0; t < n; ++t) {
+                const double ds = score_grad(pr[t], dp[t], Dsum);
+                const size_t j = kvbase + (size_t)(jlo + t);
+                for (int d = 0; d < dqk; ++d) dqi[d] += scale * ds * load(k, j * dqk + d, dtype);
+            }
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t rh = 0; rh < (int64_t)nk * G; ++rh) {
+            const int r = (int)(rh / G);
+            const int64_t b = krows[3 * r], g = krows[3 * r + 1], j = krows[3 * r + 2];
+            const int64_t h = g * G + rh % G;
+            double *pk = part + (size_t)rh * (dqk + dv), *pv = pk + dqk;
+            /* the rows that see key j: i >= j, and i < j + W in sliding-window mode */
+            const int64_t ihi = (mode == ORACLE_SWA && j + window - 1 < L - 1) ? j + window - 1 : L - 1;
+            for (int64_t i = j; i <= ihi; ++i) {
+                int64_t jlo;
+                int n;
+                double Dsum, psink;
+                if (!backward_row(mode, window, L, Hq, Hkv, dqk, dv, scale, dtype, q, k, v, sink, dout, b, h, i, a, pr,
+                                  dp, &jlo, &n, &Dsum, &psink))
+                    continue;
+                const int t = (int)(j - jlo);
+                const double ds = score_grad(pr[t], dp[t], Dsum);
+                const size_t qrow = (size_t)((b * Hq + h) * L + i);
+                for (int d = 0; d < dqk; ++d) pk[d] += scale * ds * load(q, qrow * dqk + d, dtype);
+                for (int e = 0; e < dv; ++e) pv[e] += pr[t] * load(dout, qrow * dv + e, dtype);
+            }
+        }
+        free(a);
+        free(pr);
+        free(dp);
+    }
+    for (int r = 0; r < nk; ++r) {
+        for (int d = 0; d < dqk; ++d) dk_out[(size_t)r * dqk + d] = 0.0;
+        for (int e = 0; e < dv; ++e) dv_out[(size_t)r * dv + e] = 0.0;
+        for (int hh = 0; hh < G; ++hh) {
+            const double *pk = part + ((size_t)r * G + hh) * (dqk + dv);
+            for (int d = 0; d < dqk; ++d) dk_out[(size_t)r * dqk + d] += pk[d];
+            for (int e = 0; e < dv; ++e) dv_out[(size_t)r * dv + e] += pk[dqk + e];
+        }
+    }
+    free(part);
     return 0;
 }
 

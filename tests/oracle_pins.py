@@ -537,11 +537,32 @@ def pin_backward_finite_differences(lib):
         assert abs(num - grad[idx]) < 1e-6 * max(1.0, abs(num)), f"grad {which} {idx}: {grad[idx]} vs {num}"
 
 
+def pin_backward_sampled_is_backward(lib):
+    """The sampled gradients (chosen dq rows, dk and dv of chosen keys) equal the entries of the
+    full backward, both modes, grouped heads, first, middle and last rows and keys."""
+    B, Hq, Hkv, L, dqk, dv = 2, 6, 2, 41, 16, 8
+    q = _rand((B, Hq, L, dqk), 1500)
+    k = _rand((B, Hkv, L, dqk), 1501)
+    v = _rand((B, Hkv, L, dv), 1502)
+    do = _rand((B, Hq, L, dv), 1503)
+    sink = np.array([0.5, 3.0, -1.0, 2.0, np.inf, -np.inf])
+    for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 7)):
+        dq, dk, dvv, _ = oracle.prefill_backward(q, k, v, sink, do, mode, W, 0.3, lib=lib)
+        qr = [(b, h, i) for b in range(B) for h in range(Hq) for i in (0, 6, 20, L - 1)]
+        kr = [(b, g, j) for b in range(B) for g in range(Hkv) for j in (0, 6, 33, L - 1)]
+        sq, sk, sv = oracle.prefill_backward_sampled(q, k, v, sink, do, mode, W, 0.3, qr, kr, lib=lib)
+        for n, (b, h, i) in enumerate(qr):
+            _close(sq[n], dq[b, h, i], 1e-12, 1e-14, f"dq row {(b, h, i)} mode={mode}")
+        for n, (b, g, j) in enumerate(kr):
+            _close(sk[n], dk[b, g, j], 1e-12, 1e-14, f"dk key {(b, g, j)} mode={mode}")
+            _close(sv[n], dvv[b, g, j], 1e-12, 1e-14, f"dv key {(b, g, j)} mode={mode}")
+
+
 ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
     pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes,
     pin_fp8_decode_is_decode_of_values, pin_lse, pin_rope, pin_append_then_decode_is_prefill,
-    pin_backward_autograd, pin_backward_finite_differences,
+    pin_backward_autograd, pin_backward_finite_differences, pin_backward_sampled_is_backward,
 ]

@@ -45,7 +45,7 @@ MUTATIONS = {
     "rotary pairs interleaved": ("const double a = load(x, base + i, dtype), b = load(x, base + i + half, dtype);",
                                  "const double a = load(x, base + 2 * (i % (half / 2)) + (i >= half / 2) * half, dtype), b = load(x, base + 2 * (i % (half / 2)) + 1 + (i >= half / 2) * half, dtype);"),
     "sink gradient with the wrong sign": ("dsink_part[b * Hq + h] += -psink * Dsum;", "dsink_part[b * Hq + h] += psink * Dsum;"),
-    "score gradient without the row term D": ("const double ds = pr[t] * (dp[t] - Dsum);", "const double ds = pr[t] * dp[t];"),
+    "score gradient without the row term D": ("return p * (dp - D);", "return p * dp;"),
     "key gradient without the logit scale": ("dk[j * dqk + d] += scale * ds * load(q, qrow * dqk + d, dtype);",
                                              "dk[j * dqk + d] += ds * load(q, qrow * dqk + d, dtype);"),
     "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
