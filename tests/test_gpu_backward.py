@@ -97,3 +97,47 @@ def test_backward_ga_2k_all_heads():
     for name, i in (("dq", 0), ("dk", 1), ("dv", 2)):
         assert_grad(got[i], ref[i], f"2K {name}")
     assert_dsink(got[3], ref[3], bound)
+
+
+@pytest.mark.parametrize("name", ["ga_prefill_L32768", "swa_prefill_L32768"])
+def test_backward_full_size_sampled(name):
+    """The benchmark's 32K workloads (64 query heads, dO seeded N(0,1) as the backward
+    benchmark draws it), in the launch configuration it times. Sampled entries are checked
+    against the oracle, which computes them one by one:
+    * dq rows at the first, middle and last positions and at tile edges, over several heads;
+    * dk and dv of keys with many rows (sliding window) or with the few rows near the end that
+      see them (global: a key at position j is seen by every row after it).
+    The sink gradient sums over every row; it is checked at 2K positions above."""
+    w = inputs.WORKLOADS[name]
+    L = w.seqlen
+    print(f"[case] backward full size {name}", flush=True)
+    d = inputs.prefill_inputs(w)
+    dout = inputs.normal((w.batch, w.hq, L, w.d_v), w.seed, 5)
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    s = dev_f32(d["sink"])
+    out = torch.empty((w.batch, w.hq, L, w.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.hq, L), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sa.sinkattn_prefill_chunk_workspace_bytes(w.batch, L, w.hq, w.hkv, L), dtype=torch.uint8,
+                     device="cuda")
+    sa.sinkattn_prefill_ex(w.mode, w.window, q, k, v, s, out, ws, lse=lse)
+    dq, dk, dv, _ = sa.prefill_backward(w.mode, w.window, q, k, v, s, out, dev_bf16(dout), lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    G = w.hq // w.hkv
+    qpos = [0, 31, 32, 63, 64, 127, 128, 4095, 16383, 16384, L - 33, L - 32, L - 1]
+    qrows = [(0, int(h), i) for i in qpos for h in rng.choice(w.hq, 2, replace=False)]
+    if w.mode == oracle.SWA:
+        kpos = [0, 1, 127, 128, 4000, 16384, 30001, L - 129, L - 1]
+    else:
+        kpos = [L - 1, L - 2, L - 31, L - 32, L - 33, L - 64]
+    krows = [(0, int(rng.integers(w.hkv)), j) for j in kpos]
+    rq, rk, rv = oracle.prefill_backward_sampled(d["q"], d["k"], d["v"], d["sink"], dout, w.mode, w.window,
+                                                  w.scale, qrows, krows)
+    idx = torch.tensor(qrows, dtype=torch.long)
+    got_q = dq[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy()
+    kidx = torch.tensor(krows, dtype=torch.long)
+    got_k = dk[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy()
+    got_v = dv[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy()
+    assert_grad(got_q, rq, f"{name} dq rows")
+    assert_grad(got_k, rk, f"{name} dk keys")
+    assert_grad(got_v, rv, f"{name} dv keys")
