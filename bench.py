@@ -45,6 +45,8 @@ TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
                           "sha256": "eebd41a6daa410953173992f9367b133b50ab0c97caa6a1bb7314a9d898f371d",
                           "read_GB": 3.5705, "written_GB": 0.5372},
+    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "",
+                           "read_GB": 0.0, "written_GB": 0.0},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
                                 "sha256": "4abae72239412941c0457187832f56caa0799fbffb95080e33aaeb8b8718b27d",
                                 "read_GB": 5.3880, "written_GB": 0.0179},
@@ -295,6 +297,14 @@ def main() -> int:
                            "traffic": traffic_gb("ga_decode_B8_256K_paged"),
                            "traffic_unit": "GB per call (HBM read + written)"}
 
+    swa = comp.get("swa_prefill_L32768")
+    roofline_swa = None
+    if swa:
+        roofline_swa = {"kernel": "prefill_swa_kernel (swa_prefill_L32768)", "bound": "hbm", "achieved": swa["gbps"],
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(swa["gbps"] / HBM_PEAK_GBPS, 4),
+                        "traffic": traffic_gb("swa_prefill_L32768"),
+                        "traffic_unit": "GB per call (HBM read + written)"}
+
     dec8 = comp.get("ga_decode_B8_256K_paged_fp8")
     roofline_decode_fp8 = None
     if dec8:
@@ -323,7 +333,7 @@ def main() -> int:
                    "ga_decode_fp8": "as ga_decode with an E4M3 cache, per-tensor scales 2^-6"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode,
-        "roofline_decode_fp8": roofline_decode_fp8, "cpu_baseline": cpu,
+        "roofline_decode_fp8": roofline_decode_fp8, "roofline_swa_prefill": roofline_swa, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
