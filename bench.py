@@ -43,15 +43,15 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "eebd41a6daa410953173992f9367b133b50ab0c97caa6a1bb7314a9d898f371d",
-                          "read_GB": 3.5705, "written_GB": 0.5372},
-    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "",
-                           "read_GB": 0.0, "written_GB": 0.0},
+                          "sha256": "96855fdd68fead67194bf73e348fe91165905b1973cc6419b768a08fdbc164db",
+                          "read_GB": 3.5702, "written_GB": 0.5369},
+    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "96855fdd68fead67194bf73e348fe91165905b1973cc6419b768a08fdbc164db",
+                           "read_GB": 1.0914, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "4abae72239412941c0457187832f56caa0799fbffb95080e33aaeb8b8718b27d",
+                                "sha256": "0a4495fb62d0d19647df1e1752d27c26cac02e63feeb87e6f69ceaaec1876295",
                                 "read_GB": 5.3880, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "4abae72239412941c0457187832f56caa0799fbffb95080e33aaeb8b8718b27d",
+                                    "sha256": "0a4495fb62d0d19647df1e1752d27c26cac02e63feeb87e6f69ceaaec1876295",
                                     "read_GB": 2.7037, "written_GB": 0.0179},
 }
 
