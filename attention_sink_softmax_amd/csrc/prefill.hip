@@ -782,7 +782,15 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *v, uin
 
 namespace {
 bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw == kCausalWaves; }
-constexpr int kComputeUnits = 256;  // MI355X; only the size of the ring kernel's runs depends on it
+// Compute units of the current device (256 on a whole MI355X, fewer on a partition); only the
+// length of the ring kernel's runs depends on it.
+int compute_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
 }  // namespace
 
 // Causal mode with a group size divisible by 8: the eight-wave kernel, one head per wave.
@@ -802,7 +810,8 @@ int64_t plan_prefill(PrefillParams &p) {
         p.hgroups = p.G / kSwaWaves;
         const int64_t units = (int64_t)p.B * p.Hkv * p.hgroups;
         const int64_t nqb = (p.L + 31) / 32;
-        const int64_t split = std::max<int64_t>(1, std::min<int64_t>(nqb, (kComputeUnits + units - 1) / units));
+        const int64_t cus = compute_units();
+        const int64_t split = std::max<int64_t>(1, std::min<int64_t>(nqb, (cus + units - 1) / units));
         p.chunk = (int)((nqb + split - 1) / split);
         p.n_pbw = (int)((nqb + p.chunk - 1) / p.chunk);
         const int64_t items = units * p.n_pbw;
