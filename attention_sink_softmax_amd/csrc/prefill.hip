@@ -14,9 +14,12 @@
 //     a workgroup of 8 waves, one query head each, all at the same 32 query positions, so
 //     one K / V^T tile staged in LDS feeds all eight; two waves share each SIMD and hide
 //     each other's LDS waits.
-//   * Everything else (sliding window, other group sizes): a workgroup of 4 waves, each
-//     owning HPW query heads (2 when the group size is even) and 32 positions; with two
-//     heads per wave every K and V fragment read from LDS feeds two MFMAs.
+//   * Sliding window (W <= 128, group a multiple of 8, whole sequence): the ring kernel below,
+//     8 waves walking a run of consecutive query blocks with the band's keys kept in LDS.
+//   * Everything else (other sliding-window shapes, chunked sliding-window prefill, other
+//     group sizes): a workgroup of 4 waves, each owning HPW query heads (2 when the group
+//     size is even and the mode causal) and 32 positions; with two heads per wave every K
+//     and V fragment read from LDS feeds two MFMAs.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K comes
 //     from LDS as the A operand, Q^T stays in registers as the B operand for the whole
 //     kernel.  In the output layout a lane holds one query column and 16 key rows, so the
