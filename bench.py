@@ -43,9 +43,9 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "b5754ff07d3b0aee0d3f4665821e8b8e7018892ad6878e4ad24844e736239179",
+                          "sha256": "19b1ca4ff7809548ddd02475fe4304d7d93425642b61985b48c37be198295442",
                           "read_GB": 3.5702, "written_GB": 0.5369},
-    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "b5754ff07d3b0aee0d3f4665821e8b8e7018892ad6878e4ad24844e736239179",
+    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "19b1ca4ff7809548ddd02475fe4304d7d93425642b61985b48c37be198295442",
                            "read_GB": 1.0914, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
                                 "sha256": "0a4495fb62d0d19647df1e1752d27c26cac02e63feeb87e6f69ceaaec1876295",
