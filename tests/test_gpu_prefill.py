@@ -79,6 +79,7 @@ CASES = [
     (1, 8, 1, 20, oracle.SWA, 128, True),
     (2, 16, 1, 97, oracle.SWA, 1, True),
     (1, 8, 1, 200, oracle.SWA, 16, False),
+    (33, 64, 8, 70, oracle.SWA, 128, True),  # 264 (sequence, KV head) units: one run each
 ]
 
 
