@@ -60,11 +60,13 @@ constexpr int kKT = 64;                    // keys per tile in bwd_dq
 constexpr int kPreRows = 16;               // rows per bwd_pre workgroup
 
 // Byte offset of 16-byte chunk c of row r: rows of 192 (384 B) and of 128 (256 B) elements.
-// Both row lengths are multiples of 128 B (the 32 banks), so chunk c of every row starts on the
-// same bank; the chunk index is XORed with swz(r), which takes the 8 values 0..7 over any 8
-// aligned rows (the 8 lanes of one 128-byte phase of a row read) and 4 values with distinct
-// bits 1-2 over any 4 aligned rows (the 4 rows x 2 adjacent chunks of one 16-lane phase of a
-// transposing read).
+// The chunk index is XORed with swz(r), which takes the 8 values 0..7 over any 8 aligned rows
+// and 4 values with distinct bits 1-2 over any 4 aligned rows: no two lanes of a 128-byte
+// phase of a row read, or of a 16-lane transposing read, share a bank if the banks serve
+// 128 bytes per cycle.  The hardware serves 256 bytes per cycle (16 lanes of a row read), and
+// its counters show conflicts in 12-15% of cycles here.  A swizzle built for that wider phase
+// removed them but made the dQ kernel slower (its addresses took more registers), so this
+// one stays.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 __device__ __forceinline__ int off192(int r, int c) { return r * 384 + ((c ^ swz(r)) << 4); }
 __device__ __forceinline__ int off128(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
