@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kSlice = 32;                           // keys per wave step
+constexpr float kLazyRescale = 8.f;                  // log2 growth of a max that forces a rescale
 constexpr int kKBytes = kSlice * kDqk * 2;           // 12 KB: 12 blocks of 1 KB
 constexpr int kVBytes = kSlice * kDv * 2;            // 8 KB: 8 blocks of 1 KB
 constexpr int kBufBytes = kKBytes + kVBytes;         // one slice
@@ -304,36 +305,66 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     s[cb][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][kk], s[cb][sb], 0, 0, 0);
             }
         }
-        // lane holds keys j0 + 16sb + 4q + e for column hl of each block
-        bf16x8 pf[NCB];
-        float alpha[NCB];
+        // lane holds keys j0 + 16sb + 4q + e for column hl of each block.  Keys outside a
+        // column's range become -inf, on slices that cross some column's range only (a
+        // wave-uniform test).
+        bool inside = true;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) inside &= (j0 >= lo_c[cb]) & (j0 + kSlice - 1 <= hi_c[cb]);
+        if (!__all(inside)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0 + 16 * sb + 4 * q + e;
+                        if (!((j >= lo_c[cb]) & (j <= hi_c[cb]))) s[cb][sb][e] = -INFINITY;
+                    }
+        }
+        // Running max of the scaled scores (the scale is positive, so the max of the raw
+        // scores is taken first).  The reference that the sums are kept against moves only
+        // when some column's max grows by more than 2^kLazyRescale: the weights then stay
+        // below 2^kLazyRescale, and the rare rescale (a wave-uniform branch) keeps the
+        // accumulators, the denominators and the reference consistent.
+        float mnew[NCB];
+        bool grow = false;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            float x[8];
-            float mx = m_run[cb];
+            float mx = -INFINITY;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + 16 * sb + 4 * q + e;
-                    const float v = (j >= lo_c[cb] && j <= hi_c[cb]) ? s[cb][sb][e] * p.scale_log2 : -INFINITY;
-                    x[4 * sb + e] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[cb][sb][e]);
+            mx = max_xor32(max_xor16(mx)) * p.scale_log2;
+            mnew[cb] = fmaxf(m_run[cb], mx);
+            grow |= mnew[cb] > m_run[cb] + kLazyRescale;
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                // an unchanged reference (including -inf, nothing visible yet) keeps alpha = 1
+                const float alpha = (mnew[cb] == m_run[cb]) ? 1.f : exp2f_fast(m_run[cb] - mnew[cb]);
+                l_run[cb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
+                m_run[cb] = mnew[cb];
             }
-            mx = max_xor32(max_xor16(mx));
-            const float mu = (mx == -INFINITY) ? 0.f : mx;
-            alpha[cb] = exp2f_fast(m_run[cb] - mu);
-            m_run[cb] = mx;
+        }
+        bf16x8 pf[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const float neg = (m_run[cb] == -INFINITY) ? 0.f : -m_run[cb];
             float ps = 0.f;
             uint32_t pk[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = exp2f_fast(x[2 * e] - mu), p1 = exp2f_fast(x[2 * e + 1] - mu);
+                const float p0 = exp2f_fast(__builtin_fmaf(s[cb][e >> 1][2 * (e & 1)], p.scale_log2, neg));
+                const float p1 = exp2f_fast(__builtin_fmaf(s[cb][e >> 1][2 * (e & 1) + 1], p.scale_log2, neg));
                 ps += p0 + p1;
                 pk[e] = pack_bf16x2(p0, p1);
             }
-            l_run[cb] = l_run[cb] * alpha[cb] + ps;
+            l_run[cb] += ps;
             pf[cb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
         }
 
@@ -361,7 +392,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[cb], acc[cb][db] * alpha[cb], 0, 0, 0);
+                acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[cb], acc[cb][db], 0, 0, 0);
         }
     };
 
