@@ -44,15 +44,15 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
                           "sha256": "19b1ca4ff7809548ddd02475fe4304d7d93425642b61985b48c37be198295442",
-                          "read_GB": 3.5702, "written_GB": 0.5369},
+                          "read_GB": 3.5704, "written_GB": 0.5369},
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "19b1ca4ff7809548ddd02475fe4304d7d93425642b61985b48c37be198295442",
-                           "read_GB": 1.0914, "written_GB": 0.5369},
+                           "read_GB": 1.0915, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "0a4495fb62d0d19647df1e1752d27c26cac02e63feeb87e6f69ceaaec1876295",
-                                "read_GB": 5.3880, "written_GB": 0.0179},
+                                "sha256": "19b9ace8465c966176b7ac89c1af4f4531349615b52e5f364c628b41c6b03e10",
+                                "read_GB": 5.3880, "written_GB": 0.0180},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "0a4495fb62d0d19647df1e1752d27c26cac02e63feeb87e6f69ceaaec1876295",
-                                    "read_GB": 2.7037, "written_GB": 0.0179},
+                                    "sha256": "19b9ace8465c966176b7ac89c1af4f4531349615b52e5f364c628b41c6b03e10",
+                                    "read_GB": 2.7036, "written_GB": 0.0180},
 }
 
 
