@@ -261,3 +261,30 @@ def test_decode_workspace_plan(L):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(sa.LibraryMissing):
         sa.lib(str(tmp_path / "nope.so"))
+
+
+def backward(L, mode=0, window=0, d=None, q=A, k=A, v=A, sink=None, out=A, dout=A, lse=A, dq=A, dk=A, dv=A,
+             dsink=None, ws=A, wsb=1 << 40):
+    d = d or dims(hq=64, hkv=4)
+    return L.sinkattn_prefill_backward(mode, window, ctypes.byref(d), q, k, v, sink, out, dout, lse, dq, dk, dv, dsink,
+                                       ws, wsb, None)
+
+
+def test_backward_argument_errors(L):
+    d = dims(hq=64, hkv=4)
+    need = L.sinkattn_prefill_backward_workspace_bytes(ctypes.byref(d))
+    assert need == 4 * (64 * 64 + 64 * ((64 + 15) // 16))  # D per row + sink-gradient partials
+    # empty work is a no-op success, even with NULL tensors
+    assert backward(L, d=dims(B=0, hq=64, hkv=4), q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None,
+                    dk=None, dv=None, ws=None, wsb=0) == OK
+    assert backward(L, d=dims(hq=64, hkv=4, dqk=128)) == E_UNSUP        # head size
+    assert backward(L, d=dims(hq=12, hkv=4)) == E_UNSUP                 # group of 3: not a multiple of 4
+    assert backward(L, d=dims(hq=64, hkv=5)) == E_SHAPE                 # 64 % 5
+    assert backward(L, mode=1, window=0) == E_SHAPE                     # window 0
+    assert backward(L, q=None) == E_NULL
+    assert backward(L, lse=None) == E_NULL
+    assert backward(L, sink=A, dsink=None) == E_NULL                    # a sink needs its gradient
+    assert backward(L, dq=A + 4) == E_ALIGN
+    assert backward(L, sink=A, dsink=A + 8) == E_ALIGN
+    assert backward(L, ws=None) == E_WS
+    assert backward(L, wsb=need - 1) == E_WS
