@@ -90,7 +90,7 @@ def main() -> int:
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
