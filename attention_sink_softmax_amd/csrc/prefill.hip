@@ -604,15 +604,25 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
 constexpr int kSwaWaves = 8;
 constexpr int kRingSlots = 6;
 constexpr int kSubKBytes = 32 * kDqk * 2;  // 12 KB: rows of a K tile's first 32 keys
-constexpr int kSubVBytes = kDv * 32 * 2;   // 8 KB: V^T [128 dv][32 keys]
+constexpr int kSubVBytes = 32 * kDv * 2;   // 8 KB: V [32 keys][128 dv]
 constexpr int kSlotBytes = kSubKBytes + kSubVBytes;
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// V rows of a sub-block in LDS, row-major [32 keys][128 dv] with 16-byte chunk c of key row r
+// at chunk c ^ vswz(r).  The banks serve 256 bytes per cycle and every 256-byte row starts on
+// the same bank, so vswz takes 16 distinct values over any 16 aligned rows (a 16-lane row
+// write) and 4 distinct values of bits 2-3 over any 4 aligned rows (the 4 rows x 4 adjacent
+// chunks of a 32-lane transposing read).
+__device__ __forceinline__ int vswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int v_off(int r, int c) { return r * (kDv * 2) + ((c ^ vswz(r)) << 4); }
+
 // One 32-key sub-block, global -> registers: K chunk idx lands at byte 16 idx of the K part in
-// the K tile layout (rows 0..31), V^T chunk idx at byte 16 idx of the V part: block rg holds
-// dv rows 16rg .. 16rg + 15 and the sub-block's 4 key chunks (chunk c of row r in slot 16c + r).
-// Thread t moves K chunks t and 512 + t (t < 256) and V^T chunk t; every thread issues the
-// same three loads (the second K load of threads 256 .. 511 is not stored), so the number in
-// flight is the same on every path.
+// the K tile layout (rows 0..31); thread t also moves chunk t & 15 of V row t >> 4, stored at
+// v_off.  Thread t moves K chunks t and 512 + t (t < 256); every thread issues the same three
+// loads (the second K load of threads 256 .. 511 is not stored), so the number in flight is
+// the same on every path.  Rows past the sequence end read the last row (their weights are 0).
 struct SubStage {
     u32x4 k0, k1, v;
 };
@@ -625,24 +635,32 @@ __device__ __forceinline__ void sub_load(SubStage &st, const PrefillParams &p, i
     };
     st.k0 = kchunk(tid);
     st.k1 = kchunk(512 + (tid & 255));
-    const uint16_t *vtile = p.vt + (((size_t)b * p.Hkv + kvh) * (p.lpad / kBN) + (sub >> 1)) * (kDv * kBN);
-    const int rg = tid >> 6, l = tid & 63;
-    st.v = ldg16(vtile + (16 * rg + (l & 15)) * kBN + (4 * (sub & 1) + (l >> 4)) * 8);
+    const int vrow = min(32 * sub + (tid >> 4), p.L - 1);
+    st.v = ldg16(p.v + (((size_t)b * p.Hkv + kvh) * p.L + vrow) * kDv + (tid & 15) * 8);
 }
 __device__ __forceinline__ void sub_store(const SubStage &st, char *slot, int tid) {
     *reinterpret_cast<u32x4 *>(slot + 16 * tid) = st.k0;
     if (tid < 256) *reinterpret_cast<u32x4 *>(slot + 16 * (512 + tid)) = st.k1;
-    *reinterpret_cast<u32x4 *>(slot + kSubKBytes + 16 * tid) = st.v;
+    *reinterpret_cast<u32x4 *>(slot + kSubKBytes + v_off(tid >> 4, tid & 15)) = st.v;
 }
 
-// O^T += V^T P^T from a V^T sub-block (layout of sub_store).
+// O^T += V^T P^T from the V rows of a sub-block (layout of sub_store).  The A operand of
+// k-step k2 is, for lane (g, dv row 32 db + lq), V at the keys that P^T's registers hold:
+// 16 k2 + {4g .. 4g + 3} and 16 k2 + 8 + {4g .. 4g + 3}.  Two transposing reads give them:
+// in a 16-lane group, lane 4r + c4 addresses key row r and dv columns 4 c4 .. +3 of its
+// 16-column block, and lane i receives dv column i of the 4 rows.
 __device__ __forceinline__ void pv_sub(const char *Vs, const bf16x8 (&pf)[1][2], f32x16 (&acc)[1][4], const WaveCtx &w) {
-    const int vl = (w.lq >> 4) * 1024 + w.g * 256 + (w.lq & 15) * 16;
+    const int gl = (w.lane >> 4) & 1, i = w.lane & 15, r = i >> 2, c4 = i & 3;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
+        const int col = 32 * db + 16 * gl + 4 * c4;
+        const int chunk = col >> 3, half = (col >> 2) & 1;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vs + vl + db * 2048 + k2 * 512);
+            const int r0 = 16 * k2 + 4 * w.g + r;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(Vs + v_off(r0, chunk) + 8 * half));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(Vs + v_off(r0 + 8, chunk) + 8 * half));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][k2], acc[0][db], 0, 0, 0);
         }
     }
@@ -846,7 +864,7 @@ size_t prefill_workspace_bytes(int B, int Hkv, int L) {
 
 int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     PrefillParams p = prm;
-    {
+    if (!p.ring) {  // the ring kernel reads V rows directly
         void *targs[] = {(void *)&p.v, (void *)&p.vt, (void *)&p.L, (void *)&p.lpad};
         if (hipLaunchKernel(reinterpret_cast<const void *>(&transpose_v_kernel), dim3(p.lpad / kBN, p.B * p.Hkv),
                             dim3(256), targs, 0, stream) != hipSuccess)
