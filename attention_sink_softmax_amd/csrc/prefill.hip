@@ -415,6 +415,47 @@ __device__ __forceinline__ void store_out(const PrefillParams &p, const WaveSetu
     }
 }
 
+// store_out with the same stores on every path, for a loop that prefetches across it.  A
+// branch around the stores makes the compiler's wait analysis assume the path without them,
+// so a later wait for a prefetch issued before the stores would wait for the stores as well.
+// Here every lane always issues its 16 output stores and one log-sum-exp store through a
+// buffer resource spanning the rows of its (sequence, head); a row past the sequence end, a
+// lane that does not own the log-sum-exp, or a missing log-sum-exp buffer (an empty range)
+// gets an offset past the range, and the hardware drops such stores.
+template <int HPW>
+__device__ __forceinline__ void store_out_fixed(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
+                                                const f32x16 (&acc)[HPW][4], const float (&m_run)[HPW],
+                                                const float (&l_run)[HPW], const bool (&sink_inf)[HPW]) {
+    constexpr int kRawDword3 = 0x00020000;  // untyped 32-bit data, no swizzle
+    constexpr int kDropped = 0x40000000;    // past any range below
+    const bool row_ok = w.qi < p.L;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const float lt = sum_xor32(l_run[h]);
+        const float inv = p.out_scale / lt;
+        const size_t row0 = ((size_t)ws.b * p.Hq + ws.h0 + h) * p.Lq;
+        const __amdgpu_buffer_rsrc_t orr =
+            __builtin_amdgcn_make_buffer_rsrc(p.out + row0 * kDv, 0, p.Lq * (kDv * 2), kRawDword3);
+        const __amdgpu_buffer_rsrc_t lrr =
+            __builtin_amdgcn_make_buffer_rsrc(p.lse ? p.lse + row0 : nullptr, 0, p.lse ? p.Lq * 4 : 0, kRawDword3);
+        const int ooff = row_ok ? (w.qi - p.q0) * (kDv * 2) + 8 * w.g : kDropped;
+        const int loff = row_ok && w.g == 0 ? (w.qi - p.q0) * 4 : kDropped;
+        const float lse = (m_run[h] + __builtin_amdgcn_logf(lt)) * kLn2;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lrr, loff, 0, 0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o0 = acc[h][db][4 * i] * inv, o1 = acc[h][db][4 * i + 1] * inv;
+                float o2 = acc[h][db][4 * i + 2] * inv, o3 = acc[h][db][4 * i + 3] * inv;
+                if (sink_inf[h]) o0 = o1 = o2 = o3 = 0.f;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, orr,
+                                                      ooff + (32 * db + 8 * i) * 2, 0, 0);
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ WaveCtx make_ctx(const PrefillParams &p, const WaveSetup &ws, int lane) {
     WaveCtx w;
     w.L = p.L;
@@ -756,7 +797,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
         }
         // slot (j + 1) % 6 held sub-block j - 5, outside this block's band
         sub_store(st, ring + ((j + 1) % kRingSlots) * kSlotBytes, tid);
-        store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
+        store_out_fixed<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
         __syncthreads();
     };
     for (int j = j_lo; j < j_hi; j += 2) {

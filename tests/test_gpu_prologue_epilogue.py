@@ -90,7 +90,7 @@ def test_kv_append(layout, fp8, n_new):
 
 
 @pytest.mark.parametrize("mode,W,Hq,Hkv,Lk,Lq", [(oracle.GLOBAL, 0, 64, 4, 700, 700), (oracle.SWA, 128, 64, 8, 900, 77),
-                                                 (oracle.GLOBAL, 0, 8, 4, 300, 300)])
+                                                 (oracle.GLOBAL, 0, 8, 4, 300, 300), (oracle.SWA, 128, 64, 8, 300, 300)])
 def test_prefill_epilogue(mode, W, Hq, Hkv, Lk, Lq):
     w = inputs.Workload("t", "prefill", 0, 1, Hq, Hkv, seqlen=Lk, seed=50 + Lq)
     d = inputs.prefill_inputs(w)
