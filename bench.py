@@ -43,9 +43,9 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "b98e50f6029a09b703692ebac208561ae4f8de27565eefa3ecff2ed0da7b5ca3",
-                          "read_GB": 3.5704, "written_GB": 0.5369},
-    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "b98e50f6029a09b703692ebac208561ae4f8de27565eefa3ecff2ed0da7b5ca3",
+                          "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
+                          "read_GB": 3.5705, "written_GB": 0.5369},
+    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
                            "read_GB": 1.0231, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
                                 "sha256": "19b9ace8465c966176b7ac89c1af4f4531349615b52e5f364c628b41c6b03e10",
