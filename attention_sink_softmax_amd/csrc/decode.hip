@@ -50,9 +50,28 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform).
-__device__ __forceinline__ void dma16(const uint16_t *src, char *dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+// Non-temporal loads, for data read once per call.  Over 4 GiB read in whole cache lines per
+// instruction, MI355X streamed 7.1 TB/s with them against 6.3 TB/s with the default policy,
+// for 16-byte loads into registers and into LDS alike.  Where an instruction reads only part
+// of each line and later instructions read the rest, they lose the reuse of the line: the
+// sliding-window prefill took 38% longer with its query and K/V loads non-temporal (and 3.4x
+// with its output stores so), so only the decode cache loads here use them.
+constexpr int kLoadNT = 2;  // cache-policy argument of the load-to-LDS builtins: nt
+__device__ __forceinline__ u32x4 ldg16_nt(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform), with
+// cache policy AUX.  The cache is read once per step.  With one block of columns (one-token
+// decode) non-temporal loads measured faster on two boxes: 1.3-2.7% for the paged bf16 cache
+// at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% for the 128-slot rings at B = 128.  With
+// four blocks (the q_len = 4 verify) they measured 0-3% slower, so the kernels with more than
+// one block keep the default policy.
+template <int NCB>
+constexpr int kCachePolicy = NCB == 1 ? kLoadNT : 0;
+template <int AUX>
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, AUX);
 }
 
 // LDS layout of one slice (per wave, per buffer):
@@ -215,15 +234,15 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     const int t = min(max(16 * sb + s, lo), hi);
 #pragma unroll
                     for (int i2 = 0; i2 < 3; ++i2)
-                        __builtin_amdgcn_global_load_lds(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
-                                                         (lds_void *)(kb + sb * 3072 + i2 * 1024), 16, 0, 0);
+                        dma16<kCachePolicy<NCB>>(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
+                                                 kb + sb * 3072 + i2 * 1024);
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int key = 8 * m + (lane >> 3);
                     const int t = min(max(key, lo), hi);
-                    __builtin_amdgcn_global_load_lds(vbase8 + (size_t)(off0 + t) * kDv + ((lane & 7) ^ vswz(key)) * 16,
-                                                     (lds_void *)(kb + kKBytes8 + m * 1024), 16, 0, 0);
+                    dma16<kCachePolicy<NCB>>(vbase8 + (size_t)(off0 + t) * kDv + ((lane & 7) ^ vswz(key)) * 16,
+                                             kb + kKBytes8 + m * 1024);
                 }
                 return;
             }
@@ -234,16 +253,16 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
                 for (int kk = 0; kk < 6; ++kk) {
                     if constexpr (kSingle) {
-                        kreg[sb][kk] = as_bf16x8(ldg16(kr + 32 * kk));
+                        kreg[sb][kk] = as_bf16x8(kCachePolicy<NCB> ? ldg16_nt(kr + 32 * kk) : ldg16(kr + 32 * kk));
                     } else {
-                        dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                        dma16<kCachePolicy<NCB>>(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
                     }
                 }
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int t = min(max(4 * m + r, lo), hi);
-                dma16(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kCachePolicy<NCB>>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
             }
         } else {
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
@@ -252,12 +271,12 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 const int j = min(max(j0 + 16 * sb + s, lo), hi);
                 const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * r;
 #pragma unroll
-                for (int kk = 0; kk < 6; ++kk) dma16(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                for (int kk = 0; kk < 6; ++kk) dma16<kCachePolicy<NCB>>(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int j = min(max(j0 + 4 * m + r, lo), hi);
-                dma16(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kCachePolicy<NCB>>(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
             }
         }
     };
