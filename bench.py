@@ -48,11 +48,11 @@ TRAFFIC = {
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
                            "read_GB": 1.0231, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "19b9ace8465c966176b7ac89c1af4f4531349615b52e5f364c628b41c6b03e10",
-                                "read_GB": 5.3880, "written_GB": 0.0180},
+                                "sha256": "94d9898542b329c5efcdd2d40aeac6a2d979a6b8b9bf8a8c57edee43e48c652b",
+                                "read_GB": 5.4120, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "19b9ace8465c966176b7ac89c1af4f4531349615b52e5f364c628b41c6b03e10",
-                                    "read_GB": 2.7036, "written_GB": 0.0180},
+                                    "sha256": "94d9898542b329c5efcdd2d40aeac6a2d979a6b8b9bf8a8c57edee43e48c652b",
+                                    "read_GB": 2.7528, "written_GB": 0.0179},
 }
 
 
