@@ -67,6 +67,8 @@ __device__ __forceinline__ u32x4 ldg16_nt(const uint16_t *p) {
 // at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% for the 128-slot rings at B = 128.  With
 // four blocks (the q_len = 4 verify) they measured 0-3% slower, so the kernels with more than
 // one block keep the default policy.
+__device__ __forceinline__ int kswz(int k) { return (k >> 1) & 7; }
+
 template <int NCB>
 constexpr int kCachePolicy = NCB == 1 ? kLoadNT : 0;
 template <int AUX>
@@ -75,8 +77,11 @@ __device__ __forceinline__ void dma16(const void *src, char *dst) {
 }
 
 // LDS layout of one slice (per wave, per buffer):
-//   K: block (sb, kk) = 16 keys x 64 bytes (d = 32kk .. 32kk+31); slot q*16 + key holds
-//      K[16sb + key][32kk + 8q .. +8], so the A operand of S^T is the 1 KB block itself.
+//   K: block 6 sb + 3 kh + c (1 KB) holds keys 16 sb + 8 kh .. +7 and bytes 128 c .. +127 of
+//      their rows, one whole cache line per key, so each load instruction reads whole lines.
+//      Key k (0..15 within the 16-key block) keeps its 16-byte chunk m of the line at slot
+//      8 (k & 7) + (m ^ kswz(k)): the 16 lanes of an A-operand read (keys 0..15, one chunk)
+//      hit 16 distinct 16-byte slots of a 256-byte bank phase.
 //   V: block m = keys 4m .. 4m+3, 256 bytes each; row r keeps its 16-byte chunk c in slot
 //      c ^ 2r, so the transposing reads of 4 rows x 32 bytes hit distinct banks.
 
@@ -158,6 +163,10 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     const int b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hl = lane & 15, q = lane >> 4;  // column within a block, k-group
+    // lane part of the K operand address (layout of the K loads) for even and odd k-steps:
+    // key hl of the 16-key block, chunk 4 (kk & 1) + q of line kk / 2
+    const int klane[2] = {3072 * (hl >> 3) + (8 * (hl & 7) + (q ^ kswz(hl))) * 16,
+                          3072 * (hl >> 3) + (8 * (hl & 7) + ((4 + q) ^ kswz(hl))) * 16};
     const int rows = p.G * p.q_len;
 
     const int n = p.seq_lens[b];
@@ -246,16 +255,26 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 }
                 return;
             }
+            if constexpr (kSingle) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int t = min(max(16 * sb + s, lo), hi);
-                const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int t = min(max(16 * sb + s, lo), hi);
+                    const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
 #pragma unroll
-                for (int kk = 0; kk < 6; ++kk) {
-                    if constexpr (kSingle) {
+                    for (int kk = 0; kk < 6; ++kk)
                         kreg[sb][kk] = as_bf16x8(kCachePolicy<NCB> ? ldg16_nt(kr + 32 * kk) : ldg16(kr + 32 * kk));
-                    } else {
-                        dma16<kCachePolicy<NCB>>(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const int k16 = 8 * kh + (lane >> 3);
+                        const int t = min(max(16 * sb + k16, lo), hi);
+                        const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * ((lane & 7) ^ kswz(k16));
+#pragma unroll
+                        for (int c = 0; c < 3; ++c)
+                            dma16<kCachePolicy<NCB>>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
                     }
                 }
             }
@@ -268,10 +287,14 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-                const int j = min(max(j0 + 16 * sb + s, lo), hi);
-                const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * r;
 #pragma unroll
-                for (int kk = 0; kk < 6; ++kk) dma16<kCachePolicy<NCB>>(kr + 32 * kk, kb + (sb * 6 + kk) * 1024);
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int k16 = 8 * kh + (lane >> 3);
+                    const int j = min(max(j0 + 16 * sb + k16, lo), hi);
+                    const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * ((lane & 7) ^ kswz(k16));
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) dma16<kCachePolicy<NCB>>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
+                }
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -318,7 +341,8 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     kf = e4m3x8_to_bf16(*reinterpret_cast<const v2i32 *>(
                         kb + sb * 3072 + ((2 * kk + (q >> 1)) * 16 + hl) * 16 + (q & 1) * 8));
                 else
-                    kf = kSingle ? kreg[sb][kk] : *reinterpret_cast<const bf16x8 *>(kb + (sb * 6 + kk) * 1024 + lane * 16);
+                    kf = kSingle ? kreg[sb][kk]
+                                 : *reinterpret_cast<const bf16x8 *>(kb + (6 * sb + (kk >> 1)) * 1024 + klane[kk & 1]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     s[cb][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][kk], s[cb][sb], 0, 0, 0);
