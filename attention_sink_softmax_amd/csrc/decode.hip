@@ -62,15 +62,13 @@ __device__ __forceinline__ u32x4 ldg16_nt(const uint16_t *p) {
 }
 
 // 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform), with
-// cache policy AUX.  The cache is read once per step.  With one block of columns (one-token
-// decode) non-temporal loads measured faster on two boxes: 1.3-2.7% for the paged bf16 cache
-// at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% for the 128-slot rings at B = 128.  With
-// four blocks (the q_len = 4 verify) they measured 0-3% slower, so the kernels with more than
-// one block keep the default policy.
+// cache policy AUX.  The cache is read once per step and every kernel here loads it
+// non-temporal.  Measured on two boxes against the default policy: 1.3-2.7% faster for the
+// paged bf16 cache at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% per call for the 128-slot
+// rings at B = 128; the q_len = 4 verify was 0-3% slower while its K loads read half cache
+// lines, and 3.9% faster once they read whole lines.
 __device__ __forceinline__ int kswz(int k) { return (k >> 1) & 7; }
 
-template <int NCB>
-constexpr int kCachePolicy = NCB == 1 ? kLoadNT : 0;
 template <int AUX>
 __device__ __forceinline__ void dma16(const void *src, char *dst) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, AUX);
@@ -243,14 +241,14 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     const int t = min(max(16 * sb + s, lo), hi);
 #pragma unroll
                     for (int i2 = 0; i2 < 3; ++i2)
-                        dma16<kCachePolicy<NCB>>(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
+                        dma16<kLoadNT>(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
                                                  kb + sb * 3072 + i2 * 1024);
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int key = 8 * m + (lane >> 3);
                     const int t = min(max(key, lo), hi);
-                    dma16<kCachePolicy<NCB>>(vbase8 + (size_t)(off0 + t) * kDv + ((lane & 7) ^ vswz(key)) * 16,
+                    dma16<kLoadNT>(vbase8 + (size_t)(off0 + t) * kDv + ((lane & 7) ^ vswz(key)) * 16,
                                              kb + kKBytes8 + m * 1024);
                 }
                 return;
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
 #pragma unroll
                     for (int kk = 0; kk < 6; ++kk)
-                        kreg[sb][kk] = as_bf16x8(kCachePolicy<NCB> ? ldg16_nt(kr + 32 * kk) : ldg16(kr + 32 * kk));
+                        kreg[sb][kk] = as_bf16x8(ldg16_nt(kr + 32 * kk));
                 }
             } else {
 #pragma unroll
@@ -274,14 +272,14 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                         const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * ((lane & 7) ^ kswz(k16));
 #pragma unroll
                         for (int c = 0; c < 3; ++c)
-                            dma16<kCachePolicy<NCB>>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
+                            dma16<kLoadNT>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
                     }
                 }
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int t = min(max(4 * m + r, lo), hi);
-                dma16<kCachePolicy<NCB>>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kLoadNT>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
             }
         } else {
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
@@ -293,13 +291,13 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     const int j = min(max(j0 + 16 * sb + k16, lo), hi);
                     const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * ((lane & 7) ^ kswz(k16));
 #pragma unroll
-                    for (int c = 0; c < 3; ++c) dma16<kCachePolicy<NCB>>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
+                    for (int c = 0; c < 3; ++c) dma16<kLoadNT>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
                 }
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int j = min(max(j0 + 4 * m + r, lo), hi);
-                dma16<kCachePolicy<NCB>>(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kLoadNT>(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
             }
         }
     };
