@@ -48,10 +48,10 @@ TRAFFIC = {
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
                            "read_GB": 1.0231, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "94d9898542b329c5efcdd2d40aeac6a2d979a6b8b9bf8a8c57edee43e48c652b",
-                                "read_GB": 5.4120, "written_GB": 0.0179},
+                                "sha256": "927bfee06b33d08dd89a00a8d80ff7076e8c7617d9e21e656d7b68405ee0f419",
+                                "read_GB": 5.3880, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "94d9898542b329c5efcdd2d40aeac6a2d979a6b8b9bf8a8c57edee43e48c652b",
+                                    "sha256": "927bfee06b33d08dd89a00a8d80ff7076e8c7617d9e21e656d7b68405ee0f419",
                                     "read_GB": 2.7528, "written_GB": 0.0179},
 }
 
