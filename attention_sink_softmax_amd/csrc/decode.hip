@@ -69,6 +69,36 @@ __device__ __forceinline__ u32x4 ldg16_nt(const uint16_t *p) {
 // lines, and 3.9% faster once they read whole lines.
 __device__ __forceinline__ int kswz(int k) { return (k >> 1) & 7; }
 
+// E4M3 K of a 16-key block: 16 rows of 192 bytes, 3 KB, loaded by three instructions of 64
+// lanes x 16 bytes.  Two keys 2p, 2p+1 span three whole 128-byte lines (A: key 2p chunks 0-7,
+// B: key 2p chunks 8-11 and key 2p+1 chunks 0-3, C: key 2p+1 chunks 4-11); instruction i
+// loads line A, B or C of all eight pairs, so every instruction reads whole lines.  Within an
+// instruction, chunk c of key k has residue r = (k + c) mod 16 and goes to slot r + 16 t,
+// t its rank among the four chunks of that residue there.  For a fixed chunk the 16 keys
+// have 16 residues, so an operand read of 16 keys (8 bytes each for two lane groups) meets
+// no bank twice in a 256-byte phase.
+// Instruction i, lane l -> the key k and 16-byte chunk c it loads.
+__device__ __forceinline__ void k8_lane_chunk(int i, int l, int &k, int &c) {
+    const int r = l & 15, t = l >> 4;
+    if (i == 0) c = 2 * t + (r & 1);
+    else if (i == 1) c = t < 2 ? 8 + 2 * t + (r & 1) : 2 * (t - 2) + ((r + 1) & 1);
+    else c = 4 + 2 * t + ((r + 1) & 1);
+    k = (r - c) & 15;
+}
+// Byte offset of key k, chunk c within the 3 KB block (the inverse of k8_lane_chunk).
+__device__ __forceinline__ int k8_off(int k, int c) {
+    const int r = (k + c) & 15;
+    int i, t;
+    if ((k & 1) == 0) {
+        i = c < 8 ? 0 : 1;
+        t = c < 8 ? c >> 1 : (c - 8) >> 1;
+    } else {
+        i = c < 4 ? 1 : 2;
+        t = c < 4 ? 2 + (c >> 1) : (c - 4) >> 1;
+    }
+    return i * 1024 + (r + 16 * t) * 16;
+}
+
 template <int AUX>
 __device__ __forceinline__ void dma16(const void *src, char *dst) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, AUX);
@@ -161,6 +191,11 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     const int b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hl = lane & 15, q = lane >> 4;  // column within a block, k-group
+    // E4M3 cache: lane part of the K operand address of k-step kk (key hl, chunk 2 kk + q / 2,
+    // byte half q & 1 of it), layout of k8_lane_chunk
+    int k8lane[6];
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) k8lane[kk] = k8_off(hl, 2 * kk + (q >> 1)) + (q & 1) * 8;
     // lane part of the K operand address (layout of the K loads) for even and odd k-steps:
     // key hl of the 16-key block, chunk 4 (kk & 1) + q of line kk / 2
     const int klane[2] = {3072 * (hl >> 3) + (8 * (hl & 7) + (q ^ kswz(hl))) * 16,
@@ -238,11 +273,13 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 const uint8_t *vbase8 = reinterpret_cast<const uint8_t *>(p.v) + row0 * kDv;
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
-                    const int t = min(max(16 * sb + s, lo), hi);
 #pragma unroll
-                    for (int i2 = 0; i2 < 3; ++i2)
-                        dma16<kLoadNT>(kbase8 + (size_t)(off0 + t) * kDqk + (4 * i2 + r) * 16,
-                                                 kb + sb * 3072 + i2 * 1024);
+                    for (int i2 = 0; i2 < 3; ++i2) {
+                        int kk8, c8;
+                        k8_lane_chunk(i2, lane, kk8, c8);
+                        const int t = min(max(16 * sb + kk8, lo), hi);
+                        dma16<kLoadNT>(kbase8 + (size_t)(off0 + t) * kDqk + c8 * 16, kb + sb * 3072 + i2 * 1024);
+                    }
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -336,8 +373,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             for (int kk = 0; kk < 6; ++kk) {
                 bf16x8 kf;
                 if constexpr (kFp8)
-                    kf = e4m3x8_to_bf16(*reinterpret_cast<const v2i32 *>(
-                        kb + sb * 3072 + ((2 * kk + (q >> 1)) * 16 + hl) * 16 + (q & 1) * 8));
+                    kf = e4m3x8_to_bf16(*reinterpret_cast<const v2i32 *>(kb + sb * 3072 + k8lane[kk]));
                 else
                     kf = kSingle ? kreg[sb][kk]
                                  : *reinterpret_cast<const bf16x8 *>(kb + (6 * sb + (kk >> 1)) * 1024 + klane[kk & 1]);
