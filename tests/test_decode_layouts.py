@@ -1,0 +1,67 @@
+"""Host-side checks of the decode kernels' K layouts in LDS (the index maps that
+attention_sink_softmax_amd/csrc/decode.hip implements in kswz/klane, k8_lane_chunk and k8_off).
+
+Each load instruction moves 64 lanes x 16 bytes; lane l's bytes land at slot l of the
+instruction's 1 KB block.  The properties checked: every (key, chunk) of a 16-key block is
+loaded exactly once, each instruction reads whole 128-byte cache lines, and the 16 keys of one
+operand read (one chunk) fall in 16 distinct 16-byte slots of a 256-byte bank phase.
+"""
+
+
+def bf16_slot(k, m):
+    """bf16 K: key k (0..15) of a 16-key block, chunk m (0..23) of its 384-byte row ->
+    (instruction, slot).  Instruction 3 kh + c holds keys 8 kh .. +7, line c of their rows;
+    chunk m of the line at slot 8 (k & 7) + (m ^ kswz(k)), kswz(k) = (k >> 1) & 7."""
+    kh, c, mi = k >> 3, m >> 3, m & 7
+    return 3 * kh + c, 8 * (k & 7) + (mi ^ ((k >> 1) & 7))
+
+
+def fp8_lane_chunk(i, lane):
+    r, t = lane & 15, lane >> 4
+    if i == 0:
+        c = 2 * t + (r & 1)
+    elif i == 1:
+        c = 8 + 2 * t + (r & 1) if t < 2 else 2 * (t - 2) + ((r + 1) & 1)
+    else:
+        c = 4 + 2 * t + ((r + 1) & 1)
+    return (r - c) & 15, c
+
+
+def fp8_off(k, c):
+    r = (k + c) & 15
+    if k % 2 == 0:
+        i, t = (0, c >> 1) if c < 8 else (1, (c - 8) >> 1)
+    else:
+        i, t = (1, 2 + (c >> 1)) if c < 4 else (2, (c - 4) >> 1)
+    return i * 1024 + (r + 16 * t) * 16
+
+
+def test_bf16_k_layout():
+    seen = {}
+    for k in range(16):
+        for m in range(24):
+            inst, slot = bf16_slot(k, m)
+            assert 0 <= inst < 6 and 0 <= slot < 64
+            assert (inst, slot) not in seen
+            seen[(inst, slot)] = (k, m)
+    for inst in range(6):  # whole lines: 8 keys x one 128-byte line each
+        lines = {(seen[(inst, s)][0] * 384 + seen[(inst, s)][1] * 16) // 128 for s in range(64)}
+        assert len(lines) == 8
+    for m in range(24):  # an operand read: keys 0..15, one chunk
+        assert len({(1024 * bf16_slot(k, m)[0] + 16 * bf16_slot(k, m)[1]) // 16 % 16 for k in range(16)}) == 16
+
+
+def test_fp8_k_layout():
+    seen = set()
+    for i in range(3):
+        lines = set()
+        for lane in range(64):
+            k, c = fp8_lane_chunk(i, lane)
+            assert 0 <= k < 16 and 0 <= c < 12 and (k, c) not in seen
+            seen.add((k, c))
+            assert fp8_off(k, c) == i * 1024 + lane * 16  # the read address inverts the load map
+            lines.add((k * 192 + c * 16) // 128)
+        assert len(lines) == 8  # 8 whole lines per instruction
+    assert len(seen) == 192
+    for c in range(12):
+        assert len({fp8_off(k, c) // 16 % 16 for k in range(16)}) == 16
