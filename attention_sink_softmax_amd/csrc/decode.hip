@@ -61,12 +61,7 @@ __device__ __forceinline__ u32x4 ldg16_nt(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
-// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform), with
-// cache policy AUX.  The cache is read once per step and every kernel here loads it
-// non-temporal.  Measured on two boxes against the default policy: 1.3-2.7% faster for the
-// paged bf16 cache at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% per call for the 128-slot
-// rings at B = 128; the q_len = 4 verify was 0-3% slower while its K loads read half cache
-// lines, and 3.9% faster once they read whole lines.
+// Chunk swizzle of the bf16 K layout (below): key k of a 16-key block.
 __device__ __forceinline__ int kswz(int k) { return (k >> 1) & 7; }
 
 // E4M3 K of a 16-key block: 16 rows of 192 bytes, 3 KB, loaded by three instructions of 64
@@ -99,6 +94,12 @@ __device__ __forceinline__ int k8_off(int k, int c) {
     return i * 1024 + (r + 16 * t) * 16;
 }
 
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform), with
+// cache policy AUX.  The cache is read once per step and every kernel here loads it
+// non-temporal.  Measured on two boxes against the default policy: 1.3-2.7% faster for the
+// paged bf16 cache at 8 x 256K, 0.6-1.8% for the E4M3 cache, 20% per call for the 128-slot
+// rings at B = 128; the q_len = 4 verify was 0-3% slower while its K loads read half cache
+// lines, and 3.9% faster once they read whole lines.
 template <int AUX>
 __device__ __forceinline__ void dma16(const void *src, char *dst) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, AUX);

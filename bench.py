@@ -48,10 +48,10 @@ TRAFFIC = {
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
                            "read_GB": 1.0231, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "9b7e9d3b7c1271e3fdff47f13929c504f421d9af6363c75fa1330de2d3cec463",
+                                "sha256": "1c44398e8d0164c249e6bf303dbb4c455231922391ffa01a175d1f33f9ae5809",
                                 "read_GB": 5.3880, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "9b7e9d3b7c1271e3fdff47f13929c504f421d9af6363c75fa1330de2d3cec463",
+                                    "sha256": "1c44398e8d0164c249e6bf303dbb4c455231922391ffa01a175d1f33f9ae5809",
                                     "read_GB": 2.7037, "written_GB": 0.0179},
 }
 
