@@ -5,7 +5,8 @@ package.  The library (attention_sink_softmax_amd) never does, and this package 
 imports the library: the two share no code.  The arithmetic lives in oracle.c (fp64,
 plain loops, OpenMP over output rows) and, for tiny brute-force checks, oracle_np.py.
 
-Parity status: every function here is pinned by tests/test_oracle_pins.py against the
+Parity status: every function here, the E4M3 encoder included, is pinned by
+tests/test_oracle_pins.py against the
 worked example of the paper-notes page (§4.3), torch's CPU scaled_dot_product_attention
 in float64, closed forms and brute force.
 """
@@ -67,6 +68,8 @@ def load(path: str = LIB):
     lib.oracle_rope.argtypes = [ctypes.c_int64, I, I, ctypes.c_double, I, P, P, P]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+    lib.oracle_e4m3_encode.restype = I
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_int64, P, ctypes.c_double, P]
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
                                   P, P, P, P]
@@ -253,20 +256,23 @@ def rope(x, positions, theta: float, rot: int = ROPE_DIMS, lib=None) -> np.ndarr
     return out
 
 
-def e4m3_encode(x, scale: float) -> np.ndarray:
-    """E4M3 codes (uint8) of x / scale: x as float32 (uint16 input = bf16 bits), divided in
-    float32, clamped to +-448, rounded to nearest even by torch's float8_e4m3fn conversion."""
-    import torch
-
+def e4m3_encode(x, scale: float, lib=None) -> np.ndarray:
+    """E4M3 codes (uint8, shaped like x) of x / scale, by oracle.c's encoder: the quotient in
+    float32, clamped to +-448, rounded to the nearest code with ties to even, the sign kept.
+    x: float32, or uint16 bf16 bits (widened to float32 exactly)."""
+    lib = lib or load()
     xa = np.asarray(x)
     if xa.dtype == np.uint16:
         xa = (xa.astype(np.uint32) << np.uint32(16)).view(np.float32)
-    y = np.clip(xa.astype(np.float32) / np.float32(scale), np.float32(-448), np.float32(448))
-    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    xa = np.ascontiguousarray(xa, dtype=np.float32)
+    out = np.empty(xa.shape, np.uint8)
+    if lib.oracle_e4m3_encode(xa.size, _ptr(xa), float(scale), _ptr(out)) != 0:
+        raise ValueError("oracle_e4m3_encode rejected its arguments")
+    return out
 
 
 def kv_append(k_cache, v_cache, layout: int, k_new, v_new, seq_lens, window: int = 0, block_table=None,
-              fp8_scales=None):
+              fp8_scales=None, lib=None):
     """Write n new tokens per sequence into a cache (in place): token t of sequence b, at
     position seq_lens[b] - n + t, goes to ring slot pos mod window (the last `window`
     positions only) or to page block_table[b][pos // page] at offset pos mod page.
@@ -274,7 +280,7 @@ def kv_append(k_cache, v_cache, layout: int, k_new, v_new, seq_lens, window: int
     are skipped.  Plain indexing; with fp8_scales = (k_scale, v_scale) the caches hold E4M3
     codes and the new rows are encoded by e4m3_encode first."""
     if fp8_scales is not None:
-        k_new, v_new = e4m3_encode(k_new, fp8_scales[0]), e4m3_encode(v_new, fp8_scales[1])
+        k_new, v_new = e4m3_encode(k_new, fp8_scales[0], lib), e4m3_encode(v_new, fp8_scales[1], lib)
     B, Hkv, n = k_new.shape[:3]
     for b in range(B):
         for t in range(n):

@@ -494,6 +494,47 @@ int oracle_rope(int64_t rows, int dim, int rot, double theta, int dtype, const v
 /* The value of one E4M3 code (exported for the tests). */
 double oracle_e4m3_value(int code) { return e4m3_value((uint8_t)code); }
 
+/*
+ * Writing an 8-bit cache: the E4M3 code of x / scale.  The quotient is formed in float32
+ * (as a float32 kernel forms it), clamped to the largest finite magnitude 448, and rounded
+ * to the nearest value the format holds, ties to the even code (the one whose last mantissa
+ * bit is 0).  The sign is kept, so a negative quotient that rounds to zero gives -0 (0x80).
+ * NaN gives 0x7F.  The pages size the cache at one byte per element (paper notes §3.2) and
+ * state no format; this is the E4M3 reading with one scale per tensor.
+ */
+static uint8_t e4m3_encode(double x, double scale) {
+    const float y = (float)x / (float)scale;
+    if (isnan(y)) return 0x7F;
+    const int neg = signbit(y) ? 1 : 0;
+    double a = fabs((double)y);
+    if (a > 448.0) a = 448.0;
+    /* spacing of the representable values around a: 2^-9 below the smallest normal 2^-6,
+     * else 2^(floor(log2 a) - 3) (three mantissa bits per binade) */
+    double step = ldexp(1.0, -9);
+    if (a >= ldexp(1.0, -6)) {
+        int e;
+        frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): floor(log2 a) = e - 1 */
+        step = ldexp(1.0, e - 1 - 3);
+    }
+    const double n = a / step; /* exact: step is a power of two */
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double val = r * step;
+    /* the non-negative code holding that value, found by comparing against every code */
+    for (int c = 0; c < 0x7F; ++c)
+        if (e4m3_value((uint8_t)c) == val) return (uint8_t)(c | (neg << 7));
+    return 0x7F; /* not reached: every rounded value in [0, 448] is a code */
+}
+
+/* Codes of x[0..n) / scale (float32 inputs) into out[0..n).  Returns 0, or -1 when scale is
+ * not a positive finite number. */
+int oracle_e4m3_encode(int64_t n, const float *x, double scale, uint8_t *out) {
+    if (n < 0 || !(scale > 0.0) || isinf(scale)) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode((double)x[i], scale);
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region would use (reported next to timings). */
 int oracle_threads(void) {
     int n = 1;

@@ -1,11 +1,16 @@
 """Brute-force numpy form of sink attention, for tiny inputs only.  TEST INFRASTRUCTURE.
 
-This is the eager form the architecture deep-dive page prints ("MiMo-V2-Flash
-模型架构深度拆解", CH 10.1; restated in "MiMo-V2-Flash 架构 QA", Q3.8): materialise the
-masked, scaled score matrix [S, S], append the per-head sink as one more column, take a
-softmax over the S+1 columns, drop the sink column, multiply by V.  It is written
-independently of oracle.c (whole matrices, a different reduction order, a mask built from
-index grids) so the two can check each other.  float64 throughout.
+Written from the mathematics of the sink softmax ("MiMo-V2-Flash 架构 QA", Q3.8): the
+denominator of row i is exp(sink_h) + the sum of exp(a_ij) over its visible keys, so with
+the row's log-sum-exp
+
+    LSE_i = log(exp(sink_h) + sum_{j in J(i)} exp(a_ij))
+
+every visible key gets the weight exp(a_ij - LSE_i) and the output is those weights times V.
+The sink has no value, so it only enters LSE_i.  This file works on whole matrices, takes
+LSE_i as a pairwise log-add-exp reduction (numpy's logaddexp) and builds the mask from index
+grids; oracle.c uses a max-shifted sum over explicit key lists.  The two share nothing, so
+they can check each other.  float64 throughout.
 """
 from __future__ import annotations
 
@@ -16,7 +21,8 @@ SWA = 1
 
 
 def mask_matrix(L: int, mode: int, window: int) -> np.ndarray:
-    """Boolean [L, L]: True where query i may attend key j."""
+    """Boolean [L, L]: True where query i may attend key j (causal; sliding: the `window`
+    most recent keys, the query's own included)."""
     i = np.arange(L)[:, None]
     j = np.arange(L)[None, :]
     keep = j <= i
@@ -27,30 +33,20 @@ def mask_matrix(L: int, mode: int, window: int) -> np.ndarray:
 
 def prefill(q, k, v, sink, mode: int, window: int, scale: float, return_lse: bool = False):
     """q [B,Hq,L,dqk], k [B,Hkv,L,dqk], v [B,Hkv,L,dv] (any float dtype), sink [Hq] or None.
-    Returns float64 [B,Hq,L,dv]; with return_lse also scipy's logsumexp over each row's
-    S+1 columns (the log of the softmax denominator), [B,Hq,L]."""
+    Returns float64 [B,Hq,L,dv]; with return_lse also LSE_i, [B,Hq,L]."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, Hq, L, _ = q.shape
-    Hkv = k.shape[1]
-    G = Hq // Hkv
-    kx = np.repeat(k, G, axis=1)  # query head h uses KV head h // G
-    vx = np.repeat(v, G, axis=1)
-    scores = np.einsum("bhid,bhjd->bhij", q, kx) * scale
-    scores = np.where(mask_matrix(L, mode, window)[None, None], scores, -np.inf)
+    G = Hq // k.shape[1]
+    heads = np.arange(Hq) // G                 # query head h reads KV head h // G
+    a = scale * (q @ np.swapaxes(k[:, heads], -1, -2))   # [B,Hq,L,L] logits
+    a = np.where(mask_matrix(L, mode, window), a, -np.inf)
+    lse = np.logaddexp.reduce(a, axis=-1)      # over the visible keys (-inf elsewhere)
     if sink is not None:
-        col = np.broadcast_to(np.asarray(sink, np.float64)[None, :, None, None], (B, Hq, L, 1))
-        scores = np.concatenate([scores, col], axis=-1)
-    if return_lse:
-        from scipy.special import logsumexp
-
-        lse = logsumexp(scores, axis=-1)
-    mx = scores.max(axis=-1, keepdims=True)
+        lse = np.logaddexp(lse, np.asarray(sink, np.float64)[None, :, None])
     with np.errstate(invalid="ignore"):
-        e = np.exp(scores - mx)
-        probs = e / e.sum(axis=-1, keepdims=True)
-    if sink is not None:
-        probs = probs[..., :-1]
-        probs = np.where(np.isposinf(np.asarray(sink, np.float64))[None, :, None, None], 0.0, probs)
-    return (probs @ vx, lse) if return_lse else probs @ vx
+        w = np.exp(a - lse[..., None])         # a = -inf (hidden) or lse = +inf give 0
+    w = np.where(np.isnan(w), 0.0, w)          # -inf - (-inf): a row with no mass at all
+    out = w @ v[:, heads]
+    return (out, lse) if return_lse else out

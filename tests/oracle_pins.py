@@ -349,6 +349,45 @@ def pin_e4m3_codes(lib):
     assert math.isnan(oracle.e4m3_value(0x7F, lib=lib)) and math.isnan(oracle.e4m3_value(0xFF, lib=lib))
 
 
+def pin_e4m3_encode(lib):
+    """The encoder that writes an 8-bit cache, against the format itself: every finite code
+    survives value -> encode at several scales (powers of two and not); the midpoint of two
+    neighbouring codes goes to the even one and points just off it to the nearer one;
+    magnitudes above 448 * scale clamp to 0x7E / 0xFE; the sign of zero is kept.  Then
+    against torch's float8_e4m3fn conversion (a library routine) on every bf16 value up to
+    448 in magnitude, at scales 1 and 0.5."""
+    val = {c: oracle.e4m3_value(c, lib=lib) for c in range(256)}
+    finite = [c for c in range(256) if not math.isnan(val[c])]
+    for s in (1.0, 0.5, 2.0 ** -6, 0.02, 0.37, 1.9):
+        x = np.array([val[c] * s for c in finite], np.float32)
+        got = oracle.e4m3_encode(x, s, lib=lib)
+        bad = [(finite[i], int(got[i])) for i in range(len(finite)) if got[i] != finite[i]]
+        assert not bad, f"round trip at scale {s}: {bad[:5]}"
+    for sign in (0, 0x80):
+        for c in range(0x00, 0x7E):  # neighbours c, c + 1, both finite
+            lo, hi = val[c | sign], val[(c + 1) | sign]
+            mid = (lo + hi) / 2  # exact in float32 (one more mantissa bit)
+            even = c if c % 2 == 0 else c + 1
+            got = oracle.e4m3_encode(np.array([mid, np.nextafter(np.float32(mid), np.float32(lo)),
+                                               np.nextafter(np.float32(mid), np.float32(hi))], np.float32), 1.0,
+                                     lib=lib)
+            assert list(got) == [even | sign, c | sign, (c + 1) | sign], (hex(c | sign), list(map(hex, got)))
+    for s in (1.0, 0.02):
+        big = np.array([448.0001, 464.0, 500.0, 1e6, np.inf], np.float32) * np.float32(s)
+        assert np.all(oracle.e4m3_encode(big, s, lib=lib) == 0x7E)
+        assert np.all(oracle.e4m3_encode(-big, s, lib=lib) == 0xFE)
+    z = oracle.e4m3_encode(np.array([0.0, -0.0, 1e-6, -1e-6, 2.0 ** -11, -(2.0 ** -11)], np.float32), 1.0, lib=lib)
+    assert list(z) == [0x00, 0x80, 0x00, 0x80, 0x00, 0x80], list(map(hex, z))
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    for s in (1.0, 0.5):
+        with np.errstate(invalid="ignore", over="ignore"):
+            keep = np.isfinite(xf) & (np.abs(xf / np.float32(s)) <= 448)
+        want = torch.from_numpy(xf[keep] / np.float32(s)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = oracle.e4m3_encode(bits[keep], s, lib=lib)
+        assert np.array_equal(got, want), f"torch float8_e4m3fn at scale {s}: {int((got != want).sum())} differ"
+
+
 def pin_fp8_decode_is_decode_of_values(lib):
     """Decode from an 8-bit cache equals decode from a float32 cache holding the values the
     codes stand for (scale * code value, exact in float32 for these scales), both layouts."""
@@ -389,6 +428,12 @@ def pin_lse(lib):
         out, lse = oracle.prefill_chunk(q, k, v, sink, mode, W, 0.4, lib=lib, return_lse=True)
         _, ref = oracle_np.prefill(q, k, v, sink, mode, W, 0.4, return_lse=True)
         _close(lse, ref, 1e-12, 1e-13, f"lse mode={mode}")
+        # scipy's logsumexp over the visible logits and the sink as one more column
+        from scipy.special import logsumexp
+        logits = 0.4 * np.einsum("bhid,bhjd->bhij", q.astype(np.float64), np.repeat(k, 2, axis=1).astype(np.float64))
+        logits = np.where(oracle_np.mask_matrix(L, mode, W), logits, -np.inf)
+        col = np.broadcast_to(sink[None, :, None, None], (B, Hq, L, 1))
+        _close(lse, logsumexp(np.concatenate([logits, col], axis=-1), axis=-1), 1e-12, 1e-13, f"lse scipy mode={mode}")
         _, lse0 = oracle.prefill_chunk(q, k, v, None, mode, W, 0.4, lib=lib, return_lse=True)
         _, ref0 = oracle_np.prefill(q, k, v, None, mode, W, 0.4, return_lse=True)
         _close(lse0, ref0, 1e-12, 1e-13, f"lse no sink mode={mode}")
@@ -463,6 +508,38 @@ def pin_append_then_decode_is_prefill(lib):
         for mode, Wm, pre in ((oracle.SWA, W, pre_swa), (oracle.GLOBAL, 0, pre_ga)):
             got = oracle.decode(qn, kp, vp, lens, sink, mode, Wm, 0.3, oracle.PAGED, bt, lib=lib)
             _close(got, pre[:, :, n - 1], 1e-12, 1e-14, f"pages after append n={n} mode={mode}")
+
+
+def pin_fp8_append_then_decode_is_prefill(lib):
+    """Tokens appended one step at a time into an 8-bit paged cache, then decoded with the
+    cache's scales, give the prefill rows over the values the cache holds: K and V replaced by
+    scale * value(code), each code being the encoder's code of the element at that scale."""
+    B, Hq, Hkv, dqk, dv, L, ps = 2, 4, 2, 16, 8, 45, 8
+    q = _rand((B, Hq, L, dqk), 1210)
+    k = _rand((B, Hkv, L, dqk), 1211)
+    v = _rand((B, Hkv, L, dv), 1212)
+    sink = np.array([1.0, 2.0, 0.5, 4.0])
+    ks, vs = 0.02, 0.37
+    dec = np.array([oracle.e4m3_value(c, lib=lib) for c in range(256)])
+    # the values the cache holds, rounded to float32 for the prefill oracle (relative 2^-24)
+    kq = (dec[oracle.e4m3_encode(k, ks, lib=lib)] * ks).astype(np.float32)
+    vq = (dec[oracle.e4m3_encode(v, vs, lib=lib)] * vs).astype(np.float32)
+    assert np.allclose(kq, k, rtol=2 ** -4, atol=ks * 2 ** -10) and not np.array_equal(kq, k)
+    bt = np.random.default_rng(1213).permutation(B * 6 + 2)[:B * 6].reshape(B, 6).astype(np.int32)
+    kp = np.zeros((B * 6 + 2, Hkv, ps, dqk), np.uint8)
+    vp = np.zeros((B * 6 + 2, Hkv, ps, dv), np.uint8)
+    pre = {mode: oracle.prefill(q, kq, vq, sink, mode, Wm, 0.3, lib=lib) for mode, Wm in ((oracle.SWA, 6),
+                                                                                           (oracle.GLOBAL, 0))}
+    n = 0
+    for step in (3, 1, 9, 1, 20, 11):
+        lens = np.full(B, n + step, np.int32)
+        oracle.kv_append(kp, vp, oracle.PAGED, k[:, :, n:n + step], v[:, :, n:n + step], lens, block_table=bt,
+                         fp8_scales=(ks, vs), lib=lib)
+        n += step
+        qn = np.ascontiguousarray(q[:, :, n - 1])
+        for mode, Wm in ((oracle.SWA, 6), (oracle.GLOBAL, 0)):
+            got = oracle.decode(qn, kp, vp, lens, sink, mode, Wm, 0.3, oracle.PAGED, bt, lib=lib, kv_scales=(ks, vs))
+            _close(got, pre[mode][:, :, n - 1], 1e-5, 1e-6, f"8-bit pages after append n={n} mode={mode}")
 
 
 def pin_backward_autograd(lib):
@@ -562,7 +639,8 @@ ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
-    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes,
+    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes, pin_e4m3_encode,
     pin_fp8_decode_is_decode_of_values, pin_lse, pin_rope, pin_append_then_decode_is_prefill,
+    pin_fp8_append_then_decode_is_prefill,
     pin_backward_autograd, pin_backward_finite_differences, pin_backward_sampled_is_backward,
 ]

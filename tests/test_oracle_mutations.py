@@ -48,6 +48,12 @@ MUTATIONS = {
     "score gradient without the row term D": ("return p * (dp - D);", "return p * dp;"),
     "key gradient without the logit scale": ("dk[j * dqk + d] += scale * ds * load(q, qrow * dqk + d, dtype);",
                                              "dk[j * dqk + d] += ds * load(q, qrow * dqk + d, dtype);"),
+    "E4M3 encoder multiplies by the scale": ("const float y = (float)x / (float)scale;",
+                                             "const float y = (float)x * (float)scale;"),
+    "E4M3 encoder clamps at 240": ("if (a > 448.0) a = 448.0;", "if (a > 240.0) a = 240.0;"),
+    "E4M3 encoder rounds ties up": ("(frac == 0.5 && fmod(r, 2.0) != 0.0)", "(frac == 0.5)"),
+    "E4M3 encoder drops the sign of zero": ("return (uint8_t)(c | (neg << 7));",
+                                            "return (uint8_t)(c | ((neg && c) << 7));"),
     "value row from the query position": ("vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);",
                                           "vi[cnt] = (size_t)(((b * Hkv + g) * Lk + i) * dv);"),
 }
