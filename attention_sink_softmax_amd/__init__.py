@@ -260,10 +260,12 @@ def _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out
     import torch
 
     cdt = torch.uint8 if kv_fp8 else torch.bfloat16
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,Hq,q_len,192], got shape {tuple(q.shape)}")
     B, Hq, _, dqk = q.shape
     Hkv = k_cache.shape[1]
     dv = v_cache.shape[3]
-    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(q, "q", torch.bfloat16, (B, Hq, q_len, dqk))
     _dev_tensor(out, "out", torch.bfloat16, (B, Hq, q_len, dv))
     _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
     if sink is not None:
@@ -543,10 +545,12 @@ def sinkattn_decode_fp8(mode: int, window: int, q_len: int, q, k_cache, v_cache,
     sinkattn_decode_multi_workspace_bytes(...) bytes or None."""
     import torch
 
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,Hq,q_len,192], got shape {tuple(q.shape)}")
     B, Hq, _, dqk = q.shape
     P, Hkv, ps, _ = k_cache.shape
     dv = v_cache.shape[3]
-    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(q, "q", torch.bfloat16, (B, Hq, q_len, dqk))
     _dev_tensor(out, "out", torch.bfloat16, (B, Hq, q_len, dv))
     _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
     if sink is not None:

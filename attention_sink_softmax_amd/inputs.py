@@ -185,6 +185,18 @@ def prefill_inputs(w: Workload, seed: int | None = None, seqlen: int | None = No
     return out
 
 
+def ga_parity_rows(w: Workload, n_first: int = 128, n_last: int = 128, n_rand: int = 256) -> np.ndarray:
+    """The rows of a long causal prefill that are checked against the oracle and that the
+    oracle is timed on: for every query head of sequence 0, the first 128 positions, the last
+    128 and 256 more drawn without replacement, uniformly from the rest (seeded by the
+    workload).  int64 [Hq * 512, 3] of (b, h, i)."""
+    L = w.seqlen
+    g = np.random.default_rng([w.seed, 11])
+    mid = np.sort(g.choice(np.arange(n_first, L - n_last), size=n_rand, replace=False))
+    pos = np.concatenate([np.arange(n_first), mid, np.arange(L - n_last, L)])
+    return np.array([(0, h, i) for h in range(w.hq) for i in pos], np.int64)
+
+
 # --------------------------------------------------------------------------- decode
 def decode_seq_lens(w: Workload, seed: int | None = None, batch: int | None = None) -> np.ndarray:
     s = w.seed if seed is None else seed

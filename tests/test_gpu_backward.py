@@ -141,3 +141,49 @@ def test_backward_full_size_sampled(name):
     assert_grad(got_q, rq, f"{name} dq rows")
     assert_grad(got_k, rk, f"{name} dk keys")
     assert_grad(got_v, rv, f"{name} dv keys")
+
+
+def test_backward_ga_full_size_one_head():
+    """The 32K global workload with dO zero except on one query head h: then dk and dv of KV
+    head h // 16 are that head's contributions alone, and the oracle can sum them for keys at
+    the start and in the middle of the sequence (every later row sees them).  dL/dsink of that
+    head is checked against the oracle's full rows: -sum_i exp(sink - LSE_i) dO_i . O_i over
+    all 32768 positions (the other heads' dsink is exactly 0: their D_i is 0)."""
+    w = inputs.WORKLOADS["ga_prefill_L32768"]
+    L, G, h = w.seqlen, w.hq // w.hkv, 37
+    g = h // G
+    print(f"[case] backward full size, one head h={h}", flush=True)
+    d = inputs.prefill_inputs(w)
+    dout = np.zeros((w.batch, w.hq, L, w.d_v), np.uint16)
+    dout[:, h] = inputs.normal((w.batch, 1, L, w.d_v), w.seed, 6)[:, 0]
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    s = dev_f32(d["sink"])
+    out = torch.empty((w.batch, w.hq, L, w.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.hq, L), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sa.sinkattn_prefill_chunk_workspace_bytes(w.batch, L, w.hq, w.hkv, L), dtype=torch.uint8,
+                     device="cuda")
+    sa.sinkattn_prefill_ex(w.mode, w.window, q, k, v, s, out, ws, lse=lse)
+    dq, dk, dv, dsink = sa.prefill_backward(w.mode, w.window, q, k, v, s, out, dev_bf16(dout), lse)
+    torch.cuda.synchronize()
+    # the problem of head h alone: one query head over its KV head
+    qh = np.ascontiguousarray(d["q"][:, h:h + 1])
+    kh = np.ascontiguousarray(d["k"][:, g:g + 1])
+    vh = np.ascontiguousarray(d["v"][:, g:g + 1])
+    doh = np.ascontiguousarray(dout[:, h:h + 1])
+    kpos = [0, 16391]
+    _, rk, rv = oracle.prefill_backward_sampled(qh, kh, vh, d["sink"][h:h + 1], doh, w.mode, w.window, w.scale,
+                                                np.zeros((0, 3), np.int64), [(0, 0, j) for j in kpos])
+    assert_grad(dk[0, g, kpos].cpu().numpy(), rk, "32K dk, keys 0 and 16391, one head")
+    assert_grad(dv[0, g, kpos].cpu().numpy(), rv, "32K dv, keys 0 and 16391, one head")
+    rows = np.array([(0, 0, i) for i in range(L)], np.int64)
+    o_ref, lse_ref = oracle.prefill_chunk(qh, kh, vh, d["sink"][h:h + 1], w.mode, w.window, w.scale, rows=rows,
+                                          return_lse=True)
+    do_f = inputs.bf16_to_f32(doh[0, 0]).astype(np.float64)
+    D = np.sum(do_f * o_ref, axis=1)
+    p_sink = np.exp(d["sink"][h] - lse_ref)
+    want = -np.sum(p_sink * D)
+    bound = 2 ** -6 * np.sum(p_sink * np.linalg.norm(do_f, axis=1) * np.linalg.norm(o_ref, axis=1))
+    got = dsink.cpu().numpy()
+    print(f"[parity] 32K dsink head {h}: got={got[h]:.6e} want={want:.6e} bound={bound:.3e}", flush=True)
+    assert abs(got[h] - want) <= bound
+    assert np.all(got[np.arange(w.hq) != h] == 0)

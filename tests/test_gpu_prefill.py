@@ -190,7 +190,7 @@ def test_full_size_sampled(name):
     if w.mode == oracle.SWA:
         rows = sampled_rows(w.hq, w.seqlen, 17, 160, 128, 256)
     else:
-        rows = sampled_rows(w.hq, w.seqlen, 18, 16, 8, 16)
+        rows = inputs.ga_parity_rows(w)  # 512 rows per head: the first 128, the last 128, 256 seeded
     idx = torch.from_numpy(rows).to("cuda")
     got = host_f32(out[idx[:, 0], idx[:, 1], idx[:, 2]])
     ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], w.mode, w.window, w.scale, rows=rows)
