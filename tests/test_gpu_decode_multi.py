@@ -149,3 +149,25 @@ def test_ga_verify_workload_sampled():
                         oracle.PAGED, d["block_table"][ok])
     assert_parity(got[ok], ref, w.name)
     assert np.all(np.isfinite(got))
+
+
+def test_q_shape_checked_before_launch():
+    """A q whose token axis does not match q_len is refused by the binding (ValueError) before
+    any launch: the library only receives a pointer and would read past the end of q."""
+    B, Hq, Hkv, ps = 2, 16, 1, 64
+    k = torch.zeros((4, Hkv, ps, 192), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((4, Hkv, ps, 128), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((B, 2), dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), 100, dtype=torch.int32, device="cuda")
+    q1 = torch.zeros((B, Hq, 1, 192), dtype=torch.bfloat16, device="cuda")
+    out4 = torch.empty((B, Hq, 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        sa.sinkattn_decode_multi(sa.GLOBAL, 0, 4, q1, sa.KV_PAGED, k, v, lens, 100, None, out4, None, bt)
+    with pytest.raises(ValueError):
+        sa.sinkattn_decode_ex(sa.GLOBAL, 0, 4, q1, sa.KV_PAGED, k, v, lens, 100, None, out4, None, bt)
+    k8 = torch.zeros((4, Hkv, ps, 192), dtype=torch.uint8, device="cuda")
+    v8 = torch.zeros((4, Hkv, ps, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        sa.sinkattn_decode_fp8(sa.GLOBAL, 0, 4, q1, k8, v8, lens, 100, None, 1.0, 1.0, out4, None, bt)
+    with pytest.raises(ValueError):
+        sa.sinkattn_decode_multi(sa.GLOBAL, 0, 4, q1[:, :, 0], sa.KV_PAGED, k, v, lens, 100, None, out4, None, bt)
