@@ -59,7 +59,8 @@ class Epilogue(ctypes.Structure):
 EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_prefill_chunk",
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
-           "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_rope", "sinkattn_kv_append",
+           "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_decode_ex_noalloc", "sinkattn_rope",
+           "sinkattn_kv_append",
            "sinkattn_prefill_backward", "sinkattn_prefill_backward_workspace_bytes",
            "sinkattn_status_string")
 
@@ -105,6 +106,10 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
                                      ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P,
                                      P, ctypes.c_size_t, P]
+    L.sinkattn_decode_ex_noalloc.restype = I
+    L.sinkattn_decode_ex_noalloc.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
+                                             ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P,
+                                             ctypes.POINTER(Epilogue), P, P]
     L.sinkattn_prefill_backward.restype = I
     L.sinkattn_prefill_backward.argtypes = [I, I, ctypes.POINTER(Dims), P, P, P, P, P, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P]
@@ -440,6 +445,29 @@ def sinkattn_decode_ex(mode: int, window: int, q_len: int, q, layout: int, k_cac
         rc = lib().sinkattn_decode_ex(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
                                       1 if kv_fp8 else 0, k_scale, v_scale, _ptr(seq_lens), max_seq_len, _ptr(sink),
                                       ctypes.byref(ep), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SINKATTN_NOALLOC_SCRATCH_BYTES
+
+
+def sinkattn_decode_ex_noalloc(mode: int, window: int, q_len: int, q, layout: int, k_cache, v_cache, seq_lens,
+                               max_seq_len: int, sink, out, block_table=None, kv_fp8: bool = False,
+                               k_scale: float = 1.0, v_scale: float = 1.0, out_scale: float = 1.0, lse=None,
+                               scale: float | None = None, stream=None) -> None:
+    """sinkattn_decode_ex without a workspace: the split partials go to the library's own
+    device scratch array (NOALLOC_SCRATCH_BYTES per GPU), so the call allocates nothing.
+    Calls that overlap on one GPU race."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, _, _ = _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens, sink, out,
+                                                   None, block_table, kv_fp8)
+    ep = _epilogue(out_scale, lse, (B, Hq, q_len), q.device)
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode_ex_noalloc(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
+                                              1 if kv_fp8 else 0, k_scale, v_scale, _ptr(seq_lens), max_seq_len,
+                                              _ptr(sink), ctypes.byref(ep), _ptr(out), _stream_ptr(stream, q.device))
     _raise(rc)
 
 

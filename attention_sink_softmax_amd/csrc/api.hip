@@ -173,10 +173,12 @@ size_t sinkattn_decode_multi_workspace_bytes(int mode, int window, const sinkatt
 
 namespace {
 // Decode from a bf16 cache (fp8 = 0) or an E4M3 cache with per-tensor scales (fp8 = 1).
+// use_scratch: the split partials go to the library's own device scratch array instead of
+// the caller's workspace (which is then ignored).
 int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q, const sinkattn_kv *kv,
                   const int32_t *seq_lens, int32_t max_seq_len, const float *sink, int fp8, float k_scale,
                   float v_scale, const sinkattn_epilogue *ep, void *out, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+                  void *stream, bool use_scratch = false) {
     int st = check_dims(mode, window, d);
     if (st) return st;
     st = check_epilogue(ep);
@@ -202,6 +204,16 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
         (sink && misaligned(sink)) || (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
         return SINKATTN_E_ALIGN;
     const DecodePlan pl = plan_decode(mode, window, d, q_len, max_seq_len);
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (pl.ws_bytes > decode_scratch_bytes()) return SINKATTN_E_WORKSPACE;
+        if (pl.ws_bytes > 0) {
+            workspace = decode_scratch();
+            if (!workspace) return SINKATTN_E_DEVICE;
+            workspace_bytes = decode_scratch_bytes();
+        }
+    }
     if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes) return SINKATTN_E_WORKSPACE;
         if (misaligned(workspace)) return SINKATTN_E_ALIGN;
@@ -257,6 +269,14 @@ int sinkattn_decode_ex(int mode, int window, const sinkattn_dims *d, int32_t q_l
                        void *workspace, size_t workspace_bytes, void *stream) {
     return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0, k_scale,
                          v_scale, ep, out, workspace, workspace_bytes, stream);
+}
+
+int sinkattn_decode_ex_noalloc(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                               const sinkattn_kv *kv, int kv_fp8, float k_scale, float v_scale,
+                               const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
+                               const sinkattn_epilogue *ep, void *out, void *stream) {
+    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0, k_scale,
+                         v_scale, ep, out, nullptr, 0, stream, true);
 }
 
 int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,

@@ -22,8 +22,11 @@
 //                                     transposing LDS read ds_read_b64_tr_b16.
 // Row statistics need two lane exchanges (lane ^ 16, lane ^ 32).  At the end the 4 waves'
 // states are merged through LDS.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
+#include "sinkattn.h"
 
 namespace sinkattn {
 
@@ -638,6 +641,38 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
 }
 
 }  // namespace
+
+// ---- scratch for the decode entry point that allocates nothing
+//
+// The split partials of that entry point live in this file-scope device array instead of a
+// caller's workspace.  Each GPU the library runs on holds its own copy at its own address
+// until the process ends; on the host the name only stands in for it, so the device address
+// is looked up once per device (hipGetSymbolAddress, with that device current) and only that
+// address reaches the kernels.  Calls on one GPU share the array: calls that overlap on a
+// GPU race.  No part of it needs clearing: every split writes its whole record before the
+// merge reads it.
+constexpr size_t kScratchBytes = (size_t)SINKATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+float *scratch_ptr[kMaxDevices];  // device address of each device's copy, once looked up
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+float *decode_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    return scratch_ptr[dev];
+}
 
 int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     DecodeParams p = prm;

@@ -87,6 +87,9 @@ size_t prefill_workspace_bytes(int B, int Hkv, int L);
 int64_t plan_prefill(PrefillParams &p);
 int launch_prefill(const PrefillParams &p, hipStream_t stream);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
+// The decode scratch array of this device (nullptr if its address cannot be found) and its size.
+float *decode_scratch();
+size_t decode_scratch_bytes();
 int launch_rope(const RopeParams &p, hipStream_t stream);
 int launch_kv_append(const AppendParams &p, hipStream_t stream);
 

@@ -25,6 +25,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library never
  *    allocates, frees or synchronises, and keeps no mutable global state (thread-safe).
+ *    The one exception is sinkattn_decode_ex_noalloc, which keeps its partial results in a
+ *    scratch array of its own on each device (see there).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
  *    asynchronously.  Results are valid once the stream has reached that point.
  *  - Tensors are dense, row-major, in the index order written next to each argument.
@@ -342,6 +344,28 @@ int sinkattn_decode_ex(int mode, int window, const sinkattn_dims *d, int32_t q_l
                        float v_scale, const int32_t *seq_lens, int32_t max_seq_len,
                        const float *sink, const sinkattn_epilogue *ep, void *out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * sinkattn_decode_ex for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and the
+ * same kernels, but no workspace argument.  The split partials go to a scratch array inside
+ * the library, SINKATTN_NOALLOC_SCRATCH_BYTES of device memory that each GPU the library runs
+ * on holds until the process ends (located on the first call on each device).  The call
+ * allocates and frees nothing.
+ *   Errors as sinkattn_decode_ex; SINKATTN_E_WORKSPACE when the partials these arguments
+ *   need (sinkattn_decode_multi_workspace_bytes(mode, window, d, q_len, max_seq_len)) exceed
+ *   SINKATTN_NOALLOC_SCRATCH_BYTES (one-token decode of 8 sequences x 256K over 64 query
+ *   heads needs 17.3 MB); SINKATTN_E_DEVICE when the scratch array cannot be located.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (on
+ *   different streams, or from different threads) race and give wrong results.
+ *   Serialise them.
+ */
+#define SINKATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sinkattn_decode_ex_noalloc(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                               const void *q, const sinkattn_kv *kv, int kv_fp8, float k_scale,
+                               float v_scale, const int32_t *seq_lens, int32_t max_seq_len,
+                               const float *sink, const sinkattn_epilogue *ep, void *out,
+                               void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(int status);
