@@ -73,6 +73,9 @@ def load(path: str = LIB):
     lib.oracle_decode.restype = I
     lib.oracle_decode.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
                                   P, P, P, P]
+    lib.oracle_decode_side.restype = I
+    lib.oracle_decode_side.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.c_double, I, P, P, P, P, I, I, I,
+                                       P, P, P, P, P, P]
     lib.oracle_threads.restype = I
     lib.oracle_threads.argtypes = []
     if path == LIB:
@@ -149,14 +152,17 @@ def prefill_chunk(q, k, v, sink, mode: int, window: int, scale: float, rows=None
 
 
 def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout: int,
-           block_table=None, lib=None, kv_scales=None, return_lse=False):
+           block_table=None, lib=None, kv_scales=None, return_lse=False, k_new=None, v_new=None):
     """q [B,Hq,dqk] (one new token per sequence) or [B,Hq,q_len,dqk] (q_len new tokens at
     positions seq_lens-q_len .. seq_lens-1); RING: k [B,Hkv,W,dqk], v [B,Hkv,W,dv];
     PAGED: k [P,Hkv,page,dqk], v [P,Hkv,page,dv] with block_table [B,max_pages].
     Returns float64 [B,Hq,dv] or [B,Hq,q_len,dv], matching q.
     uint8 k and v are E4M3 codes of an 8-bit cache; kv_scales = (k_scale, v_scale) then
     gives the per-tensor scales (element = scale * code value).  With return_lse also each
-    row's log-sum-exp, shaped like the output without its last axis."""
+    row's log-sum-exp, shaped like the output without its last axis.
+    k_new [B,Hkv,q_len,dqk], v_new [B,Hkv,q_len,dv] (same dtype as q): the new tokens' keys and
+    values held beside the cache, which then holds the positions before seq_lens - q_len only
+    (RING caches too, any q_len)."""
     lib = lib or load()
     qa, dt = _arr(q, None)
     fp8 = np.asarray(k).dtype == np.uint8
@@ -178,7 +184,17 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
         bt, ps, mp, npg = None, 0, 0, 0
     out = np.empty(qa.shape[:-1] + (dv,), np.float64)
     lse = np.empty(out.shape[:-1], np.float64)
-    if fp8:
+    if k_new is not None:
+        if fp8:
+            raise TypeError("keys beside the cache need a cache of the queries' dtype")
+        kn, dtk = _arr(k_new, None)
+        vn, dtv = _arr(v_new, None)
+        if not (dtk == dtv == dt) or kn.shape != (B, Hkv, q_len, dqk) or vn.shape != (B, Hkv, q_len, dv):
+            raise ValueError("k_new / v_new must be [B,Hkv,q_len,d] in the queries' dtype")
+        rc = lib.oracle_decode_side(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
+                                    _ptr(va), _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(kn), _ptr(vn), _ptr(s),
+                                    _ptr(out), _ptr(lse))
+    elif fp8:
         ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
         rc = lib.oracle_decode_fp8(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dt, _ptr(qa), _ptr(ka),
                                    _ptr(va), ks, vs, _ptr(bt), ps, mp, npg, _ptr(lens), _ptr(s), _ptr(out),
@@ -189,6 +205,17 @@ def decode(q, k, v, seq_lens, sink, mode: int, window: int, scale: float, layout
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return (out, lse) if return_lse else out
+
+
+def prefill_cached(q, k_chunk, v_chunk, k_cache, v_cache, kv_lens, sink, mode: int, window: int, scale: float,
+                   layout: int, block_table=None, lib=None, return_lse=False):
+    """Chunked prefill over a cached prefix: q [B,Hq,Lq,dqk] are positions kv_lens[b] - Lq ..
+    kv_lens[b] - 1 of each sequence, k_chunk [B,Hkv,Lq,dqk] and v_chunk [B,Hkv,Lq,dv] their keys
+    and values; the prefix (positions before kv_lens - Lq) is read from a RING (sliding mode,
+    its last `window` positions) or a PAGED cache.  The same definition as decode with the new
+    tokens beside the cache, with Lq new tokens (oracle_decode_side)."""
+    return decode(q, k_cache, v_cache, kv_lens, sink, mode, window, scale, layout, block_table, lib=lib,
+                  return_lse=return_lse, k_new=k_chunk, v_new=v_chunk)
 
 
 def prefill_backward(q, k, v, sink, dout, mode: int, window: int, scale: float, lib=None):

@@ -61,19 +61,42 @@ static double load(const void *p, size_t idx, int dtype) {
     return (double)((const float *)p)[idx];
 }
 
-/* One output row.  qrow: index of q[0] of the row; key j of the visible list lives at
- * kidx[t]*dqk in k and vidx[t]*dv in v.  n keys.  Writes dv doubles to out and returns the
- * row's log-sum-exp over the sink and the visible logits, log(exp(sink) + sum_j exp(a_j))
- * (natural log; -inf when both are empty, +inf for a sink of +inf). */
-static double attend_row(int dtype, const void *q, size_t qrow, int kvdtype, double kscale, double vscale,
-                       const void *k, const void *v, const size_t *kidx, const size_t *vidx, int n, int dqk,
-                       int dv, double scale, int has_sink, double sink, double *a, double *out) {
+/* The visible keys of one row: n keys of a cache (k, v in kvdtype, element = kscale or
+ * vscale times the stored value), key t at kidx[t] in k and vidx[t] in v, then n2 more keys
+ * held beside the cache (k2, v2 in the query's dtype, unscaled), key t at kidx2[t], vidx2[t]. */
+typedef struct {
+    int kvdtype;
+    double kscale, vscale;
+    const void *k, *v;
+    const size_t *kidx, *vidx;
+    int n;
+    const void *k2, *v2;
+    const size_t *kidx2, *vidx2;
+    int n2;
+} key_list;
+
+static double key_elem(const key_list *kl, int t, int d, int dtype) {
+    if (t < kl->n) return kl->kscale * load(kl->k, kl->kidx[t] + d, kl->kvdtype);
+    return load(kl->k2, kl->kidx2[t - kl->n] + d, dtype);
+}
+static double value_elem(const key_list *kl, int t, int e, int dtype) {
+    if (t < kl->n) return kl->vscale * load(kl->v, kl->vidx[t] + e, kl->kvdtype);
+    return load(kl->v2, kl->vidx2[t - kl->n] + e, dtype);
+}
+
+/* One output row.  qrow: index of q[0] of the row; kl: its visible keys.  Writes dv doubles
+ * to out and returns the row's log-sum-exp over the sink and the visible logits,
+ * log(exp(sink) + sum_j exp(a_j)) (natural log; -inf when both are empty, +inf for a sink of
+ * +inf). */
+static double attend_row(int dtype, const void *q, size_t qrow, const key_list *kl, int dqk, int dv, double scale,
+                         int has_sink, double sink, double *a, double *out) {
+    const int n = kl->n + kl->n2;
     for (int e = 0; e < dv; ++e) out[e] = 0.0;
     if (has_sink && isinf(sink) && sink > 0) return INFINITY; /* all mass on the sink */
     double m = has_sink ? sink : -INFINITY;
     for (int t = 0; t < n; ++t) {
         double dot = 0.0;
-        for (int d = 0; d < dqk; ++d) dot += load(q, qrow + d, dtype) * (kscale * load(k, kidx[t] + d, kvdtype));
+        for (int d = 0; d < dqk; ++d) dot += load(q, qrow + d, dtype) * key_elem(kl, t, d, dtype);
         a[t] = scale * dot;
         if (a[t] > m) m = a[t];
     }
@@ -82,7 +105,7 @@ static double attend_row(int dtype, const void *q, size_t qrow, int kvdtype, dou
     for (int t = 0; t < n; ++t) z += exp(a[t] - m);
     for (int t = 0; t < n; ++t) {
         double s = exp(a[t] - m) / z;
-        for (int e = 0; e < dv; ++e) out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));
+        for (int e = 0; e < dv; ++e) out[e] += s * value_elem(kl, t, e, dtype);
     }
     return m + log(z);
 }
@@ -145,9 +168,9 @@ int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, in
                 ki[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dqk);
                 vi[cnt] = (size_t)(((b * Hkv + g) * Lk + j) * dv);
             }
-            const double l = attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), dtype, 1.0, 1.0, k, v, ki,
-                                        vi, cnt, dqk, dv, scale, sink != NULL, sink ? sink[h] : 0.0, a,
-                                        out + (size_t)n * dv);
+            const key_list kl = {dtype, 1.0, 1.0, k, v, ki, vi, cnt, NULL, NULL, NULL, NULL, 0};
+            const double l = attend_row(dtype, q, (size_t)(((b * Hq + h) * Lq + r) * dqk), &kl, dqk, dv, scale,
+                                        sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)n * dv);
             if (lse) lse[n] = l;
         }
         free(a);
@@ -159,16 +182,22 @@ int oracle_prefill_chunk(int mode, int window, int B, int Lq, int Lk, int Hq, in
 
 /*
  * Decode: q_len new queries per sequence at positions n_b - q_len .. n_b - 1, where
- * n_b = seq_lens[b] counts the new tokens (their keys and values are already in the cache).
- * q_len = 1 is ordinary one-token decoding; q_len > 1 is the parallel verification of
- * drafted tokens ("MiMo-V2-Flash 模型架构深度拆解", CH 4.4; paper notes §6.4): each new
- * token is a causal query that sees the cache up to and including its own position, so
- * the result equals the last q_len rows of a prefill over the whole sequence.
- * A position below 0 (n_b < q_len) has an empty visible set: its output row is 0.
- * q [B][Hq][q_len][dqk]; sink [Hq] or NULL; out [B][Hq][q_len][dv].
- * RING  (sliding mode and q_len = 1 only): k [B][Hkv][window][dqk], v [B][Hkv][window][dv];
- *       position p lives in slot p mod window.  (With q_len > 1 the earlier queries would
- *       need keys the ring has already overwritten.)
+ * n_b = seq_lens[b] counts the new tokens.  q_len = 1 is ordinary one-token decoding;
+ * q_len > 1 is the parallel verification of drafted tokens ("MiMo-V2-Flash 模型架构深度拆解",
+ * CH 4.4; paper notes §6.4): each new token is a causal query that sees the keys up to and
+ * including its own position, so the result equals the last q_len rows of a prefill over the
+ * whole sequence.  A position below 0 (n_b < q_len) has an empty visible set: its output row
+ * is 0.  q [B][Hq][q_len][dqk]; sink [Hq] or NULL; out [B][Hq][q_len][dv].
+ * Where the new tokens' keys and values are:
+ *   k_new == NULL: already in the cache, at their positions;
+ *   k_new != NULL: beside the cache, k_new [B][Hkv][q_len][dqk], v_new [B][Hkv][q_len][dv]
+ *                  (token t = position n_b - q_len + t), in the query's dtype; the cache
+ *                  holds the positions before n_b - q_len only (drafts whose acceptance is
+ *                  not known yet must not overwrite a ring's committed keys).
+ * The cache:
+ * RING  (sliding mode): k [B][Hkv][window][dqk], v [B][Hkv][window][dv]; position p lives in
+ *       slot p mod window.  Without k_new only q_len = 1 (the earlier queries of several
+ *       would need keys the ring has already overwritten).
  * PAGED (either mode): k [num_pages][Hkv][page_size][dqk], v [num_pages][Hkv][page_size][dv];
  *       position p of sequence b lives in page block_table[b*max_pages + p/page_size] at
  *       offset p mod page_size.
@@ -178,17 +207,19 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
                        int q_len, double scale, int dtype, const void *q, int kvdtype, double kscale,
                        double vscale, const void *k, const void *v, const int32_t *block_table,
                        int page_size, int max_pages, int num_pages, const int32_t *seq_lens,
-                       const double *sink, double *out, double *lse) {
+                       const void *k_new, const void *v_new, const double *sink, double *out, double *lse) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || dqk <= 0 || dv <= 0) return -1;
     if (mode == ORACLE_SWA && window <= 0) return -1;
     if (q_len <= 0) return -1;
-    if (layout == ORACLE_RING && (mode != ORACLE_SWA || q_len != 1)) return -1;
+    if (layout == ORACLE_RING && (mode != ORACLE_SWA || (q_len != 1 && !k_new))) return -1;
     if (layout == ORACLE_PAGED && (!block_table || page_size <= 0 || max_pages < 0)) return -1;
+    if (!k_new != !v_new) return -1;
     const int G = Hq / Hkv;
     int bad = 0;
     int64_t maxn = 1;
     for (int b = 0; b < B; ++b) {
-        if (layout == ORACLE_PAGED && seq_lens[b] > (int64_t)max_pages * page_size) bad = 1;
+        const int64_t cached = k_new ? (int64_t)seq_lens[b] - q_len : seq_lens[b];
+        if (layout == ORACLE_PAGED && cached > (int64_t)max_pages * page_size) bad = 1;
         if (seq_lens[b] > maxn) maxn = seq_lens[b];
     }
     if (bad) return -1;
@@ -197,25 +228,35 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
         double *a = (double *)malloc(sizeof(double) * (size_t)maxn);
         size_t *ki = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
         size_t *vi = (size_t *)malloc(sizeof(size_t) * (size_t)maxn);
+        size_t *ki2 = (size_t *)malloc(sizeof(size_t) * (size_t)q_len);
+        size_t *vi2 = (size_t *)malloc(sizeof(size_t) * (size_t)q_len);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < (int64_t)B * Hq * q_len; ++r) {
             const int64_t b = r / ((int64_t)Hq * q_len), h = (r / q_len) % Hq, g = h / G;
             const int64_t nb = seq_lens[b];
             const int64_t i = nb - q_len + r % q_len; /* this query's position */
+            const int64_t nc = k_new ? nb - q_len : nb; /* positions below nc are in the cache */
             const int64_t jlo = (mode == ORACLE_SWA) ? (i - window + 1 > 0 ? i - window + 1 : 0) : 0;
-            int n = 0;
+            int n = 0, n2 = 0;
             int local_bad = 0;
-            for (int64_t j = jlo; j <= i; ++j, ++n) {
-                if (layout == ORACLE_RING) {
+            for (int64_t j = jlo; j <= i; ++j) {
+                if (j >= nc) { /* a new token beside the cache */
+                    const int64_t t = j - nc;
+                    ki2[n2] = (size_t)(((b * Hkv + g) * q_len + t) * dqk);
+                    vi2[n2] = (size_t)(((b * Hkv + g) * q_len + t) * dv);
+                    ++n2;
+                } else if (layout == ORACLE_RING) {
                     const int64_t slot = j % window;
                     ki[n] = (size_t)(((b * Hkv + g) * window + slot) * dqk);
                     vi[n] = (size_t)(((b * Hkv + g) * window + slot) * dv);
+                    ++n;
                 } else {
                     const int64_t page = block_table[b * max_pages + j / page_size];
                     if (page < 0 || page >= num_pages) local_bad = 1;
                     const int64_t off = j % page_size;
                     ki[n] = (size_t)(((page * Hkv + g) * page_size + off) * dqk);
                     vi[n] = (size_t)(((page * Hkv + g) * page_size + off) * dv);
+                    ++n;
                 }
             }
             if (local_bad) {
@@ -223,13 +264,16 @@ static int decode_impl(int mode, int window, int layout, int B, int Hq, int Hkv,
                 bad = 1;
                 continue;
             }
-            const double l = attend_row(dtype, q, (size_t)r * dqk, kvdtype, kscale, vscale, k, v, ki, vi, n, dqk,
-                                        dv, scale, sink != NULL, sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
+            const key_list kl = {kvdtype, kscale, vscale, k, v, ki, vi, n, k_new, v_new, ki2, vi2, n2};
+            const double l = attend_row(dtype, q, (size_t)r * dqk, &kl, dqk, dv, scale, sink != NULL,
+                                        sink ? sink[h] : 0.0, a, out + (size_t)r * dv);
             if (lse) lse[r] = l;
         }
         free(a);
         free(ki);
         free(vi);
+        free(ki2);
+        free(vi2);
     }
     return bad ? -1 : 0;
 }
@@ -239,7 +283,22 @@ int oracle_decode(int mode, int window, int layout, int B, int Hq, int Hkv, int 
                   const int32_t *block_table, int page_size, int max_pages, int num_pages,
                   const int32_t *seq_lens, const double *sink, double *out, double *lse) {
     return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, dtype, 1.0, 1.0, k, v,
-                       block_table, page_size, max_pages, num_pages, seq_lens, sink, out, lse);
+                       block_table, page_size, max_pages, num_pages, seq_lens, NULL, NULL, sink, out, lse);
+}
+
+/* Decode with the q_len new tokens' keys and values beside the cache (k_new, v_new, in the
+ * cache's dtype; see decode_impl).  This is also chunked prefill over a cached prefix (the
+ * model card's serving set-up prefills long prompts in chunks): the chunk's q_len tokens are
+ * the new ones, their keys and values given contiguously, the prefix read through the page
+ * table (or, in sliding mode, from a ring holding its last `window` positions). */
+int oracle_decode_side(int mode, int window, int layout, int B, int Hq, int Hkv, int dqk, int dv,
+                       int q_len, double scale, int dtype, const void *q, const void *k, const void *v,
+                       const int32_t *block_table, int page_size, int max_pages, int num_pages,
+                       const int32_t *seq_lens, const void *k_new, const void *v_new, const double *sink,
+                       double *out, double *lse) {
+    if (!k_new || !v_new) return -1;
+    return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, dtype, 1.0, 1.0, k, v,
+                       block_table, page_size, max_pages, num_pages, seq_lens, k_new, v_new, sink, out, lse);
 }
 
 /*
@@ -255,7 +314,8 @@ int oracle_decode_fp8(int mode, int window, int layout, int B, int Hq, int Hkv, 
                       double *out, double *lse) {
     if (!(kscale > 0) || !(vscale > 0)) return -1;
     return decode_impl(mode, window, layout, B, Hq, Hkv, dqk, dv, q_len, scale, dtype, q, ORACLE_FP8_E4M3, kscale,
-                       vscale, k, v, block_table, page_size, max_pages, num_pages, seq_lens, sink, out, lse);
+                       vscale, k, v, block_table, page_size, max_pages, num_pages, seq_lens, NULL, NULL, sink, out,
+                       lse);
 }
 
 /*

@@ -317,6 +317,112 @@ def pin_decode_multi_matches_prefill(lib):
                 assert np.array_equal(got3, got[:, :, 0]), "q_len = 1 differs from one-token decode"
 
 
+def pin_decode_side_matches_prefill(lib):
+    """q_len new tokens whose keys and values are held beside the cache (the cache holds only
+    the committed positions) give the last q_len prefill rows: a ring of W slots (sliding
+    mode, the ring holding the last W committed positions, slots rotated), and permuted pages
+    in both modes (pages past the committed length hold other data, never read).  Lengths
+    below q_len give zero rows before position 0; q_len = 1 with a ring equals the one-token
+    ring decode of the sequence with the token written into the ring."""
+    B, Hq, Hkv, dqk, dv, L, W = 3, 4, 2, 16, 8, 60, 9
+    q = _rand((B, Hq, L, dqk), 1300)
+    k = _rand((B, Hkv, L, dqk), 1301)
+    v = _rand((B, Hkv, L, dv), 1302)
+    sink = np.array([1.0, 0.0, 3.0, 2.0])
+    pre = {oracle.SWA: oracle.prefill(q, k, v, sink, oracle.SWA, W, 0.3, lib=lib),
+           oracle.GLOBAL: oracle.prefill(q, k, v, sink, oracle.GLOBAL, 0, 0.3, lib=lib)}
+    for q_len in (1, 2, 4, 7):
+        lens = np.array([L, 31, max(1, q_len - 2)], np.int32)
+        qm = np.zeros((B, Hq, q_len, dqk), np.float32)
+        kn = np.zeros((B, Hkv, q_len, dqk), np.float32)
+        vn = np.zeros((B, Hkv, q_len, dv), np.float32)
+        kr = np.zeros((B, Hkv, W, dqk), np.float32)
+        vr = np.zeros((B, Hkv, W, dv), np.float32)
+        kpd = np.full((B * 8 + 3, Hkv, 8, dqk), 7.0, np.float32)  # data nobody may read
+        vpd = np.full((B * 8 + 3, Hkv, 8, dv), 7.0, np.float32)
+        bt = np.random.default_rng(1303 + q_len).permutation(B * 8 + 3)[:B * 8].reshape(B, 8).astype(np.int32)
+        for b in range(B):
+            nc = int(lens[b]) - q_len
+            for t in range(q_len):
+                if nc + t >= 0:
+                    qm[b, :, t] = q[b, :, nc + t]
+                    kn[b, :, t] = k[b, :, nc + t]
+                    vn[b, :, t] = v[b, :, nc + t]
+            for j in range(max(0, nc - W), max(0, nc)):
+                kr[b, :, j % W] = k[b, :, j]
+                vr[b, :, j % W] = v[b, :, j]
+            for j in range(max(0, nc)):
+                kpd[bt[b, j // 8], :, j % 8] = k[b, :, j]
+                vpd[bt[b, j // 8], :, j % 8] = v[b, :, j]
+        got = oracle.decode(qm, kr, vr, lens, sink, oracle.SWA, W, 0.3, oracle.RING, lib=lib, k_new=kn, v_new=vn)
+        cases = [(oracle.SWA, got)]
+        for mode, Wm in ((oracle.SWA, W), (oracle.GLOBAL, 0)):
+            cases.append((mode, oracle.decode(qm, kpd, vpd, lens, sink, mode, Wm, 0.3, oracle.PAGED, bt, lib=lib,
+                                              k_new=kn, v_new=vn)))
+        for mode, out in cases:
+            for b in range(B):
+                for t in range(q_len):
+                    i = int(lens[b]) - q_len + t
+                    if i < 0:
+                        assert np.all(out[b, :, t] == 0), (q_len, b, t)
+                    else:
+                        _close(out[b, :, t], pre[mode][b, :, i], 1e-12, 1e-14, f"side q_len={q_len} mode={mode} b={b}")
+    # q_len = 1 beside a ring = one-token ring decode with the token written in
+    lens = np.array([L, 31, 5], np.int32)
+    kr = np.zeros((B, Hkv, W, dqk), np.float32)
+    vr = np.zeros((B, Hkv, W, dv), np.float32)
+    for b in range(B):
+        for j in range(max(0, lens[b] - W), lens[b]):
+            kr[b, :, j % W] = k[b, :, j]
+            vr[b, :, j % W] = v[b, :, j]
+    qn = np.stack([q[b, :, lens[b] - 1] for b in range(B)])
+    ref = oracle.decode(qn, kr, vr, lens, sink, oracle.SWA, W, 0.3, oracle.RING, lib=lib)
+    kn = np.stack([k[b, :, lens[b] - 1] for b in range(B)])[:, :, None]
+    vn = np.stack([v[b, :, lens[b] - 1] for b in range(B)])[:, :, None]
+    got = oracle.decode(qn[:, :, None], kr, vr, lens, sink, oracle.SWA, W, 0.3, oracle.RING, lib=lib,
+                        k_new=np.ascontiguousarray(kn), v_new=np.ascontiguousarray(vn))[:, :, 0]
+    _close(got, ref, 1e-12, 1e-14, "side q_len=1 vs ring decode")
+
+
+def pin_prefill_cached_is_prefill_rows(lib):
+    """A chunk of Lq tokens after a prefix held in permuted pages (both modes) or, in sliding
+    mode, in a ring of the prefix's last W positions gives exactly the prefill rows of those
+    positions; pages and slots outside the prefix hold data nobody may read."""
+    B, Hq, Hkv, dqk, dv, L, W, ps = 2, 4, 2, 16, 8, 150, 11, 16
+    q = _rand((B, Hq, L, dqk), 1400)
+    k = _rand((B, Hkv, L, dqk), 1401)
+    v = _rand((B, Hkv, L, dv), 1402)
+    sink = np.array([0.5, 2.0, -1.0, 3.0])
+    pre = {oracle.SWA: oracle.prefill(q, k, v, sink, oracle.SWA, W, 0.3, lib=lib),
+           oracle.GLOBAL: oracle.prefill(q, k, v, sink, oracle.GLOBAL, 0, 0.3, lib=lib)}
+    npg = B * (L // ps + 1) + 3
+    bt = np.random.default_rng(1403).permutation(npg)[:B * (L // ps + 1)].reshape(B, -1).astype(np.int32)
+    for kv_len, Lq in ((150, 1), (150, 60), (97, 90), (40, 40), (33, 7)):
+        q0 = kv_len - Lq
+        lens = np.full(B, kv_len, np.int32)
+        kp = np.full((npg, Hkv, ps, dqk), 9.0, np.float32)
+        vp = np.full((npg, Hkv, ps, dv), 9.0, np.float32)
+        kr = np.full((B, Hkv, W, dqk), 9.0, np.float32)
+        vr = np.full((B, Hkv, W, dv), 9.0, np.float32)
+        for b in range(B):
+            for j in range(q0):
+                kp[bt[b, j // ps], :, j % ps] = k[b, :, j]
+                vp[bt[b, j // ps], :, j % ps] = v[b, :, j]
+            for j in range(max(0, q0 - W), q0):
+                kr[b, :, j % W] = k[b, :, j]
+                vr[b, :, j % W] = v[b, :, j]
+        qc = np.ascontiguousarray(q[:, :, q0:kv_len])
+        kc = np.ascontiguousarray(k[:, :, q0:kv_len])
+        vc = np.ascontiguousarray(v[:, :, q0:kv_len])
+        runs = [(oracle.SWA, oracle.RING, kr, vr, None)] + \
+            [(mode, oracle.PAGED, kp, vp, bt) for mode in (oracle.SWA, oracle.GLOBAL)]
+        for mode, layout, kc_, vc_, btx in runs:
+            got = oracle.prefill_cached(qc, kc, vc, kc_, vc_, lens, sink, mode, W if mode == oracle.SWA else 0, 0.3,
+                                        layout, btx, lib=lib)
+            _close(got, pre[mode][:, :, q0:kv_len], 1e-12, 1e-14, f"cached prefix kv_len={kv_len} Lq={Lq} "
+                                                                   f"mode={mode} layout={layout}")
+
+
 def pin_prefill_chunk_is_prefill_rows(lib):
     """A chunk of Lq new tokens after a prefix of Lk - Lq tokens gives exactly the prefill rows
     Lk - Lq .. Lk - 1 of the whole sequence (model card serving set-up: chunked prefill)."""
@@ -639,7 +745,8 @@ ALL_PINS = [
     pin_worked_example, pin_worked_example_range, pin_no_sink_is_sdpa, pin_sink_is_eager_concat,
     pin_sink_closed_form, pin_wide_window_is_global, pin_mass_below_one, pin_window_is_slice,
     pin_gqa_grouping, pin_brute_force, pin_decode_matches_prefill, pin_decode_mixed_lengths,
-    pin_decode_multi_matches_prefill, pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes, pin_e4m3_encode,
+    pin_decode_multi_matches_prefill, pin_decode_side_matches_prefill, pin_prefill_cached_is_prefill_rows,
+    pin_prefill_chunk_is_prefill_rows, pin_e4m3_codes, pin_e4m3_encode,
     pin_fp8_decode_is_decode_of_values, pin_lse, pin_rope, pin_append_then_decode_is_prefill,
     pin_fp8_append_then_decode_is_prefill,
     pin_backward_autograd, pin_backward_finite_differences, pin_backward_sampled_is_backward,

@@ -37,8 +37,11 @@ MUTATIONS = {
                                                 "const int64_t i = r;"),
     "E4M3 exponent bias off by one": ("else x = ldexp(1.0 + m / 8.0, e - 7);", "else x = ldexp(1.0 + m / 8.0, e - 8);"),
     "E4M3 subnormals without the 2^-9 scale": ("if (e == 0) x = ldexp((double)m, -9);", "if (e == 0) x = ldexp((double)m, -6);"),
-    "cache scale applied to the value twice": ("out[e] += s * (vscale * load(v, vidx[t] + e, kvdtype));",
-                                               "out[e] += s * (vscale * vscale * load(v, vidx[t] + e, kvdtype));"),
+    "cache scale applied to the value twice": ("if (t < kl->n) return kl->vscale * load(kl->v, kl->vidx[t] + e, kl->kvdtype);",
+                                               "if (t < kl->n) return kl->vscale * kl->vscale * load(kl->v, kl->vidx[t] + e, kl->kvdtype);"),
+    "drafts beside the cache taken one token late": ("const int64_t t = j - nc;", "const int64_t t = (j - nc + 1) % q_len;"),
+    "drafts beside the cache ignored (cache read instead)": ("if (j >= nc) { /* a new token beside the cache */",
+                                                             "if (0) { /* a new token beside the cache */"),
     "log-sum-exp without the row max": ("    return m + log(z);", "    return log(z);"),
     "rotary sine with the wrong sign": ("out[base + i] = a * c - b * sn;", "out[base + i] = a * c + b * sn;"),
     "rotary frequencies over all 192 dimensions": ("pow(theta, -2.0 * i / rot)", "pow(theta, -2.0 * i / dim)"),
