@@ -59,7 +59,8 @@ class Epilogue(ctypes.Structure):
 EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_prefill_chunk",
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
-           "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_decode_ex_noalloc", "sinkattn_rope",
+           "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_decode_ex_noalloc", "sinkattn_decode_verify",
+           "sinkattn_prefill_cached", "sinkattn_prefill_cached_workspace_bytes", "sinkattn_rope",
            "sinkattn_kv_append",
            "sinkattn_prefill_backward", "sinkattn_prefill_backward_workspace_bytes",
            "sinkattn_status_string")
@@ -106,6 +107,14 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
                                      ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P,
                                      P, ctypes.c_size_t, P]
+    L.sinkattn_prefill_cached_workspace_bytes.restype = ctypes.c_size_t
+    L.sinkattn_prefill_cached_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
+    L.sinkattn_prefill_cached.restype = I
+    L.sinkattn_prefill_cached.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, P, P, ctypes.POINTER(KVDesc),
+                                          P, ctypes.POINTER(Epilogue), P, P, ctypes.c_size_t, P]
+    L.sinkattn_decode_verify.restype = I
+    L.sinkattn_decode_verify.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), P, P,
+                                         P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P, P, ctypes.c_size_t, P]
     L.sinkattn_decode_ex_noalloc.restype = I
     L.sinkattn_decode_ex_noalloc.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
                                              ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P,
@@ -446,6 +455,115 @@ def sinkattn_decode_ex(mode: int, window: int, q_len: int, q, layout: int, k_cac
                                       1 if kv_fp8 else 0, k_scale, v_scale, _ptr(seq_lens), max_seq_len, _ptr(sink),
                                       ctypes.byref(ep), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
     _raise(rc)
+
+
+def sinkattn_prefill_cached_workspace_bytes(mode: int, window: int, batch: int, seqlen: int, hq: int, hkv: int,
+                                            kv_len: int) -> int:
+    d = Dims(batch, seqlen, hq, hkv, D_QK, D_V, D_QK ** -0.5)
+    n = lib().sinkattn_prefill_cached_workspace_bytes(mode, window, ctypes.byref(d), kv_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise SinkAttnError(2, "invalid sizes")
+    return n
+
+
+def sinkattn_prefill_cached(mode: int, window: int, kv_len: int, q, k, v, layout: int, k_cache, v_cache, sink, out,
+                            workspace, block_table=None, out_scale: float = 1.0, lse=None, scale: float | None = None,
+                            stream=None) -> None:
+    """Chunked prefill over a cached prefix: q bf16 [B,Hq,Lq,192] at positions kv_len-Lq ..
+    kv_len-1, k bf16 [B,Hkv,Lq,192] and v bf16 [B,Hkv,Lq,128] the chunk's keys and values; the
+    prefix in a RING ([B,Hkv,W,d], sliding window) or PAGED ([P,Hkv,page,d] + block_table) cache;
+    out bf16 [B,Hq,Lq,128]; workspace of sinkattn_prefill_cached_workspace_bytes(...) bytes."""
+    import torch
+
+    B, Hq, Lq, dqk = q.shape
+    Hkv = k.shape[1]
+    _dev_tensor(q, "q", torch.bfloat16)
+    _dev_tensor(k, "k", torch.bfloat16, (B, Hkv, Lq, dqk))
+    _dev_tensor(v, "v", torch.bfloat16, (B, Hkv, Lq, v.shape[3]))
+    _dev_tensor(out, "out", torch.bfloat16, (B, Hq, Lq, v.shape[3]))
+    if sink is not None:
+        _dev_tensor(sink, "sink", torch.float32, (Hq,))
+    if layout == KV_RING:
+        W = k_cache.shape[2]
+        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (B, Hkv, W, dqk))
+        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (B, Hkv, W, v.shape[3]))
+        desc = KVDesc(KV_RING, k_cache.data_ptr(), v_cache.data_ptr(), None, 0, 0, 0)
+    elif layout == KV_PAGED:
+        P, _, ps, _ = k_cache.shape
+        _dev_tensor(k_cache, "k_cache", torch.bfloat16, (P, Hkv, ps, dqk))
+        _dev_tensor(v_cache, "v_cache", torch.bfloat16, (P, Hkv, ps, v.shape[3]))
+        _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
+        desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps,
+                      block_table.shape[1], P)
+    else:
+        raise ValueError("layout must be KV_RING or KV_PAGED")
+    _dev_tensor(workspace, "workspace", workspace.dtype)
+    for t in (k, v, out, sink, k_cache, v_cache, block_table, workspace):
+        if t is not None and t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    ep = _epilogue(out_scale, lse, (B, Hq, Lq), q.device)
+    d = Dims(B, Lq, Hq, Hkv, dqk, v.shape[3], dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_prefill_cached(mode, window, ctypes.byref(d), kv_len, _ptr(q), _ptr(k), _ptr(v),
+                                           ctypes.byref(desc), _ptr(sink), ctypes.byref(ep), _ptr(out),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def prefill_cached(mode: int, window: int, kv_len: int, q, k, v, layout: int, k_cache, v_cache, sink=None,
+                   block_table=None, workspace=None, scale: float | None = None, stream=None):
+    """Allocate out (and the workspace if none is given) and run sinkattn_prefill_cached."""
+    import torch
+
+    B, Hq, Lq, _ = q.shape
+    if workspace is None:
+        n = sinkattn_prefill_cached_workspace_bytes(mode, window, B, Lq, Hq, k.shape[1], kv_len)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, Lq, v.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_prefill_cached(mode, window, kv_len, q, k, v, layout, k_cache, v_cache, sink, out, workspace,
+                            block_table, scale=scale, stream=stream)
+    return out
+
+
+def sinkattn_decode_verify(mode: int, window: int, q_len: int, q, layout: int, k_cache, v_cache, k_new, v_new,
+                           seq_lens, max_seq_len: int, sink, out, workspace, block_table=None, out_scale: float = 1.0,
+                           lse=None, scale: float | None = None, stream=None) -> None:
+    """Drafted tokens checked against a cache that does not hold them: q bf16 [B,Hq,q_len,192],
+    k_new bf16 [B,Hkv,q_len,192], v_new bf16 [B,Hkv,q_len,128] (the drafts' keys and values),
+    a RING ([B,Hkv,W,d], the last W committed positions) or PAGED cache of the committed
+    positions; seq_lens counts the committed tokens plus the q_len drafts.  out bf16
+    [B,Hq,q_len,128]; workspace of sinkattn_decode_multi_workspace_bytes(...) bytes or None."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, ws_ptr, ws_bytes = _decode_args(q, q_len, layout, window, k_cache, v_cache, seq_lens,
+                                                               sink, out, workspace, block_table)
+    _dev_tensor(k_new, "k_new", torch.bfloat16, (B, Hkv, q_len, dqk))
+    _dev_tensor(v_new, "v_new", torch.bfloat16, (B, Hkv, q_len, dv))
+    for t in (k_new, v_new):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    ep = _epilogue(out_scale, lse, (B, Hq, q_len), q.device)
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q.device):
+        rc = lib().sinkattn_decode_verify(mode, window, ctypes.byref(d), q_len, _ptr(q), ctypes.byref(desc),
+                                          _ptr(k_new), _ptr(v_new), _ptr(seq_lens), max_seq_len, _ptr(sink),
+                                          ctypes.byref(ep), _ptr(out), ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    _raise(rc)
+
+
+def decode_verify(mode: int, window: int, q, layout: int, k_cache, v_cache, k_new, v_new, seq_lens, max_seq_len: int,
+                  sink=None, block_table=None, workspace=None, scale: float | None = None, stream=None):
+    """Allocate out (and the workspace if none is given) and run sinkattn_decode_verify."""
+    import torch
+
+    B, Hq, q_len, _ = q.shape
+    if workspace is None:
+        workspace = decode_multi_workspace(mode, window, B, Hq, k_cache.shape[1], q_len, max_seq_len, q.device)
+    out = torch.empty((B, Hq, q_len, v_cache.shape[3]), dtype=torch.bfloat16, device=q.device)
+    sinkattn_decode_verify(mode, window, q_len, q, layout, k_cache, v_cache, k_new, v_new, seq_lens, max_seq_len,
+                           sink, out, workspace, block_table, scale=scale, stream=stream)
+    return out
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # SINKATTN_NOALLOC_SCRATCH_BYTES

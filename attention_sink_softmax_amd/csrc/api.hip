@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.h"
 #include "sinkattn.h"
 
@@ -158,6 +160,114 @@ int sinkattn_prefill_ex(int mode, int window, const sinkattn_dims *d, int32_t kv
     return launch_prefill(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Chunked prefill over a cached prefix: the rows gathered for the attention kernels are
+// positions base .. kv_len - 1 (global: from 0; sliding window: from the first key the chunk's
+// first query sees), then the workspace holds K and V of those rows and the V^T copy.
+struct CachedLayout {
+    int base, Lc;
+    size_t k_off, v_off, vt_off, bytes;
+};
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+CachedLayout cached_layout(int mode, int window, const sinkattn_dims *d, int32_t kv_len) {
+    CachedLayout c{};
+    const int q0 = kv_len - d->seqlen;
+    c.base = mode == SINKATTN_SWA ? std::max(0, q0 - window + 1) : 0;
+    c.Lc = kv_len - c.base;
+    const size_t rows = (size_t)d->batch * d->hkv * c.Lc;
+    c.k_off = 0;
+    c.v_off = round256(rows * kDqkSupported * 2);
+    c.vt_off = c.v_off + round256(rows * kDvSupported * 2);
+    c.bytes = c.vt_off + prefill_workspace_bytes(d->batch, d->hkv, c.Lc);
+    return c;
+}
+}  // namespace
+
+extern "C" {
+
+size_t sinkattn_prefill_cached_workspace_bytes(int mode, int window, const sinkattn_dims *d, int32_t kv_len) {
+    if (check_dims(mode, window, d) || d->seqlen < 0 || kv_len < d->seqlen) return (size_t)-1;
+    return cached_layout(mode, window, d, kv_len).bytes;
+}
+
+int sinkattn_prefill_cached(int mode, int window, const sinkattn_dims *d, int32_t kv_len, const void *q, const void *k,
+                            const void *v, const sinkattn_kv *prefix, const float *sink, const sinkattn_epilogue *ep,
+                            void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_dims(mode, window, d);
+    if (st) return st;
+    st = check_epilogue(ep);
+    if (st) return st;
+    if (d->seqlen < 0 || kv_len < d->seqlen) return SINKATTN_E_SHAPE;
+    if ((int64_t)kv_len * kDqkSupported * 2 > INT32_MAX) return SINKATTN_E_SHAPE;  // 32-bit row offsets
+    if (!prefix) return SINKATTN_E_NULL;
+    if (prefix->layout != SINKATTN_KV_RING && prefix->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
+    if (prefix->layout == SINKATTN_KV_RING && mode != SINKATTN_SWA) return SINKATTN_E_UNSUPPORTED;
+    const int q0 = kv_len - d->seqlen;
+    if (prefix->layout == SINKATTN_KV_PAGED &&
+        (prefix->page_size <= 0 || prefix->max_pages <= 0 || prefix->num_pages <= 0 ||
+         (int64_t)prefix->max_pages * prefix->page_size < q0))
+        return SINKATTN_E_SHAPE;
+    if (d->batch > 65535 || (int64_t)d->batch * d->hkv > 65535) return SINKATTN_E_SHAPE;
+    if (d->batch == 0 || d->seqlen == 0) return SINKATTN_OK;
+    if (!q || !k || !v || !out) return SINKATTN_E_NULL;
+    if (q0 > 0 && (!prefix->k || !prefix->v || (prefix->layout == SINKATTN_KV_PAGED && !prefix->block_table)))
+        return SINKATTN_E_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (sink && misaligned(sink)) ||
+        (q0 > 0 && (misaligned(prefix->k) || misaligned(prefix->v))))
+        return SINKATTN_E_ALIGN;
+    const CachedLayout c = cached_layout(mode, window, d, kv_len);
+    if (!workspace || workspace_bytes < c.bytes) return SINKATTN_E_WORKSPACE;
+    if (misaligned(workspace)) return SINKATTN_E_ALIGN;
+    char *ws = static_cast<char *>(workspace);
+
+    GatherParams g{};
+    g.k_chunk = static_cast<const uint16_t *>(k);
+    g.v_chunk = static_cast<const uint16_t *>(v);
+    g.k_cache = static_cast<const uint16_t *>(prefix->k);
+    g.v_cache = static_cast<const uint16_t *>(prefix->v);
+    g.block_table = prefix->layout == SINKATTN_KV_PAGED ? prefix->block_table : nullptr;
+    g.k_out = reinterpret_cast<uint16_t *>(ws + c.k_off);
+    g.v_out = reinterpret_cast<uint16_t *>(ws + c.v_off);
+    g.B = d->batch;
+    g.Hkv = d->hkv;
+    g.Lq = d->seqlen;
+    g.Lc = c.Lc;
+    g.base = c.base;
+    g.q0 = q0;
+    g.paged = prefix->layout == SINKATTN_KV_PAGED;
+    g.window = window;
+    g.page_size = g.paged ? prefix->page_size : 0;
+    g.max_pages = g.paged ? prefix->max_pages : 0;
+    g.num_pages = g.paged ? prefix->num_pages : 0;
+
+    PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = g.k_out;
+    p.v = g.v_out;
+    p.sink = sink;
+    p.out = static_cast<uint16_t *>(out);
+    p.vt = reinterpret_cast<uint16_t *>(ws + c.vt_off);
+    p.lpad = (c.Lc + 63) / 64 * 64;
+    p.B = d->batch;
+    p.L = c.Lc;
+    p.Lq = d->seqlen;
+    p.q0 = q0 - c.base;  // positions relative to the first gathered row: masks depend on differences only
+    p.Hq = d->hq;
+    p.Hkv = d->hkv;
+    p.G = d->hq / d->hkv;
+    p.swa = mode == SINKATTN_SWA;
+    p.window = p.swa ? window : 0;
+    p.scale_log2 = (float)((double)d->scale * kLog2eD);
+    p.out_scale = ep ? ep->out_scale : 1.f;
+    p.lse = ep ? ep->lse : nullptr;
+    if (plan_prefill(p) > INT32_MAX) return SINKATTN_E_SHAPE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_gather_prefix(g, s)) return SINKATTN_E_DEVICE;
+    return launch_prefill(p, s) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
 size_t sinkattn_decode_workspace_bytes(int mode, int window, const sinkattn_dims *d, int32_t max_seq_len) {
     if (check_dims(mode, window, d) || max_seq_len < 1) return (size_t)-1;
     return plan_decode(mode, window, d, 1, max_seq_len).ws_bytes;
@@ -175,10 +285,11 @@ namespace {
 // Decode from a bf16 cache (fp8 = 0) or an E4M3 cache with per-tensor scales (fp8 = 1).
 // use_scratch: the split partials go to the library's own device scratch array instead of
 // the caller's workspace (which is then ignored).
+// k_new / v_new: the new tokens' keys and values beside the cache (both NULL: they are in it).
 int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q, const sinkattn_kv *kv,
-                  const int32_t *seq_lens, int32_t max_seq_len, const float *sink, int fp8, float k_scale,
-                  float v_scale, const sinkattn_epilogue *ep, void *out, void *workspace, size_t workspace_bytes,
-                  void *stream, bool use_scratch = false) {
+                  const void *k_new, const void *v_new, const int32_t *seq_lens, int32_t max_seq_len,
+                  const float *sink, int fp8, float k_scale, float v_scale, const sinkattn_epilogue *ep, void *out,
+                  void *workspace, size_t workspace_bytes, void *stream, bool use_scratch = false) {
     int st = check_dims(mode, window, d);
     if (st) return st;
     st = check_epilogue(ep);
@@ -188,17 +299,23 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
         if (kv->layout != SINKATTN_KV_PAGED || kv->page_size <= 0 || kv->page_size % 32) return SINKATTN_E_UNSUPPORTED;
         if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)) return SINKATTN_E_SHAPE;
     }
+    const bool side = k_new || v_new;
+    if (side && fp8) return SINKATTN_E_UNSUPPORTED;
     if (q_len < 1 || q_len > kMaxQLen) return SINKATTN_E_SHAPE;
     if (!kv) return SINKATTN_E_NULL;
     if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
-    if (kv->layout == SINKATTN_KV_RING && (mode != SINKATTN_SWA || q_len != 1)) return SINKATTN_E_UNSUPPORTED;
+    if (kv->layout == SINKATTN_KV_RING && (mode != SINKATTN_SWA || (q_len != 1 && !side)))
+        return SINKATTN_E_UNSUPPORTED;
     if (max_seq_len < 1) return SINKATTN_E_SHAPE;
     if (kv->layout == SINKATTN_KV_PAGED) {
         if (kv->page_size <= 0 || kv->max_pages <= 0 || kv->num_pages <= 0) return SINKATTN_E_SHAPE;
-        if ((int64_t)max_seq_len > (int64_t)kv->max_pages * kv->page_size) return SINKATTN_E_SHAPE;
+        // the page table covers the cached positions: all of them, or all but the new tokens
+        if ((int64_t)max_seq_len - (side ? q_len : 0) > (int64_t)kv->max_pages * kv->page_size)
+            return SINKATTN_E_SHAPE;
     }
     if (d->batch == 0) return SINKATTN_OK;
-    if (!q || !out || !seq_lens || !kv->k || !kv->v) return SINKATTN_E_NULL;
+    if (!q || !out || !seq_lens || !kv->k || !kv->v || (side && (!k_new || !v_new))) return SINKATTN_E_NULL;
+    if (side && (misaligned(k_new) || misaligned(v_new))) return SINKATTN_E_ALIGN;
     if (kv->layout == SINKATTN_KV_PAGED && !kv->block_table) return SINKATTN_E_NULL;
     if (misaligned(q) || misaligned(out) || misaligned(seq_lens) || misaligned(kv->k) || misaligned(kv->v) ||
         (sink && misaligned(sink)) || (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
@@ -223,6 +340,8 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(kv->k);
     p.v = static_cast<const uint16_t *>(kv->v);
+    p.k_new = static_cast<const uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
     p.block_table = kv->layout == SINKATTN_KV_PAGED ? kv->block_table : nullptr;
     p.seq_lens = seq_lens;
     p.sink = sink;
@@ -259,32 +378,41 @@ extern "C" {
 int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                           const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
                           void *out, void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 0, 1.f, 1.f, nullptr, out,
-                         workspace, workspace_bytes, stream);
+    return decode_common(mode, window, d, q_len, q, kv, nullptr, nullptr, seq_lens, max_seq_len, sink, 0, 1.f, 1.f,
+                         nullptr, out, workspace, workspace_bytes, stream);
 }
 
 int sinkattn_decode_ex(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                        const sinkattn_kv *kv, int kv_fp8, float k_scale, float v_scale, const int32_t *seq_lens,
                        int32_t max_seq_len, const float *sink, const sinkattn_epilogue *ep, void *out,
                        void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0, k_scale,
-                         v_scale, ep, out, workspace, workspace_bytes, stream);
+    return decode_common(mode, window, d, q_len, q, kv, nullptr, nullptr, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0,
+                         k_scale, v_scale, ep, out, workspace, workspace_bytes, stream);
 }
 
 int sinkattn_decode_ex_noalloc(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                                const sinkattn_kv *kv, int kv_fp8, float k_scale, float v_scale,
                                const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
                                const sinkattn_epilogue *ep, void *out, void *stream) {
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0, k_scale,
-                         v_scale, ep, out, nullptr, 0, stream, true);
+    return decode_common(mode, window, d, q_len, q, kv, nullptr, nullptr, seq_lens, max_seq_len, sink, kv_fp8 ? 1 : 0,
+                         k_scale, v_scale, ep, out, nullptr, 0, stream, true);
+}
+
+int sinkattn_decode_verify(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
+                           const sinkattn_kv *kv, const void *k_new, const void *v_new, const int32_t *seq_lens,
+                           int32_t max_seq_len, const float *sink, const sinkattn_epilogue *ep, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (!k_new || !v_new) return SINKATTN_E_NULL;
+    return decode_common(mode, window, d, q_len, q, kv, k_new, v_new, seq_lens, max_seq_len, sink, 0, 1.f, 1.f, ep,
+                         out, workspace, workspace_bytes, stream);
 }
 
 int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q,
                         const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len, const float *sink,
                         float k_scale, float v_scale, void *out, void *workspace, size_t workspace_bytes,
                         void *stream) {
-    return decode_common(mode, window, d, q_len, q, kv, seq_lens, max_seq_len, sink, 1, k_scale, v_scale, nullptr,
-                         out, workspace, workspace_bytes, stream);
+    return decode_common(mode, window, d, q_len, q, kv, nullptr, nullptr, seq_lens, max_seq_len, sink, 1, k_scale,
+                         v_scale, nullptr, out, workspace, workspace_bytes, stream);
 }
 
 size_t sinkattn_prefill_backward_workspace_bytes(const sinkattn_dims *d) {

@@ -136,10 +136,14 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(v2i32 c) {
     return bf16x8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
 }
 
-// Row of key j (general path): ring slot j, or page block_table[b][j / page_size].
+// Row of key j (general path): ring slot j, or page block_table[b][j / page_size].  With
+// the new tokens' keys beside the cache (p.k_new), j is a position: positions from n - q_len
+// on are rows of `side`, earlier ones ring slot j mod window or the page lookup.
 __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, int kvh, int j, const uint16_t *base,
-                                                  int width, bool &bad) {
-    if (!p.paged) return base + (((size_t)b * p.Hkv + kvh) * p.window + j) * width;
+                                                  const uint16_t *side, int width, int n, bool &bad) {
+    if (p.k_new && j >= n - p.q_len)
+        return side + (((size_t)b * p.Hkv + kvh) * p.q_len + (j - (n - p.q_len))) * width;
+    if (!p.paged) return base + (((size_t)b * p.Hkv + kvh) * p.window + (p.k_new ? j % p.window : j)) * width;
     const int page = p.block_table[(size_t)b * p.max_pages + j / p.page_size];
     if (page < 0 || page >= p.num_pages) {
         bad = true;
@@ -150,9 +154,10 @@ __device__ __forceinline__ const uint16_t *kv_row(const DecodeParams &p, int b, 
 
 // Keys that sequence b's queries can see, as the range the splits walk: [kbeg, kend).  The
 // new queries sit at positions n - q_len .. n - 1; a ring enumerates its slots [0, min(n, W))
-// (one query, every valid slot visible).
+// (one query, every valid slot visible), except with the new tokens beside it, when keys are
+// walked by position as in a paged cache.
 __device__ __forceinline__ void key_range(const DecodeParams &p, int n, int &kbeg, int &kend) {
-    if (!p.paged) {
+    if (!p.paged && !p.k_new) {
         kbeg = 0;
         kend = min(n, p.window);
     } else {
@@ -162,7 +167,8 @@ __device__ __forceinline__ void key_range(const DecodeParams &p, int n, int &kbe
 }
 
 __device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
-    return n >= 1 && n <= p.max_seq_len && (!p.paged || n <= p.max_pages * p.page_size);
+    const int cached = p.k_new ? n - p.q_len : n;  // positions the page table must cover
+    return n >= 1 && n <= p.max_seq_len && (!p.paged || cached <= p.max_pages * p.page_size);
 }
 
 // Columns: the G * q_len (query head, new token) pairs of one KV head, column c = head-in-
@@ -227,8 +233,9 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         const bool ok = c < rows;
         const int hq = kvh * p.G + (ok ? c / p.q_len : 0), tok = ok ? c % p.q_len : 0;
         const int pos = n - p.q_len + tok;
-        lo_c[cb] = max(kbeg, (p.paged && p.swa) ? pos - p.window + 1 : 0);
-        hi_c[cb] = min(s_hi, p.paged ? pos + 1 : kend) - 1;
+        const bool by_pos = p.paged || p.k_new;  // keys walked by position
+        lo_c[cb] = max(kbeg, (by_pos && p.swa) ? pos - p.window + 1 : 0);
+        hi_c[cb] = min(s_hi, by_pos ? pos + 1 : kend) - 1;
         const uint16_t *qrow = p.q + (((size_t)b * p.Hq + hq) * p.q_len + tok) * kDqk + 8 * q;
 #pragma unroll
         for (int kk = 0; kk < 6; ++kk) qf[cb][kk] = as_bf16x8(ok ? ldg16(qrow + 32 * kk) : u32x4{0, 0, 0, 0});
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 for (int kh = 0; kh < 2; ++kh) {
                     const int k16 = 8 * kh + (lane >> 3);
                     const int j = min(max(j0 + 16 * sb + k16, lo), hi);
-                    const uint16_t *kr = kv_row(p, b, kvh, j, p.k, kDqk, bad) + 8 * ((lane & 7) ^ kswz(k16));
+                    const uint16_t *kr = kv_row(p, b, kvh, j, p.k, p.k_new, kDqk, n, bad) + 8 * ((lane & 7) ^ kswz(k16));
 #pragma unroll
                     for (int c = 0; c < 3; ++c) dma16<kLoadNT>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
                 }
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int j = min(max(j0 + 4 * m + r, lo), hi);
-                dma16<kLoadNT>(kv_row(p, b, kvh, j, p.v, kDv, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kLoadNT>(kv_row(p, b, kvh, j, p.v, p.v_new, kDv, n, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
             }
         }
     };
@@ -678,9 +685,11 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     DecodeParams p = prm;
     void *args[] = {&p};
     const dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B);
-    const bool fast = !p.paged || (p.page_size % kSlice == 0);
+    // keys beside the cache take the general path (rows looked up one by one)
+    const bool fast = !p.k_new && (!p.paged || (p.page_size % kSlice == 0));
     // a ring of at most 128 visible slots in one split: one slice per wave
-    const bool single = !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
+    const bool single =
+        !p.k_new && !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
     const void *fn;
     if (p.fp8) {
         if (!p.paged || !fast) return -1;

@@ -31,6 +31,7 @@ struct PrefillParams {
 
 struct DecodeParams {
     const uint16_t *q, *k, *v;
+    const uint16_t *k_new, *v_new;  // the new tokens' keys and values beside the cache, or nullptr
     const int32_t *block_table;  // paged layout only
     const int32_t *seq_lens;
     const float *sink;  // [Hq] or nullptr
@@ -80,6 +81,19 @@ struct BwdParams {
 };
 size_t backward_workspace_bytes(int B, int Hq, int L);
 int launch_backward(const BwdParams &p, hipStream_t stream);
+
+// Chunked prefill over a cached prefix: the keys and values of positions base .. base + Lc - 1
+// gathered into contiguous rows, the prefix (positions below q0) from a ring or pages, the
+// chunk (q0 .. q0 + Lq - 1) from its own rows.
+struct GatherParams {
+    const uint16_t *k_chunk, *v_chunk;  // [B][Hkv][Lq][kDqk], [B][Hkv][Lq][kDv]
+    const uint16_t *k_cache, *v_cache;  // ring [B][Hkv][window][d] or pages [num_pages][Hkv][page_size][d]
+    const int32_t *block_table;         // [B][max_pages] (paged)
+    uint16_t *k_out, *v_out;            // [B][Hkv][Lc][kDqk], [B][Hkv][Lc][kDv]
+    int B, Hkv, Lq, Lc, base, q0;
+    int paged, window, page_size, max_pages, num_pages;
+};
+int launch_gather_prefix(const GatherParams &g, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int B, int Hkv, int L);
 // Fills the work layout of p from B, L, Hkv, G and swa; returns the number of workgroups to

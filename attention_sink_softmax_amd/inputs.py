@@ -159,7 +159,13 @@ GA_DECODE_FP8 = Workload("ga_decode_B8_256K_paged_fp8", "decode", MODE_GLOBAL, 8
                          layout="paged", ctx_lo=262144, ctx_hi=262144, page_size=64, kv_fp8=True)
 FP8_KV_SCALE = 2.0 ** -6
 
-WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE, GA_VERIFY, GA_DECODE_FP8)}
+# the sliding-window decode workload with 4 drafted tokens per sequence, their keys and values
+# held beside the rings (the rings hold the committed positions only)
+SWA_VERIFY = Workload("swa_verify_B128_ring_q4", "decode", MODE_SWA, 128, 64, 8, window=128, seed=7,
+                      layout="ring", ctx_lo=4096, ctx_hi=65536, q_len=4)
+
+WORKLOADS = {w.name: w for w in (TINY, SWA_PREFILL, GA_PREFILL, SWA_DECODE, GA_DECODE, GA_VERIFY, GA_DECODE_FP8,
+                                 SWA_VERIFY)}
 
 
 # --------------------------------------------------------------------------- prefill
@@ -197,6 +203,37 @@ def ga_parity_rows(w: Workload, n_first: int = 128, n_last: int = 128, n_rand: i
     return np.array([(0, h, i) for h in range(w.hq) for i in pos], np.int64)
 
 
+def prefill_cached_inputs(w: Workload, Lq: int, page_size: int = 64) -> dict:
+    """A prefill workload's last Lq positions as a chunk after a prefix held in a cache: q, k, v
+    of the chunk [B,H,Lq,d]; the prefix (positions 0 .. L-Lq-1) in seeded, permuted pages
+    (k_pages, v_pages [P,Hkv,page,d], block_table [B,max_pages], pool of twice the pages needed)
+    and in rings of its last `window` positions (k_ring, v_ring [B,Hkv,W,d]); sink."""
+    d = prefill_inputs(w)
+    L, q0 = w.seqlen, w.seqlen - Lq
+    out = {n: np.ascontiguousarray(d[n][:, :, q0:]) for n in ("q", "k", "v")}
+    out["sink"] = d["sink"]
+    mp = max(1, (q0 + page_size - 1) // page_size)
+    out["block_table"] = page_table(w.batch, mp, 2 * w.batch * mp, w.seed + 100)
+    P = 2 * w.batch * mp
+    kp = np.zeros((P, w.hkv, page_size, w.d_qk), np.uint16)
+    vp = np.zeros((P, w.hkv, page_size, w.d_v), np.uint16)
+    for b in range(w.batch):
+        for i in range(mp):
+            j0, j1 = i * page_size, min(q0, (i + 1) * page_size)
+            pg = out["block_table"][b, i]
+            kp[pg, :, :j1 - j0] = d["k"][b, :, j0:j1]
+            vp[pg, :, :j1 - j0] = d["v"][b, :, j0:j1]
+    out["k_pages"], out["v_pages"] = kp, vp
+    W = max(1, w.window)
+    kr = np.zeros((w.batch, w.hkv, W, w.d_qk), np.uint16)
+    vr = np.zeros((w.batch, w.hkv, W, w.d_v), np.uint16)
+    for j in range(max(0, q0 - W), q0):
+        kr[:, :, j % W] = d["k"][:, :, j]
+        vr[:, :, j % W] = d["v"][:, :, j]
+    out["k_ring"], out["v_ring"] = kr, vr
+    return out
+
+
 # --------------------------------------------------------------------------- decode
 def decode_seq_lens(w: Workload, seed: int | None = None, batch: int | None = None) -> np.ndarray:
     s = w.seed if seed is None else seed
@@ -223,6 +260,19 @@ def decode_ring_inputs(w: Workload, seed: int | None = None, batch: int | None =
         "seq_lens": lens,
         "sink": sink_values(w.hq, s),
     }
+
+
+def decode_ring_verify_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Rings of the committed positions and q_len drafted tokens beside them: q [B,Hq,q_len,dqk],
+    k_new [B,Hkv,q_len,dqk], v_new [B,Hkv,q_len,dv] (bf16 bits), ring caches k [B,Hkv,W,dqk],
+    v [B,Hkv,W,dv] filled with N(0,1) data (the slots stand for the last W committed positions),
+    seq_lens (committed + q_len) and sink."""
+    s = w.seed if seed is None else seed
+    lens = decode_seq_lens(w, s)
+    B = w.batch
+    return {"q": normal((B, w.hq, w.q_len, w.d_qk), s, 0), "k": normal((B, w.hkv, w.window, w.d_qk), s, 1),
+            "v": normal((B, w.hkv, w.window, w.d_v), s, 2), "k_new": normal((B, w.hkv, w.q_len, w.d_qk), s, 3),
+            "v_new": normal((B, w.hkv, w.q_len, w.d_v), s, 4), "seq_lens": lens, "sink": sink_values(w.hq, s)}
 
 
 def page_table(batch: int, pages_per_seq: int, num_pages: int, seed: int, permute: bool = True) -> np.ndarray:

@@ -193,6 +193,58 @@ def main() -> int:
 
         runs[w.name] = (call, flops, nbytes)
 
+    # --- sliding-window verify: the B = 128 rings with 4 drafted tokens per sequence whose keys
+    # and values are held beside the rings (the rings are only read); 4 input sets rotate
+    w = inputs.SWA_VERIFY
+    if not only or w.name in only:
+        sets = []
+        for r in range(4):
+            d = inputs.decode_ring_verify_inputs(w, seed=w.seed * 100 + r)
+            sets.append(dict(q=up(d["q"]), k=up(d["k"]), v=up(d["v"]), kn=up(d["k_new"]), vn=up(d["v_new"]),
+                             lens=torch.from_numpy(d["seq_lens"]).to(dev), sink=torch.from_numpy(d["sink"]).to(dev)))
+        out = torch.empty((w.batch, w.hq, w.q_len, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_multi_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, w.q_len, w.ctx_hi, dev)
+        # draft t sees the W - t - 1 newest ring keys and drafts 0..t (W keys); the ring and the
+        # drafts are read once for all four
+        flops = w.batch * w.q_len * w.window * w.hq * FLOP_PER_PAIR
+        nbytes = w.batch * (w.window - 1 + w.q_len) * w.hkv * (w.d_qk + w.d_v) * 2
+        state = {"i": 0}
+
+        def call(w=w, sets=sets, out=out, ws=ws, state=state):
+            s = sets[state["i"] % len(sets)]
+            state["i"] += 1
+            sa.sinkattn_decode_verify(w.mode, w.window, w.q_len, s["q"], sa.KV_RING, s["k"], s["v"], s["kn"], s["vn"],
+                                      s["lens"], w.ctx_hi, s["sink"], out, ws)
+
+        runs[w.name] = (call, flops, nbytes)
+
+    # --- chunked prefill over a cached prefix: the 32K prefill workloads' last 16384 positions
+    # after a 16384-token prefix in 64-token permuted pages (global) or a 128-slot ring (sliding)
+    for w, layout, name in ((inputs.GA_PREFILL, sa.KV_PAGED, "ga_prefill_chunk16K_after16K_paged"),
+                            (inputs.SWA_PREFILL, sa.KV_RING, "swa_prefill_chunk16K_after16K_ring")):
+        if only and name not in only:
+            continue
+        Lq = 16384
+        d = inputs.prefill_cached_inputs(w, Lq)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        kc = up(d["k_pages"] if layout == sa.KV_PAGED else d["k_ring"])
+        vc = up(d["v_pages"] if layout == sa.KV_PAGED else d["v_ring"])
+        bt = torch.from_numpy(d["block_table"]).to(dev) if layout == sa.KV_PAGED else None
+        sink = torch.from_numpy(d["sink"]).to(dev)
+        del d
+        out = torch.empty((w.batch, w.hq, Lq, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(sa.sinkattn_prefill_cached_workspace_bytes(w.mode, w.window, w.batch, Lq, w.hq, w.hkv,
+                                                                    w.seqlen), dtype=torch.uint8, device=dev)
+        pairs = pairs_prefill(w.seqlen, w.mode, w.window) - pairs_prefill(w.seqlen - Lq, w.mode, w.window)
+        flops = pairs * w.hq * w.batch * FLOP_PER_PAIR
+        kv_seen = w.seqlen if w.mode == 0 else Lq + w.window - 1
+        nbytes = (q.numel() + out.numel()) * 2 + w.batch * w.hkv * kv_seen * (w.d_qk + w.d_v) * 2
+
+        def call(w=w, q=q, k=k, v=v, layout=layout, kc=kc, vc=vc, bt=bt, sink=sink, out=out, ws=ws):
+            sa.sinkattn_prefill_cached(w.mode, w.window, w.seqlen, q, k, v, layout, kc, vc, sink, out, ws, bt)
+
+        runs[name] = (call, flops, nbytes)
+
     # --- backward of the 32K global prefill (q, k, v, sink gradients), from the forward's
     # output and log-sum-exp; dO seeded N(0,1)
     name = "ga_prefill_backward_L32768"

@@ -171,6 +171,40 @@ int sinkattn_prefill_chunk(int mode, int window, const sinkattn_dims *d, int32_t
                            void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace sinkattn_prefill_cached needs: the gathered keys and values of
+ * the rows the chunk sees (global: all kv_len positions; sliding window: the chunk and the
+ * window - 1 positions before it) and their V^T copy.  (size_t)-1 for invalid arguments.
+ */
+size_t sinkattn_prefill_cached_workspace_bytes(int mode, int window, const sinkattn_dims *d,
+                                               int32_t kv_len);
+
+/*
+ * Chunked prefill over a prefix that is already in a KV cache: the chunk's d->seqlen = Lq
+ * queries at positions kv_len - Lq .. kv_len - 1 attend causally (or within the window) to the
+ * prefix, read from the cache, and to the chunk's own keys, given contiguously.  The model
+ * card's serving set-up prefills long prompts in chunks of 16384 tokens over a paged cache
+ * ("MiMo-V2-Flash", SGLang quick start: chunked prefill size, page size); the result is the
+ * prefill definition's rows kv_len - Lq .. kv_len - 1.
+ *   q          bf16 [batch][hq][Lq][d_qk]
+ *   k, v       bf16 [batch][hkv][Lq][d_qk], [batch][hkv][Lq][d_v]: the chunk's keys and values
+ *   prefix     the cache holding positions 0 .. kv_len - Lq - 1: PAGED (either mode; the
+ *              table covers them) or RING (sliding-window mode; it holds the prefix's last
+ *              `window` positions, position p in slot p mod window).  Only read.
+ *   sink, ep, out (bf16 [batch][hq][Lq][d_v]), stream as sinkattn_prefill_ex
+ *   workspace  at least sinkattn_prefill_cached_workspace_bytes(mode, window, d, kv_len)
+ * A first kernel gathers the visible prefix rows and the chunk into the workspace (one pass
+ * over the keys the chunk sees); the prefill kernels then run on them.  A prefix page id
+ * outside [0, num_pages) is never read: every output row that sees that page is NaN, and so
+ * may be rows that share a 32-key block with it.  Errors as
+ * sinkattn_prefill_ex; a ring in global mode is SINKATTN_E_UNSUPPORTED; a page table too short
+ * for the prefix is SINKATTN_E_SHAPE.
+ */
+int sinkattn_prefill_cached(int mode, int window, const sinkattn_dims *d, int32_t kv_len,
+                            const void *q, const void *k, const void *v, const sinkattn_kv *prefix,
+                            const float *sink, const sinkattn_epilogue *ep, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sinkattn_prefill_chunk with an epilogue (lse: float32 [batch][hq][seqlen]).  Errors as
  * sinkattn_prefill_chunk; a non-finite out_scale is SINKATTN_E_SHAPE, a misaligned lse
  * SINKATTN_E_ALIGN.
@@ -241,6 +275,33 @@ int sinkattn_decode_multi(int mode, int window, const sinkattn_dims *d, int32_t 
                           const void *q, const sinkattn_kv *kv, const int32_t *seq_lens,
                           int32_t max_seq_len, const float *sink, void *out, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * Verification of drafted tokens whose keys and values are NOT in the cache: the q_len new
+ * tokens (positions seq_lens[b] - q_len .. seq_lens[b] - 1) attend causally, as in
+ * sinkattn_decode_multi, to the cached positions before them and to the new tokens up to
+ * their own position, whose keys and values are read from k_new / v_new.  The main model
+ * checks the drafts of its multi-token-prediction head in one parallel pass ("MiMo-V2-Flash
+ * 模型架构深度拆解", CH 4.4), and the drafts after the first mismatch are rejected (paper-notes
+ * page "MiMo-V2-Flash Technical Report", §6.4): writing them into a sliding-window ring first
+ * would overwrite committed keys that a rejection cannot restore, so the cache is only read
+ * here and the caller appends the accepted tokens afterwards (sinkattn_kv_append).
+ *   kv         RING (sliding-window mode; it holds the last `window` committed positions,
+ *              position p in slot p mod window) or PAGED (either mode; the table covers the
+ *              committed positions 0 .. seq_lens[b] - q_len - 1).  bf16 only.
+ *   k_new      bf16 [batch][hkv][q_len][d_qk], v_new bf16 [batch][hkv][q_len][d_v]: token t at
+ *              position seq_lens[b] - q_len + t (already rotated, as the cache's keys)
+ *   q_len      1 .. 256; seq_lens counts the committed tokens plus the q_len new ones
+ *   q, out, seq_lens, max_seq_len, sink, ep, workspace (sinkattn_decode_multi_workspace_bytes),
+ *   stream     as sinkattn_decode_ex.
+ * Errors as sinkattn_decode_ex; k_new or v_new NULL is SINKATTN_E_NULL.  The cache and the
+ * new tokens' rows are read with a row lookup per key (no page-aligned fast path).
+ */
+int sinkattn_decode_verify(int mode, int window, const sinkattn_dims *d, int32_t q_len,
+                           const void *q, const sinkattn_kv *kv, const void *k_new,
+                           const void *v_new, const int32_t *seq_lens, int32_t max_seq_len,
+                           const float *sink, const sinkattn_epilogue *ep, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Decode (q_len >= 1 new tokens, as sinkattn_decode_multi) from a KV cache held in 8-bit

@@ -288,3 +288,50 @@ def test_backward_argument_errors(L):
     assert backward(L, sink=A, dsink=A + 8) == E_ALIGN
     assert backward(L, ws=None) == E_WS
     assert backward(L, wsb=need - 1) == E_WS
+
+
+def test_decode_verify_argument_errors(L):
+    def ver(mode=1, window=128, desc=None, q_len=4, kn=A, vn=A, ml=65536):
+        d = dims(B=128, hq=64, hkv=8)
+        desc = desc if desc is not None else kv(layout=0, bt=None)
+        return L.sinkattn_decode_verify(mode, window, ctypes.byref(d), q_len, A, ctypes.byref(desc), kn, vn, A, ml,
+                                        None, None, A, A, 1 << 30, None)
+    assert ver(kn=None) == E_NULL
+    assert ver(vn=None) == E_NULL
+    assert ver(mode=0, window=0) == E_UNSUP           # a ring in global mode
+    assert ver(q_len=0) == E_SHAPE
+    assert ver(q_len=257) == E_SHAPE
+    assert ver(kn=A + 4) == E_ALIGN
+    assert ver(desc=kv(layout=1, ps=64, mp=2)) == E_SHAPE   # the table must cover the committed positions
+    # pages covering the committed positions only (the drafts are beside the cache): accepted
+    # as far as the host checks go (the workspace is too small, so nothing is launched)
+    d = dims(B=8, hq=64, hkv=4)
+    desc = kv(layout=1, ps=64, mp=4096)
+    assert L.sinkattn_decode_verify(0, 0, ctypes.byref(d), 4, A, ctypes.byref(desc), A, A, A, 262144 + 4, None, None,
+                                    A, A, 0, None) == E_WS
+
+
+def test_prefill_cached_argument_errors(L):
+    def cached(mode=0, window=0, kv_len=1000, desc=None, d=None, ws=A, wsb=1 << 40, q=A):
+        d = d or dims(Lq=300, hq=64, hkv=4)
+        desc = desc if desc is not None else kv(layout=1, ps=64, mp=16)
+        return L.sinkattn_prefill_cached(mode, window, ctypes.byref(d), kv_len, q, A, A, ctypes.byref(desc), None, None,
+                                         A, ws, wsb, None)
+    assert cached(kv_len=299) == E_SHAPE                       # fewer keys than chunk tokens
+    assert cached(desc=kv(layout=0, bt=None)) == E_UNSUP       # a ring in global mode
+    assert cached(desc=kv(layout=1, ps=64, mp=10)) == E_SHAPE  # the table does not cover the 700-token prefix
+    assert cached(wsb=1000) == E_WS
+    assert cached(q=None) == E_NULL
+    assert cached(desc=kv(layout=1, ps=64, mp=16, bt=None)) == E_NULL
+    assert cached(d=dims(Lq=0, hq=64, hkv=4), q=None) == OK
+    assert L.sinkattn_prefill_cached(0, 0, ctypes.byref(dims()), 100, A, A, A, None, None, None, A, A, 1 << 40,
+                                     None) == E_NULL
+
+
+def test_prefill_cached_workspace_size(L):
+    # global: all kv_len rows gathered (K + V) and their V^T copy
+    assert sa.sinkattn_prefill_cached_workspace_bytes(0, 0, 1, 16384, 64, 4, 32768) == 4 * 32768 * (384 + 256 + 256)
+    # sliding window: the chunk and the window - 1 positions before it
+    rows = 16384 + 127
+    assert sa.sinkattn_prefill_cached_workspace_bytes(1, 128, 1, 16384, 64, 8, 32768) == \
+        8 * rows * (384 + 256) + 8 * 128 * ((rows + 63) // 64 * 64) * 2
