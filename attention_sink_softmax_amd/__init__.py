@@ -60,7 +60,7 @@ EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_pre
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
            "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_decode_ex_noalloc", "sinkattn_decode_verify",
-           "sinkattn_prefill_cached", "sinkattn_prefill_cached_workspace_bytes", "sinkattn_rope",
+           "sinkattn_prefill_cached", "sinkattn_prefill_cached_workspace_bytes", "sinkattn_decode_prologue", "sinkattn_rope",
            "sinkattn_kv_append",
            "sinkattn_prefill_backward", "sinkattn_prefill_backward_workspace_bytes",
            "sinkattn_status_string")
@@ -107,6 +107,9 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_ex.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32, P, ctypes.POINTER(KVDesc), I,
                                      ctypes.c_float, ctypes.c_float, P, ctypes.c_int32, P, ctypes.POINTER(Epilogue), P,
                                      P, ctypes.c_size_t, P]
+    L.sinkattn_decode_prologue.restype = I
+    L.sinkattn_decode_prologue.argtypes = [ctypes.c_double, I, ctypes.POINTER(Dims), ctypes.c_int32, P, P, P, P,
+                                           ctypes.POINTER(KVDesc), I, ctypes.c_float, ctypes.c_float, P, P]
     L.sinkattn_prefill_cached_workspace_bytes.restype = ctypes.c_size_t
     L.sinkattn_prefill_cached_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
     L.sinkattn_prefill_cached.restype = I
@@ -679,6 +682,45 @@ def sinkattn_kv_append(layout: int, k_cache, v_cache, k_new, v_new, seq_lens, wi
     with torch.cuda.device(k_new.device):
         rc = lib().sinkattn_kv_append(ctypes.byref(desc), window, B, Hkv, n, _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
                                       1 if kv_fp8 else 0, k_scale, v_scale, _stream_ptr(stream, k_new.device))
+    _raise(rc)
+
+
+def sinkattn_decode_prologue(theta: float, layout: int, q_in, q_out, k_new, v_new, k_cache, v_cache, seq_lens,
+                             window: int = 0, block_table=None, kv_fp8: bool = False, k_scale: float = 1.0,
+                             v_scale: float = 1.0, stream=None) -> None:
+    """RoPE of the new queries q_in bf16 [B,Hq,n,192] into q_out (may be q_in) and of the new keys
+    k_new bf16 [B,Hkv,n,192], then the cache write of the rotated keys and v_new bf16
+    [B,Hkv,n,128] at positions seq_lens[b] - n .. seq_lens[b] - 1 into a ring ([B,Hkv,window,d])
+    or pages ([P,Hkv,page,d]), bf16 or uint8 E4M3 codes (kv_fp8); one kernel."""
+    import torch
+
+    B, Hq, n, _ = q_in.shape
+    Hkv = k_new.shape[1]
+    cdt = torch.uint8 if kv_fp8 else torch.bfloat16
+    _dev_tensor(q_in, "q_in", torch.bfloat16, (B, Hq, n, 192))
+    _dev_tensor(q_out, "q_out", torch.bfloat16, (B, Hq, n, 192))
+    _dev_tensor(k_new, "k_new", torch.bfloat16, (B, Hkv, n, 192))
+    _dev_tensor(v_new, "v_new", torch.bfloat16, (B, Hkv, n, 128))
+    _dev_tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    if layout == KV_RING:
+        _dev_tensor(k_cache, "k_cache", cdt, (B, Hkv, window, 192))
+        _dev_tensor(v_cache, "v_cache", cdt, (B, Hkv, window, 128))
+        desc = KVDesc(KV_RING, k_cache.data_ptr(), v_cache.data_ptr(), None, 0, 0, 0)
+    else:
+        P, _, ps, _ = k_cache.shape
+        _dev_tensor(k_cache, "k_cache", cdt, (P, Hkv, ps, 192))
+        _dev_tensor(v_cache, "v_cache", cdt, (P, Hkv, ps, 128))
+        _dev_tensor(block_table, "block_table", torch.int32, (B, block_table.shape[1]))
+        desc = KVDesc(KV_PAGED, k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), ps,
+                      block_table.shape[1], P)
+    for t in (q_out, k_new, v_new, seq_lens, k_cache, v_cache, block_table):
+        if t is not None and t.device != q_in.device:
+            raise ValueError("all tensors must be on one device")
+    d = Dims(B, 0, Hq, Hkv, 192, 128, 192 ** -0.5)
+    with torch.cuda.device(q_in.device):
+        rc = lib().sinkattn_decode_prologue(theta, window, ctypes.byref(d), n, _ptr(q_in), _ptr(q_out), _ptr(k_new),
+                                            _ptr(v_new), ctypes.byref(desc), 1 if kv_fp8 else 0, k_scale, v_scale,
+                                            _ptr(seq_lens), _stream_ptr(stream, q_in.device))
     _raise(rc)
 
 

@@ -482,9 +482,13 @@ int sinkattn_rope(double theta, int32_t batch, int32_t heads, int32_t rows, void
     return launch_rope(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 
-int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t hkv, int32_t n_new,
-                       const void *k_new, const void *v_new, const int32_t *seq_lens, int kv_fp8, float k_scale,
-                       float v_scale, void *stream) {
+}  // extern "C"
+
+namespace {
+// Checks of a cache write (shared by the append and the fused prologue) and its parameters.
+int append_params(const sinkattn_kv *kv, int window, int32_t batch, int32_t hkv, int32_t n_new, const void *k_new,
+                  const void *v_new, const int32_t *seq_lens, int kv_fp8, float k_scale, float v_scale,
+                  AppendParams &p) {
     if (!kv) return SINKATTN_E_NULL;
     if (kv->layout != SINKATTN_KV_RING && kv->layout != SINKATTN_KV_PAGED) return SINKATTN_E_UNSUPPORTED;
     if (batch < 0 || hkv < 1 || n_new < 0 || batch > 65535) return SINKATTN_E_SHAPE;
@@ -493,13 +497,13 @@ int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t
         return SINKATTN_E_SHAPE;
     if (kv_fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)))
         return SINKATTN_E_SHAPE;
-    if (batch == 0 || n_new == 0) return SINKATTN_OK;
+    if (batch == 0 || n_new == 0) return -1;  // nothing to do (not an error)
     if (!kv->k || !kv->v || !k_new || !v_new || !seq_lens) return SINKATTN_E_NULL;
     if (kv->layout == SINKATTN_KV_PAGED && !kv->block_table) return SINKATTN_E_NULL;
     if (misaligned(kv->k) || misaligned(kv->v) || misaligned(k_new) || misaligned(v_new) || misaligned(seq_lens) ||
         (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
         return SINKATTN_E_ALIGN;
-    AppendParams p{};
+    p = AppendParams{};
     p.k_new = static_cast<const uint16_t *>(k_new);
     p.v_new = static_cast<const uint16_t *>(v_new);
     // the descriptor is shared with decode, which only reads; appending writes the cache
@@ -520,7 +524,39 @@ int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t
     p.fp8 = kv_fp8 ? 1 : 0;
     p.k_scale = kv_fp8 ? k_scale : 1.f;
     p.v_scale = kv_fp8 ? v_scale : 1.f;
+    return SINKATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t hkv, int32_t n_new,
+                       const void *k_new, const void *v_new, const int32_t *seq_lens, int kv_fp8, float k_scale,
+                       float v_scale, void *stream) {
+    AppendParams p;
+    const int st = append_params(kv, window, batch, hkv, n_new, k_new, v_new, seq_lens, kv_fp8, k_scale, v_scale, p);
+    if (st) return st < 0 ? SINKATTN_OK : st;
     return launch_kv_append(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+int sinkattn_decode_prologue(double theta, int window, const sinkattn_dims *d, int32_t n_new, const void *q_in,
+                             void *q_out, const void *k_new, const void *v_new, const sinkattn_kv *kv, int kv_fp8,
+                             float k_scale, float v_scale, const int32_t *seq_lens, void *stream) {
+    if (!d) return SINKATTN_E_NULL;
+    if (d->d_qk != kDqkSupported || d->d_v != kDvSupported) return SINKATTN_E_UNSUPPORTED;
+    if (d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv || d->hkv > 65535) return SINKATTN_E_SHAPE;
+    if (!(theta > 0.0) || !isfinite(theta)) return SINKATTN_E_SHAPE;
+    PrologueParams pp{};
+    const int st =
+        append_params(kv, window, d->batch, d->hkv, n_new, k_new, v_new, seq_lens, kv_fp8, k_scale, v_scale, pp.a);
+    if (st) return st < 0 ? SINKATTN_OK : st;
+    if (!q_in || !q_out) return SINKATTN_E_NULL;
+    if (misaligned(q_in) || misaligned(q_out)) return SINKATTN_E_ALIGN;
+    pp.q_in = static_cast<const uint16_t *>(q_in);
+    pp.q_out = static_cast<uint16_t *>(q_out);
+    pp.hq = d->hq;
+    for (int i = 0; i < 32; ++i) pp.inv_freq[i] = pow(theta, -2.0 * i / 64.0);
+    return launch_decode_prologue(pp, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 
 int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,

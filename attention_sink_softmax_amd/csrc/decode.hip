@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     bf16x8 kreg[2][6];  // single-slice path: this wave's K operands
     // Issue the 20 loads of slice i (of this wave): K and V direct to LDS at `dst` (single-
     // slice path: K into kreg, V to `dst`).
-    auto issue = [&](int i, char *dst) {
+    auto issue = [&](int i, char *dst) __attribute__((always_inline)) {
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
         char *kb = dst;
         char *vb = kSingle ? dst : kb + kKBytes;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     }
 
     // Slice i: put slice i+1 in flight into `nxt`, wait for slice i, compute it from `cur`.
-    auto step = [&](int i, const char *cur, char *nxt) {
+    auto step = [&](int i, const char *cur, char *nxt) __attribute__((always_inline)) {
         if (i + 1 < nmine) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of `nxt` are done
             issue(i + 1, nxt);

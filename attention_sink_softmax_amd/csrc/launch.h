@@ -67,6 +67,16 @@ struct AppendParams {
     float k_scale, v_scale;  // fp8: codes of value / scale
 };
 
+// The decode prologue fused: RoPE of q (into q_out) and of the new keys, and the cache write.
+struct PrologueParams {
+    AppendParams a;          // the new keys and values and the cache they go to
+    const uint16_t *q_in;    // [batch][hq][n_new][kDqk]
+    uint16_t *q_out;         // the same shape; may be q_in (rotated in place)
+    int hq;
+    double inv_freq[32];     // theta^(-2i/64)
+};
+int launch_decode_prologue(const PrologueParams &p, hipStream_t stream);
+
 // Backward of prefill (q, k, v, out, dout bf16; lse, delta, gradients float32).
 struct BwdParams {
     const uint16_t *q, *k, *v, *out, *dout;

@@ -13,31 +13,63 @@ namespace {
 
 constexpr int kRopeDims = 64;            // rotated leading dimensions of the 192
 constexpr int kRopePairs = kRopeDims / 2;
-constexpr int kRopeRowsPerBlock = 8;     // 8 rows x 32 pairs = 256 threads
 constexpr double kTwoPi = 6.283185307179586;
 
-// One thread per (sequence, row, pair i); it turns dimensions i and i + 32 of that row in
-// every head by pos * theta^(-2i/64).  The angle is formed and reduced to [-pi, pi] in double
-// precision (a position near 262144 times a frequency near 1 would lose about 0.02 rad in
-// float), then its sine and cosine are taken in float.
+// cos and sin of pos * theta^(-2i/64) for the 32 pairs, into LDS (threads 0..31).  The angle
+// is formed and reduced to [-pi, pi] in double precision (a position near 262144 times a
+// frequency near 1 would lose about 0.02 rad in float), then its sine and cosine are taken
+// in float.
+__device__ __forceinline__ void rope_angles(const double *inv_freq, int pos, float *cs, float *sn) {
+    const int i = threadIdx.x;
+    if (i < kRopePairs) {
+        double ang = (double)pos * inv_freq[i];
+        ang -= kTwoPi * __builtin_rint(ang / kTwoPi);
+        sincosf((float)ang, &sn[i], &cs[i]);
+    }
+}
+
+// Rotation task c (0..3) of one 192-wide row: dimensions 8c .. 8c+7 turn with 32 + 8c ..
+// 32 + 8c + 7 (pairs i = 8c + e), two 16-byte loads and two 16-byte stores; results rounded
+// to bf16 (nearest even).  src and dst may be the same row.
+__device__ __forceinline__ void rope_task(const uint16_t *src, uint16_t *dst, int c, const float *cs, const float *sn,
+                                          u32x4 &lo_out, u32x4 &hi_out) {
+    const u32x4 lo = ldg16(src + 8 * c), hi = ldg16(src + kRopePairs + 8 * c);
+    uint32_t rl[4], rh[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float ro[2], rp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 8 * c + 2 * w + h;
+            const float a = __builtin_bit_cast(float, h ? (lo[w] & 0xffff0000u) : (lo[w] << 16));
+            const float b = __builtin_bit_cast(float, h ? (hi[w] & 0xffff0000u) : (hi[w] << 16));
+            ro[h] = a * cs[i] - b * sn[i];
+            rp[h] = b * cs[i] + a * sn[i];
+        }
+        rl[w] = pack_bf16x2(ro[0], ro[1]);
+        rh[w] = pack_bf16x2(rp[0], rp[1]);
+    }
+    lo_out = u32x4{rl[0], rl[1], rl[2], rl[3]};
+    hi_out = u32x4{rh[0], rh[1], rh[2], rh[3]};
+    if (dst) {
+        *reinterpret_cast<u32x4 *>(dst + 8 * c) = lo_out;
+        *reinterpret_cast<u32x4 *>(dst + kRopePairs + 8 * c) = hi_out;
+    }
+}
+
+// One workgroup per (sequence, row): the row's 32 angles once, then one thread per (head,
+// rotation task): 16-byte loads and stores.  The 128 trailing dimensions are not touched.
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
-    const int i = threadIdx.x & (kRopePairs - 1);
-    const int r = blockIdx.x * kRopeRowsPerBlock + (threadIdx.x >> 5);
-    const int b = blockIdx.y;
-    if (r >= p.rows) return;
+    __shared__ float cs[kRopePairs], sn[kRopePairs];
+    const int r = blockIdx.x, b = blockIdx.y;
     const int pos = (p.seq_lens ? p.seq_lens[b] - p.rows : p.pos0) + r;
-    double ang = (double)pos * p.inv_freq[i];
-    ang -= kTwoPi * __builtin_rint(ang / kTwoPi);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
-    uint16_t *x = p.x + (((size_t)b * p.heads) * p.rows + r) * kDqk;
-    const size_t head_stride = (size_t)p.rows * kDqk;
-    for (int h = 0; h < p.heads; ++h, x += head_stride) {
-        const float a = __builtin_bit_cast(float, (uint32_t)x[i] << 16);
-        const float c = __builtin_bit_cast(float, (uint32_t)x[i + kRopePairs] << 16);
-        const uint32_t pk = pack_bf16x2(a * cs - c * sn, c * cs + a * sn);
-        x[i] = (uint16_t)(pk & 0xffffu);
-        x[i + kRopePairs] = (uint16_t)(pk >> 16);
+    rope_angles(p.inv_freq, pos, cs, sn);
+    __syncthreads();
+    for (int task = threadIdx.x; task < p.heads * 4; task += blockDim.x) {
+        const int h = task >> 2, c = task & 3;
+        uint16_t *x = p.x + (((size_t)b * p.heads + h) * p.rows + r) * kDqk;
+        u32x4 lo, hi;
+        rope_task(x, x, c, cs, sn, lo, hi);
     }
 }
 
@@ -98,12 +130,103 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     }
 }
 
+// Cache row (in units of one key, for KV head 0) of position pos of sequence b with n tokens,
+// or -1 when the position is not written: before the sequence, overwritten in a ring by a
+// later token of the same call, or a page id outside the pool.
+__device__ __forceinline__ int64_t cache_row(const AppendParams &p, int b, int n, int pos) {
+    if (pos < 0) return -1;
+    if (!p.paged) {
+        if (pos < n - p.window) return -1;
+        return ((int64_t)b * p.hkv) * p.window + pos % p.window;
+    }
+    if (pos / p.page_size >= p.max_pages) return -1;
+    const int page = p.block_table[(size_t)b * p.max_pages + pos / p.page_size];
+    if (page < 0 || page >= p.num_pages) return -1;
+    return ((int64_t)page * p.hkv) * p.page_size + pos % p.page_size;
+}
+
+// 16 bytes of bf16 (8 elements) into the cache at element offset `elem`, as bf16 or as E4M3
+// codes of value / scale.
+__device__ __forceinline__ void cache_store(const AppendParams &p, bool isk, size_t elem, u32x4 v) {
+    if (p.fp8) {
+        uint8_t *dst = (isk ? p.k_cache8 : p.v_cache8) + elem;
+        *reinterpret_cast<u32x2 *>(dst) = bf16x8_to_e4m3(v, isk ? p.k_scale : p.v_scale);
+    } else {
+        *reinterpret_cast<u32x4 *>((isk ? p.k_cache : p.v_cache) + elem) = v;
+    }
+}
+
+// The decode prologue in one pass ("MiMo-V2-Flash 模型架构深度拆解", CH 10.3 forward steps 3-6):
+// one workgroup per (sequence, new token, KV head) computes the token's 32 rotary angles,
+// then rotates the rows of the KV head's query heads into q_out, rotates the new key row and
+// writes it with the value row into the cache (bf16 or E4M3), all in 16-byte pieces: at one
+// new token and 8 query heads per KV head that is one piece per thread.  The rotated keys are
+// rounded to bf16 before an 8-bit cache encodes them, as a separate rotation and append would.
+__global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueParams pp) {
+    __shared__ float cs[kRopePairs], sn[kRopePairs];
+    const AppendParams &p = pp.a;
+    const int t = blockIdx.x, b = blockIdx.y, g = blockIdx.z;
+    const int G = pp.hq / p.hkv;
+    const int n = p.seq_lens[b];
+    const int pos = n - p.n_new + t;
+    rope_angles(pp.inv_freq, pos, cs, sn);
+    const int64_t row = cache_row(p, b, n, pos);
+    const size_t head_rows = p.paged ? (size_t)p.page_size : (size_t)p.window;
+    __syncthreads();
+    constexpr int kCopy = (kDqk - kRopeDims) / 8;  // 16 plain 16-byte pieces of a q or k row
+    const bool q_copy = pp.q_out != pp.q_in;
+    const int nq = G * (4 + (q_copy ? kCopy : 0));  // tasks: this KV head's query rows
+    const int nk = 4 + kCopy;                       // its rotated key row
+    const int nv = kDv / 8;                         // its value row
+    const int total = nq + (row >= 0 ? nk + nv : 0);
+    for (int task = threadIdx.x; task < total; task += blockDim.x) {
+        if (task < nq) {
+            const int per = 4 + (q_copy ? kCopy : 0);
+            const int h = g * G + task / per, c = task % per;
+            const size_t off = (((size_t)b * pp.hq + h) * p.n_new + t) * kDqk;
+            if (c < 4) {
+                u32x4 lo, hi;
+                rope_task(pp.q_in + off, pp.q_out + off, c, cs, sn, lo, hi);
+            } else {
+                const int e = kRopeDims + 8 * (c - 4);
+                *reinterpret_cast<u32x4 *>(pp.q_out + off + e) = ldg16(pp.q_in + off + e);
+            }
+        } else if (task < nq + nk) {
+            const int h = g, c = task - nq;
+            const uint16_t *src = p.k_new + (((size_t)b * p.hkv + h) * p.n_new + t) * kDqk;
+            const size_t dst = ((size_t)row + h * head_rows) * kDqk;
+            if (c < 4) {
+                u32x4 lo, hi;
+                rope_task(src, nullptr, c, cs, sn, lo, hi);
+                cache_store(p, true, dst + 8 * c, lo);
+                cache_store(p, true, dst + kRopePairs + 8 * c, hi);
+            } else {
+                const int e = kRopeDims + 8 * (c - 4);
+                cache_store(p, true, dst + e, ldg16(src + e));
+            }
+        } else {
+            const int h = g, c = task - nq - nk;
+            const uint16_t *src = p.v_new + (((size_t)b * p.hkv + h) * p.n_new + t) * kDv;
+            cache_store(p, false, ((size_t)row + h * head_rows) * kDv + 8 * c, ldg16(src + 8 * c));
+        }
+    }
+}
+
 }  // namespace
+
+int launch_decode_prologue(const PrologueParams &prm, hipStream_t stream) {
+    PrologueParams p = prm;
+    void *args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&decode_prologue_kernel),
+                           dim3(p.a.n_new, p.a.batch, p.a.hkv), dim3(256), args, 0, stream) == hipSuccess
+               ? 0
+               : -1;
+}
 
 int launch_rope(const RopeParams &prm, hipStream_t stream) {
     RopeParams p = prm;
     void *args[] = {&p};
-    const dim3 grid((p.rows + kRopeRowsPerBlock - 1) / kRopeRowsPerBlock, p.batch);
+    const dim3 grid(p.rows, p.batch);
     return hipLaunchKernel(reinterpret_cast<const void *>(&rope_kernel), grid, dim3(256), args, 0, stream) ==
                    hipSuccess
                ? 0

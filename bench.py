@@ -82,8 +82,8 @@ def pairs_prefill(L, mode, W):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of workloads to run (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -192,6 +192,46 @@ def main() -> int:
                                      bt)
 
         runs[w.name] = (call, flops, nbytes)
+
+    # --- whole decode steps: the fused prologue (RoPE of q and the new key, cache write) then the
+    # attention, on the sliding-window rings (4 input sets rotate) and on the 256K pages
+    for w, name in ((inputs.SWA_DECODE, "swa_decode_step_B128_ring"), (inputs.GA_DECODE, "ga_decode_step_B8_256K_paged")):
+        if only and name not in only:
+            continue
+        nsets = 4 if w.layout == "ring" else 1
+        sets = []
+        for r in range(nsets):
+            if w.layout == "ring":
+                d = inputs.decode_ring_inputs(w, seed=w.seed * 100 + r)
+            else:
+                d = inputs.decode_paged_inputs(w)
+            ss = w.seed * 1000 + r
+            sets.append(dict(q=up(d["q"]).unsqueeze(2), k=up(d["k"]), v=up(d["v"]),
+                             kn=up(inputs.normal((w.batch, w.hkv, 1, w.d_qk), ss, 3)),
+                             vn=up(inputs.normal((w.batch, w.hkv, 1, w.d_v), ss, 4)),
+                             bt=torch.from_numpy(d["block_table"]).to(dev) if w.layout == "paged" else None,
+                             lens=torch.from_numpy(d["seq_lens"]).to(dev), sink=torch.from_numpy(d["sink"]).to(dev)))
+            del d
+        qr = torch.empty_like(sets[0]["q"])
+        out = torch.empty((w.batch, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
+        ws = sa.decode_workspace(w.mode, w.window, w.batch, w.hq, w.hkv, w.ctx_hi, dev)
+        layout = sa.KV_RING if w.layout == "ring" else sa.KV_PAGED
+        theta = sa.SWA_ROPE_THETA if w.mode == 1 else sa.GA_ROPE_THETA
+        visible = w.batch * (w.window if w.mode == 1 else w.ctx_hi)
+        flops = visible * w.hq * FLOP_PER_PAIR
+        # the attention's K/V bytes plus the prologue's: q read and written, k/v read, the row written
+        nbytes = visible * w.hkv * (w.d_qk + w.d_v) * 2 + w.batch * (2 * w.hq * w.d_qk + 2 * w.hkv * (w.d_qk + w.d_v)) * 2
+        state = {"i": 0}
+
+        def call(w=w, sets=sets, qr=qr, out=out, ws=ws, layout=layout, theta=theta, state=state):
+            s = sets[state["i"] % len(sets)]
+            state["i"] += 1
+            sa.sinkattn_decode_prologue(theta, layout, s["q"], qr, s["kn"], s["vn"], s["k"], s["v"], s["lens"],
+                                        window=w.window, block_table=s["bt"])
+            sa.sinkattn_decode(w.mode, w.window, qr[:, :, 0], layout, s["k"], s["v"], s["lens"], w.ctx_hi, s["sink"],
+                               out, ws, s["bt"])
+
+        runs[name] = (call, flops, nbytes)
 
     # --- sliding-window verify: the B = 128 rings with 4 drafted tokens per sequence whose keys
     # and values are held beside the rings (the rings are only read); 4 input sets rotate
@@ -319,18 +359,20 @@ def main() -> int:
     for n in names:
         ms = [a.elapsed_time(b) for a, b in ev[n]]
         avg = float(np.mean(ms))
+        med = float(np.median(ms))
         _, flops, nbytes = runs[n]
-        comp[n] = {"ms_avg": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
+        # rates from the median call (a long kernel's median and mean agree within drift)
+        comp[n] = {"ms_median": round(med, 5), "ms_avg": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
                    "ms_max": round(float(np.max(ms)), 5),
-                   "tflops": round(flops / (avg * 1e-3) / 1e12, 3),
-                   "gbps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                   "tflops": round(flops / (med * 1e-3) / 1e12, 3),
+                   "gbps": round(nbytes / (med * 1e-3) / 1e9, 1),
                    "algorithmic_gflop": round(flops / 1e9, 3), "algorithmic_gb": round(nbytes / 1e9, 4)}
 
     pre = [n for n in ("swa_prefill_L32768", "ga_prefill_L32768") if n in comp]
     value = None
     if pre:
         fl = sum(runs[n][1] for n in pre)
-        t = sum(comp[n]["ms_avg"] for n in pre) * 1e-3
+        t = sum(comp[n]["ms_median"] for n in pre) * 1e-3
         value = round(fl / t / 1e12, 3)
     dec = comp.get("ga_decode_B8_256K_paged")
 
@@ -382,6 +424,11 @@ def main() -> int:
                    "swa_decode": "B=128 ctx~U[4096,65536] 128-slot ring Hq=64 Hkv=8",
                    "ga_decode": "B=8 ctx=262144 64-token pages, permuted table, Hq=64 Hkv=4",
                    "ga_verify": "as ga_decode with q_len=4 new tokens per sequence",
+                   "swa_verify": "as swa_decode with q_len=4 drafted tokens whose K/V are held beside the rings",
+                   "prefill_chunk": "the 32K prefills' last 16384 positions after a 16384-token prefix in 64-token "
+                                    "permuted pages (GA) or a 128-slot ring (SWA)",
+                   "decode_step": "fused prologue (RoPE of q and the new key, cache write) + attention, on "
+                                  "swa_decode and ga_decode",
                    "ga_decode_fp8": "as ga_decode with an E4M3 cache, per-tensor scales 2^-6"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode,
@@ -411,33 +458,67 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
 
 
 def cpu_baseline():
-    """The CPU oracle (fp64, OpenMP) on a fixed sample of both prefill workloads: all 64 heads
-    at 16384 seeded positions of the sliding workload and 1024 seeded positions of the global
-    one (about 0.75 TFLOP of algorithmic work, 10-20 s on 16 host cores)."""
+    """The CPU oracle (fp64 plain loops, OpenMP over output rows) timed on the host cores, on
+    each workload's own inputs (seeded as the GPU's):
+      tiny_swa_L512, swa_prefill_L32768, swa_decode_B128_ring and ga_decode_B8_256K_paged over
+      their whole output;
+      ga_prefill_L32768 on the fixed sample its parity test checks (every head at the first
+      128, the last 128 and 256 seeded positions, 0.34 TFLOP), with the whole call's time
+      extrapolated by the ratio of (query head, key) pairs and labelled as such.
+    One run each, about 15 s in all on 16 host cores.  Rates are algorithmic flops (640 per
+    pair) over the oracle's wall time."""
     import oracle
     from attention_sink_softmax_amd import inputs
 
-    total_flops, total_t = 0, 0.0
-    parts = []
-    for w, npos in ((inputs.SWA_PREFILL, 16384), (inputs.GA_PREFILL, 1024)):
-        d = inputs.prefill_inputs(w)
-        rng = np.random.default_rng([w.seed, 123])
-        pos = np.sort(rng.choice(w.seqlen, size=npos, replace=False))
-        rows = np.array([(0, h, i) for h in range(w.hq) for i in pos], np.int64)
-        fl = sum(min(i + 1, w.window) if w.mode == 1 else i + 1 for i in pos) * w.hq * FLOP_PER_PAIR
-        oracle.load()
+    oracle.load()
+    threads = oracle.threads()
+    out = {}
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.prefill(d["q"], d["k"], d["v"], d["sink"], w.mode, w.window, w.scale, rows=rows)
-        dt = time.perf_counter() - t0
-        total_flops += fl
-        total_t += dt
-        parts.append(f"{w.name}: {w.hq} heads x {npos} positions, {fl / 1e9:.1f} GFLOP in {dt:.2f} s")
+        fn()
+        return time.perf_counter() - t0
+
+    for w in (inputs.TINY, inputs.SWA_PREFILL):
+        d = inputs.prefill_inputs(w)
+        dt = timed(lambda: oracle.prefill(d["q"], d["k"], d["v"], d["sink"], w.mode, w.window, w.scale))
+        fl = pairs_prefill(w.seqlen, w.mode, w.window) * w.hq * w.batch * FLOP_PER_PAIR
+        out[w.name] = {"s": round(dt, 3), "gflops": round(fl / dt / 1e9, 2), "sample": "whole output"}
+        del d
+    w = inputs.GA_PREFILL
+    d = inputs.prefill_inputs(w)
+    rows = inputs.ga_parity_rows(w)
+    dt = timed(lambda: oracle.prefill(d["q"], d["k"], d["v"], d["sink"], w.mode, w.window, w.scale, rows=rows))
+    pairs = int(np.sum(rows[:, 2] + 1))
+    full = pairs_prefill(w.seqlen, w.mode, w.window) * w.hq
+    out[w.name] = {"s": round(dt, 3), "gflops": round(pairs * FLOP_PER_PAIR / dt / 1e9, 2),
+                   "sample": f"{len(rows)} rows (every head x 512 positions), {pairs / full:.4f} of the pairs",
+                   "extrapolated_full_s": round(dt * full / pairs, 1)}
+    del d
+    w = inputs.SWA_DECODE
+    d = inputs.decode_ring_inputs(w, seed=w.seed * 100)
+    dt = timed(lambda: oracle.decode(d["q"], d["k"], d["v"], d["seq_lens"], d["sink"], w.mode, w.window, w.scale,
+                                     oracle.RING))
+    fl = w.batch * w.window * w.hq * FLOP_PER_PAIR
+    out[w.name] = {"s": round(dt, 4), "gflops": round(fl / dt / 1e9, 2), "sample": "whole output"}
+    w = inputs.GA_DECODE
+    d = inputs.decode_paged_inputs(w)
+    dt = timed(lambda: oracle.decode(d["q"], d["k"], d["v"], d["seq_lens"], d["sink"], w.mode, w.window, w.scale,
+                                     oracle.PAGED, d["block_table"]))
+    fl = w.batch * w.ctx_hi * w.hq * FLOP_PER_PAIR
+    out[w.name] = {"s": round(dt, 3), "gflops": round(fl / dt / 1e9, 2), "sample": "whole output"}
+    del d
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": round(total_flops / total_t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "host_cores_visible": cores, "kind": "oracle", "sample": "; ".join(parts)}
+    tot_fl = sum(v["gflops"] * v["s"] for v in out.values())
+    tot_s = sum(v["s"] for v in out.values())
+    return {"value": round(tot_fl / tot_s / 1e3, 6), "unit": "TFLOP/s", "cores": threads, "host_cores_visible": cores,
+            "kind": "oracle",
+            "sample": "tiny, SWA prefill 32K, SWA decode B=128 and GA decode 8x256K over their whole output; GA "
+                      "prefill 32K on 64 heads x 512 positions (its full time extrapolated by the pair ratio)",
+            "configs": out}
 
 
 if __name__ == "__main__":

@@ -394,6 +394,28 @@ int sinkattn_kv_append(const sinkattn_kv *kv, int window, int32_t batch, int32_t
                        float k_scale, float v_scale, void *stream);
 
 /*
+ * The steps before decode attention in one kernel ("MiMo-V2-Flash 模型架构深度拆解", CH 10.3
+ * forward steps 3-6): the partial RoPE of the new tokens' queries and keys (as sinkattn_rope,
+ * at positions seq_lens[b] - n_new + t) and the cache write of the rotated keys and the values
+ * (as sinkattn_kv_append), reading each input once.  The results are bit-identical to
+ * sinkattn_rope on q, sinkattn_rope on k_new and sinkattn_kv_append in turn (the rotated keys
+ * are rounded to bf16 before an 8-bit cache encodes them), except that k_new is not modified.
+ *   theta        10 000 (sliding-window layers) or 5 000 000 (global layers); > 0, finite
+ *   window       ring slots (RING caches)
+ *   d            batch, hq, hkv (d_qk = 192, d_v = 128; seqlen and scale are not read)
+ *   n_new        new tokens per sequence
+ *   q_in         bf16 [batch][hq][n_new][192]: the new queries before rotation
+ *   q_out        bf16 [batch][hq][n_new][192]: written, rotated; may be q_in (in place)
+ *   k_new, v_new bf16 [batch][hkv][n_new][192 / 128]: the new keys (before rotation), values
+ *   kv, kv_fp8, k_scale, v_scale, seq_lens  as sinkattn_kv_append
+ * Then call the decode entry point on q_out.  Errors as sinkattn_rope and sinkattn_kv_append.
+ */
+int sinkattn_decode_prologue(double theta, int window, const sinkattn_dims *d, int32_t n_new,
+                             const void *q_in, void *q_out, const void *k_new, const void *v_new,
+                             const sinkattn_kv *kv, int kv_fp8, float k_scale, float v_scale,
+                             const int32_t *seq_lens, void *stream);
+
+/*
  * Decode with every option: q_len new tokens (as sinkattn_decode_multi), a bf16 cache
  * (kv_fp8 = 0; k_scale and v_scale ignored) or an E4M3 cache (kv_fp8 = 1, as
  * sinkattn_decode_fp8), and an epilogue (lse: float32 [batch][hq][q_len]).  Errors as those

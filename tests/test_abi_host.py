@@ -335,3 +335,21 @@ def test_prefill_cached_workspace_size(L):
     rows = 16384 + 127
     assert sa.sinkattn_prefill_cached_workspace_bytes(1, 128, 1, 16384, 64, 8, 32768) == \
         8 * rows * (384 + 256) + 8 * 128 * ((rows + 63) // 64 * 64) * 2
+
+
+def test_decode_prologue_argument_errors(L):
+    def pro(theta=1e4, d=None, n=1, q_in=A, q_out=A, desc=None, fp8=0, ks=1.0, window=128):
+        d = d or dims(B=2, hq=64, hkv=8)
+        desc = desc if desc is not None else kv(layout=0, bt=None)
+        return L.sinkattn_decode_prologue(theta, window, ctypes.byref(d), n, q_in, q_out, A, A, ctypes.byref(desc),
+                                          fp8, ks, 1.0, A, None)
+    assert L.sinkattn_decode_prologue(1e4, 128, None, 1, A, A, A, A, None, 0, 1.0, 1.0, A, None) == E_NULL
+    assert pro(theta=0.0) == E_SHAPE
+    assert pro(theta=float("nan")) == E_SHAPE
+    assert pro(d=dims(B=2, hq=64, hkv=8, dqk=128)) == E_UNSUP
+    assert pro(d=dims(B=2, hq=60, hkv=8)) == E_SHAPE
+    assert pro(window=0) == E_SHAPE
+    assert pro(fp8=1, ks=0.0) == E_SHAPE
+    assert pro(q_in=None) == E_NULL
+    assert pro(q_out=A + 8) == E_ALIGN
+    assert pro(n=0, q_in=None) == OK

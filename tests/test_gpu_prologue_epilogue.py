@@ -138,10 +138,12 @@ def test_decode_epilogue(fp8, q_len, long):
     check_lse(lse.cpu().numpy(), ref_lse, f"decode fp8={fp8} long={long}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_decode_step_chain(fp8):
+def test_decode_step_chain(fp8, fused):
     """One decode step of 2 new tokens on 256 + 2 positions: RoPE on q and the new keys, append
-    into pages, attention with the value scale and lse -- against the oracle's chain."""
+    into pages (separate kernels, or the fused prologue), attention with the value scale and
+    lse -- against the oracle's chain."""
     B, Hq, Hkv, ps, n_old, n_new = 2, 16, 2, 32, 256, 2
     theta = sa.GA_ROPE_THETA
     ks = vs = 0.03
@@ -169,9 +171,14 @@ def test_decode_step_chain(fp8):
     tdev = (lambda a: torch.from_numpy(a).to("cuda")) if fp8 else dev_bf16
     kpd, vpd = tdev(kp), tdev(vp)
     qd, knd, vnd, lensd, btd = dev_bf16(q), dev_bf16(kn), dev_bf16(vn), dev_i32(lens), dev_i32(bt)
-    sa.sinkattn_rope(theta, qd, seq_lens=lensd)
-    sa.sinkattn_rope(theta, knd, seq_lens=lensd)
-    sa.sinkattn_kv_append(sa.KV_PAGED, kpd, vpd, knd, vnd, lensd, block_table=btd, kv_fp8=fp8, k_scale=ks, v_scale=vs)
+    if fused:
+        sa.sinkattn_decode_prologue(theta, sa.KV_PAGED, qd, qd, knd, vnd, kpd, vpd, lensd, block_table=btd, kv_fp8=fp8,
+                                    k_scale=ks, v_scale=vs)
+    else:
+        sa.sinkattn_rope(theta, qd, seq_lens=lensd)
+        sa.sinkattn_rope(theta, knd, seq_lens=lensd)
+        sa.sinkattn_kv_append(sa.KV_PAGED, kpd, vpd, knd, vnd, lensd, block_table=btd, kv_fp8=fp8, k_scale=ks,
+                              v_scale=vs)
     out = torch.empty((B, Hq, n_new, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, n_new), dtype=torch.float32, device="cuda")
     sa.sinkattn_decode_ex(oracle.GLOBAL, 0, n_new, qd, sa.KV_PAGED, kpd, vpd, lensd, L, dev_f32(sink), out, None, btd,
@@ -186,3 +193,56 @@ def test_decode_step_chain(fp8):
                                  kv_scales=(ks, vs) if fp8 else None, return_lse=True)
     assert_parity(host_f32(out), 0.707 * ref, f"decode step chain fp8={fp8}")
     check_lse(lse.cpu().numpy(), ref_lse, f"decode step chain fp8={fp8}")
+
+
+@pytest.mark.parametrize("layout,fp8", [(sa.KV_RING, False), (sa.KV_PAGED, False), (sa.KV_PAGED, True),
+                                        (sa.KV_RING, True)])
+@pytest.mark.parametrize("n_new,in_place", [(1, True), (4, False), (130, True)])
+def test_fused_prologue_is_separate_kernels(layout, fp8, n_new, in_place):
+    """The fused prologue gives, bit for bit, the rotated queries and the cache contents of
+    sinkattn_rope (q), sinkattn_rope (k) and sinkattn_kv_append in turn, and leaves k_new as it
+    was; rings (W = 128, a call longer than the ring) and pages, bf16 and E4M3."""
+    B, Hq, Hkv, W, ps = 3, 64, 8, 128, 64
+    theta = sa.SWA_ROPE_THETA if layout == sa.KV_RING else sa.GA_ROPE_THETA
+    lens = np.array([max(1, n_new - 2), 1000, 20000], np.int32)
+    q = inputs.normal((B, Hq, n_new, 192), 80 + n_new, 0)
+    kn = inputs.normal((B, Hkv, n_new, 192), 80 + n_new, 1)
+    vn = inputs.normal((B, Hkv, n_new, 128), 80 + n_new, 2)
+    cdt = np.uint8 if fp8 else np.uint16
+    rng = np.random.default_rng(81)
+    if layout == sa.KV_RING:
+        shape_k, shape_v, bt = (B, Hkv, W, 192), (B, Hkv, W, 128), None
+    else:
+        mp = (int(lens.max()) + ps - 1) // ps
+        npg = B * mp + 4
+        shape_k, shape_v = (npg, Hkv, ps, 192), (npg, Hkv, ps, 128)
+        bt = dev_i32(inputs.page_table(B, mp, npg, 82, True))
+    kc = rng.integers(0, 255, shape_k).astype(cdt)
+    vc = rng.integers(0, 255, shape_v).astype(cdt)
+
+    def dev_cache(c):
+        t = torch.from_numpy(c.view(np.int16) if not fp8 else c).to("cuda")
+        return t if fp8 else t.view(torch.bfloat16)
+
+    def raw(t):
+        return t.view(torch.uint8).cpu().numpy() if fp8 else host_bits(t)
+
+    kw = dict(window=W, block_table=bt, kv_fp8=fp8, k_scale=0.05 if fp8 else 1.0, v_scale=0.03 if fp8 else 1.0)
+    lensd = dev_i32(lens)
+    # separate kernels
+    qa, ka, va = dev_bf16(q), dev_bf16(kn), dev_bf16(vn)
+    kca, vca = dev_cache(kc), dev_cache(vc)
+    sa.sinkattn_rope(theta, qa, seq_lens=lensd)
+    sa.sinkattn_rope(theta, ka, seq_lens=lensd)
+    sa.sinkattn_kv_append(layout, kca, vca, ka, va, lensd, **kw)
+    # fused
+    qb, kb, vb = dev_bf16(q), dev_bf16(kn), dev_bf16(vn)
+    kcb, vcb = dev_cache(kc), dev_cache(vc)
+    qo = qb if in_place else torch.empty_like(qb)
+    sa.sinkattn_decode_prologue(theta, layout, qb, qo, kb, vb, kcb, vcb, lensd, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qo), host_bits(qa)), "rotated queries differ"
+    assert np.array_equal(raw(kcb), raw(kca)) and np.array_equal(raw(vcb), raw(vca)), "cache contents differ"
+    assert np.array_equal(host_bits(kb), kn), "k_new was modified"
+    if not in_place:
+        assert np.array_equal(host_bits(qb), q), "q_in was modified"
