@@ -635,131 +635,6 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
 }
 
-// ---- causal kernel, two heads per wave: four waves, one per SIMD, each owning two query
-// heads at the same 32 positions (the workgroup covers the same 8 heads x 32 positions as the
-// eight-wave kernel).  Every K and V^T fragment read from LDS feeds two MFMAs, one per head,
-// which halves the LDS reads per MFMA; with one wave per SIMD nothing else hides a stall, so
-// each phase of the pipeline below is laid out explicitly: the LDS operand reads run ahead
-// of the MFMAs that use them, and the softmax arithmetic of the other sub-block fills the
-// issue slots between MFMAs.  Phases, barriers and buffers as in the eight-wave kernel.
-constexpr int kPairWaves = 4;
-
-// Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile.
-__device__ __forceinline__ void dma_k_quarter(char *Kt, const TileSrc &src, int kb, int L, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) dma_k_block_opaque(Kt, src, kb, L, wave + kPairWaves * i, lane);
-}
-__device__ __forceinline__ void dma_vt_quarter(char *Vt, const TileSrc &src, int kb, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma_vt_block_opaque(Vt, src, kb, wave + kPairWaves * i, lane);
-}
-
-// Phase layouts (scheduling groups; the counts are upper bounds).  QK phase: 12 K fragment
-// reads, 24 MFMAs, the exps of the other sub-block.  PV phase: 8 V^T fragment reads, 16 MFMAs,
-// the row max of the other sub-block.
-__device__ __forceinline__ void sched_qk_phase() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    }
-}
-__device__ __forceinline__ void sched_pv_phase() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-}
-
-__global__ __launch_bounds__(64 * kPairWaves, 1) void prefill_causal_pair_kernel(PrefillParams p) {
-    constexpr int HPW = 2;
-    __shared__ __attribute__((aligned(1024))) char K0[kKTileBytes];
-    __shared__ __attribute__((aligned(1024))) char K1[kKTileBytes];
-    __shared__ __attribute__((aligned(1024))) char K2[kKTileBytes];
-    __shared__ __attribute__((aligned(1024))) char V0[kVTileBytes];
-    __shared__ __attribute__((aligned(1024))) char V1[kVTileBytes];
-    __shared__ __attribute__((aligned(1024))) char V2[kVTileBytes];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-    const WaveSetup ws = wave_setup<HPW>(p, wave);
-    if (!ws.valid) return;  // padding workgroup (uniform: before any barrier)
-    const WaveCtx w = make_ctx(p, ws, lane);
-
-    bf16x8 qf[HPW][12];
-    load_q<HPW>(p, ws, w, qf);
-    float m_run[HPW], l_run[HPW];
-    bool sink_inf[HPW];
-    f32x16 acc[HPW][4];
-    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
-
-    const TileSrc src = tile_src(p, ws.b, ws.kvh);
-    const int t1 = (ws.wg_q1 - 1) / kBN;  // tiles 0..t1
-
-    auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
-
-    issue_tile(K0, V0, src, 0, p.L, wave, lane);
-    if (t1 >= 1) issue_tile(K1, V1, src, kBN, p.L, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-
-    f32x16 s0[HPW], s1[HPW];
-    bf16x8 pf[HPW][2];
-    qk_scores<HPW>(K0, 0, qf, s0, w);
-    if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
-    row_update<HPW>(s0, acc, m_run, l_run, w);
-
-    // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf), loaded
-    // unconditionally (past the last tile they re-read tile t1 into a buffer nobody reads).
-    auto step = [&](int t, const char *Kc, const char *Kn, const char *Vc, char *Kf, char *Vf) {
-        const int kb = t * kBN;
-        const int kb_next = min(t + 2, t1) * kBN;
-        float mnew[HPW];
-        bool grow;
-        // phase A: S(t,1) with P(t,0)
-        qk_scores<HPW>(Kc, 1, qf, s1, w);
-        probs<HPW>(s0, m_run, l_run, pf, w);
-        sched_qk_phase();
-        if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
-        // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
-        pv_accum<HPW>(Vc, 0, pf, acc, w);
-        grow = row_max<HPW>(s1, m_run, mnew, w);
-        sched_pv_phase();
-        rescale<HPW>(grow, mnew, acc, m_run, l_run);
-        // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        // phase C: S(t+1,0) with P(t,1), after the K loads of tile t+2
-        dma_k_quarter(Kf, src, kb_next, p.L, wave, lane);
-        qk_scores<HPW>(Kn, 0, qf, s0, w);
-        probs<HPW>(s1, m_run, l_run, pf, w);
-        sched_qk_phase();
-        if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
-        // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0), after the V^T loads of tile t+2
-        dma_vt_quarter(Vf, src, kb_next, wave, lane);
-        pv_accum<HPW>(Vc, 1, pf, acc, w);
-        grow = row_max<HPW>(s0, m_run, mnew, w);
-        sched_pv_phase();
-        if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
-    };
-    for (int t = 0; t <= t1; t += 3) {
-        step(t, K0, K1, V0, K2, V2);
-        if (t + 1 <= t1) step(t + 1, K1, K2, V1, K0, V0);
-        if (t + 2 <= t1) step(t + 2, K2, K0, V2, K1, V1);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
-    store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
-}
-
 // ---- sliding-window ring kernel (window <= 128, group size a multiple of 8, whole-sequence
 // prefill).  A workgroup of 8 waves, one query head each, owns a run of consecutive 32-position
 // blocks of one (sequence, KV head, 8 heads).  The keys a block sees, [32j - W + 1, 32j + 31],
@@ -1014,7 +889,6 @@ int launch_gather_prefix(const GatherParams &g, hipStream_t stream) {
 
 namespace {
 bool causal_layout(const PrefillParams &p) { return !p.swa && p.hpw == 1 && p.hw == kCausalWaves; }
-bool causal_pair_layout(const PrefillParams &p) { return !p.swa && p.hpw == 2 && p.hw == 2 * kPairWaves; }
 // Compute units of the current device (256 on a whole MI355X, fewer on a partition); only the
 // length of the ring kernel's runs depends on it.
 int compute_units() {
@@ -1052,13 +926,8 @@ int64_t plan_prefill(PrefillParams &p) {
         return items;
     }
     if (!p.swa && p.G % kCausalWaves == 0) {
-#ifdef SINKATTN_CAUSAL_PAIR
-        p.hpw = 2;
-        p.hw = 2 * kPairWaves;
-#else
         p.hpw = 1;
         p.hw = kCausalWaves;
-#endif
         p.pw = 1;
     } else {
         p.hpw = (!p.swa && p.G % 2 == 0) ? 2 : 1;
@@ -1095,10 +964,6 @@ int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     if (causal_layout(p)) {
         return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_causal_kernel), dim3(grid),
                                dim3(64 * kCausalWaves), args, 0, stream) == hipSuccess ? 0 : -1;
-    }
-    if (causal_pair_layout(p)) {
-        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_causal_pair_kernel), dim3(grid),
-                               dim3(64 * kPairWaves), args, 0, stream) == hipSuccess ? 0 : -1;
     }
     const void *fn = p.hpw == 2 ? reinterpret_cast<const void *>(&prefill_kernel<2>)
                                 : reinterpret_cast<const void *>(&prefill_kernel<1>);
