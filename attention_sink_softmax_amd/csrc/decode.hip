@@ -196,9 +196,10 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     constexpr int kBufA = kSingle ? kVBytes + 256 : kSliceBytes;
     __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufA];
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y % p.Hkv, hc = blockIdx.y / p.Hkv;
-    const int b = blockIdx.z;
+    const int split = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+    const int by = p.reverse ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+    const int kvh = by % p.Hkv, hc = by / p.Hkv;
+    const int b = p.reverse ? gridDim.z - 1 - blockIdx.z : blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hl = lane & 15, q = lane >> 4;  // column within a block, k-group
     // E4M3 cache: lane part of the K operand address of k-step kk (key hl, chunk 2 kk + q / 2,
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 // dim t.  Merges the splits' partials and adds the sink term once.
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     __shared__ float red[128];
-    const size_t row = blockIdx.x;  // (b * Hq + h) * q_len + token
+    const size_t row = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;  // (b * Hq + h) * q_len + token
     const int tok = (int)(row % p.q_len);
     const int h = (int)((row / p.q_len) % p.Hq), b = (int)(row / ((size_t)p.q_len * p.Hq));
     const int t = threadIdx.x;
@@ -683,6 +684,7 @@ float *decode_scratch() {
 
 int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     DecodeParams p = prm;
+    p.reverse = grid_reversed();
     void *args[] = {&p};
     const dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B);
     // keys beside the cache take the general path (rows looked up one by one)

@@ -27,6 +27,7 @@ struct PrefillParams {
     int n_items;       // n_pbw * B * Hkv * hgroups
     int ring;          // 1: the sliding-window ring kernel (then n_items = workgroups)
     int chunk;         // ring kernel: 32-position blocks per workgroup
+    int reverse;       // 1: workgroups take their work items in reverse order (grid_reversed())
 };
 
 struct DecodeParams {
@@ -46,6 +47,7 @@ struct DecodeParams {
     float out_scale;   // multiplies the output (8-bit cache: times the V scale)
     float *lse;        // optional: natural-log log-sum-exp per row [B][Hq][q_len], or nullptr
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
+    int reverse;        // 1: workgroups take their work items in reverse order (grid_reversed())
 };
 
 // Partial rotary embedding of x [batch][heads][rows][kDqk] in place; row r of sequence b sits
@@ -110,6 +112,10 @@ size_t prefill_workspace_bytes(int B, int Hkv, int L);
 // launch (the caller rejects counts that do not fit a grid).
 int64_t plan_prefill(PrefillParams &p);
 int launch_prefill(const PrefillParams &p, hipStream_t stream);
+// Race check: with SINKATTN_GRID_ORDER=reversed in the environment the attention kernels map
+// workgroup ids to their work in reverse order, so work runs in a different order and next to
+// different neighbours; every output must come out bit-identical.  Read at each launch.
+int grid_reversed();
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 // The decode scratch array of this device (nullptr if its address cannot be found) and its size.
 float *decode_scratch();

@@ -43,6 +43,9 @@
 //     and band-edge sub-blocks take a masked path.
 //   * Workgroup ids are remapped so that the workgroups sharing one KV head and position
 //     block land on the same XCD (each XCD has its own L2), heaviest causal rows first.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -321,7 +324,7 @@ template <int HPW>
 __device__ __forceinline__ WaveSetup wave_setup(const PrefillParams &p, int wave) {
     WaveSetup ws;
     const int C = p.hgroups;
-    const int bid = blockIdx.x;
+    const int bid = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
     const int lam = (((slot / C) * 8 + xcd) * C) + slot % C;
     ws.valid = lam < p.n_items;
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
     // before q0 in that block are computed but not stored) to the last.
     const int nqb = (p.L + kBQ - 1) / kBQ, jb0 = p.q0 / kBQ;
     const int nchunk = (nqb - jb0 + p.chunk - 1) / p.chunk;
-    int u = blockIdx.x;
+    int u = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
     const int hg = u % p.hgroups;
     u /= p.hgroups;
     const int kvh = u % p.Hkv;
@@ -948,8 +951,14 @@ size_t prefill_workspace_bytes(int B, int Hkv, int L) {
     return (size_t)B * Hkv * kDv * lpad * 2;
 }
 
+int grid_reversed() {
+    const char *e = getenv("SINKATTN_GRID_ORDER");
+    return e && strcmp(e, "reversed") == 0;
+}
+
 int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     PrefillParams p = prm;
+    p.reverse = grid_reversed();
     if (!p.ring) {  // the ring kernel reads V rows directly
         void *targs[] = {(void *)&p.v, (void *)&p.vt, (void *)&p.L, (void *)&p.lpad};
         if (hipLaunchKernel(reinterpret_cast<const void *>(&transpose_v_kernel), dim3(p.lpad / kBN, p.B * p.Hkv),

@@ -19,6 +19,10 @@ OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 0, 1, 2, 3, 4, 5
 
 @pytest.fixture(scope="module")
 def L():
+    test_lib = os.environ.get("SINKATTN_TEST_LIB")  # a differently built library (the sanitizer run)
+    if test_lib:
+        sa._lib = sa.lib(test_lib)
+        return sa._lib
     if not os.path.exists(sa.LIB_PATH):
         from attention_sink_softmax_amd import build
         build.build()

@@ -1,0 +1,81 @@
+"""Race check: every attention kernel, run a second time with its workgroups taking their work
+in reverse order (SINKATTN_GRID_ORDER=reversed), so that the work runs in another order and
+next to other neighbours, must give bit-identical outputs; a race on LDS or on the split
+partials would show as a difference.  Small prefill and decode cases of every kernel path."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attention_sink_softmax_amd as sa
+from attention_sink_softmax_amd import inputs
+import oracle
+from gpu_util import assert_parity, dev_bf16, dev_f32, dev_i32, host_f32
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 192 ** -0.5
+
+
+def both_orders(fn):
+    os.environ.pop("SINKATTN_GRID_ORDER", None)
+    a = fn()
+    os.environ["SINKATTN_GRID_ORDER"] = "reversed"
+    try:
+        b = fn()
+    finally:
+        os.environ.pop("SINKATTN_GRID_ORDER", None)
+    return a, b
+
+
+@pytest.mark.parametrize("mode,W,Hq,Hkv,L", [(oracle.GLOBAL, 0, 64, 4, 700), (oracle.SWA, 128, 64, 8, 900),
+                                             (oracle.GLOBAL, 0, 8, 4, 333), (oracle.SWA, 100, 16, 2, 517)])
+def test_prefill_grid_order(mode, W, Hq, Hkv, L):
+    print(f"[case] grid order prefill mode={mode} W={W} Hq={Hq} Hkv={Hkv} L={L}", flush=True)
+    d = inputs.prefill_inputs(inputs.Workload("t", "prefill", mode, 2, Hq, Hkv, seqlen=L, seed=L + Hq))
+    q, k, v, s = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), dev_f32(d["sink"])
+
+    def run():
+        out = sa.prefill(mode, W, q, k, v, s)
+        torch.cuda.synchronize()
+        return host_f32(out)
+
+    a, b = both_orders(run)
+    assert np.array_equal(a, b), "prefill output depends on the workgroup order"
+    assert_parity(b, oracle.prefill(d["q"], d["k"], d["v"], d["sink"], mode, W, SCALE), "reversed order vs oracle")
+
+
+@pytest.mark.parametrize("layout,mode,W,q_len,L", [(sa.KV_RING, oracle.SWA, 128, 1, 3000),
+                                                   (sa.KV_PAGED, oracle.GLOBAL, 0, 1, 20000),
+                                                   (sa.KV_PAGED, oracle.GLOBAL, 0, 4, 9000),
+                                                   (sa.KV_PAGED, oracle.SWA, 128, 3, 5000)])
+def test_decode_grid_order(layout, mode, W, q_len, L):
+    print(f"[case] grid order decode layout={layout} mode={mode} q_len={q_len} L={L}", flush=True)
+    B, Hq, Hkv, ps = 4, 64, 4 if mode == oracle.GLOBAL else 8, 64
+    d = inputs.prefill_inputs(inputs.Workload("t", "prefill", mode, B, Hq, Hkv, seqlen=L, seed=q_len + L))
+    lens = np.array([L, L // 2, 77, L - 5], np.int32)
+    qm = np.stack([np.stack([d["q"][b, :, lens[b] - q_len + t] for t in range(q_len)], axis=1) for b in range(B)])
+    if layout == sa.KV_RING:
+        kc = np.zeros((B, Hkv, W, 192), np.uint16)
+        vc = np.zeros((B, Hkv, W, 128), np.uint16)
+        for b in range(B):
+            for j in range(max(0, lens[b] - W), lens[b]):
+                kc[b, :, j % W] = d["k"][b, :, j]
+                vc[b, :, j % W] = d["v"][b, :, j]
+        bt = None
+    else:
+        kc, vc, bt = inputs.pages_from_sequence(d["k"], d["v"], L, ps, B * (L // ps + 1) + 3, seed=L)
+    qd, kd, vd, ld, sd = dev_bf16(qm), dev_bf16(kc), dev_bf16(vc), dev_i32(lens), dev_f32(d["sink"])
+    btd = None if bt is None else dev_i32(bt)
+
+    def run():
+        out = sa.decode_multi(mode, W, qd, layout, kd, vd, ld, L, sd, btd)
+        torch.cuda.synchronize()
+        return host_f32(out)
+
+    a, b = both_orders(run)
+    assert np.array_equal(a, b), "decode output depends on the workgroup order"
+    ref = oracle.decode(qm, kc, vc, lens, d["sink"], mode, W, SCALE,
+                        oracle.RING if layout == sa.KV_RING else oracle.PAGED, bt)
+    assert_parity(b, ref, "reversed order vs oracle")
