@@ -43,16 +43,17 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
-                          "read_GB": 3.5705, "written_GB": 0.5369},
-    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"), "sha256": "5ce9dbb982e8b024c7cae4231c2cb8e10472f74f7b30483214aaea9adc2dc1ca",
-                           "read_GB": 1.0231, "written_GB": 0.5369},
+                          "sha256": "f2a9ba37b12732c51e470a422b21c038e7a34cb456b05fabb73ccafb2844186d",
+                          "read_GB": 3.5703, "written_GB": 0.5369},
+    "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
+                           "sha256": "f2a9ba37b12732c51e470a422b21c038e7a34cb456b05fabb73ccafb2844186d",
+                           "read_GB": 1.0230, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "1c44398e8d0164c249e6bf303dbb4c455231922391ffa01a175d1f33f9ae5809",
-                                "read_GB": 5.3880, "written_GB": 0.0179},
+                                "sha256": "9b34272b4c02ac5816aa1232302c94d05e971aea7d43fdc70a89a5346640e041",
+                                "read_GB": 5.3879, "written_GB": 0.0179},
     "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "1c44398e8d0164c249e6bf303dbb4c455231922391ffa01a175d1f33f9ae5809",
-                                    "read_GB": 2.7037, "written_GB": 0.0179},
+                                    "sha256": "9b34272b4c02ac5816aa1232302c94d05e971aea7d43fdc70a89a5346640e041",
+                                    "read_GB": 2.7036, "written_GB": 0.0179},
 }
 
 
