@@ -53,6 +53,45 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds, int vo
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// The same loads written as inline asm, for the tile loops.  The compiler does not see them,
+// so it adds no wait for them before reads of other LDS buffers (its own tracking of loads
+// into LDS loses the buffer across the loop and waits for the next tile's loads as well).
+// The kernels wait for these loads themselves (vmcnt) before each barrier.  m0 carries the
+// LDS address (one wait state before the load) and is restored for the compiler's use; the
+// asm has no register output, so no load in flight can land in a register.
+__device__ __forceinline__ void dma16_async(__amdgpu_buffer_rsrc_t r, char *lds, int voff, int soff) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r), "s"(soff)
+        : "memory");
+}
+__device__ __forceinline__ void dma4_async(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r), "s"(soff)
+        : "memory");
+}
+
+// Workgroup barrier over LDS: this wave's LDS writes are complete, then every wave meets.
+// The caller first waits for the loads into LDS that the next step reads (vmcnt); the
+// barrier itself does not wait for the others, which stay in flight across it.  (A
+// __syncthreads() fence would wait for every outstanding load.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr int kQT = 32;                    // query rows per tile
 constexpr int kKeysPerWave = 32;
 constexpr int kKeysPerWg = 4 * kKeysPerWave;  // bwd_dkdv
@@ -183,6 +222,15 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int nblk) {
 }
 
 // ---- dK and dV
+// One workgroup per 128 keys of a (sequence, KV head), eight waves.  Key group kg = wave % 4
+// owns keys kb0 + 32 kg .. +31, and its two waves split the products of every item (query
+// tile, head) between them:
+//   wave kg     (role P):  S = Q K^T, P = exp(scale S - LSE), dV += P^T dO;  P goes to LDS
+//   wave kg + 4 (role dS): dP = dO V^T, dS = P (dP - D),    dK += dS^T Q   (one item later)
+// Each role keeps half of the per-key state in registers (K and dV, or V and dK), so two
+// waves share a SIMD and one's products run while the other waits or does its softmax
+// arithmetic.  The P tile passes in float32, so the results are those of computing both
+// halves in one wave.
 // LDS tile of one query tile: Q [32][192] (12 KB = 12 blocks of 1 KB), dO [32][128] (8 blocks),
 // and the LSE and D of its rows (64 floats each: the 32 rows of the tile and 32 unused).
 constexpr int kDkQBytes = kQT * kDqk * 2, kDkOBytes = kQT * kDv * 2;
@@ -192,10 +240,13 @@ struct DkTile {
     float *lse, *d;
 };
 
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char qa[kDkQBytes], qb[kDkQBytes], qc[kDkQBytes];
-    __shared__ __attribute__((aligned(1024))) char oa[kDkOBytes], ob[kDkOBytes], oc[kDkOBytes];
-    __shared__ __attribute__((aligned(256))) float la[64], lb[64], lc[64], da[64], db_[64], dc[64];
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char q0b[kDkQBytes], q1b[kDkQBytes], q2b[kDkQBytes], q3b[kDkQBytes];
+    __shared__ __attribute__((aligned(1024))) char o0b[kDkOBytes], o1b[kDkOBytes], o2b[kDkOBytes], o3b[kDkOBytes];
+    __shared__ __attribute__((aligned(256))) float l0[64], l1[64], l2[64], l3[64], d0[64], d1[64], d2[64], d3[64];
+    // P of one item per key group, float32, [key group][register quad j][lane] of 16 bytes;
+    // two slots: role P writes slot it % 2 during step it, role dS reads it during step it + 1
+    __shared__ __attribute__((aligned(1024))) f32x4 pslot[2][4][4][64];
 
     // workgroup -> (key block, sequence, KV head): KV heads vary fastest, so that the
     // workgroups that the hardware places on one XCD (ids equal mod 8) share a KV head, and
@@ -207,33 +258,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int kb0 = (bid / p.B) * kKeysPerWg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3;
+    const bool role_p = wave < 4;
     const int n = lane & 31, g = lane >> 5;
-    const int kw0 = kb0 + kKeysPerWave * wave;  // this wave's first key
-    const int key = kw0 + n;                    // this lane's key (B-operand column)
-
-    // this wave's K and V rows as the B operands of S = Q K^T and dP = dO V^T
-    bf16x8 kB[12], vB[8];
-    {
-        const bool ok = key < p.L;
-        const size_t kr = ((size_t)b * p.Hkv + kvh) * p.L + (ok ? key : 0);
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk)
-            kB[kk] = as_bf16x8(ok ? ldg16(p.k + kr * kDqk + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            vB[kk] = as_bf16x8(ok ? ldg16(p.v + kr * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
-        // parked in AGPRs (the matrix unit reads them there), leaving the VGPRs to the
-        // operands streamed from LDS
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk) asm volatile("" : "+a"(kB[kk]));
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(vB[kk]));
-    }
-    f32x16 dK[6], dV[4];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
+    const int kw0 = kb0 + kKeysPerWave * kg;  // this key group's first key
+    const int key = kw0 + n;                  // this lane's key (B-operand column)
+    const bool key_ok = key < p.L;
+    const size_t krow = ((size_t)b * p.Hkv + kvh) * p.L + (key_ok ? key : 0);
 
     // query tiles that can see keys kb0 .. kb0 + 127
     const int qt_lo = kb0 / kQT;
@@ -244,138 +275,199 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // Item it = (query tile qt_hi - it / G, head it % G): every workgroup walks the query
     // tiles from the last one down, so the workgroups of one KV head that run together read
-    // the same tiles at about the same time (shared in L2).  Wave w loads blocks w, w + 4,
-    // w + 8 of Q and w, w + 4 of dO; waves 0 and 1 also load the LSE and D rows.
-    const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (wave + 4) + lane),
-              qsrc2 = src_of_slot<192>(64 * (wave + 8) + lane);
-    const int osrc0 = src_of_slot<128>(64 * wave + lane), osrc1 = src_of_slot<128>(64 * (wave + 4) + lane);
+    // the same tiles at about the same time (shared in L2).  Wave w loads Q block w and dO
+    // block w; waves 0-3 also Q block w + 8, wave 4 the LSE rows, wave 5 the D rows: three
+    // load instructions per item on waves 0-5, two on waves 6 and 7.
+    const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (8 + kg) + lane);
+    const int osrc0 = src_of_slot<128>(64 * wave + lane);
     auto issue = [&](int it, const DkTile &t) {
         const int hq = kvh * p.G + it % p.G, q0 = (qt_hi - it / p.G) * kQT;
         const size_t rbase = ((size_t)b * p.Hq + hq) * p.L;
         const auto rq = region(p.q + rbase * kDqk, (size_t)p.L * kDqk * 2);
         const auto ro = region(p.dout + rbase * kDv, (size_t)p.L * kDv * 2);
-        dma16(rq, t.q + 1024 * wave, qsrc0, q0 * (kDqk * 2));
-        dma16(rq, t.q + 1024 * (wave + 4), qsrc1, q0 * (kDqk * 2));
-        dma16(rq, t.q + 1024 * (wave + 8), qsrc2, q0 * (kDqk * 2));
-        dma16(ro, t.o + 1024 * wave, osrc0, q0 * (kDv * 2));
-        dma16(ro, t.o + 1024 * (wave + 4), osrc1, q0 * (kDv * 2));
-        if (wave == 0) dma4(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
-        if (wave == 1) dma4(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
+        dma16_async(rq, t.q + 1024 * wave, qsrc0, q0 * (kDqk * 2));
+        if (wave < 4) dma16_async(rq, t.q + 1024 * (8 + kg), qsrc1, q0 * (kDqk * 2));
+        dma16_async(ro, t.o + 1024 * wave, osrc0, q0 * (kDv * 2));
+        if (wave == 4) dma4_async(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
+        if (wave == 5) dma4_async(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
     };
-    auto compute = [&](const DkTile &t, int it) {
-        const int q0 = (qt_hi - it / p.G) * kQT;
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(t.q, 0, kk, lane), kB[kk], s, 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(t.o, 0, kk, lane), vB[kk], dp, 0, 0, 0);
-        // lane: key column n, query rows mrow(e, g) = 8 (e / 4) + 4 g + e % 4
-        if (!all_visible(p, q0, kw0)) {  // wave-uniform
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (!visible(p, q0 + mrow(e, g), key)) s[e] = -INFINITY;
-        }
-        f32x16 pr, ds;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(t.lse + 8 * j + 4 * g);
-            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(t.d + 8 * j + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * j + i;
-                const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, -l4[i] * kLog2e));
-                pr[e] = pv;
-                ds[e] = pv * (dp[e] - d4[i]);
-            }
-        }
-        const bf16x8 pa0 = pack8(pr, 0), pa1 = pack8(pr, 8), da0 = pack8(ds, 0), da1 = pack8(ds, 8);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(t.o, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
-            dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(t.o, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int nb = 0; nb < 6; ++nb) {
-            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(t.q, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
-            dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
-        }
-    };
-    // Item it uses buffer it % 3 and its loads are issued two items ahead: after the barrier
-    // of item it - 2, when every wave has finished item it - 3, the last reader of that
-    // buffer.  Before the barrier of item it each wave waits for all but its newest loads
-    // (those of item it + 1: six instructions on waves 0 and 1, five on the others); past
-    // the last item the loads repeat the last item, so that the count never changes.
-    const DkTile ta{qa, oa, la, da}, tb{qb, ob, lb, db_}, tc{qc, oc, lc, dc};
-    auto step = [&](int it, const DkTile &cur, const DkTile &fut) {
-        if (wave < 2) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
-        else __builtin_amdgcn_s_waitcnt(0x0F75);           // vmcnt(5)
-        __syncthreads();
-        issue(min(it + 2, total - 1), fut);
-        compute(cur, it);
+    // Item it uses buffer it % 4; its loads are issued two items ahead, after the barrier of
+    // item it - 2, when role P has finished item it - 4 and role dS item it - 5 (the last
+    // readers of that buffer) and loads go into it again.  Step s runs item s on role P and
+    // item s - 1 on role dS; there are total + 1 steps.  Before the barrier of each step
+    // every wave waits for all but its newest loads (those of the item after the next);
+    // past the last item the loads repeat it, so that the count never changes.
+    const DkTile t0{q0b, o0b, l0, d0}, t1{q1b, o1b, l1, d1}, t2{q2b, o2b, l2, d2}, t3{q3b, o3b, l3, d3};
+    const int nsteps = total > 0 ? total + 1 : 0;
+    auto sync_issue = [&](int s, const DkTile &fut) {
+        if (wave < 6) __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+        else __builtin_amdgcn_s_waitcnt(0x0F72);           // vmcnt(2)
+        lds_barrier();
+        issue(min(s + 2, total - 1), fut);
     };
     if (total > 0) {
-        issue(0, ta);
-        issue(min(1, total - 1), tb);
+        issue(0, t0);
+        issue(min(1, total - 1), t1);
     }
-    int it = 0;
-    for (; it + 2 < total; it += 3) {
-        step(it, ta, tc);
-        step(it + 1, tb, ta);
-        step(it + 2, tc, tb);
-    }
-    if (it < total) step(it, ta, tc);
-    if (it + 1 < total) step(it + 1, tb, ta);
-    wait_dma();  // no load into LDS outlives the workgroup
-
-    // rows: this wave's keys mrow(e, g); columns: dims 32 nb + n
     const float scale = p.scale;
+
+    if (role_p) {
+        // this key group's K rows as the B operand of S = Q K^T (in AGPRs, which the matrix
+        // unit reads directly)
+        bf16x8 kB[12];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int kr = kw0 + mrow(e, g);
-        if (kr >= p.L) continue;
-        const size_t row = ((size_t)b * p.Hkv + kvh) * p.L + kr;
+        for (int kk = 0; kk < 12; ++kk)
+            kB[kk] = as_bf16x8(key_ok ? ldg16(p.k + krow * kDqk + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
 #pragma unroll
-        for (int nb = 0; nb < 6; ++nb) p.dk[row * kDqk + 32 * nb + n] = dK[nb][e] * scale;
+        for (int kk = 0; kk < 12; ++kk) asm volatile("" : "+a"(kB[kk]));
+        f32x16 dV[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) p.dv[row * kDv + 32 * nb + n] = dV[nb][e];
+        for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
+        auto compute = [&](const DkTile &t, int it) __attribute__((always_inline)) {
+            const int q0 = (qt_hi - it / p.G) * kQT;
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 12; ++kk)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(t.q, 0, kk, lane), kB[kk], s, 0, 0, 0);
+            // lane: key column n, query rows mrow(e, g) = 8 (e / 4) + 4 g + e % 4
+            if (!all_visible(p, q0, kw0)) {  // wave-uniform
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (!visible(p, q0 + mrow(e, g), key)) s[e] = -INFINITY;
+            }
+            f32x16 pr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(t.lse + 8 * j + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pr[4 * j + i] = exp2f_fast(__builtin_fmaf(s[4 * j + i], p.scale_log2, -l4[i] * kLog2e));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pslot[it & 1][kg][j][lane] = f32x4{pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]};
+            const bf16x8 pa0 = pack8(pr, 0), pa1 = pack8(pr, 8);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(t.o, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
+                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(t.o, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
+            }
+        };
+        auto step = [&](int s, const DkTile &cur, const DkTile &fut) __attribute__((always_inline)) {
+            sync_issue(s, fut);
+            if (s < total) compute(cur, s);
+        };
+        int s = 0;
+        for (; s + 3 < nsteps; s += 4) {
+            step(s, t0, t2);
+            step(s + 1, t1, t3);
+            step(s + 2, t2, t0);
+            step(s + 3, t3, t1);
+        }
+        if (s < nsteps) step(s, t0, t2);
+        if (s + 1 < nsteps) step(s + 1, t1, t3);
+        if (s + 2 < nsteps) step(s + 2, t2, t0);
+        wait_dma();  // no load into LDS outlives the workgroup
+        // rows: this group's keys mrow(e, g); columns: dims 32 nb + n
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int kr = kw0 + mrow(e, g);
+            if (kr >= p.L) continue;
+            const size_t row = ((size_t)b * p.Hkv + kvh) * p.L + kr;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) p.dv[row * kDv + 32 * nb + n] = dV[nb][e];
+        }
+    } else {
+        // this key group's V rows as the B operand of dP = dO V^T
+        bf16x8 vB[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            vB[kk] = as_bf16x8(key_ok ? ldg16(p.v + krow * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(vB[kk]));
+        f32x16 dK[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
+        auto compute = [&](const DkTile &t, int it) __attribute__((always_inline)) {
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(t.o, 0, kk, lane), vB[kk], dp, 0, 0, 0);
+            f32x16 ds;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(t.d + 8 * j + 4 * g);
+                const f32x4 p4 = pslot[it & 1][kg][j][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ds[4 * j + i] = p4[i] * (dp[4 * j + i] - d4[i]);
+            }
+            const bf16x8 da0 = pack8(ds, 0), da1 = pack8(ds, 8);
+#pragma unroll
+            for (int nb = 0; nb < 6; ++nb) {
+                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(t.q, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
+                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
+            }
+        };
+        // step s: item s - 1, in buffer (s - 1) % 4
+        auto step = [&](int s, const DkTile &prev, const DkTile &fut) __attribute__((always_inline)) {
+            sync_issue(s, fut);
+            if (s >= 1) compute(prev, s - 1);
+        };
+        int s = 0;
+        for (; s + 3 < nsteps; s += 4) {
+            step(s, t3, t2);
+            step(s + 1, t0, t3);
+            step(s + 2, t1, t0);
+            step(s + 3, t2, t1);
+        }
+        if (s < nsteps) step(s, t3, t2);
+        if (s + 1 < nsteps) step(s + 1, t0, t3);
+        if (s + 2 < nsteps) step(s + 2, t1, t0);
+        wait_dma();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int kr = kw0 + mrow(e, g);
+            if (kr >= p.L) continue;
+            const size_t row = ((size_t)b * p.Hkv + kvh) * p.L + kr;
+#pragma unroll
+            for (int nb = 0; nb < 6; ++nb) p.dk[row * kDqk + 32 * nb + n] = dK[nb][e] * scale;
+        }
     }
 }
 
 // ---- dQ
-// LDS tile of 64 keys: K [64][192] (24 blocks of 1 KB) and V [64][128] (16 blocks), triple
-// buffered (120 KB).  Each wave runs a software pipeline over 32-key sub-blocks so that the
-// softmax arithmetic of one sub-block overlaps the products of the next:
-//   phase A: S^T, dP^T of (t, 1)       with  dS^T of (t, 0)
-//   phase B: dQ^T += K(t, 0)^T dS^T(t, 0)
-//   barrier: tile t + 1 has landed, the buffer of tile t - 1 is free; tile t + 2 starts
-//   phase C: S^T, dP^T of (t + 1, 0)   with  dS^T of (t, 1)
-//   phase D: dQ^T += K(t, 1)^T dS^T(t, 1)
-// Sub-blocks past the last row or before the window are computed and masked to zero, and
-// past the last tile the loads and scores repeat the last tile unused, so that no branch
-// splits a phase.
+// One workgroup per 64 query rows of four query heads of one KV head, eight waves: wave w
+// takes head 4 hgroup + w % 4 and rows q0 + 32 (w / 4) .. +31, keeps that head's Q and dO
+// operands and dQ^T in registers, and walks the key tiles.  LDS tile of 64 keys: K [64][192]
+// (24 blocks of 1 KB) and V [64][128] (16 blocks), triple buffered (120 KB), shared by the
+// eight waves; two waves per SIMD, so one's products run while the other does its softmax
+// arithmetic.  Per 32-key sub-block:
+//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+// A sub-block that none of the wave's rows sees is skipped (wave-uniform); one that crosses
+// the diagonal, the window's edge or the sequence end is masked.
 constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;
+constexpr int kDqRows = 2 * kQT;  // query rows per workgroup
 
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char K0[kDqKBytes], K1[kDqKBytes], K2[kDqKBytes];
     __shared__ __attribute__((aligned(1024))) char V0[kDqVBytes], V1[kDqVBytes], V2[kDqVBytes];
 
-    // workgroup -> (query tile, sequence, group of four heads): head groups vary fastest and
-    // the query tiles with the most key tiles come first
+    // workgroup -> (query block, sequence, group of four heads): head groups vary fastest and
+    // the query blocks with the most key tiles come first
     int bid = blockIdx.x;
     const int hgroup = bid % (p.Hq / 4);
     bid /= p.Hq / 4;
     const int b = bid % p.B;
-    const int q0 = ((p.L + kQT - 1) / kQT - 1 - bid / p.B) * kQT;
+    const int qb0 = ((p.L + kDqRows - 1) / kDqRows - 1 - bid / p.B) * kDqRows;
+    if (qb0 >= p.L) return;  // uniform over the workgroup
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
-    const int hq = hgroup * 4 + wave, kvh = (hgroup * 4) / p.G;
-    const int qpos = q0 + n;  // this lane's query (B-operand column)
+    const int hq = hgroup * 4 + (wave & 3), kvh = (hgroup * 4) / p.G;
+    const int q0 = qb0 + kQT * (wave >> 2);  // this wave's first row
+    const int qpos = q0 + n;                 // this lane's query (B-operand column)
     const size_t qrow = ((size_t)b * p.Hq + hq) * p.L + (qpos < p.L ? qpos : 0);
     const bool qok = qpos < p.L;
-    if (q0 >= p.L) return;  // uniform over the workgroup
 
     bf16x8 qB[12], oB[8];
 #pragma unroll
@@ -384,45 +476,45 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     for (int kk = 0; kk < 8; ++kk) oB[kk] = as_bf16x8(qok ? ldg16(p.dout + qrow * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
     // a row past the sequence end has every pair masked; its LSE only has to be finite
     const float nlse2 = qok ? -p.lse[qrow] * kLog2e : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
+    // these loads land before the loop: the compiler does not count the tile loads, so a wait
+    // for them inside the loop would wait for every tile load in flight
+    wait_dma();
     f32x16 dQ[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) dQ[i] = f32x16{};
 
-    // key tiles that rows q0 .. q0 + 31 see
-    const int q_hi = min(p.L, q0 + kQT) - 1;
-    const int k_lo = p.swa ? max(0, q0 - p.window + 1) : 0;
+    // key tiles that rows qb0 .. qb0 + 63 see, and the keys this wave's rows see
+    const int q_hi = min(p.L, qb0 + kDqRows) - 1;
+    const int k_lo = p.swa ? max(0, qb0 - p.window + 1) : 0;
     const int t0 = k_lo / kKT, t1 = q_hi / kKT;
+    const int wk_hi = min(p.L, q0 + kQT) - 1;                       // last key of any row
+    const int wk_lo = p.swa ? q0 - p.window + 1 : INT32_MIN / 2;  // first key of the last row
     const size_t kvbase = ((size_t)b * p.Hkv + kvh) * p.L;
     const auto rk = region(p.k + kvbase * kDqk, (size_t)p.L * kDqk * 2);
     const auto rv = region(p.v + kvbase * kDv, (size_t)p.L * kDv * 2);
 
-    // wave w loads blocks w + 4 i of K (24 blocks) and of V (16 blocks)
-    int ksrc[6], vsrc[4];
+    // wave w loads blocks w, w + 8, w + 16 of K (24 blocks) and w, w + 8 of V (16 blocks)
+    int ksrc[3], vsrc[2];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 4 * i) + lane);
+    for (int i = 0; i < 3; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 8 * i) + lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vsrc[i] = src_of_slot<128>(64 * (wave + 4 * i) + lane);
+    for (int i = 0; i < 2; ++i) vsrc[i] = src_of_slot<128>(64 * (wave + 8 * i) + lane);
     auto issue = [&](int t, char *kt, char *vt) {
         const int kbase = t * kKT;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) dma16(rk, kt + 1024 * (wave + 4 * i), ksrc[i], kbase * (kDqk * 2));
+        for (int i = 0; i < 3; ++i) dma16_async(rk, kt + 1024 * (wave + 8 * i), ksrc[i], kbase * (kDqk * 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(rv, vt + 1024 * (wave + 4 * i), vsrc[i], kbase * (kDv * 2));
+        for (int i = 0; i < 2; ++i) dma16_async(rv, vt + 1024 * (wave + 8 * i), vsrc[i], kbase * (kDv * 2));
     };
-    // S^T = K Q^T and dP^T = V dO^T of sub-block sb of a tile
-    auto scores = [&](const char *kt, const char *vt, int sb, f32x16 &s, f32x16 &dp) {
-        s = f32x16{};
-        dp = f32x16{};
+    // one 32-key sub-block: lane holds query column n, key rows kbase + mrow(e, g)
+    auto sub = [&](const char *kt, const char *vt, int sb, int kbase) __attribute__((always_inline)) {
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
-    };
-    // dS^T = P^T (dP^T - D) of the sub-block whose first key is kbase, as two bf16 k-steps;
-    // lane: query column n, key rows mrow(e, g)
-    auto dscores = [&](f32x16 s, const f32x16 &dp, int kbase, bf16x8 &d0, bf16x8 &d1) {
         if (!all_visible(p, q0, kbase)) {  // uniform
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -434,40 +526,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
             const float pv = exp2f_fast(__builtin_fmaf(s[e], p.scale_log2, nlse2));
             ds[e] = pv * (dp[e] - d_q);
         }
-        d0 = pack8(ds, 0);
-        d1 = pack8(ds, 8);
-    };
-    auto dq_acc = [&](const char *kt, int sb, const bf16x8 &d0, const bf16x8 &d1) {
+        const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
 #pragma unroll
         for (int db = 0; db < 6; ++db) {
             dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
             dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
         }
     };
-
-    f32x16 s0, dp0, s1, dp1;
-    bf16x8 da, db;
-    auto step = [&](int t, const char *Kc, const char *Vc, const char *Kn, const char *Vn, char *Kf, char *Vf) {
-        const int kb = t * kKT;
-        scores(Kc, Vc, 1, s1, dp1);        // phase A
-        dscores(s0, dp0, kb, da, db);
-        dq_acc(Kc, 0, da, db);             // phase B
-        wait_dma();
-        __syncthreads();
+    // Tile t uses buffer (t - t0) % 3; its loads are issued two tiles ahead, after the barrier
+    // of tile t - 2, when every wave has finished tile t - 3, the last reader of that buffer.
+    // Before each barrier a wave waits for all but its newest five loads (those of the next
+    // tile); past the last tile the loads repeat it, so that the count never changes.
+    auto step = [&](int t, const char *Kc, const char *Vc, char *Kf, char *Vf) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+        lds_barrier();
         issue(min(t + 2, t1), Kf, Vf);
-        scores(Kn, Vn, 0, s0, dp0);        // phase C (unused after the last tile)
-        dscores(s1, dp1, kb + 32, da, db);
-        dq_acc(Kc, 1, da, db);             // phase D
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int kbase = t * kKT + 32 * sb;
+            const bool dead = q0 >= p.L || kbase > wk_hi || kbase + 31 < wk_lo;  // uniform
+            if (!dead) sub(Kc, Vc, sb, kbase);
+        }
     };
     issue(t0, K0, V0);
     issue(min(t0 + 1, t1), K1, V1);
-    wait_dma();
-    __syncthreads();
-    scores(K0, V0, 0, s0, dp0);
     for (int t = t0; t <= t1; t += 3) {
-        step(t, K0, V0, K1, V1, K2, V2);
-        if (t + 1 <= t1) step(t + 1, K1, V1, K2, V2, K0, V0);
-        if (t + 2 <= t1) step(t + 2, K2, V2, K0, V0, K1, V1);
+        step(t, K0, V0, K2, V2);
+        if (t + 1 <= t1) step(t + 1, K1, V1, K0, V0);
+        if (t + 2 <= t1) step(t + 2, K2, V2, K1, V1);
     }
     wait_dma();  // no load into LDS outlives the workgroup
     if (!qok) return;
@@ -497,10 +583,10 @@ int launch_backward(const BwdParams &prm, hipStream_t stream) {
                         stream) != hipSuccess)
         return -1;
     if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dkdv_kernel),
-                        dim3(((p.L + kKeysPerWg - 1) / kKeysPerWg) * p.Hkv * p.B), dim3(256), args, 0, stream) != hipSuccess)
+                        dim3(((p.L + kKeysPerWg - 1) / kKeysPerWg) * p.Hkv * p.B), dim3(512), args, 0, stream) != hipSuccess)
         return -1;
-    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel), dim3(((p.L + kQT - 1) / kQT) * (p.Hq / 4) * p.B),
-                        dim3(256), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel),
+                        dim3(((p.L + kDqRows - 1) / kDqRows) * (p.Hq / 4) * p.B), dim3(512), args, 0, stream) != hipSuccess)
         return -1;
     if (p.sink) {
         void *args2[] = {&p, (void *)&nblk};

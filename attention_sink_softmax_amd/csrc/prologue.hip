@@ -2,8 +2,8 @@
 // forward steps 3-6): partial rotary position embedding of q and k, and writing the new
 // tokens' keys and values into the KV cache (ring slots or pages, bf16 or E4M3).
 //
-// Both are elementwise and memory-bound: each element is read and written once with 16-byte
-// (append) or coalesced 2-byte (rotation) accesses.
+// Both are elementwise and memory-bound: each element is read and written once, in 16-byte
+// pieces.
 #include "common.h"
 #include "launch.h"
 
