@@ -98,55 +98,73 @@ constexpr int kKeysPerWg = 4 * kKeysPerWave;  // bwd_dkdv
 constexpr int kKT = 64;                    // keys per tile in bwd_dq
 constexpr int kPreRows = 16;               // rows per bwd_pre workgroup
 
-// Byte offset of 16-byte chunk c of row r: rows of 192 (384 B) and of 128 (256 B) elements.
-// The chunk index is XORed with swz(r), which takes the 8 values 0..7 over any 8 aligned rows
-// and 4 values with distinct bits 1-2 over any 4 aligned rows: no two lanes of a 128-byte
-// phase of a row read, or of a 16-lane transposing read, share a bank if the banks serve
-// 128 bytes per cycle.  The hardware serves 256 bytes per cycle (16 lanes of a row read), and
-// its counters show conflicts in 12-15% of cycles here.  A swizzle built for that wider phase
-// removed them but made the dQ kernel slower (its addresses took more registers), so this
-// one stays.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int off192(int r, int c) { return r * 384 + ((c ^ swz(r)) << 4); }
-__device__ __forceinline__ int off128(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
-
+// Byte offset of 16-byte chunk c of row r in an LDS tile of W-element rows.  Rows are 448
+// bytes apart for W = 192 and 320 for W = 128 (64 bytes unused at the end of each), and chunk c
+// sits at c ^ ((r >> 2) & 3).  With banks serving 256 bytes per cycle (16 lanes of a 16-byte
+// read, 32 lanes of an 8-byte transposing read):
+//   * a transposing read (4 rows of a 4-aligned group x 4 chunks of a 4-aligned group) puts
+//     each row's 4 chunks in a run of 4 slots that the XOR only permutes, and the row stride
+//     (28 or 20 slots, 4 mod 8) sets the 4 runs 4 slots apart;
+//   * a row read (rows r .. r + 15 of a 16-aligned group, one chunk) gets 4 bank positions
+//     from the stride (r mod 4) and the other 4 from the XOR ((r >> 2) & 3).
+// The XOR touches only the low two bits of the chunk index, which are lane bits in the
+// transposing reads and half lane bits in the row reads, so each read's address is a lane
+// register plus a constant offset (two registers per operand kind).
+template <int W>
+constexpr int kTileRow = W == 192 ? 448 : 320;
 template <int W>
 __device__ __forceinline__ int tile_off(int r, int c) {
-    if constexpr (W == 192) return off192(r, c);
-    else return off128(r, c);
+    return r * kTileRow<W> + ((c ^ ((r >> 2) & 3)) << 4);
 }
 // Source offset (bytes, from the tile's first row) of the chunk that lands in 16-byte slot
-// `slot` of a swizzled tile of W-element rows.
+// `slot` of a tile of W-element rows.  The unused slots at a row's end take a copy of one of
+// the row's chunks (nobody reads them), so that every lane of a load instruction loads.
 template <int W>
 __device__ __forceinline__ int src_of_slot(int slot) {
-    constexpr int kChunks = W / 8;
-    const int r = slot / kChunks, c = (slot % kChunks) ^ swz(r);
-    return r * (W * 2) + c * 16;
+    constexpr int kSlots = kTileRow<W> / 16, kChunks = W / 8;
+    const int r = slot / kSlots, pc = slot % kSlots;
+    return r * (W * 2) + ((pc % kChunks) ^ ((r >> 2) & 3)) * 16;
 }
 
 // Row m of a 32x32 MFMA result held in register e by lane group g.
 __device__ __forceinline__ int mrow(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
 
-// 8 elements of column `col0 + (lane & 31)` of a swizzled row-major tile, from rows
-// rbase + {4g .. 4g+3} and rbase + 8 + {4g .. 4g+3} (g = lane >> 5): the operand, in the k
-// order of a score tile's registers, of a product that contracts over those rows.
+// The lane-dependent parts of the operand reads of a tile of W-element rows.  Every read
+// starts at a row rbase that is a multiple of 16, so (row >> 2) & 3 depends on the lane only,
+// and the XOR stays in the low two bits of the chunk index: each address is one of these
+// registers plus a compile-time offset.
+//   row[p]: row rbase + (lane & 31), chunk 2 kk + g with kk & 1 = p (g = lane >> 5);
+//   col[h]: row rbase + 8h + 4g + (i >> 2), chunk 4 nb + 2 gl + (c4 >> 1), half c4 & 1
+//           (i = lane & 15, gl = (lane >> 4) & 1, c4 = i & 3).
 template <int W>
-__device__ __forceinline__ bf16x8 col_operand(const char *tile, int rbase, int col0, int lane) {
-    const int g = lane >> 5, gl = (lane >> 4) & 1, i = lane & 15;
-    const int r = i >> 2, c4 = i & 3;
-    const int col = col0 + 16 * gl + 4 * c4;
-    const int chunk = col >> 3, half = (col >> 2) & 1;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(tile + tile_off<W>(rbase + 4 * g + r, chunk) + 8 * half));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(tile + tile_off<W>(rbase + 8 + 4 * g + r, chunk) + 8 * half));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+struct LaneOff {
+    int row[2], col[2];
+    __device__ __forceinline__ explicit LaneOff(int lane) {
+        constexpr int S = kTileRow<W>;
+        const int g = lane >> 5, gl = (lane >> 4) & 1, i = lane & 15, c4 = i & 3, r = lane & 31;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) row[p] = r * S + (((2 * p + g) ^ ((r >> 2) & 3)) << 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            col[h] = (4 * g + (i >> 2)) * S + (((2 * gl + (c4 >> 1)) ^ ((2 * h + g) & 3)) << 4) + 8 * (c4 & 1);
+    }
+};
+
+// 8 elements of column `col0 + (lane & 31)` of a tile, from rows rbase + {4g .. 4g+3} and
+// rbase + 8 + {4g .. 4g+3} (g = lane >> 5): the operand, in the k order of a score tile's
+// registers, of a product that contracts over those rows.  col0 is a multiple of 32.
+template <int W>
+__device__ __forceinline__ bf16x8 col_operand(const char *tile, int rbase, int col0, const LaneOff<W> &lo) {
+    const char *base = tile + rbase * kTileRow<W> + 2 * col0;  // chunk 4 nb = col0 / 8
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + lo.col[0]));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(base + 8 * kTileRow<W> + lo.col[1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 8 elements of row rbase + (lane & 31), chunk 2kk + g, of a swizzled row-major tile.
+// 8 elements of row rbase + (lane & 31), chunk 2kk + g, of a tile.
 template <int W>
-__device__ __forceinline__ bf16x8 row_operand(const char *tile, int rbase, int kk, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(tile + tile_off<W>(rbase + (lane & 31), 2 * kk + (lane >> 5)));
+__device__ __forceinline__ bf16x8 row_operand(const char *tile, int rbase, int kk, const LaneOff<W> &lo) {
+    return *reinterpret_cast<const bf16x8 *>(tile + rbase * kTileRow<W> + (kk >> 1) * 64 + lo.row[kk & 1]);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
@@ -231,9 +249,9 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int nblk) {
 // waves share a SIMD and one's products run while the other waits or does its softmax
 // arithmetic.  The P tile passes in float32, so the results are those of computing both
 // halves in one wave.
-// LDS tile of one query tile: Q [32][192] (12 KB = 12 blocks of 1 KB), dO [32][128] (8 blocks),
+// LDS tile of one query tile: Q [32][192] (14 blocks of 1 KB) and dO [32][128] (10 blocks),
 // and the LSE and D of its rows (64 floats each: the 32 rows of the tile and 32 unused).
-constexpr int kDkQBytes = kQT * kDqk * 2, kDkOBytes = kQT * kDv * 2;
+constexpr int kDkQBytes = kQT * kTileRow<192>, kDkOBytes = kQT * kTileRow<128>;  // 14 and 10 KB
 
 struct DkTile {
     char *q, *o;
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     // workgroup -> (key block, sequence, KV head): KV heads vary fastest, so that the
     // workgroups that the hardware places on one XCD (ids equal mod 8) share a KV head, and
     // the key blocks with the most query tiles come first
-    int bid = blockIdx.x;
+    int bid = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
     const int kvh = bid % p.Hkv;
     bid /= p.Hkv;
     const int b = bid % p.B;
@@ -260,6 +278,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave & 3;
     const bool role_p = wave < 4;
+    const LaneOff<192> lq(lane);  // Q tiles
+    const LaneOff<128> lo(lane);  // dO tiles
     const int n = lane & 31, g = lane >> 5;
     const int kw0 = kb0 + kKeysPerWave * kg;  // this key group's first key
     const int key = kw0 + n;                  // this lane's key (B-operand column)
@@ -275,33 +295,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // Item it = (query tile qt_hi - it / G, head it % G): every workgroup walks the query
     // tiles from the last one down, so the workgroups of one KV head that run together read
-    // the same tiles at about the same time (shared in L2).  Wave w loads Q block w and dO
-    // block w; waves 0-3 also Q block w + 8, wave 4 the LSE rows, wave 5 the D rows: three
-    // load instructions per item on waves 0-5, two on waves 6 and 7.
-    const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (8 + kg) + lane);
-    const int osrc0 = src_of_slot<128>(64 * wave + lane);
+    // the same tiles at about the same time (shared in L2).  Wave w loads blocks w of Q and
+    // dO, waves 0-5 also block w + 8 of Q, waves 0-1 block w + 8 of dO, wave 6 the LSE rows and
+    // wave 7 the D rows: four load instructions per item on waves 0-1, three on the others.
+    const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (wave + 8) + lane);
+    const int osrc0 = src_of_slot<128>(64 * wave + lane), osrc1 = src_of_slot<128>(64 * (wave + 8) + lane);
     auto issue = [&](int it, const DkTile &t) {
         const int hq = kvh * p.G + it % p.G, q0 = (qt_hi - it / p.G) * kQT;
         const size_t rbase = ((size_t)b * p.Hq + hq) * p.L;
         const auto rq = region(p.q + rbase * kDqk, (size_t)p.L * kDqk * 2);
         const auto ro = region(p.dout + rbase * kDv, (size_t)p.L * kDv * 2);
         dma16_async(rq, t.q + 1024 * wave, qsrc0, q0 * (kDqk * 2));
-        if (wave < 4) dma16_async(rq, t.q + 1024 * (8 + kg), qsrc1, q0 * (kDqk * 2));
+        if (wave < 6) dma16_async(rq, t.q + 1024 * (wave + 8), qsrc1, q0 * (kDqk * 2));
         dma16_async(ro, t.o + 1024 * wave, osrc0, q0 * (kDv * 2));
-        if (wave == 4) dma4_async(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
-        if (wave == 5) dma4_async(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
+        if (wave < 2) dma16_async(ro, t.o + 1024 * (wave + 8), osrc1, q0 * (kDv * 2));
+        if (wave == 6) dma4_async(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
+        if (wave == 7) dma4_async(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
     };
     // Item it uses buffer it % 4; its loads are issued two items ahead, after the barrier of
-    // item it - 2, when role P has finished item it - 4 and role dS item it - 5 (the last
-    // readers of that buffer) and loads go into it again.  Step s runs item s on role P and
+    // step it - 2, by when the previous item in that buffer, it - 4, is done (role P ran it
+    // in step it - 4, role dS in step it - 3).  Step s runs item s on role P and
     // item s - 1 on role dS; there are total + 1 steps.  Before the barrier of each step
     // every wave waits for all but its newest loads (those of the item after the next);
     // past the last item the loads repeat it, so that the count never changes.
     const DkTile t0{q0b, o0b, l0, d0}, t1{q1b, o1b, l1, d1}, t2{q2b, o2b, l2, d2}, t3{q3b, o3b, l3, d3};
     const int nsteps = total > 0 ? total + 1 : 0;
     auto sync_issue = [&](int s, const DkTile &fut) {
-        if (wave < 6) __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
-        else __builtin_amdgcn_s_waitcnt(0x0F72);           // vmcnt(2)
+        if (wave < 2) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F73);           // vmcnt(3)
         lds_barrier();
         issue(min(s + 2, total - 1), fut);
     };
@@ -328,7 +349,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             f32x16 s = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 12; ++kk)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(t.q, 0, kk, lane), kB[kk], s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(t.q, 0, kk, lq), kB[kk], s, 0, 0, 0);
             // lane: key column n, query rows mrow(e, g) = 8 (e / 4) + 4 g + e % 4
             if (!all_visible(p, q0, kw0)) {  // wave-uniform
 #pragma unroll
@@ -349,8 +370,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             const bf16x8 pa0 = pack8(pr, 0), pa1 = pack8(pr, 8);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(t.o, 0, 32 * nb, lane), dV[nb], 0, 0, 0);
-                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(t.o, 16, 32 * nb, lane), dV[nb], 0, 0, 0);
+                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, col_operand<128>(t.o, 0, 32 * nb, lo), dV[nb], 0, 0, 0);
+                dV[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, col_operand<128>(t.o, 16, 32 * nb, lo), dV[nb], 0, 0, 0);
             }
         };
         auto step = [&](int s, const DkTile &cur, const DkTile &fut) __attribute__((always_inline)) {
@@ -392,7 +413,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             f32x16 dp = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(t.o, 0, kk, lane), vB[kk], dp, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(t.o, 0, kk, lo), vB[kk], dp, 0, 0, 0);
             f32x16 ds;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -404,8 +425,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             const bf16x8 da0 = pack8(ds, 0), da1 = pack8(ds, 8);
 #pragma unroll
             for (int nb = 0; nb < 6; ++nb) {
-                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(t.q, 0, 32 * nb, lane), dK[nb], 0, 0, 0);
-                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lane), dK[nb], 0, 0, 0);
+                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da0, col_operand<192>(t.q, 0, 32 * nb, lq), dK[nb], 0, 0, 0);
+                dK[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da1, col_operand<192>(t.q, 16, 32 * nb, lq), dK[nb], 0, 0, 0);
             }
         };
         // step s: item s - 1, in buffer (s - 1) % 4
@@ -439,13 +460,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 // One workgroup per 64 query rows of four query heads of one KV head, eight waves: wave w
 // takes head 4 hgroup + w % 4 and rows q0 + 32 (w / 4) .. +31, keeps that head's Q and dO
 // operands and dQ^T in registers, and walks the key tiles.  LDS tile of 64 keys: K [64][192]
-// (24 blocks of 1 KB) and V [64][128] (16 blocks), triple buffered (120 KB), shared by the
+// (28 blocks of 1 KB) and V [64][128] (20 blocks), triple buffered (144 KB), shared by the
 // eight waves; two waves per SIMD, so one's products run while the other does its softmax
 // arithmetic.  Per 32-key sub-block:
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // A sub-block that none of the wave's rows sees is skipped (wave-uniform); one that crosses
 // the diagonal, the window's edge or the sequence end is masked.
-constexpr int kDqKBytes = kKT * kDqk * 2, kDqVBytes = kKT * kDv * 2;
+constexpr int kDqKBytes = kKT * kTileRow<192>, kDqVBytes = kKT * kTileRow<128>;  // 28 and 20 KB
 constexpr int kDqRows = 2 * kQT;  // query rows per workgroup
 
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 
     // workgroup -> (query block, sequence, group of four heads): head groups vary fastest and
     // the query blocks with the most key tiles come first
-    int bid = blockIdx.x;
+    int bid = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
     const int hgroup = bid % (p.Hq / 4);
     bid /= p.Hq / 4;
     const int b = bid % p.B;
@@ -464,6 +485,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
     const int hq = hgroup * 4 + (wave & 3), kvh = (hgroup * 4) / p.G;
+    const LaneOff<192> lk(lane);  // K tiles
+    const LaneOff<128> lv(lane);  // V tiles
     const int q0 = qb0 + kQT * (wave >> 2);  // this wave's first row
     const int qpos = q0 + n;                 // this lane's query (B-operand column)
     const size_t qrow = ((size_t)b * p.Hq + hq) * p.L + (qpos < p.L ? qpos : 0);
@@ -493,28 +516,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const auto rk = region(p.k + kvbase * kDqk, (size_t)p.L * kDqk * 2);
     const auto rv = region(p.v + kvbase * kDv, (size_t)p.L * kDv * 2);
 
-    // wave w loads blocks w, w + 8, w + 16 of K (24 blocks) and w, w + 8 of V (16 blocks)
-    int ksrc[3], vsrc[2];
+    // wave w loads blocks w, w + 8, w + 16 of K and w, w + 8 of V, and waves 0-3 also block
+    // w + 24 of K and w + 16 of V: seven load instructions per tile on waves 0-3, five on 4-7
+    int ksrc[4], vsrc[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 8 * i) + lane);
+    for (int i = 0; i < 4; ++i) ksrc[i] = src_of_slot<192>(64 * (wave + 8 * i) + lane);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vsrc[i] = src_of_slot<128>(64 * (wave + 8 * i) + lane);
+    for (int i = 0; i < 3; ++i) vsrc[i] = src_of_slot<128>(64 * (wave + 8 * i) + lane);
     auto issue = [&](int t, char *kt, char *vt) {
         const int kbase = t * kKT;
 #pragma unroll
         for (int i = 0; i < 3; ++i) dma16_async(rk, kt + 1024 * (wave + 8 * i), ksrc[i], kbase * (kDqk * 2));
+        if (wave < 4) dma16_async(rk, kt + 1024 * (wave + 24), ksrc[3], kbase * (kDqk * 2));
 #pragma unroll
         for (int i = 0; i < 2; ++i) dma16_async(rv, vt + 1024 * (wave + 8 * i), vsrc[i], kbase * (kDv * 2));
+        if (wave < 4) dma16_async(rv, vt + 1024 * (wave + 16), vsrc[2], kbase * (kDv * 2));
     };
     // one 32-key sub-block: lane holds query column n, key rows kbase + mrow(e, g)
     auto sub = [&](const char *kt, const char *vt, int sb, int kbase) __attribute__((always_inline)) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lane), qB[kk], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<192>(kt, 32 * sb, kk, lk), qB[kk], s, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lane), oB[kk], dp, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<128>(vt, 32 * sb, kk, lv), oB[kk], dp, 0, 0, 0);
         if (!all_visible(p, q0, kbase)) {  // uniform
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -529,16 +555,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         const bf16x8 d0 = pack8(ds, 0), d1 = pack8(ds, 8);
 #pragma unroll
         for (int db = 0; db < 6; ++db) {
-            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lane), d0, dQ[db], 0, 0, 0);
-            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lane), d1, dQ[db], 0, 0, 0);
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb, 32 * db, lk), d0, dQ[db], 0, 0, 0);
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_operand<192>(kt, 32 * sb + 16, 32 * db, lk), d1, dQ[db], 0, 0, 0);
         }
     };
     // Tile t uses buffer (t - t0) % 3; its loads are issued two tiles ahead, after the barrier
     // of tile t - 2, when every wave has finished tile t - 3, the last reader of that buffer.
-    // Before each barrier a wave waits for all but its newest five loads (those of the next
-    // tile); past the last tile the loads repeat it, so that the count never changes.
+    // Before each barrier a wave waits for all but its newest loads (those of the next tile);
+    // past the last tile the loads repeat it, so that the count never changes.
     auto step = [&](int t, const char *Kc, const char *Vc, char *Kf, char *Vf) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+        if (wave < 4) __builtin_amdgcn_s_waitcnt(0x0F77);  // vmcnt(7)
+        else __builtin_amdgcn_s_waitcnt(0x0F75);           // vmcnt(5)
         lds_barrier();
         issue(min(t + 2, t1), Kf, Vf);
 #pragma unroll
@@ -577,6 +604,7 @@ size_t backward_workspace_bytes(int B, int Hq, int L) {
 
 int launch_backward(const BwdParams &prm, hipStream_t stream) {
     BwdParams p = prm;
+    p.reverse = grid_reversed();
     const int nblk = (p.L + kPreRows - 1) / kPreRows;
     void *args[] = {&p};
     if (hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel), dim3(nblk, p.Hq, p.B), dim3(256), args, 0,

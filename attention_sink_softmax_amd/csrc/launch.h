@@ -90,6 +90,7 @@ struct BwdParams {
     float *dsink_part;    // workspace [B][Hq][ceil(L / 16)]
     int B, L, Hq, Hkv, G, swa, window;
     float scale, scale_log2;
+    int reverse;  // workgroups take their work in reverse order (race check)
 };
 size_t backward_workspace_bytes(int B, int Hq, int L);
 int launch_backward(const BwdParams &p, hipStream_t stream);

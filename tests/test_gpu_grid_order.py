@@ -79,3 +79,32 @@ def test_decode_grid_order(layout, mode, W, q_len, L):
     ref = oracle.decode(qm, kc, vc, lens, d["sink"], mode, W, SCALE,
                         oracle.RING if layout == sa.KV_RING else oracle.PAGED, bt)
     assert_parity(b, ref, "reversed order vs oracle")
+
+
+@pytest.mark.parametrize("mode,W,Hq,Hkv,L,B", [(oracle.GLOBAL, 0, 16, 4, 333, 2), (oracle.SWA, 128, 16, 2, 517, 1)])
+def test_backward_grid_order(mode, W, Hq, Hkv, L, B):
+    """The dK/dV kernel's two waves per key group exchange P through LDS and both backward
+    kernels share quadruple- and triple-buffered tiles: the gradients must not depend on the
+    workgroup order."""
+    print(f"[case] grid order backward mode={mode} W={W} Hq={Hq} Hkv={Hkv} L={L} B={B}", flush=True)
+    d = inputs.prefill_inputs(inputs.Workload("t", "prefill", mode, B, Hq, Hkv, seqlen=L, seed=L + 7))
+    dout = inputs.normal((B, Hq, L, 128), L, 5)
+    q, k, v, s = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), dev_f32(d["sink"])
+    out = torch.empty((B, Hq, L, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sa.sinkattn_prefill_chunk_workspace_bytes(B, L, Hq, Hkv, L), dtype=torch.uint8, device="cuda")
+    sa.sinkattn_prefill_ex(mode, W, q, k, v, s, out, ws, lse=lse)
+    do = dev_bf16(dout)
+
+    def run():
+        g = sa.prefill_backward(mode, W, q, k, v, s, out, do, lse)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in g]
+
+    a, b = both_orders(run)
+    for name, x, y in zip(("dq", "dk", "dv", "dsink"), a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{name} depends on the workgroup order"
+    ref = oracle.prefill_backward(d["q"], d["k"], d["v"], d["sink"], dout, mode, W, SCALE)
+    for name, x, r in zip(("dq", "dk", "dv"), b, ref):
+        rel = np.linalg.norm(x - r) / np.linalg.norm(r)
+        assert rel <= 5e-3, f"{name}: rel-L2 {rel:.3e} against the oracle"
