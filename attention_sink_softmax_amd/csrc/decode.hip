@@ -38,6 +38,7 @@ constexpr float kLazyRescale = 8.f;                  // log2 growth of a max tha
 constexpr int kKBytes = kSlice * kDqk * 2;           // 12 KB: 12 blocks of 1 KB
 constexpr int kVBytes = kSlice * kDv * 2;            // 8 KB: 8 blocks of 1 KB
 constexpr int kBufBytes = kKBytes + kVBytes;         // one slice
+constexpr int kObRow = kDv + 4;                      // floats per column record in the wave merge
 constexpr int kPart = kDv + 4;                       // partial record: o[128], m, l, 2 pad
 constexpr int kDmaPerSlice = (kKBytes + kVBytes) / 1024;  // 20 wave-wide 1 KB loads
 // 8-bit (E4M3) cache: the same slice in half the bytes
@@ -115,7 +116,10 @@ __device__ __forceinline__ void dma16(const void *src, char *dst) {
 //      8 (k & 7) + (m ^ kswz(k)): the 16 lanes of an A-operand read (keys 0..15, one chunk)
 //      hit 16 distinct 16-byte slots of a 256-byte bank phase.
 //   V: block m = keys 4m .. 4m+3, 256 bytes each; row r keeps its 16-byte chunk c in slot
-//      c ^ 2r, so the transposing reads of 4 rows x 32 bytes hit distinct banks.
+//      c ^ 2r ^ 8 (m & 1).  A transposing read takes 4 rows x 32 bytes of one block per
+//      16-lane group, and the two groups that the banks serve together read blocks of
+//      opposite parity, so the 32 lanes hit 32 distinct 8-byte bank slots of a 256-byte
+//      phase (without the 8 (m & 1) term they met in pairs).
 
 // 8-bit cache layout of one slice (per wave, per buffer):
 //   K: for each 16-key half sb (3 KB), 16-byte chunk c (d = 16c .. 16c+15) of key k sits in
@@ -178,7 +182,7 @@ __device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
 // kSingle: every wave holds at most one slice (a split of at most 4 x 32 keys, e.g. a
 // 128-slot ring).  Its K goes straight into registers (the direct-to-LDS layout below is
 // lane-private: lane l writes exactly the 16 bytes it later reads as its MFMA operand) and
-// only V passes through LDS, 33 KB per workgroup, so four workgroups share a CU and a whole
+// only V passes through LDS, 34 KB per workgroup, so four workgroups share a CU and a whole
 // batch of rings is in flight at once.
 //
 // kFp8: K and V are E4M3 codes (8-bit cache, fast paged layout only); they are converted to
@@ -193,8 +197,10 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     // when a wave has more than one slice) so that the compiler can tell the loads in flight
     // into one from the reads of the other.  The single-slice buffer holds V only, plus room
     // for the merge's row statistics.
-    constexpr int kBufA = kSingle ? kVBytes + 256 : kSliceBytes;
+    constexpr int kBufA = kSingle ? kVBytes + 512 : kSliceBytes;
     __shared__ __attribute__((aligned(1024))) char bufA[kWaves][kBufA];
+    static_assert((kWaves * 16 * kObRow + 2 * kWaves * 16 + kWaves) * 4 <= kWaves * kBufA,
+                  "the wave merge's records fit in the slice buffers");
 
     const int split = p.reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
     const int by = p.reverse ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int t = min(max(4 * m + r, lo), hi);
-                dma16<kLoadNT>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kLoadNT>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r) ^ (8 * (m & 1))), vb + m * 1024);
             }
         } else {
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
@@ -346,7 +352,8 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int j = min(max(j0 + 4 * m + r, lo), hi);
-                dma16<kLoadNT>(kv_row(p, b, kvh, j, p.v, p.v_new, kDv, n, bad) + 8 * (s ^ (2 * r)), vb + m * 1024);
+                dma16<kLoadNT>(kv_row(p, b, kvh, j, p.v, p.v_new, kDv, n, bad) + 8 * (s ^ (2 * r) ^ (8 * (m & 1))),
+                               vb + m * 1024);
             }
         }
     };
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 vf = e4m3x8_to_bf16(codes);
             } else {
                 const int c = 2 * db + (c4 >> 1);
-                const int off = r * 256 + ((c ^ (2 * r)) * 16) + (c4 & 1) * 8;
+                const int off = r * 256 + ((c ^ (2 * r) ^ (8 * (q & 1))) * 16) + (c4 & 1) * 8;  // blocks q, 4 + q
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + q * 1024 + off));
                 const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (4 + q) * 1024 + off));
                 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -497,10 +504,11 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     }
 
     // ---- merge the 4 waves' states through LDS (reusing the slice buffers), one block of
-    // 16 columns at a time
+    // 16 columns at a time.  A column's record is padded to kObRow floats, so that the 16
+    // lanes of a 16-byte write (16 columns, the same 4 dv) hit 16 distinct bank slots.
     const bool wave_bad = __any(bad);
-    float *ob = reinterpret_cast<float *>(&bufA[0][0]);  // [4 waves][16 columns][128 dv]
-    float *red_m = ob + kWaves * 16 * kDv, *red_l = red_m + kWaves * 16, *red_bad = red_l + kWaves * 16;
+    float *ob = reinterpret_cast<float *>(&bufA[0][0]);  // [4 waves][16 columns][kObRow]
+    float *red_m = ob + kWaves * 16 * kObRow, *red_l = red_m + kWaves * 16, *red_bad = red_l + kWaves * 16;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const float lsum = sum_xor32(sum_xor16(l_run[cb]));
@@ -513,7 +521,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ob[(wave * 16 + hl) * kDv + 16 * db + 4 * q + e] = acc[cb][db][e];
+            for (int e = 0; e < 4; ++e) ob[(wave * 16 + hl) * kObRow + 16 * db + 4 * q + e] = acc[cb][db][e];
         __syncthreads();
 
         const bool any_bad = (red_bad[0] + red_bad[1] + red_bad[2] + red_bad[3]) != 0.f;
@@ -533,7 +541,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 const float sc = exp2f_fast(red_m[w * 16 + hh] - Mu);
                 L += sc * red_l[w * 16 + hh];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kDv + d0 + e];
+                for (int e = 0; e < 8; ++e) o[e] += sc * ob[(w * 16 + hh) * kObRow + d0 + e];
             }
             if (p.nsplit == 1) {
                 // final output: add the sink term once, normalise, scale, round to bf16; the

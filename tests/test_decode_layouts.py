@@ -65,3 +65,55 @@ def test_fp8_k_layout():
     assert len(seen) == 192
     for c in range(12):
         assert len({fp8_off(k, c) // 16 % 16 for k in range(16)}) == 16
+
+
+def bank_cycles(addrs, nbytes, group):
+    """Cycles of one LDS read: lanes served `group` at a time by 64 banks of 4 bytes (256
+    bytes per cycle); a bank that must serve k distinct words serialises k cycles."""
+    cyc = 0
+    for g0 in range(0, len(addrs), group):
+        words = {}
+        for a in addrs[g0:g0 + group]:
+            for wd in range(a // 4, (a + nbytes) // 4):
+                words.setdefault(wd % 64, set()).add(wd)
+        cyc += max(len(v) for v in words.values())
+    return cyc
+
+
+def bf16_v_slot(key, c):
+    """bf16 V: key (0..31) of a slice, 16-byte chunk c (0..15) of its 256-byte row ->
+    byte offset: block m = key / 4, row r = key % 4, slot c ^ 2r ^ 8 (m & 1)."""
+    m, r = key >> 2, key & 3
+    return m * 1024 + r * 256 + ((c ^ (2 * r) ^ (8 * (m & 1))) << 4)
+
+
+def test_bf16_v_layout():
+    # the load of block m: lane 16 r + s fetches chunk s ^ 2r ^ 8 (m & 1) of key 4m + r
+    seen = set()
+    for m in range(8):
+        for lane in range(64):
+            r, s = lane >> 4, lane & 15
+            c = s ^ (2 * r) ^ (8 * (m & 1))
+            assert bf16_v_slot(4 * m + r, c) == m * 1024 + lane * 16
+            seen.add((4 * m + r, c))
+    assert len(seen) == 32 * 16
+    # the transposing reads (two per dv block db): lane group q reads rows of block q (then
+    # 4 + q), row r = (lane & 15) >> 2 at chunk 2 db + ((lane & 3) >> 1), half lane & 1
+    for db in range(8):
+        for hi in (0, 1):
+            addrs = []
+            for lane in range(64):
+                q, hl = lane >> 4, lane & 15
+                r, c4 = hl >> 2, lane & 3
+                addrs.append(bf16_v_slot(4 * (4 * hi + q) + r, 2 * db + (c4 >> 1)) + 8 * (c4 & 1))
+            assert bank_cycles(addrs, 8, 32) == 2
+
+
+def test_wave_merge_records():
+    """The merge writes lane (hl, q)'s 4 floats of dv 16 db + 4 q to column hl's record:
+    with records of 132 floats the 16 lanes of one write cycle hit 16 distinct slots."""
+    for db in range(8):
+        addrs = [((lane & 15) * 132 + 16 * db + 4 * (lane >> 4)) * 4 for lane in range(64)]
+        assert bank_cycles(addrs, 16, 16) == 4
+        unpadded = [((lane & 15) * 128 + 16 * db + 4 * (lane >> 4)) * 4 for lane in range(64)]
+        assert bank_cycles(unpadded, 16, 16) == 64
