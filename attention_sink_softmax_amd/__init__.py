@@ -60,7 +60,8 @@ EXPORTS = ("sinkattn_prefill", "sinkattn_prefill_workspace_bytes", "sinkattn_pre
            "sinkattn_prefill_chunk_workspace_bytes", "sinkattn_prefill_ex", "sinkattn_decode",
            "sinkattn_decode_workspace_bytes", "sinkattn_decode_multi", "sinkattn_decode_multi_workspace_bytes",
            "sinkattn_decode_fp8", "sinkattn_decode_ex", "sinkattn_decode_ex_noalloc", "sinkattn_decode_verify",
-           "sinkattn_prefill_cached", "sinkattn_prefill_cached_workspace_bytes", "sinkattn_decode_prologue", "sinkattn_rope",
+           "sinkattn_prefill_cached", "sinkattn_prefill_cached_workspace_bytes", "sinkattn_decode_prologue",
+           "sinkattn_decode_step", "sinkattn_rope",
            "sinkattn_kv_append",
            "sinkattn_prefill_backward", "sinkattn_prefill_backward_workspace_bytes",
            "sinkattn_status_string")
@@ -110,6 +111,9 @@ def lib(path: str = LIB_PATH):
     L.sinkattn_decode_prologue.restype = I
     L.sinkattn_decode_prologue.argtypes = [ctypes.c_double, I, ctypes.POINTER(Dims), ctypes.c_int32, P, P, P, P,
                                            ctypes.POINTER(KVDesc), I, ctypes.c_float, ctypes.c_float, P, P]
+    L.sinkattn_decode_step.restype = I
+    L.sinkattn_decode_step.argtypes = [ctypes.c_double, I, ctypes.POINTER(Dims), P, P, P, ctypes.POINTER(KVDesc), P,
+                                       ctypes.c_int32, P, ctypes.POINTER(Epilogue), P, P]
     L.sinkattn_prefill_cached_workspace_bytes.restype = ctypes.c_size_t
     L.sinkattn_prefill_cached_workspace_bytes.argtypes = [I, I, ctypes.POINTER(Dims), ctypes.c_int32]
     L.sinkattn_prefill_cached.restype = I
@@ -721,6 +725,31 @@ def sinkattn_decode_prologue(theta: float, layout: int, q_in, q_out, k_new, v_ne
         rc = lib().sinkattn_decode_prologue(theta, window, ctypes.byref(d), n, _ptr(q_in), _ptr(q_out), _ptr(k_new),
                                             _ptr(v_new), ctypes.byref(desc), 1 if kv_fp8 else 0, k_scale, v_scale,
                                             _ptr(seq_lens), _stream_ptr(stream, q_in.device))
+    _raise(rc)
+
+
+def sinkattn_decode_step(theta: float, window: int, q_in, k_new, v_new, k_cache, v_cache, seq_lens, max_seq_len: int,
+                         sink, out, out_scale: float = 1.0, lse=None, scale: float | None = None, stream=None) -> None:
+    """One sliding-window decode step in one kernel: RoPE of the new token's queries q_in bf16
+    [B,Hq,1,192] and key k_new bf16 [B,Hkv,1,192] at position seq_lens[b] - 1, the write of the
+    rotated key and v_new bf16 [B,Hkv,1,128] into ring slot (seq_lens[b] - 1) mod window of
+    k_cache [B,Hkv,window,192] / v_cache [B,Hkv,window,128] (bf16), and the attention; out bf16
+    [B,Hq,1,128], lse float32 [B,Hq,1] or None.  q_in, k_new and v_new are not modified."""
+    import torch
+
+    B, Hq, Hkv, dqk, dv, desc, _, _ = _decode_args(q_in, 1, KV_RING, window, k_cache, v_cache, seq_lens, sink, out,
+                                                   None, None)
+    _dev_tensor(k_new, "k_new", torch.bfloat16, (B, Hkv, 1, dqk))
+    _dev_tensor(v_new, "v_new", torch.bfloat16, (B, Hkv, 1, dv))
+    for t in (k_new, v_new):
+        if t.device != q_in.device:
+            raise ValueError("all tensors must be on one device")
+    ep = _epilogue(out_scale, lse, (B, Hq, 1), q_in.device)
+    d = Dims(B, 0, Hq, Hkv, dqk, dv, dqk ** -0.5 if scale is None else scale)
+    with torch.cuda.device(q_in.device):
+        rc = lib().sinkattn_decode_step(theta, window, ctypes.byref(d), _ptr(q_in), _ptr(k_new), _ptr(v_new),
+                                        ctypes.byref(desc), _ptr(seq_lens), max_seq_len, _ptr(sink), ctypes.byref(ep),
+                                        _ptr(out), _stream_ptr(stream, q_in.device))
     _raise(rc)
 
 

@@ -20,6 +20,7 @@ constexpr int kDecodeKeyBlock = 128;                // keys per decode workgroup
 constexpr int kDecodeMaxChunk = 8192;               // keys per split at most (64 slices per wave)
 constexpr int kDecodeSingleSplit = 1024;            // key ranges this short are not split
 constexpr double kLog2eD = 1.4426950408889634;
+constexpr int kDecodeStepMaxSlots = 128;  // the fused decode step's single-slice kernel: 4 waves x 32 keys
 
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -286,10 +287,18 @@ namespace {
 // use_scratch: the split partials go to the library's own device scratch array instead of
 // the caller's workspace (which is then ignored).
 // k_new / v_new: the new tokens' keys and values beside the cache (both NULL: they are in it).
+// The fused decode step's extra inputs: the new token's key and value rows (before rotation)
+// and the RoPE base.
+struct StepArgs {
+    const void *k_step, *v_step;
+    double theta;
+};
+
 int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, const void *q, const sinkattn_kv *kv,
                   const void *k_new, const void *v_new, const int32_t *seq_lens, int32_t max_seq_len,
                   const float *sink, int fp8, float k_scale, float v_scale, const sinkattn_epilogue *ep, void *out,
-                  void *workspace, size_t workspace_bytes, void *stream, bool use_scratch = false) {
+                  void *workspace, size_t workspace_bytes, void *stream, bool use_scratch = false,
+                  const StepArgs *step = nullptr) {
     int st = check_dims(mode, window, d);
     if (st) return st;
     st = check_epilogue(ep);
@@ -321,6 +330,14 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
         (sink && misaligned(sink)) || (kv->layout == SINKATTN_KV_PAGED && misaligned(kv->block_table)))
         return SINKATTN_E_ALIGN;
     const DecodePlan pl = plan_decode(mode, window, d, q_len, max_seq_len);
+    if (step) {
+        // one kernel: a ring of at most 128 visible slots, one block of 16 query columns
+        if (kv->layout != SINKATTN_KV_RING || q_len != 1 || fp8 || side || pl.nsplit != 1 || pl.ncb != 1 ||
+            std::min(window, max_seq_len) > kDecodeStepMaxSlots)
+            return SINKATTN_E_UNSUPPORTED;
+        if (!step->k_step || !step->v_step) return SINKATTN_E_NULL;
+        if (misaligned(step->k_step) || misaligned(step->v_step)) return SINKATTN_E_ALIGN;
+    }
     if (use_scratch) {
         workspace = nullptr;
         workspace_bytes = 0;
@@ -367,6 +384,11 @@ int decode_common(int mode, int window, const sinkattn_dims *d, int32_t q_len, c
     p.lse = ep ? ep->lse : nullptr;
     p.nsplit = pl.nsplit;
     p.chunk = pl.chunk;
+    if (step) {
+        p.k_step = static_cast<const uint16_t *>(step->k_step);
+        p.v_step = static_cast<const uint16_t *>(step->v_step);
+        for (int i = 0; i < 32; ++i) p.inv_freq[i] = pow(step->theta, -2.0 * i / 64.0);
+    }
     if ((int64_t)p.Hkv * p.hchunks > 65535 || p.B > 65535 || (int64_t)p.B * p.Hq * p.q_len > INT32_MAX)
         return SINKATTN_E_SHAPE;
     return launch_decode(p, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
@@ -557,6 +579,16 @@ int sinkattn_decode_prologue(double theta, int window, const sinkattn_dims *d, i
     pp.hq = d->hq;
     for (int i = 0; i < 32; ++i) pp.inv_freq[i] = pow(theta, -2.0 * i / 64.0);
     return launch_decode_prologue(pp, static_cast<hipStream_t>(stream)) ? SINKATTN_E_DEVICE : SINKATTN_OK;
+}
+
+int sinkattn_decode_step(double theta, int window, const sinkattn_dims *d, const void *q_in, const void *k_new,
+                         const void *v_new, const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len,
+                         const float *sink, const sinkattn_epilogue *ep, void *out, void *stream) {
+    if (!d) return SINKATTN_E_NULL;
+    if (!(theta > 0.0) || !isfinite(theta)) return SINKATTN_E_SHAPE;
+    const StepArgs step{k_new, v_new, theta};
+    return decode_common(SINKATTN_SWA, window, d, 1, q_in, kv, nullptr, nullptr, seq_lens, max_seq_len, sink, 0, 1.f,
+                         1.f, ep, out, nullptr, 0, stream, false, &step);
 }
 
 int sinkattn_decode(int mode, int window, const sinkattn_dims *d, const void *q, const sinkattn_kv *kv,

@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "rope.h"
 #include "sinkattn.h"
 
 namespace sinkattn {
@@ -188,9 +189,17 @@ __device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
 // kFp8: K and V are E4M3 codes (8-bit cache, fast paged layout only); they are converted to
 // bf16 after the LDS read, the K scale is part of the logit scale and the V scale multiplies
 // the unnormalised output.
-template <bool kFast, bool kSingle, int NCB, bool kFp8 = false>
+//
+// kStep (with kSingle): the decode step fused ("MiMo-V2-Flash 模型架构深度拆解", CH 10.3 forward
+// steps 3-6 and the attention): the queries are rotated in registers (a lane holds both
+// halves of its rotation pairs), and the wave whose slice holds the new token's slot loads
+// the new key and value rows in place of that slot's old rows, rotates the key in
+// registers, and writes both to the ring.  Bit-identical to the prologue kernel followed by
+// the attention.
+template <bool kFast, bool kSingle, int NCB, bool kFp8 = false, bool kStep = false>
 __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(DecodeParams p) {
     static_assert(!kFp8 || (kFast && !kSingle), "8-bit caches use the double-buffered fast path");
+    static_assert(!kStep || (kFast && kSingle && NCB == 1 && !kFp8), "the fused step is a single-slice ring path");
     constexpr int kSliceBytes = kFp8 ? kBufBytes8 : kBufBytes;
     constexpr int kDma = kFp8 ? kDmaPerSlice8 : kDmaPerSlice;
     // slice buffers: even slices in bufA, odd ones in a second object (declared below, only
@@ -247,6 +256,18 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
         for (int kk = 0; kk < 6; ++kk) qf[cb][kk] = as_bf16x8(ok ? ldg16(qrow + 32 * kk) : u32x4{0, 0, 0, 0});
     }
+
+    // fused step: the rotary angles of position n - 1 (the queries are rotated once the slice
+    // has landed, next to the new key)
+    __shared__ float rope_cs[kRopePairs], rope_sn[kRopePairs];
+    if constexpr (kStep) {
+        rope_angles(p.inv_freq, n - 1, rope_cs, rope_sn);
+        __syncthreads();
+    }
+    // fused step: the new token's ring slot, and its key offset in this wave's slice
+    const int slot_new = n >= 1 ? (n - 1) % max(p.window, 1) : -1;
+    const int t_new = slot_new - (s_lo + kSlice * wave);
+    const bool step_owner = kStep && n >= 1 && t_new >= 0 && t_new < kSlice;  // wave-uniform
 
     bool bad = false;
 
@@ -313,6 +334,10 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 for (int sb = 0; sb < 2; ++sb) {
                     const int t = min(max(16 * sb + s, lo), hi);
                     const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
+                    // fused step: the new token's key (before rotation) in place of its slot's
+                    // old row
+                    if (kStep && step_owner && 16 * sb + s == t_new)
+                        kr = p.k_step + ((size_t)b * p.Hkv + kvh) * kDqk + 8 * r;
 #pragma unroll
                     for (int kk = 0; kk < 6; ++kk)
                         kreg[sb][kk] = as_bf16x8(ldg16_nt(kr + 32 * kk));
@@ -334,7 +359,9 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int t = min(max(4 * m + r, lo), hi);
-                dma16<kLoadNT>(vbase + (size_t)(off0 + t) * kDv + 8 * (s ^ (2 * r) ^ (8 * (m & 1))), vb + m * 1024);
+                const uint16_t *vr = vbase + (size_t)(off0 + t) * kDv;
+                if (kStep && step_owner && 4 * m + r == t_new) vr = p.v_step + ((size_t)b * p.Hkv + kvh) * kDv;  // new value
+                dma16<kLoadNT>(vr + 8 * (s ^ (2 * r) ^ (8 * (m & 1))), vb + m * 1024);
             }
         } else {
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
@@ -381,7 +408,44 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
         const char *kb = cur;
         const char *vb = kSingle ? cur : kb + (kFp8 ? kKBytes8 : kKBytes);
         const int j0 = s_lo + kSlice * (wave + kWaves * i);
-
+        if constexpr (kStep) {
+            // the queries: lane (hl, q) holds dimensions 8q .. 8q+7 in k-step 0 and their
+            // rotation partners 32 + 8q .. in k-step 1
+            {
+                u32x4 lo, hi;
+                rope_rotate8(__builtin_bit_cast(u32x4, qf[0][0]), __builtin_bit_cast(u32x4, qf[0][1]), 8 * q, rope_cs,
+                             rope_sn, lo, hi);
+                qf[0][0] = as_bf16x8(lo);
+                qf[0][1] = as_bf16x8(hi);
+            }
+            if (step_owner) {
+                // the lanes that hold the new key (lane (r, s): key 16 sb + s, dimensions
+                // 32 kk + 8 r) rotate it and write it to the ring; lane c < 16 moves chunk c
+                // of the new value row from the V tile to the ring
+                const int r = lane >> 4, s = lane & 15;
+                const size_t ring_row = ((size_t)b * p.Hkv + kvh) * p.window + slot_new;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (16 * sb + s == t_new) {
+                        u32x4 lo, hi;
+                        rope_rotate8(__builtin_bit_cast(u32x4, kreg[sb][0]), __builtin_bit_cast(u32x4, kreg[sb][1]),
+                                     8 * r, rope_cs, rope_sn, lo, hi);
+                        kreg[sb][0] = as_bf16x8(lo);
+                        kreg[sb][1] = as_bf16x8(hi);
+                        uint16_t *kdst = const_cast<uint16_t *>(p.k) + ring_row * kDqk + 8 * r;
+#pragma unroll
+                        for (int kk = 0; kk < 6; ++kk)
+                            *reinterpret_cast<u32x4 *>(kdst + 32 * kk) = __builtin_bit_cast(u32x4, kreg[sb][kk]);
+                    }
+                }
+                if (lane < 16) {
+                    const int m = t_new >> 2, rr = t_new & 3;
+                    const u32x4 vv =
+                        *reinterpret_cast<const u32x4 *>(vb + m * 1024 + rr * 256 + ((lane ^ (2 * rr) ^ (8 * (m & 1))) << 4));
+                    *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(p.v) + ring_row * kDv + 8 * lane) = vv;
+                }
+            }
+        }
         // ---- scores: S^T tiles of 16 keys x 16 columns
         f32x4 s[NCB][2];
 #pragma unroll
@@ -701,7 +765,11 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     const bool single =
         !p.k_new && !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
     const void *fn;
-    if (p.fp8) {
+    if (p.k_step) {
+        // the fused decode step: a ring of at most 128 visible slots, one 16-column block
+        if (!single || p.fp8 || p.q_len != 1) return -1;
+        fn = reinterpret_cast<const void *>(&decode_split_kernel<true, true, 1, false, true>);
+    } else if (p.fp8) {
         if (!p.paged || !fast) return -1;
         fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 4, true>)
              : p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 2, true>)

@@ -48,6 +48,12 @@ struct DecodeParams {
     float *lse;        // optional: natural-log log-sum-exp per row [B][Hq][q_len], or nullptr
     int nsplit, chunk;  // splits per sequence; keys per split (multiple of 128)
     int reverse;        // 1: workgroups take their work items in reverse order (grid_reversed())
+    // Fused decode step (a ring, one new token): q holds the new token's queries before
+    // rotation; its key (before rotation) and value rows k_step, v_step [B][Hkv][kDqk or kDv]
+    // are rotated (key) and written to ring slot (n - 1) mod window, and the attention uses them
+    // there.  nullptr otherwise.
+    const uint16_t *k_step, *v_step;
+    double inv_freq[32];  // theta^(-2i/64)
 };
 
 // Partial rotary embedding of x [batch][heads][rows][kDqk] in place; row r of sequence b sits

@@ -6,27 +6,11 @@
 // pieces.
 #include "common.h"
 #include "launch.h"
+#include "rope.h"
 
 namespace sinkattn {
 
 namespace {
-
-constexpr int kRopeDims = 64;            // rotated leading dimensions of the 192
-constexpr int kRopePairs = kRopeDims / 2;
-constexpr double kTwoPi = 6.283185307179586;
-
-// cos and sin of pos * theta^(-2i/64) for the 32 pairs, into LDS (threads 0..31).  The angle
-// is formed and reduced to [-pi, pi] in double precision (a position near 262144 times a
-// frequency near 1 would lose about 0.02 rad in float), then its sine and cosine are taken
-// in float.
-__device__ __forceinline__ void rope_angles(const double *inv_freq, int pos, float *cs, float *sn) {
-    const int i = threadIdx.x;
-    if (i < kRopePairs) {
-        double ang = (double)pos * inv_freq[i];
-        ang -= kTwoPi * __builtin_rint(ang / kTwoPi);
-        sincosf((float)ang, &sn[i], &cs[i]);
-    }
-}
 
 // Rotation task c (0..3) of one 192-wide row: dimensions 8c .. 8c+7 turn with 32 + 8c ..
 // 32 + 8c + 7 (pairs i = 8c + e), two 16-byte loads and two 16-byte stores; results rounded
@@ -34,23 +18,7 @@ __device__ __forceinline__ void rope_angles(const double *inv_freq, int pos, flo
 __device__ __forceinline__ void rope_task(const uint16_t *src, uint16_t *dst, int c, const float *cs, const float *sn,
                                           u32x4 &lo_out, u32x4 &hi_out) {
     const u32x4 lo = ldg16(src + 8 * c), hi = ldg16(src + kRopePairs + 8 * c);
-    uint32_t rl[4], rh[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        float ro[2], rp[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int i = 8 * c + 2 * w + h;
-            const float a = __builtin_bit_cast(float, h ? (lo[w] & 0xffff0000u) : (lo[w] << 16));
-            const float b = __builtin_bit_cast(float, h ? (hi[w] & 0xffff0000u) : (hi[w] << 16));
-            ro[h] = a * cs[i] - b * sn[i];
-            rp[h] = b * cs[i] + a * sn[i];
-        }
-        rl[w] = pack_bf16x2(ro[0], ro[1]);
-        rh[w] = pack_bf16x2(rp[0], rp[1]);
-    }
-    lo_out = u32x4{rl[0], rl[1], rl[2], rl[3]};
-    hi_out = u32x4{rh[0], rh[1], rh[2], rh[3]};
+    rope_rotate8(lo, hi, 8 * c, cs, sn, lo_out, hi_out);
     if (dst) {
         *reinterpret_cast<u32x4 *>(dst + 8 * c) = lo_out;
         *reinterpret_cast<u32x4 *>(dst + kRopePairs + 8 * c) = hi_out;

@@ -194,8 +194,9 @@ def main() -> int:
 
         runs[w.name] = (call, flops, nbytes)
 
-    # --- whole decode steps: the fused prologue (RoPE of q and the new key, cache write) then the
-    # attention, on the sliding-window rings (4 input sets rotate) and on the 256K pages
+    # --- whole decode steps: RoPE of q and the new key, the cache write and the attention; one
+    # kernel on the sliding-window rings (4 input sets rotate), the prologue kernel then the
+    # attention on the 256K pages
     for w, name in ((inputs.SWA_DECODE, "swa_decode_step_B128_ring"), (inputs.GA_DECODE, "ga_decode_step_B8_256K_paged")):
         if only and name not in only:
             continue
@@ -220,13 +221,18 @@ def main() -> int:
         theta = sa.SWA_ROPE_THETA if w.mode == 1 else sa.GA_ROPE_THETA
         visible = w.batch * (w.window if w.mode == 1 else w.ctx_hi)
         flops = visible * w.hq * FLOP_PER_PAIR
-        # the attention's K/V bytes plus the prologue's: q read and written, k/v read, the row written
-        nbytes = visible * w.hkv * (w.d_qk + w.d_v) * 2 + w.batch * (2 * w.hq * w.d_qk + 2 * w.hkv * (w.d_qk + w.d_v)) * 2
+        # the attention's K/V bytes plus the step's own: q and the new key and value read, the
+        # new row written
+        nbytes = visible * w.hkv * (w.d_qk + w.d_v) * 2 + w.batch * (w.hq * w.d_qk + 2 * w.hkv * (w.d_qk + w.d_v)) * 2
         state = {"i": 0}
 
         def call(w=w, sets=sets, qr=qr, out=out, ws=ws, layout=layout, theta=theta, state=state):
             s = sets[state["i"] % len(sets)]
             state["i"] += 1
+            if layout == sa.KV_RING:
+                sa.sinkattn_decode_step(theta, w.window, s["q"], s["kn"], s["vn"], s["k"], s["v"], s["lens"], w.ctx_hi,
+                                        s["sink"], out.view(w.batch, w.hq, 1, w.d_v))
+                return
             sa.sinkattn_decode_prologue(theta, layout, s["q"], qr, s["kn"], s["vn"], s["k"], s["v"], s["lens"],
                                         window=w.window, block_table=s["bt"])
             sa.sinkattn_decode(w.mode, w.window, qr[:, :, 0], layout, s["k"], s["v"], s["lens"], w.ctx_hi, s["sink"],
@@ -428,8 +434,8 @@ def main() -> int:
                    "swa_verify": "as swa_decode with q_len=4 drafted tokens whose K/V are held beside the rings",
                    "prefill_chunk": "the 32K prefills' last 16384 positions after a 16384-token prefix in 64-token "
                                     "permuted pages (GA) or a 128-slot ring (SWA)",
-                   "decode_step": "fused prologue (RoPE of q and the new key, cache write) + attention, on "
-                                  "swa_decode and ga_decode",
+                   "decode_step": "RoPE of q and the new key, cache write and attention: one kernel on "
+                                  "swa_decode's rings, the prologue kernel + attention on ga_decode's pages",
                    "ga_decode_fp8": "as ga_decode with an E4M3 cache, per-tensor scales 2^-6"},
         "decode_kv_read_GBps": dec["gbps"] if dec else None,
         "components": comp, "roofline": roofline, "roofline_decode": roofline_decode,

@@ -416,6 +416,32 @@ int sinkattn_decode_prologue(double theta, int window, const sinkattn_dims *d, i
                              const int32_t *seq_lens, void *stream);
 
 /*
+ * One whole sliding-window decode step in a single kernel ("MiMo-V2-Flash 模型架构深度拆解",
+ * CH 10.3 forward steps 3-6 and the attention): the partial RoPE of the new token's queries
+ * and key at position seq_lens[b] - 1, the write of the rotated key and the value into ring
+ * slot (seq_lens[b] - 1) mod window, and the sink attention of the new token over the ring.
+ * The output and the ring contents are bit-identical to sinkattn_decode_prologue (n_new = 1)
+ * followed by sinkattn_decode_ex on its rotated queries.
+ *   theta        10 000 for the sliding-window layers; > 0, finite
+ *   window       ring slots W (<= 128), the window of the attention
+ *   d            batch, hq, hkv (hq / hkv <= 16), scale (d_qk = 192, d_v = 128)
+ *   q_in         bf16 [batch][hq][1][192]: the new token's queries before rotation (not modified)
+ *   k_new, v_new bf16 [batch][hkv][1][192 / 128]: its key (before rotation) and value (not modified)
+ *   kv           a RING bf16 cache, [batch][hkv][W][192] and [batch][hkv][W][128]: written
+ *                at the new token's slot, read at every slot of the window
+ *   seq_lens     device int32 [batch]: tokens per sequence including the new one; a length
+ *                <= 0 writes nothing and gives a zero row; above max_seq_len, a NaN row
+ *   max_seq_len  an upper bound of seq_lens (>= 1)
+ *   sink, ep, out (bf16 [batch][hq][1][128]), stream  as sinkattn_decode_ex
+ * No workspace (one split).  Errors: SINKATTN_E_UNSUPPORTED for any other cache layout, a ring
+ * of more than 128 visible slots or more than 16 query heads per KV head (use
+ * sinkattn_decode_prologue and sinkattn_decode_ex there); otherwise as sinkattn_decode_ex.
+ */
+int sinkattn_decode_step(double theta, int window, const sinkattn_dims *d, const void *q_in, const void *k_new,
+                         const void *v_new, const sinkattn_kv *kv, const int32_t *seq_lens, int32_t max_seq_len,
+                         const float *sink, const sinkattn_epilogue *ep, void *out, void *stream);
+
+/*
  * Decode with every option: q_len new tokens (as sinkattn_decode_multi), a bf16 cache
  * (kv_fp8 = 0; k_scale and v_scale ignored) or an E4M3 cache (kv_fp8 = 1, as
  * sinkattn_decode_fp8), and an epilogue (lse: float32 [batch][hq][q_len]).  Errors as those

@@ -357,3 +357,24 @@ def test_decode_prologue_argument_errors(L):
     assert pro(q_in=None) == E_NULL
     assert pro(q_out=A + 8) == E_ALIGN
     assert pro(n=0, q_in=None) == OK
+
+
+def test_decode_step_argument_errors(L):
+    def step(theta=1e4, window=128, d=None, desc=None, kn=A, vn=A, q=A, ml=65536, ep=None):
+        d = d or dims(B=128, hq=64, hkv=8)
+        desc = desc if desc is not None else kv(layout=0, bt=None)
+        return L.sinkattn_decode_step(theta, window, ctypes.byref(d), q, kn, vn, ctypes.byref(desc), A, ml, None,
+                                      ep, A, None)
+    assert L.sinkattn_decode_step(1e4, 128, None, A, A, A, None, A, 100, None, None, A, None) == E_NULL
+    assert step(theta=0.0) == E_SHAPE
+    assert step(theta=float("inf")) == E_SHAPE
+    assert step(window=0) == E_SHAPE
+    assert step(desc=kv(layout=1, ps=64, mp=4096)) == E_UNSUP      # pages: prologue + decode instead
+    assert step(window=256) == E_UNSUP                             # more than 128 visible slots
+    assert step(d=dims(B=8, hq=64, hkv=2)) == E_UNSUP              # 32 query heads per KV head
+    assert step(kn=None) == E_NULL
+    assert step(vn=None) == E_NULL
+    assert step(q=None) == E_NULL
+    assert step(vn=A + 4) == E_ALIGN
+    assert step(ml=0) == E_SHAPE
+    assert step(d=dims(B=0, hq=64, hkv=8), q=None) == OK

@@ -108,3 +108,29 @@ def test_backward_grid_order(mode, W, Hq, Hkv, L, B):
     for name, x, r in zip(("dq", "dk", "dv"), b, ref):
         rel = np.linalg.norm(x - r) / np.linalg.norm(r)
         assert rel <= 5e-3, f"{name}: rel-L2 {rel:.3e} against the oracle"
+
+
+def test_decode_step_grid_order():
+    """The one-kernel decode step writes each ring's new slot from one wave and reads it back
+    from registers and LDS: the output and the rings must not depend on the workgroup order."""
+    print("[case] grid order fused decode step B=16 W=128", flush=True)
+    B, Hq, Hkv, W = 16, 64, 8, 128
+    lens = np.array([1, 5, 127, 128, 129, 300, 4000, 65536] * 2, np.int32)
+    q = inputs.normal((B, Hq, 1, 192), 95, 0)
+    kn = inputs.normal((B, Hkv, 1, 192), 95, 1)
+    vn = inputs.normal((B, Hkv, 1, 128), 95, 2)
+    kc = inputs.normal((B, Hkv, W, 192), 96, 1)
+    vc = inputs.normal((B, Hkv, W, 128), 96, 2)
+    sink = dev_f32(inputs.sink_values(Hq, 97))
+    qd, knd, vnd, ld = dev_bf16(q), dev_bf16(kn), dev_bf16(vn), dev_i32(lens)
+
+    def run():
+        kcd, vcd = dev_bf16(kc), dev_bf16(vc)
+        out = torch.empty((B, Hq, 1, 128), dtype=torch.bfloat16, device="cuda")
+        sa.sinkattn_decode_step(sa.SWA_ROPE_THETA, W, qd, knd, vnd, kcd, vcd, ld, int(lens.max()), sink, out)
+        torch.cuda.synchronize()
+        return [t.view(torch.int16).cpu().numpy() for t in (out, kcd, vcd)]
+
+    a, b = both_orders(run)
+    for name, x, y in zip(("output", "k ring", "v ring"), a, b):
+        assert np.array_equal(x, y), f"decode step {name} depends on the workgroup order"

@@ -246,3 +246,53 @@ def test_fused_prologue_is_separate_kernels(layout, fp8, n_new, in_place):
     assert np.array_equal(host_bits(kb), kn), "k_new was modified"
     if not in_place:
         assert np.array_equal(host_bits(qb), q), "q_in was modified"
+
+
+@pytest.mark.parametrize("out_scale,with_lse", [(1.0, False), (0.707, True)])
+def test_fused_decode_step(out_scale, with_lse):
+    """sinkattn_decode_step (RoPE, ring write and attention in one kernel) gives, bit for bit,
+    the output, log-sum-exp and ring contents of sinkattn_decode_prologue followed by
+    sinkattn_decode_ex, leaves its inputs unchanged, and matches the oracle's chain.  Lengths
+    cover a first token, a ring not yet full, exactly full, wrapped, and an empty sequence."""
+    B, Hq, Hkv, W = 10, 64, 8, 128
+    theta = sa.SWA_ROPE_THETA
+    lens = np.array([1, 2, 64, 127, 128, 129, 200, 4096, 0, 65536], np.int32)
+    ml = int(lens.max())
+    q = inputs.normal((B, Hq, 1, 192), 90, 0)
+    kn = inputs.normal((B, Hkv, 1, 192), 90, 1)
+    vn = inputs.normal((B, Hkv, 1, 128), 90, 2)
+    kc = inputs.normal((B, Hkv, W, 192), 91, 1)
+    vc = inputs.normal((B, Hkv, W, 128), 91, 2)
+    sink = inputs.sink_values(Hq, 92)
+    lensd, sinkd = dev_i32(lens), dev_f32(sink)
+    # separate kernels
+    qa, ka, va, kca, vca = dev_bf16(q), dev_bf16(kn), dev_bf16(vn), dev_bf16(kc), dev_bf16(vc)
+    qr = torch.empty_like(qa)
+    sa.sinkattn_decode_prologue(theta, sa.KV_RING, qa, qr, ka, va, kca, vca, lensd, window=W)
+    out_a = torch.empty((B, Hq, 1, 128), dtype=torch.bfloat16, device="cuda")
+    lse_a = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda") if with_lse else None
+    sa.sinkattn_decode_ex(oracle.SWA, W, 1, qr, sa.KV_RING, kca, vca, lensd, ml, sinkd, out_a, None,
+                          out_scale=out_scale, lse=lse_a)
+    # one kernel
+    qb, kb, vb, kcb, vcb = dev_bf16(q), dev_bf16(kn), dev_bf16(vn), dev_bf16(kc), dev_bf16(vc)
+    out_b = torch.empty((B, Hq, 1, 128), dtype=torch.bfloat16, device="cuda")
+    lse_b = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda") if with_lse else None
+    sa.sinkattn_decode_step(theta, W, qb, kb, vb, kcb, vcb, lensd, ml, sinkd, out_b, out_scale=out_scale, lse=lse_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out_b), host_bits(out_a)), "output differs from prologue + decode"
+    if with_lse:
+        assert np.array_equal(lse_b.cpu().numpy().view(np.uint32), lse_a.cpu().numpy().view(np.uint32))
+    assert np.array_equal(host_bits(kcb), host_bits(kca)) and np.array_equal(host_bits(vcb), host_bits(vca)), \
+        "ring contents differ from the prologue's"
+    for t, ref, name in ((qb, q, "q_in"), (kb, kn, "k_new"), (vb, vn, "v_new")):
+        assert np.array_equal(host_bits(t), ref), f"{name} was modified"
+    # the oracle's chain: rotated rows rounded to bf16 as the GPU stores them
+    pos = (lens - 1)[:, None, None]
+    qo = inputs.bf16_bits(oracle.rope(q, np.broadcast_to(pos, q.shape[:3]), theta).astype(np.float32))
+    kno = inputs.bf16_bits(oracle.rope(kn, np.broadcast_to(pos, kn.shape[:3]), theta).astype(np.float32))
+    kco, vco = kc.copy(), vc.copy()
+    oracle.kv_append(kco, vco, oracle.RING, kno, vn, lens, window=W)
+    ref, ref_lse = oracle.decode(qo, kco, vco, lens, sink, oracle.SWA, W, SCALE, oracle.RING, return_lse=True)
+    assert_parity(host_f32(out_b), out_scale * ref, "fused decode step vs oracle chain")
+    if with_lse:
+        check_lse(lse_b.cpu().numpy(), ref_lse, "fused decode step")
