@@ -197,7 +197,7 @@ __device__ __forceinline__ bool seq_valid(const DecodeParams &p, int n) {
 // registers, and writes both to the ring.  Bit-identical to the prologue kernel followed by
 // the attention.
 template <bool kFast, bool kSingle, int NCB, bool kFp8 = false, bool kStep = false>
-__global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, kSingle ? (kFast ? 4 : 2) : 1) void decode_split_kernel(DecodeParams p) {
     static_assert(!kFp8 || (kFast && !kSingle), "8-bit caches use the double-buffered fast path");
     static_assert(!kStep || (kFast && kSingle && NCB == 1 && !kFp8), "the fused step is a single-slice ring path");
     constexpr int kSliceBytes = kFp8 ? kBufBytes8 : kBufBytes;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                     const uint16_t *kr = kbase + (size_t)(off0 + t) * kDqk + 8 * r;
                     // fused step: the new token's key (before rotation) in place of its slot's
                     // old row
-                    if (kStep && step_owner && 16 * sb + s == t_new)
+                    if (kStep && step_owner && i == 0 && 16 * sb + s == t_new)
                         kr = p.k_step + ((size_t)b * p.Hkv + kvh) * kDqk + 8 * r;
 #pragma unroll
                     for (int kk = 0; kk < 6; ++kk)
@@ -360,20 +360,33 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
             for (int m = 0; m < 8; ++m) {
                 const int t = min(max(4 * m + r, lo), hi);
                 const uint16_t *vr = vbase + (size_t)(off0 + t) * kDv;
-                if (kStep && step_owner && 4 * m + r == t_new) vr = p.v_step + ((size_t)b * p.Hkv + kvh) * kDv;  // new value
+                if (kStep && step_owner && i == 0 && 4 * m + r == t_new) vr = p.v_step + ((size_t)b * p.Hkv + kvh) * kDv;  // new value
                 dma16<kLoadNT>(vr + 8 * (s ^ (2 * r) ^ (8 * (m & 1))), vb + m * 1024);
             }
         } else {
             const int lo = max(kbeg, j0), hi = min(kend, j0 + kSlice) - 1;
+            if constexpr (kSingle) {
+                // K rows looked up one by one, straight into the operand registers (lane (r, s):
+                // key 16 sb + s, dimensions 32 kk + 8 r)
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int j = min(max(j0 + 16 * sb + s, lo), hi);
+                    const uint16_t *kr = kv_row(p, b, kvh, j, p.k, p.k_new, kDqk, n, bad) + 8 * r;
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const int k16 = 8 * kh + (lane >> 3);
-                    const int j = min(max(j0 + 16 * sb + k16, lo), hi);
-                    const uint16_t *kr = kv_row(p, b, kvh, j, p.k, p.k_new, kDqk, n, bad) + 8 * ((lane & 7) ^ kswz(k16));
+                    for (int kk = 0; kk < 6; ++kk) kreg[sb][kk] = as_bf16x8(ldg16_nt(kr + 32 * kk));
+                }
+            } else {
 #pragma unroll
-                    for (int c = 0; c < 3; ++c) dma16<kLoadNT>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
+                for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const int k16 = 8 * kh + (lane >> 3);
+                        const int j = min(max(j0 + 16 * sb + k16, lo), hi);
+                        const uint16_t *kr =
+                            kv_row(p, b, kvh, j, p.k, p.k_new, kDqk, n, bad) + 8 * ((lane & 7) ^ kswz(k16));
+#pragma unroll
+                        for (int c = 0; c < 3; ++c) dma16<kLoadNT>(kr + 64 * c, kb + (6 * sb + 3 * kh + c) * 1024);
+                    }
                 }
             }
 #pragma unroll
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
 
     // Slice i: put slice i+1 in flight into `nxt`, wait for slice i, compute it from `cur`.
     auto step = [&](int i, const char *cur, char *nxt) __attribute__((always_inline)) {
-        if (i + 1 < nmine) {
+        if (!kSingle && i + 1 < nmine) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of `nxt` are done
             issue(i + 1, nxt);
             // vmcnt(kDma): the loads just issued may stay in flight; slice i has landed
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
                 qf[0][0] = as_bf16x8(lo);
                 qf[0][1] = as_bf16x8(hi);
             }
-            if (step_owner) {
+            if (step_owner && i == 0) {
                 // the lanes that hold the new key (lane (r, s): key 16 sb + s, dimensions
                 // 32 kk + 8 r) rotate it and write it to the ring; lane c < 16 moves chunk c
                 // of the new value row from the V tile to the ring
@@ -557,8 +570,18 @@ __global__ __launch_bounds__(256, kSingle ? 4 : 1) void decode_split_kernel(Deco
     };
 
     if (nmine > 0) issue(0, bufA[wave]);
-    if constexpr (kSingle) {
+    if constexpr (kSingle && kFast) {
         if (nmine > 0) step(0, bufA[wave], bufA[wave]);
+    } else if constexpr (kSingle) {
+        // one buffer: a wave's next slice (drafts beside a ring: at most two per wave) loads
+        // after it has read the current one
+        for (int i = 0; i < nmine; ++i) {
+            if (i > 0) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of its V tile are done
+                issue(i, bufA[wave]);
+            }
+            step(i, bufA[wave], bufA[wave]);
+        }
     } else {
         __shared__ __attribute__((aligned(1024))) char bufB[kWaves][kSliceBytes];
         for (int i = 0; i < nmine; i += 2) {
@@ -764,6 +787,10 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
     // a ring of at most 128 visible slots in one split: one slice per wave
     const bool single =
         !p.k_new && !p.paged && p.nsplit == 1 && p.ncb == 1 && min(p.window, p.max_seq_len) <= kWaves * kSlice;
+    // drafts beside a ring, whose keys (window + q_len - 1, from a 32-aligned start) take at
+    // most two slices per wave: K in registers, one slice buffer, two or more workgroups per CU
+    const bool single_side = p.k_new && !p.paged && !p.fp8 && p.nsplit == 1 && p.ncb <= 2 &&
+                             p.window + p.q_len - 1 + kSlice - 1 <= 2 * kWaves * kSlice;
     const void *fn;
     if (p.k_step) {
         // the fused decode step: a ring of at most 128 visible slots, one 16-column block
@@ -776,6 +803,9 @@ int launch_decode(const DecodeParams &prm, hipStream_t stream) {
                           : reinterpret_cast<const void *>(&decode_split_kernel<true, false, 1, true>);
     } else if (single) {
         fn = reinterpret_cast<const void *>(&decode_split_kernel<true, true, 1>);
+    } else if (single_side) {
+        fn = p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<false, true, 2>)
+                        : reinterpret_cast<const void *>(&decode_split_kernel<false, true, 1>);
     } else if (fast) {
         fn = p.ncb == 4   ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 4>)
              : p.ncb == 2 ? reinterpret_cast<const void *>(&decode_split_kernel<true, false, 2>)

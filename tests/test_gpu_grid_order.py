@@ -134,3 +134,27 @@ def test_decode_step_grid_order():
     a, b = both_orders(run)
     for name, x, y in zip(("output", "k ring", "v ring"), a, b):
         assert np.array_equal(x, y), f"decode step {name} depends on the workgroup order"
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(4, 64, 8), (1, 16, 2)])
+def test_ring_verify_grid_order(q_len, Hq, Hkv):
+    """Drafts beside a ring take the single-buffer kernel with K in registers and up to two
+    slices per wave: the output must not depend on the workgroup order."""
+    print(f"[case] grid order ring verify q_len={q_len} Hq={Hq} Hkv={Hkv}", flush=True)
+    W = 128
+    lens = np.array([1, 3, 127, 128, 131, 132, 500, 4096], np.int32)
+    B = len(lens)
+    q = dev_bf16(inputs.normal((B, Hq, q_len, 192), 98, 0))
+    kn = dev_bf16(inputs.normal((B, Hkv, q_len, 192), 98, 1))
+    vn = dev_bf16(inputs.normal((B, Hkv, q_len, 128), 98, 2))
+    kr = dev_bf16(inputs.normal((B, Hkv, W, 192), 98, 3))
+    vr = dev_bf16(inputs.normal((B, Hkv, W, 128), 98, 4))
+    sink, ld = dev_f32(inputs.sink_values(Hq, 99)), dev_i32(lens)
+
+    def run():
+        out = sa.decode_verify(sa.SWA, W, q, sa.KV_RING, kr, vr, kn, vn, ld, int(lens.max()), sink)
+        torch.cuda.synchronize()
+        return out.view(torch.int16).cpu().numpy()
+
+    a, b = both_orders(run)
+    assert np.array_equal(a, b), "ring verify output depends on the workgroup order"
