@@ -265,7 +265,17 @@ int sinkattn_prefill_cached(int mode, int window, const sinkattn_dims *d, int32_
     p.lse = ep ? ep->lse : nullptr;
     if (plan_prefill(p) > INT32_MAX) return SINKATTN_E_SHAPE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_gather_prefix(g, s)) return SINKATTN_E_DEVICE;
+    if (p.ring && !g.paged) {
+        // the ring kernel reads a ring prefix in place and the chunk's own rows: no gather
+        p.k = g.k_chunk;
+        p.v = g.v_chunk;
+        p.prefix_k = g.k_cache;
+        p.prefix_v = g.v_cache;
+        p.prefix_w = window;
+        p.prefix_base = c.base;
+    } else if (launch_gather_prefix(g, s)) {
+        return SINKATTN_E_DEVICE;
+    }
     return launch_prefill(p, s) ? SINKATTN_E_DEVICE : SINKATTN_OK;
 }
 

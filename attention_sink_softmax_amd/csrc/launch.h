@@ -28,6 +28,11 @@ struct PrefillParams {
     int ring;          // 1: the sliding-window ring kernel (then n_items = workgroups)
     int chunk;         // ring kernel: 32-position blocks per workgroup
     int reverse;       // 1: workgroups take their work items in reverse order (grid_reversed())
+    // Ring kernel over a prefix held in a ring cache, read in place: rows below q0 (positions
+    // prefix_base + row) come from prefix_k / prefix_v ([B][Hkv][prefix_w][d], position p in
+    // slot p mod prefix_w), and k / v then hold only the chunk's Lq rows.  nullptr otherwise.
+    const uint16_t *prefix_k, *prefix_v;
+    int prefix_w, prefix_base;
 };
 
 struct DecodeParams {

@@ -671,17 +671,27 @@ __device__ __forceinline__ int v_off(int r, int c) { return r * (kDv * 2) + ((c 
 struct SubStage {
     u32x4 k0, k1, v;
 };
+// Row `row` (0 .. L-1) of K or V: from k / v, or (kPrefix: a ring-cache prefix read in place)
+// rows below q0 from the ring and the rest from the chunk's rows.
+template <bool kPrefix>
+__device__ __forceinline__ const uint16_t *kv_src(const PrefillParams &p, const uint16_t *chunk,
+                                                  const uint16_t *prefix, int width, size_t bkv, int row) {
+    if constexpr (!kPrefix) return chunk + (bkv * p.L + row) * width;
+    if (row < p.q0) return prefix + (bkv * p.prefix_w + (p.prefix_base + row) % p.prefix_w) * width;
+    return chunk + (bkv * p.Lq + (row - p.q0)) * width;
+}
+template <bool kPrefix>
 __device__ __forceinline__ void sub_load(SubStage &st, const PrefillParams &p, int b, int kvh, int sub, int tid) {
-    const uint16_t *kbase = p.k + ((size_t)b * p.Hkv + kvh) * p.L * kDqk;
+    const size_t bkv = (size_t)b * p.Hkv + kvh;
     auto kchunk = [&](int idx) {
         const int blk = idx >> 6, l = idx & 63;
         const int row = min(32 * sub + 16 * (blk / 6) + (l & 15), p.L - 1);
-        return ldg16(kbase + (size_t)row * kDqk + (4 * (blk % 6) + (l >> 4)) * 8);
+        return ldg16(kv_src<kPrefix>(p, p.k, p.prefix_k, kDqk, bkv, row) + (4 * (blk % 6) + (l >> 4)) * 8);
     };
     st.k0 = kchunk(tid);
     st.k1 = kchunk(512 + (tid & 255));
     const int vrow = min(32 * sub + (tid >> 4), p.L - 1);
-    st.v = ldg16(p.v + (((size_t)b * p.Hkv + kvh) * p.L + vrow) * kDv + (tid & 15) * 8);
+    st.v = ldg16(kv_src<kPrefix>(p, p.v, p.prefix_v, kDv, bkv, vrow) + (tid & 15) * 8);
 }
 __device__ __forceinline__ void sub_store(const SubStage &st, char *slot, int tid) {
     *reinterpret_cast<u32x4 *>(slot + 16 * tid) = st.k0;
@@ -711,6 +721,7 @@ __device__ __forceinline__ void pv_sub(const char *Vs, const bf16x8 (&pf)[1][2],
     }
 }
 
+template <bool kPrefix>
 __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillParams p) {
     constexpr int HPW = 1;
     __shared__ __attribute__((aligned(1024))) char ring[kRingSlots * kSlotBytes];
@@ -750,7 +761,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int sub = j_lo - 4 + i;
-            if (sub >= 0) sub_load(st[i], p, b, kvh, sub, tid);
+            if (sub >= 0) sub_load<kPrefix>(st[i], p, b, kvh, sub, tid);
         }
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
@@ -776,7 +787,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
     // compiler can count them exactly and wait for nothing but what each use needs.
     auto step = [&](int j, const bf16x8 (&qc)[HPW][12], bf16x8 (&qn)[HPW][12]) {
         SubStage st;
-        sub_load(st, p, b, kvh, min(j + 1, nqb - 1), tid);
+        sub_load<kPrefix>(st, p, b, kvh, min(j + 1, nqb - 1), tid);
         {
             const WaveCtx wn = setup_block(min(j + 1, j_hi - 1));
             load_q<HPW>(p, ws, wn, qn);
@@ -967,7 +978,9 @@ int launch_prefill(const PrefillParams &prm, hipStream_t stream) {
     }
     void *args[] = {&p};
     if (p.ring)
-        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_swa_kernel), dim3(p.n_items),
+        return hipLaunchKernel(p.prefix_k ? reinterpret_cast<const void *>(&prefill_swa_kernel<true>)
+                                          : reinterpret_cast<const void *>(&prefill_swa_kernel<false>),
+                               dim3(p.n_items),
                                dim3(64 * kSwaWaves), args, 0, stream) == hipSuccess ? 0 : -1;
     const int grid = ((p.n_items + 8 * p.hgroups - 1) / (8 * p.hgroups)) * 8 * p.hgroups;
     if (causal_layout(p)) {
