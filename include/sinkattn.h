@@ -193,7 +193,9 @@ size_t sinkattn_prefill_cached_workspace_bytes(int mode, int window, const sinka
  *   sink, ep, out (bf16 [batch][hq][Lq][d_v]), stream as sinkattn_prefill_ex
  *   workspace  at least sinkattn_prefill_cached_workspace_bytes(mode, window, d, kv_len)
  * A first kernel gathers the visible prefix rows and the chunk into the workspace (one pass
- * over the keys the chunk sees); the prefill kernels then run on them.  A prefix page id
+ * over the keys the chunk sees); the prefill kernels then run on them.  A ring prefix with a
+ * window of at most 128 and a multiple of 8 query heads per KV head is read in place by the
+ * sliding-window kernel instead, and the workspace is not touched.  A prefix page id
  * outside [0, num_pages) is never read: every output row that sees that page is NaN, and so
  * may be rows that share a 32-key block with it.  Errors as
  * sinkattn_prefill_ex; a ring in global mode is SINKATTN_E_UNSUPPORTED; a page table too short
