@@ -43,17 +43,17 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "f2a9ba37b12732c51e470a422b21c038e7a34cb456b05fabb73ccafb2844186d",
-                          "read_GB": 3.5703, "written_GB": 0.5369},
+                          "sha256": "4033b609f4a013377c482cdb2cd6f898ee1bebdad117c185dc619baa859f6416",
+                          "read_GB": 3.5702, "written_GB": 0.5369},
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                           "sha256": "f2a9ba37b12732c51e470a422b21c038e7a34cb456b05fabb73ccafb2844186d",
-                           "read_GB": 1.0230, "written_GB": 0.5369},
-    "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                "sha256": "9b34272b4c02ac5816aa1232302c94d05e971aea7d43fdc70a89a5346640e041",
-                                "read_GB": 5.3879, "written_GB": 0.0179},
-    "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "common.h", "launch.h"),
-                                    "sha256": "9b34272b4c02ac5816aa1232302c94d05e971aea7d43fdc70a89a5346640e041",
-                                    "read_GB": 2.7036, "written_GB": 0.0179},
+                           "sha256": "4033b609f4a013377c482cdb2cd6f898ee1bebdad117c185dc619baa859f6416",
+                           "read_GB": 1.0234, "written_GB": 0.5369},
+    "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "rope.h", "common.h", "launch.h"),
+                                "sha256": "c2932efa1b9310d5a4ca2e16e3a3283dddac92d511d9989fe6ff5da9e140cb42",
+                                "read_GB": 5.3879, "written_GB": 0.0180},
+    "ga_decode_B8_256K_paged_fp8": {"sources": ("decode.hip", "rope.h", "common.h", "launch.h"),
+                                    "sha256": "c2932efa1b9310d5a4ca2e16e3a3283dddac92d511d9989fe6ff5da9e140cb42",
+                                    "read_GB": 2.7036, "written_GB": 0.0180},
 }
 
 
