@@ -66,13 +66,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // A 16-lane group of an MFMA operand read (16 consecutive rows, one chunk) is one
 // contiguous 256-byte run, and for a fixed lane the offsets of all (sub-block, k-step)
 // reads differ only by compile-time constants.
-__device__ __forceinline__ int k_off(int row, int chunk) {
+[[maybe_unused]] __device__ __forceinline__ int k_off(int row, int chunk) {
     return ((row >> 4) * 6 + (chunk >> 2)) * 1024 + ((chunk & 3) * 16 + (row & 15)) * 16;
 }
 // ---- V^T tile [128 dv][64 keys] of bf16: 16 blocks of 1 KB; block (rg, kg) holds dv rows
 // 16rg..16rg+15 and key chunks 4kg..4kg+3 (8 keys each, in MFMA k-order); chunk c of row r
 // sits in slot 16c + r.  Byte offsets.
-__device__ __forceinline__ int vt_off(int row, int chunk) {
+[[maybe_unused]] __device__ __forceinline__ int vt_off(int row, int chunk) {
     return ((row >> 4) * 2 + (chunk >> 2)) * 1024 + ((chunk & 3) * 16 + (row & 15)) * 16;
 }
 // Key (within a 64-key tile) supplied as element e by lane group g for the 16-key group gam.
@@ -147,17 +147,6 @@ __device__ __forceinline__ void dma16_opaque(__amdgpu_buffer_rsrc_t r, char *lds
         : "s"(base), "v"(voff), "s"(r)
         : "memory");
 }
-__device__ __forceinline__ void dma_k_block_opaque(char *Kt, const TileSrc &src, int kb, int L, int blk, int lane) {
-    const int rg = blk / 6, cg = blk % 6;
-    const int row = min(kb + 16 * rg + (lane & 15), L - 1);
-    dma16_opaque(src.k, Kt + blk * 1024, row * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16);
-}
-__device__ __forceinline__ void dma_vt_block_opaque(char *Vt, const TileSrc &src, int kb, int blk, int lane) {
-    const int rg = blk >> 1, kg = blk & 1;
-    const int row = 16 * rg + (lane & 15);
-    dma16_opaque(src.vt, Vt + blk * 1024, kb * (kDv * 2) + row * (kBN * 2) + (4 * kg + (lane >> 4)) * 16);
-}
-
 // Wave w issues blocks w, w+4, ... of the 24 K and 16 V^T blocks of a tile (10 per wave).
 __device__ __forceinline__ void issue_tile(char *Kt, char *Vt, const TileSrc &src, int kb, int L, int wave, int lane) {
 #pragma unroll
@@ -209,9 +198,10 @@ __device__ __forceinline__ bool row_max(const f32x16 (&s)[HPW], const float (&m_
     bool grow = false;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-        float mx = -INFINITY;
+        // one v_max then seven v_max3
+        float mx = __builtin_fmaxf(s[h][0], s[h][1]);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[h][r], s[h][r + 1]));
+        for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[h][r]), s[h][r + 1]);
         mx = max_xor32(mx) * w.c;
         mnew[h] = fmaxf(m_run[h], mx);
         grow |= mnew[h] > m_run[h] + kLazyRescale;
@@ -219,11 +209,19 @@ __device__ __forceinline__ bool row_max(const f32x16 (&s)[HPW], const float (&m_
     return grow;
 }
 
+// The exponent offset of probs: -m, or 0 while a row has no reference yet (m = -inf).  Kept
+// beside m and recomputed only when m moves.
+template <int HPW>
+__device__ __forceinline__ void neg_ref(const float (&m_run)[HPW], float (&neg)[HPW]) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) neg[h] = (m_run[h] == -INFINITY) ? 0.f : -m_run[h];
+}
+
 // Lazy rescale: when some row of the wave grew past the threshold, every row moves its
 // reference to its new max and rescales its accumulator and denominator.
 template <int HPW>
 __device__ __forceinline__ void rescale(bool grow, const float (&mnew)[HPW], f32x16 (&acc)[HPW][4],
-                                        float (&m_run)[HPW], float (&l_run)[HPW]) {
+                                        float (&m_run)[HPW], float (&l_run)[HPW], float (&neg)[HPW]) {
     if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
@@ -235,32 +233,33 @@ __device__ __forceinline__ void rescale(bool grow, const float (&mnew)[HPW], f32
             for (int db = 0; db < 4; ++db) acc[h][db] *= alpha;
             m_run[h] = mnew[h];
         }
+        neg_ref<HPW>(m_run, neg);
     }
 }
 
 // Running max and lazy rescale together (general kernel).
 template <int HPW>
 __device__ __forceinline__ void row_update(const f32x16 (&s)[HPW], f32x16 (&acc)[HPW][4], float (&m_run)[HPW],
-                                           float (&l_run)[HPW], const WaveCtx &w) {
+                                           float (&l_run)[HPW], float (&neg)[HPW], const WaveCtx &w) {
     float mnew[HPW];
     const bool grow = row_max<HPW>(s, m_run, mnew, w);
-    rescale<HPW>(grow, mnew, acc, m_run, l_run);
+    rescale<HPW>(grow, mnew, acc, m_run, l_run, neg);
 }
 
 // P = 2^(c*s - m) rounded to bf16 in the B-operand layout of the PV product; l += sum(P).
+// neg is neg_ref of the running max.
 template <int HPW>
-__device__ __forceinline__ void probs(const f32x16 (&s)[HPW], const float (&m_run)[HPW], float (&l_run)[HPW],
+__device__ __forceinline__ void probs(const f32x16 (&s)[HPW], const float (&neg)[HPW], float (&l_run)[HPW],
                                       bf16x8 (&pf)[HPW][2], const WaveCtx &w) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-        const float neg = (m_run[h] == -INFINITY) ? 0.f : -m_run[h];
-        float ps = 0.f;
+        float ps;
         uint32_t pk[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float p0 = exp2f_fast(__builtin_fmaf(s[h][2 * r], w.c, neg));
-            const float p1 = exp2f_fast(__builtin_fmaf(s[h][2 * r + 1], w.c, neg));
-            ps += p0 + p1;
+            const float p0 = exp2f_fast(__builtin_fmaf(s[h][2 * r], w.c, neg[h]));
+            const float p1 = exp2f_fast(__builtin_fmaf(s[h][2 * r + 1], w.c, neg[h]));
+            ps = r == 0 ? p0 + p1 : ps + (p0 + p1);
             pk[r] = pack_bf16x2(p0, p1);
         }
         l_run[h] += ps;
@@ -293,7 +292,7 @@ __device__ __forceinline__ void pv_accum(const char *Vt, int sb, const bf16x8 (&
 template <int HPW>
 __device__ __forceinline__ void compute_tile(const char *Kt, const char *Vt, int kb, const bf16x8 (&qf)[HPW][12],
                                              f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
-                                             const WaveCtx &w) {
+                                             float (&neg)[HPW], const WaveCtx &w) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         const int k0 = kb + 32 * sb;
@@ -303,9 +302,9 @@ __device__ __forceinline__ void compute_tile(const char *Kt, const char *Vt, int
         f32x16 s[HPW];
         qk_scores<HPW>(Kt, sb, qf, s, w);
         if (!full) mask_scores<HPW>(s, kb, sb, w);
-        row_update<HPW>(s, acc, m_run, l_run, w);
+        row_update<HPW>(s, acc, m_run, l_run, neg, w);
         bf16x8 pf[HPW][2];
-        probs<HPW>(s, m_run, l_run, pf, w);
+        probs<HPW>(s, neg, l_run, pf, w);
         pv_accum<HPW>(Vt, sb, pf, acc, w);
     }
 }
@@ -365,7 +364,8 @@ __device__ __forceinline__ void load_q(const PrefillParams &p, const WaveSetup &
 // on one lane of the pair that shares the row).  No sink: m = -inf, l = 0.
 template <int HPW>
 __device__ __forceinline__ void init_state_from(const float (&sink)[HPW], const WaveCtx &w, f32x16 (&acc)[HPW][4],
-                                                float (&m_run)[HPW], float (&l_run)[HPW], bool (&sink_inf)[HPW]) {
+                                                float (&m_run)[HPW], float (&l_run)[HPW], bool (&sink_inf)[HPW],
+                                                float (&neg)[HPW]) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
         const float sk = sink[h];
@@ -376,6 +376,7 @@ __device__ __forceinline__ void init_state_from(const float (&sink)[HPW], const 
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[h][db] = f32x16{};
     }
+    neg_ref<HPW>(m_run, neg);
 }
 template <int HPW>
 __device__ __forceinline__ void load_sink(const PrefillParams &p, const WaveSetup &ws, float (&sink)[HPW]) {
@@ -385,10 +386,10 @@ __device__ __forceinline__ void load_sink(const PrefillParams &p, const WaveSetu
 template <int HPW>
 __device__ __forceinline__ void init_state(const PrefillParams &p, const WaveSetup &ws, const WaveCtx &w,
                                            f32x16 (&acc)[HPW][4], float (&m_run)[HPW], float (&l_run)[HPW],
-                                           bool (&sink_inf)[HPW]) {
+                                           bool (&sink_inf)[HPW], float (&neg)[HPW]) {
     float sink[HPW];
     load_sink<HPW>(p, ws, sink);
-    init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf);
+    init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf, neg);
 }
 
 // O = out_scale * acc / l rounded to bf16; lane holds dv 32db + 8i + 4g + j of query qi (row
@@ -496,10 +497,10 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 
     bf16x8 qf[HPW][12];
     load_q<HPW>(p, ws, w, qf);
-    float m_run[HPW], l_run[HPW];
+    float m_run[HPW], l_run[HPW], neg[HPW];
     bool sink_inf[HPW];
     f32x16 acc[HPW][4];
-    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
+    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf, neg);
 
     const TileSrc src = tile_src(p, ws.b, ws.kvh);
     const int k_lo = p.swa ? max(0, ws.wg_q0 - p.window + 1) : 0;
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
     auto step = [&](int kt, const char *Kc, const char *Vc, char *Kn, char *Vn) {
         const bool more = kt < t1;
         if (more) issue_tile(Kn, Vn, src, (kt + 1) * kBN, p.L, wave, lane);
-        if (wave_live) compute_tile<HPW>(Kc, Vc, kt * kBN, qf, acc, m_run, l_run, w);
+        if (wave_live) compute_tile<HPW>(Kc, Vc, kt * kBN, qf, acc, m_run, l_run, neg, w);
         if (more) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 has landed
         __syncthreads();
     };
@@ -543,6 +544,50 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 // reference max, so the accumulator and the denominator always share one reference.
 constexpr int kCausalWaves = 8;
 
+// The tile of keys kb .. kb + 63 of one (sequence, KV head) as buffer resources that start at
+// row kb, so that the lane part of every load is the same for all tiles.  K rows past the
+// sequence end fall outside the K range and read zeros (their scores are masked); the V^T
+// copy is padded to whole tiles.
+__device__ __forceinline__ TileSrc tile_src_at(const PrefillParams &p, int b, int kvh, int kb) {
+    constexpr int kRawDword3 = 0x00020000;  // untyped 32-bit data, no swizzle
+    const size_t bh = (size_t)b * p.Hkv + kvh;
+    TileSrc t;
+    t.k = __builtin_amdgcn_make_buffer_rsrc((void *)(p.k + (bh * p.L + kb) * kDqk), 0, (p.L - kb) * (kDqk * 2),
+                                            kRawDword3);
+    t.vt = __builtin_amdgcn_make_buffer_rsrc((void *)(p.vt + bh * kDv * p.lpad + (size_t)kb * kDv), 0,
+                                             (p.lpad - kb) * (kDv * 2), kRawDword3);
+    return t;
+}
+
+// An LDS address in a register the compiler cannot see into.  Reads at constant distances from
+// it take the distance as the instruction's 16-bit offset; from a known buffer address the
+// compiler would add every offset above 64 KB with an instruction of its own.
+__device__ __forceinline__ uint32_t lds_reg(const char *p) {
+    uint32_t a = (uint32_t)(uintptr_t)(lds_void *)p;
+    asm("" : "+v"(a));
+    return a;
+}
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t a, int off) { return *(lds_bf16x8 *)(a + off); }
+
+// qk_scores and pv_accum of one head reading through such registers: kr = K tile + klane,
+// vr = V^T tile + vlane.
+__device__ __forceinline__ void qk_scores_r(uint32_t kr, int sb, const bf16x8 (&qf)[1][12], f32x16 (&s)[1]) {
+    s[0] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(kr, sb * 12288 + (kk >> 1) * 1024 + (kk & 1) * 512),
+                                                       qf[0][kk], s[0], 0, 0, 0);
+}
+__device__ __forceinline__ void pv_accum_r(uint32_t vr, int sb, const bf16x8 (&pf)[1][2], f32x16 (&acc)[1][4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(vr, db * 4096 + sb * 1024 + k2 * 512),
+                                                                 pf[0][k2], acc[0][db], 0, 0, 0);
+}
+
 // Wave w of the causal kernel issues blocks w, w+8, ... of the 24 K and 16 V^T blocks.
 __device__ __forceinline__ void dma_k_part(char *Kt, const TileSrc &src, int kb, int L, int wave, int lane) {
 #pragma unroll
@@ -570,16 +615,31 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
 
     bf16x8 qf[HPW][12];
     load_q<HPW>(p, ws, w, qf);
-    float m_run[HPW], l_run[HPW];
+    float m_run[HPW], l_run[HPW], neg[HPW];
     bool sink_inf[HPW];
     f32x16 acc[HPW][4];
-    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf);
+    init_state<HPW>(p, ws, w, acc, m_run, l_run, sink_inf, neg);
 
     const TileSrc src = tile_src(p, ws.b, ws.kvh);
     const int t1 = (ws.wg_q1 - 1) / kBN;  // tiles 0..t1
 
     // a sub-block needs masking when its last key lies past the first query row
     auto masked = [&](int t, int sb) { return t * kBN + 32 * sb + 31 > w.qpos0; };
+    // lane parts of this wave's tile loads (K blocks wave + 8i, V^T blocks wave + 8j) against
+    // resources that start at the tile's first row
+    int kl[3], vl[2];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int blk = wave + kCausalWaves * i, rg = blk / 6, cg = blk % 6;
+        kl[i] = (16 * rg + (lane & 15)) * (kDqk * 2) + (4 * cg + (lane >> 4)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int blk = wave + kCausalWaves * j, rg = blk >> 1, kg = blk & 1;
+        vl[j] = (16 * rg + (lane & 15)) * (kBN * 2) + (4 * kg + (lane >> 4)) * 16;
+    }
+    const uint32_t kr0 = lds_reg(K0 + w.klane), kr1 = lds_reg(K1 + w.klane), kr2 = lds_reg(K2 + w.klane);
+    const uint32_t vr0 = lds_reg(V0 + w.vlane), vr1 = lds_reg(V1 + w.vlane), vr2 = lds_reg(V2 + w.vlane);
 
     dma_k_part(K0, src, 0, p.L, wave, lane);
     dma_vt_part(V0, src, 0, wave, lane);
@@ -594,45 +654,45 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     bf16x8 pf[HPW][2];
     qk_scores<HPW>(K0, 0, qf, s0, w);
     if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
-    row_update<HPW>(s0, acc, m_run, l_run, w);
+    row_update<HPW>(s0, acc, m_run, l_run, neg, w);
 
     // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).  The loads of
     // tile t+2 are issued unconditionally (past the last tile they re-read tile t1 into a
     // buffer nobody reads any more), so that no branch splits phases C and D.
-    auto step = [&](int t, const char *Kc, const char *Kn, const char *Vc, char *Kf, char *Vf) {
+    auto step = [&](int t, uint32_t Kc, uint32_t Kn, uint32_t Vc, char *Kf, char *Vf) {
         const int kb = t * kBN;
-        const int kb_next = min(t + 2, t1) * kBN;
+        const TileSrc nsrc = tile_src_at(p, ws.b, ws.kvh, min(t + 2, t1) * kBN);
         float mnew[HPW];
         bool grow;
         // phase A: S(t,1) with P(t,0)
-        qk_scores<HPW>(Kc, 1, qf, s1, w);
-        probs<HPW>(s0, m_run, l_run, pf, w);
+        qk_scores_r(Kc, 1, qf, s1);
+        probs<HPW>(s0, neg, l_run, pf, w);
         if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
         // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
-        pv_accum<HPW>(Vc, 0, pf, acc, w);
+        pv_accum_r(Vc, 0, pf, acc);
         grow = row_max<HPW>(s1, m_run, mnew, w);
-        rescale<HPW>(grow, mnew, acc, m_run, l_run);
+        rescale<HPW>(grow, mnew, acc, m_run, l_run, neg);
         // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         // phase C: S(t+1,0) with P(t,1) and the K loads of tile t+2 (the scores of tile t+1
         // are unused after the last tile)
-        qk_scores<HPW>(Kn, 0, qf, s0, w);
-        probs<HPW>(s1, m_run, l_run, pf, w);
+        qk_scores_r(Kn, 0, qf, s0);
+        probs<HPW>(s1, neg, l_run, pf, w);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) dma_k_block_opaque(Kf, src, kb_next, p.L, wave + kCausalWaves * i, lane);
+        for (int i = 0; i < 3; ++i) dma16_opaque(nsrc.k, Kf + (wave + kCausalWaves * i) * 1024, kl[i]);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
         // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
-        pv_accum<HPW>(Vc, 1, pf, acc, w);
+        pv_accum_r(Vc, 1, pf, acc);
         grow = row_max<HPW>(s0, m_run, mnew, w);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma_vt_block_opaque(Vf, src, kb_next, wave + kCausalWaves * i, lane);
-        if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run);
+        for (int i = 0; i < 2; ++i) dma16_opaque(nsrc.vt, Vf + (wave + kCausalWaves * i) * 1024, vl[i]);
+        if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run, neg);
     };
     for (int t = 0; t <= t1; t += 3) {
-        step(t, K0, K1, V0, K2, V2);
-        if (t + 1 <= t1) step(t + 1, K1, K2, V1, K0, V0);
-        if (t + 2 <= t1) step(t + 2, K2, K0, V2, K1, V1);
+        step(t, kr0, kr1, vr0, K2, V2);
+        if (t + 1 <= t1) step(t + 1, kr1, kr2, vr1, K0, V0);
+        if (t + 2 <= t1) step(t + 2, kr2, kr0, vr2, K1, V1);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
     store_out<HPW>(p, ws, w, true, acc, m_run, l_run, sink_inf);
@@ -793,10 +853,10 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
             load_q<HPW>(p, ws, wn, qn);
         }
         const WaveCtx w = setup_block(j);
-        float m_run[HPW], l_run[HPW];
+        float m_run[HPW], l_run[HPW], neg[HPW];
         bool sink_inf[HPW];
         f32x16 acc[HPW][4];
-        init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf);
+        init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf, neg);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int sub = j - 4 + i, k0 = kBQ * sub;
@@ -807,9 +867,9 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
             f32x16 sc[HPW];
             qk_scores<HPW>(slot, 0, qc, sc, w);
             if (!full) mask_scores<HPW>(sc, k0, 0, w);
-            row_update<HPW>(sc, acc, m_run, l_run, w);
+            row_update<HPW>(sc, acc, m_run, l_run, neg, w);
             bf16x8 pf[HPW][2];
-            probs<HPW>(sc, m_run, l_run, pf, w);
+            probs<HPW>(sc, neg, l_run, pf, w);
             pv_sub(slot + kSubKBytes, pf, acc, w);
         }
         // slot (j + 1) % 6 held sub-block j - 5, outside this block's band
