@@ -532,10 +532,10 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 // overlaps the matrix products of another:
 //
 //   phase A: S(t,1) = K(t)Q^T              with  P(t,0) = exp(S(t,0))
-//   phase B: O += V(t)^T P(t,0)            with  max of S(t,1), then the rare rescale
+//   phase B: O += V(t)^T P(t,0)            with  growth test of S(t,1), then the rare rescale
 //   barrier; tiles t+2 start streaming in
 //   phase C: S(t+1,0) = K(t+1)Q^T          with  P(t,1) = exp(S(t,1))
-//   phase D: O += V(t)^T P(t,1)            with  max of S(t+1,0), then the rare rescale
+//   phase D: O += V(t)^T P(t,1)            with  growth test of S(t+1,0), then the rare rescale
 //
 // K runs one tile ahead of V, so both are triple buffered (120 KB of LDS); loads issued
 // after the barrier of tile t land by the barrier of tile t+1.  The loop is unrolled by 3
@@ -569,6 +569,26 @@ __device__ __forceinline__ uint32_t lds_reg(const char *p) {
 }
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t a, int off) { return *(lds_bf16x8 *)(a + off); }
+
+// The lazy-rescale test of one sub-block without the row max: a lane's largest raw score
+// against thr = (m + kLazyRescale) / c, the threshold in raw-score units (the scale is
+// positive).  Only the rare rescale needs the max of the row, from both lanes of the pair.
+__device__ __forceinline__ bool lane_grows(const f32x16 &s, float thr, float &mx) {
+    mx = __builtin_fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
+    return mx > thr;
+}
+__device__ __forceinline__ float grow_threshold(float m, const WaveCtx &w) { return (m + kLazyRescale) / w.c; }
+// The rescale of rescale(), for lanes whose largest raw score is mx; thr follows the new max.
+__device__ __forceinline__ void rescale_lane(bool grow, float mx, f32x16 (&acc)[1][4], float (&m_run)[1],
+                                             float (&l_run)[1], float (&neg)[1], float &thr, const WaveCtx &w) {
+    if (__builtin_expect(__any(grow), 0)) {
+        float mnew[1] = {fmaxf(m_run[0], max_xor32(mx) * w.c)};
+        rescale<1>(true, mnew, acc, m_run, l_run, neg);
+        thr = grow_threshold(m_run[0], w);
+    }
+}
 
 // qk_scores and pv_accum of one head reading through such registers: kr = K tile + klane,
 // vr = V^T tile + vlane.
@@ -655,6 +675,7 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     qk_scores<HPW>(K0, 0, qf, s0, w);
     if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
     row_update<HPW>(s0, acc, m_run, l_run, neg, w);
+    float thr = grow_threshold(m_run[0], w);
 
     // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).  The loads of
     // tile t+2 are issued unconditionally (past the last tile they re-read tile t1 into a
@@ -662,16 +683,16 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     auto step = [&](int t, uint32_t Kc, uint32_t Kn, uint32_t Vc, char *Kf, char *Vf) {
         const int kb = t * kBN;
         const TileSrc nsrc = tile_src_at(p, ws.b, ws.kvh, min(t + 2, t1) * kBN);
-        float mnew[HPW];
+        float mx;
         bool grow;
         // phase A: S(t,1) with P(t,0)
         qk_scores_r(Kc, 1, qf, s1);
         probs<HPW>(s0, neg, l_run, pf, w);
         if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
-        // phase B: O += V(t)^T P(t,0) with the max of S(t,1)
+        // phase B: O += V(t)^T P(t,0) with the growth test of S(t,1)
         pv_accum_r(Vc, 0, pf, acc);
-        grow = row_max<HPW>(s1, m_run, mnew, w);
-        rescale<HPW>(grow, mnew, acc, m_run, l_run, neg);
+        grow = lane_grows(s1[0], thr, mx);
+        rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
         // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
@@ -682,12 +703,13 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
 #pragma unroll
         for (int i = 0; i < 3; ++i) dma16_opaque(nsrc.k, Kf + (wave + kCausalWaves * i) * 1024, kl[i]);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
-        // phase D: O += V(t)^T P(t,1) with the max of S(t+1,0) and the V^T loads of tile t+2
+        // phase D: O += V(t)^T P(t,1) with the growth test of S(t+1,0) and the V^T loads of
+        // tile t+2
         pv_accum_r(Vc, 1, pf, acc);
-        grow = row_max<HPW>(s0, m_run, mnew, w);
+        grow = lane_grows(s0[0], thr, mx);
 #pragma unroll
         for (int i = 0; i < 2; ++i) dma16_opaque(nsrc.vt, Vf + (wave + kCausalWaves * i) * 1024, vl[i]);
-        if (t < t1) rescale<HPW>(grow, mnew, acc, m_run, l_run, neg);
+        if (t < t1) rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
     };
     for (int t = 0; t <= t1; t += 3) {
         step(t, kr0, kr1, vr0, K2, V2);
