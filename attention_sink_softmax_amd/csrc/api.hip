@@ -483,7 +483,8 @@ int sinkattn_prefill_backward(int mode, int window, const sinkattn_dims *d, cons
     p.dv = dv;
     p.dsink = dsink;
     p.delta = static_cast<float *>(workspace);
-    p.dsink_part = p.delta + (size_t)d->batch * d->hq * d->seqlen;
+    p.nlse2 = p.delta + (size_t)d->batch * d->hq * d->seqlen;
+    p.dsink_part = p.nlse2 + (size_t)d->batch * d->hq * d->seqlen;
     p.B = d->batch;
     p.L = d->seqlen;
     p.Hq = d->hq;

@@ -45,15 +45,9 @@ constexpr int kRawDword3 = 0x00020000;  // untyped 32-bit data, no swizzle
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t region(const void *base, size_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRawDword3);
 }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, voff, soff, 0, 0);
-}
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// The same loads written as inline asm, for the tile loops.  The compiler does not see them,
+// The loads are written as inline asm.  The compiler does not see them,
 // so it adds no wait for them before reads of other LDS buffers (its own tracking of loads
 // into LDS loses the buffer across the loop and waits for the next tile's loads as well).
 // The kernels wait for these loads themselves (vmcnt) before each barrier.  m0 carries the
@@ -184,7 +178,7 @@ __device__ __forceinline__ bool all_visible(const BwdParams &p, int q0, int k0) 
     return k0 + 31 <= q0 && q0 + 31 < p.L && (!p.swa || k0 > q0 + 31 - p.window);
 }
 
-// ---- D_i = dO_i . O_i and the sink gradient's partial sums
+// ---- D_i = dO_i . O_i, -LSE_i log2(e), and the sink gradient's partial sums
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     __shared__ float part[256 / 16];
     const int h = blockIdx.y, b = blockIdx.z;
@@ -206,6 +200,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     if (i < p.L && c == 0) {
         const size_t row = ((size_t)b * p.Hq + h) * p.L + i;
         p.delta[row] = dsum;
+        p.nlse2[row] = -p.lse[row] * kLog2e;
         if (p.sink) {
             const float sk = p.sink[h];
             // the sink's weight exp(sink - LSE); with a sink of +inf every output is 0 (D = 0)
@@ -250,12 +245,13 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdParams p, int nblk) {
 // arithmetic.  The P tile passes in float32, so the results are those of computing both
 // halves in one wave.
 // LDS tile of one query tile: Q [32][192] (14 blocks of 1 KB) and dO [32][128] (10 blocks),
-// and the LSE and D of its rows (64 floats each: the 32 rows of the tile and 32 unused).
+// and -LSE log2(e) and D of its rows (64 floats each: the 32 rows of the tile and 32 unused;
+// the pre-pass writes -LSE log2(e), so P is one fused multiply-add and an exp2 per element).
 constexpr int kDkQBytes = kQT * kTileRow<192>, kDkOBytes = kQT * kTileRow<128>;  // 14 and 10 KB
 
 struct DkTile {
     char *q, *o;
-    float *lse, *d;
+    float *nl2, *d;  // -lse log2(e) and D of the tile's rows
 };
 
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
@@ -296,8 +292,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     // Item it = (query tile qt_hi - it / G, head it % G): every workgroup walks the query
     // tiles from the last one down, so the workgroups of one KV head that run together read
     // the same tiles at about the same time (shared in L2).  Wave w loads blocks w of Q and
-    // dO, waves 0-5 also block w + 8 of Q, waves 0-1 block w + 8 of dO, wave 6 the LSE rows and
-    // wave 7 the D rows: four load instructions per item on waves 0-1, three on the others.
+    // dO, waves 0-5 also block w + 8 of Q, waves 0-1 block w + 8 of dO, wave 6 the -LSE log2(e)
+    // rows and wave 7 the D rows: four load instructions per item on waves 0-1, three on the
+    // others.
     const int qsrc0 = src_of_slot<192>(64 * wave + lane), qsrc1 = src_of_slot<192>(64 * (wave + 8) + lane);
     const int osrc0 = src_of_slot<128>(64 * wave + lane), osrc1 = src_of_slot<128>(64 * (wave + 8) + lane);
     auto issue = [&](int it, const DkTile &t) {
@@ -309,7 +306,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
         if (wave < 6) dma16_async(rq, t.q + 1024 * (wave + 8), qsrc1, q0 * (kDqk * 2));
         dma16_async(ro, t.o + 1024 * wave, osrc0, q0 * (kDv * 2));
         if (wave < 2) dma16_async(ro, t.o + 1024 * (wave + 8), osrc1, q0 * (kDv * 2));
-        if (wave == 6) dma4_async(region(p.lse + rbase, (size_t)p.L * 4), t.lse, 4 * lane, 4 * q0);
+        if (wave == 6) dma4_async(region(p.nlse2 + rbase, (size_t)p.L * 4), t.nl2, 4 * lane, 4 * q0);
         if (wave == 7) dma4_async(region(p.delta + rbase, (size_t)p.L * 4), t.d, 4 * lane, 4 * q0);
     };
     // Item it uses buffer it % 4; its loads are issued two items ahead, after the barrier of
@@ -359,10 +356,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
             f32x16 pr;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(t.lse + 8 * j + 4 * g);
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(t.nl2 + 8 * j + 4 * g);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pr[4 * j + i] = exp2f_fast(__builtin_fmaf(s[4 * j + i], p.scale_log2, -l4[i] * kLog2e));
+                for (int i = 0; i < 4; ++i) pr[4 * j + i] = exp2f_fast(__builtin_fmaf(s[4 * j + i], p.scale_log2, l4[i]));
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -498,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) oB[kk] = as_bf16x8(qok ? ldg16(p.dout + qrow * kDv + 16 * kk + 8 * g) : u32x4{0, 0, 0, 0});
     // a row past the sequence end has every pair masked; its LSE only has to be finite
-    const float nlse2 = qok ? -p.lse[qrow] * kLog2e : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
+    const float nlse2 = qok ? p.nlse2[qrow] : 0.f, d_q = qok ? p.delta[qrow] : 0.f;
     // these loads land before the loop: the compiler does not count the tile loads, so a wait
     // for them inside the loop would wait for every tile load in flight
     wait_dma();
@@ -599,7 +595,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 
 size_t backward_workspace_bytes(int B, int Hq, int L) {
     const size_t nblk = ((size_t)L + kPreRows - 1) / kPreRows;
-    return ((size_t)B * Hq * L + (size_t)B * Hq * nblk) * sizeof(float);
+    return (2 * (size_t)B * Hq * L + (size_t)B * Hq * nblk) * sizeof(float);
 }
 
 int launch_backward(const BwdParams &prm, hipStream_t stream) {

@@ -98,6 +98,7 @@ struct BwdParams {
     float *dq, *dk, *dv;  // [B][Hq][L][kDqk], [B][Hkv][L][kDqk], [B][Hkv][L][kDv]
     float *dsink;         // [Hq] (sink given)
     float *delta;         // workspace [B][Hq][L]: dO . O
+    float *nlse2;         // workspace [B][Hq][L]: -lse log2(e), the exponent offset of P
     float *dsink_part;    // workspace [B][Hq][ceil(L / 16)]
     int B, L, Hq, Hkv, G, swa, window;
     float scale, scale_log2;

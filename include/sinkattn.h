@@ -328,7 +328,7 @@ int sinkattn_decode_fp8(int mode, int window, const sinkattn_dims *d, int32_t q_
                         void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of device workspace sinkattn_prefill_backward needs: 4 * batch * hq * (seqlen +
+ * Bytes of device workspace sinkattn_prefill_backward needs: 4 * batch * hq * (2 * seqlen +
  * ceil(seqlen / 16)).  Returns (size_t)-1 for invalid sizes.
  */
 size_t sinkattn_prefill_backward_workspace_bytes(const sinkattn_dims *d);

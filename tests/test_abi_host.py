@@ -277,7 +277,7 @@ def backward(L, mode=0, window=0, d=None, q=A, k=A, v=A, sink=None, out=A, dout=
 def test_backward_argument_errors(L):
     d = dims(hq=64, hkv=4)
     need = L.sinkattn_prefill_backward_workspace_bytes(ctypes.byref(d))
-    assert need == 4 * (64 * 64 + 64 * ((64 + 15) // 16))  # D per row + sink-gradient partials
+    assert need == 4 * (2 * 64 * 64 + 64 * ((64 + 15) // 16))  # D and -LSE log2(e) per row + sink-gradient partials
     # empty work is a no-op success, even with NULL tensors
     assert backward(L, d=dims(B=0, hq=64, hkv=4), q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None,
                     dk=None, dv=None, ws=None, wsb=0) == OK
