@@ -879,6 +879,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
         bool sink_inf[HPW];
         f32x16 acc[HPW][4];
         init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf, neg);
+        float thr = grow_threshold(m_run[0], w);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int sub = j - 4 + i, k0 = kBQ * sub;
@@ -889,7 +890,9 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
             f32x16 sc[HPW];
             qk_scores<HPW>(slot, 0, qc, sc, w);
             if (!full) mask_scores<HPW>(sc, k0, 0, w);
-            row_update<HPW>(sc, acc, m_run, l_run, neg, w);
+            float mx;
+            const bool grow = lane_grows(sc[0], thr, mx);
+            rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
             bf16x8 pf[HPW][2];
             probs<HPW>(sc, neg, l_run, pf, w);
             pv_sub(slot + kSubKBytes, pf, acc, w);
