@@ -398,12 +398,16 @@ __global__ __launch_bounds__(256, kSingle ? (kFast ? 4 : 2) : 1) void decode_spl
         }
     };
 
-    float m_run[NCB], l_run[NCB];
+    // m: the reference the sums are kept against (log2 units of the scaled logits); thr =
+    // (m + kLazyRescale) / scale, the growth threshold in raw-score units (the scale is
+    // positive), moves only with m.
+    float m_run[NCB], l_run[NCB], thr[NCB];
     f32x4 acc[NCB][8];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
+        thr[cb] = -INFINITY;
 #pragma unroll
         for (int db = 0; db < 8; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -495,33 +499,32 @@ __global__ __launch_bounds__(256, kSingle ? (kFast ? 4 : 2) : 1) void decode_spl
                         if (!((j >= lo_c[cb]) & (j <= hi_c[cb]))) s[cb][sb][e] = -INFINITY;
                     }
         }
-        // Running max of the scaled scores (the scale is positive, so the max of the raw
-        // scores is taken first).  The reference that the sums are kept against moves only
-        // when some column's max grows by more than 2^kLazyRescale: the weights then stay
-        // below 2^kLazyRescale, and the rare rescale (a wave-uniform branch) keeps the
+        // The reference that the sums are kept against moves only when some column's max
+        // grows by more than 2^kLazyRescale: the weights then stay below 2^kLazyRescale.  The
+        // test compares each lane's largest raw score with the threshold; only the rare
+        // rescale (a wave-uniform branch) forms the columns' maxima and keeps the
         // accumulators, the denominators and the reference consistent.
-        float mnew[NCB];
+        float mxl[NCB];
         bool grow = false;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            float mx = -INFINITY;
+            float mx = fmaxf(s[cb][0][0], s[cb][0][1]);
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[cb][sb][e]);
-            mx = max_xor32(max_xor16(mx)) * p.scale_log2;
-            mnew[cb] = fmaxf(m_run[cb], mx);
-            grow |= mnew[cb] > m_run[cb] + kLazyRescale;
+            for (int e = 2; e < 8; e += 2) mx = fmaxf(fmaxf(mx, s[cb][e >> 2][e & 3]), s[cb][e >> 2][(e & 3) + 1]);
+            mxl[cb] = mx;
+            grow |= mx > thr[cb];
         }
-        if (__any(grow)) {
+        if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
+                const float mnew = fmaxf(m_run[cb], max_xor32(max_xor16(mxl[cb])) * p.scale_log2);
                 // an unchanged reference (including -inf, nothing visible yet) keeps alpha = 1
-                const float alpha = (mnew[cb] == m_run[cb]) ? 1.f : exp2f_fast(m_run[cb] - mnew[cb]);
+                const float alpha = (mnew == m_run[cb]) ? 1.f : exp2f_fast(m_run[cb] - mnew);
                 l_run[cb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
-                m_run[cb] = mnew[cb];
+                m_run[cb] = mnew;
+                thr[cb] = (mnew + kLazyRescale) / p.scale_log2;
             }
         }
         bf16x8 pf[NCB];
