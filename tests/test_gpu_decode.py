@@ -70,6 +70,61 @@ def test_paged(mode, W, ps, Hq, Hkv, perm):
     assert_parity(got.reshape(-1, 128), pre, "paged vs prefill rows")
 
 
+def growing_keys(d, rate):
+    """Key norms that grow along the sequence (1 + position / rate) and V scaled by 1/4, as in
+    the prefill test of growing logits: the scores of later slices exceed the lazy-rescale
+    threshold again and again, and the nearly one-hot outputs stay where the absolute bound
+    is not dominated by the output's own bf16 rounding."""
+    k = inputs.bf16_to_f32(d["k"])
+    k *= (1.0 + np.arange(k.shape[2], dtype=np.float32) / rate)[None, None, :, None]
+    d["k"] = inputs.bf16_bits(k)
+    d["v"] = inputs.bf16_bits(inputs.bf16_to_f32(d["v"]) * 0.25)
+    return d
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_growing_scores_rescale(q_len):
+    """Paged decode with one and with four new tokens (16 and 64 columns per workgroup) while
+    the column maxima keep growing within each wave's slices and across splits."""
+    lens = np.array([700, 5000, 4097], np.int32)
+    B, L, Hq, Hkv, ps = len(lens), 5000, 64, 4, 64
+    print(f"[case] growing scores q_len={q_len}", flush=True)
+    d = growing_keys(seq_data(B, Hq, Hkv, L, seed=31 + q_len), 200.0)
+    kp, vp, bt = inputs.pages_from_sequence(d["k"], d["v"], L, ps, B * (L // ps + 1) + 3, seed=4)
+    q = np.zeros((B, Hq, q_len, 192), np.uint16)
+    for b in range(B):
+        q[b] = d["q"][b, :, lens[b] - q_len:lens[b]]
+    if q_len == 1:
+        got = gpu_decode(oracle.GLOBAL, 0, sa.KV_PAGED, q[:, :, 0], kp, vp, lens, L, d["sink"], bt)[:, :, None]
+    else:
+        out = sa.decode_multi(oracle.GLOBAL, 0, dev_bf16(q), sa.KV_PAGED, dev_bf16(kp), dev_bf16(vp), dev_i32(lens), L,
+                              dev_f32(d["sink"]), dev_i32(bt))
+        torch.cuda.synchronize()
+        got = host_f32(out)
+    rows = np.array([(b, h, lens[b] - q_len + t) for b in range(B) for h in range(Hq) for t in range(q_len)])
+    ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], oracle.GLOBAL, 0, SCALE, rows=rows)
+    assert_parity(got.reshape(-1, 128), ref, f"growing scores q_len={q_len}")
+
+
+def test_growing_scores_ring():
+    """Ring decode (W = 128) with growing key norms: each wave's single slice grows past the
+    threshold and the waves' records merge across different references."""
+    W, Hq, Hkv = 128, 16, 2
+    lens = np.array([128, 300, 1000], np.int32)
+    B, L = len(lens), int(lens.max())
+    d = growing_keys(seq_data(B, Hq, Hkv, L, seed=41), 20.0)
+    kr = np.zeros((B, Hkv, W, 192), np.uint16)
+    vr = np.zeros((B, Hkv, W, 128), np.uint16)
+    for b in range(B):
+        k1, v1 = inputs.ring_from_sequence(d["k"][b:b + 1], d["v"][b:b + 1], int(lens[b]), W)
+        kr[b], vr[b] = k1[0], v1[0]
+    qn = np.stack([d["q"][b, :, lens[b] - 1] for b in range(B)])
+    got = gpu_decode(oracle.SWA, W, sa.KV_RING, qn, kr, vr, lens, L, d["sink"])
+    rows = np.array([(b, h, lens[b] - 1) for b in range(B) for h in range(Hq)])
+    ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], oracle.SWA, W, SCALE, rows=rows)
+    assert_parity(got.reshape(-1, 128), ref, "growing scores ring")
+
+
 def test_contiguous_equals_permuted_pages():
     lens = np.array([3000, 2048], np.int32)
     d = seq_data(2, 16, 2, 3000, seed=5)
