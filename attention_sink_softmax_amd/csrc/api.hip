@@ -15,9 +15,13 @@ using namespace sinkattn;
 
 constexpr int kDqkSupported = 192;
 constexpr int kDvSupported = 128;
-constexpr int64_t kDecodeTargetWorkgroups = 2048;  // ~8 per CU on a 256-CU MI355X
+// Decode workgroups to aim for: two rounds of the bf16 split kernel on a 256-CU MI355X (one
+// workgroup per CU, 160 KB of LDS), one round of the E4M3 kernel (two per CU).  Every
+// workgroup pays its first loads and its merge once, so fewer, longer splits win (8 x 256K
+// GA decode: 853 us at 2048 workgroups, 818 at 1024, 794 at 512; 256 leaves half of the
+// CUs idle for the E4M3 kernel).
+constexpr int64_t kDecodeTargetWorkgroups = 512;
 constexpr int kDecodeKeyBlock = 128;                // keys per decode workgroup iteration
-constexpr int kDecodeMaxChunk = 8192;               // keys per split at most (64 slices per wave)
 constexpr int kDecodeSingleSplit = 1024;            // key ranges this short are not split
 constexpr double kLog2eD = 1.4426950408889634;
 constexpr int kDecodeStepMaxSlots = 128;  // the fused decode step's single-slice kernel: 4 waves x 32 keys

@@ -271,13 +271,17 @@ __global__ __launch_bounds__(256, kSingle ? (kFast ? 4 : 2) : 1) void decode_spl
 
     bool bad = false;
 
-    // Page of each of this wave's slices (lane i: slice i; a split holds at most 8192 keys,
-    // so a wave has at most 64 slices), loaded before the loop so that no table read sits
-    // between the direct-to-LDS loads (fast paged path).
-    int page_reg = 0;
-    if (kFast && p.paged && lane < nmine) {
-        const int j0 = s_lo + kSlice * (wave + kWaves * lane);
-        page_reg = p.block_table[(size_t)b * p.max_pages + j0 / p.page_size];
+    // Page of each of this wave's slices (register r, lane i: slice 64 r + i), loaded before
+    // the loop so that no table read sits between the direct-to-LDS loads (fast paged path).
+    constexpr int kPageRegs = (kDecodeMaxChunk / (kSlice * kWaves) + 63) / 64;
+    int page_reg[kPageRegs];
+#pragma unroll
+    for (int r = 0; r < kPageRegs; ++r) {
+        page_reg[r] = 0;
+        if (kFast && p.paged && 64 * r + lane < nmine) {
+            const int j0 = s_lo + kSlice * (wave + kWaves * (64 * r + lane));
+            page_reg[r] = p.block_table[(size_t)b * p.max_pages + j0 / p.page_size];
+        }
     }
 
     bf16x8 kreg[2][6];  // single-slice path: this wave's K operands
@@ -295,7 +299,10 @@ __global__ __launch_bounds__(256, kSingle ? (kFast ? 4 : 2) : 1) void decode_spl
             size_t row0;  // cache row of key offset 0 of this slice's page (or ring)
             int off0;
             if (p.paged) {
-                const int page = __builtin_amdgcn_readlane(page_reg, i);
+                int preg = page_reg[0];
+#pragma unroll
+                for (int r = 1; r < kPageRegs; ++r) preg = (i >> 6) == r ? page_reg[r] : preg;  // i is uniform
+                const int page = __builtin_amdgcn_readlane(preg, i & 63);
                 const bool ok = page >= 0 && page < p.num_pages;
                 bad |= !ok;
                 row0 = ((size_t)(ok ? page : 0) * p.Hkv + kvh) * p.page_size;

@@ -35,6 +35,10 @@ struct PrefillParams {
     int prefix_w, prefix_base;
 };
 
+// Keys per decode split at most: each of the 4 waves of a split walks 32-key slices, and
+// holds the page ids of up to 64 of them per register.
+constexpr int kDecodeMaxChunk = 16384;
+
 struct DecodeParams {
     const uint16_t *q, *k, *v;
     const uint16_t *k_new, *v_new;  // the new tokens' keys and values beside the cache, or nullptr

@@ -150,8 +150,9 @@ def test_decode_multi_workspace_plan(L):
         assert sa.sinkattn_decode_multi_workspace_bytes(*args[:5], 1, args[5]) == \
             sa.sinkattn_decode_workspace_bytes(*args)
     # 256K global, four drafted tokens: one workgroup covers all 16 heads x 4 tokens of a KV
-    # head, so the split is the same 64 x 4096 keys and the partials grow by q_len
-    assert sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 4, 262144) == 8 * 64 * 4 * 64 * 132 * 4
+    # head, so the split is the same 16 x 16384 keys (512 workgroups) and the partials grow
+    # by q_len
+    assert sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 4, 262144) == 8 * 64 * 4 * 16 * 132 * 4
     assert sa.sinkattn_decode_multi_workspace_bytes(1, 128, 128, 64, 8, 4, 65536) == 0
     with pytest.raises(sa.SinkAttnError):
         sa.sinkattn_decode_multi_workspace_bytes(0, 0, 8, 64, 4, 0, 262144)
@@ -248,9 +249,10 @@ def test_prefill_workspace_size(L):
 
 
 def test_decode_workspace_plan(L):
-    # 256K global decode: 8 sequences x 4 KV heads, split into 64 pieces of 4096 keys
+    # 256K global decode: 8 sequences x 4 KV heads, split into 16 pieces of 16384 keys (512
+    # workgroups)
     n = sa.sinkattn_decode_workspace_bytes(0, 0, 8, 64, 4, 262144)
-    assert n == 8 * 64 * 64 * 132 * 4
+    assert n == 8 * 64 * 16 * 132 * 4
     # sliding ring decode: one split per (sequence, KV head), no workspace
     assert sa.sinkattn_decode_workspace_bytes(1, 128, 128, 64, 8, 65536) == 0
     assert sa.sinkattn_decode_workspace_bytes(1, 128, 1, 64, 8, 100) == 0
