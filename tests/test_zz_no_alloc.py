@@ -68,8 +68,8 @@ def test_noalloc_matches_workspace_entry(kv_fp8):
 
 
 def test_noalloc_refuses_partials_beyond_scratch():
-    """8 sequences of 256K with 4 drafted tokens need 69 MB of partials: refused before any launch."""
-    B, Hq, Hkv, ps, L, q_len = 8, 64, 4, 64, 262144, 4
+    """8 sequences of 256K with 16 drafted tokens need 69 MB of partials: refused before any launch."""
+    B, Hq, Hkv, ps, L, q_len = 8, 64, 4, 64, 262144, 16
     need = sa.sinkattn_decode_multi_workspace_bytes(sa.GLOBAL, 0, B, Hq, Hkv, q_len, L)
     assert need > sa.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((B, Hq, q_len, 192), dtype=torch.bfloat16, device="cuda")
