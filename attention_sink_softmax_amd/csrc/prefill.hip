@@ -531,11 +531,11 @@ __global__ __launch_bounds__(256, 3 - HPW) void prefill_kernel(PrefillParams p) 
 // software pipeline over 32-key sub-blocks so that the softmax arithmetic of one sub-block
 // overlaps the matrix products of another:
 //
-//   phase A: S(t,1) = K(t)Q^T              with  P(t,0) = exp(S(t,0))
-//   phase B: O += V(t)^T P(t,0)            with  growth test of S(t,1), then the rare rescale
+//   phase A: S(t,1) = K(t)Q^T              with  P(t,0) = exp(S(t,0)), its test, the rare rescale
+//   phase B: O += V(t)^T P(t,0)
 //   barrier; tiles t+2 start streaming in
-//   phase C: S(t+1,0) = K(t+1)Q^T          with  P(t,1) = exp(S(t,1))
-//   phase D: O += V(t)^T P(t,1)            with  growth test of S(t+1,0), then the rare rescale
+//   phase C: S(t+1,0) = K(t+1)Q^T          with  P(t,1) = exp(S(t,1)), its test, the rare rescale
+//   phase D: O += V(t)^T P(t,1)
 //
 // K runs one tile ahead of V, so both are triple buffered (120 KB of LDS); loads issued
 // after the barrier of tile t land by the barrier of tile t+1.  The loop is unrolled by 3
@@ -588,6 +588,49 @@ __device__ __forceinline__ void rescale_lane(bool grow, float mx, f32x16 (&acc)[
         rescale<1>(true, mnew, acc, m_run, l_run, neg);
         thr = grow_threshold(m_run[0], w);
     }
+}
+
+// The weights P = 2^(c s - m) of one head's sub-block as probs() forms them, without adding
+// them to the denominator; returns the lane's sum of its 16 weights.
+__device__ __forceinline__ float weights(const f32x16 &s, float neg, bf16x8 (&pf)[1][2], const WaveCtx &w) {
+    float ps;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float p0 = exp2f_fast(__builtin_fmaf(s[2 * r], w.c, neg));
+        const float p1 = exp2f_fast(__builtin_fmaf(s[2 * r + 1], w.c, neg));
+        ps = r == 0 ? p0 + p1 : ps + (p0 + p1);
+        pk[r] = pack_bf16x2(p0, p1);
+    }
+    pf[0][0] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+    pf[0][1] = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+    return ps;
+}
+// The limit on a lane's weight sum that keeps the reference: 2^kLazyRescale, or -1 while the
+// row has no reference yet (m = -inf), so that its first visible sub-block takes the rescale.
+__device__ __forceinline__ float sum_limit(float m) { return m == -INFINITY ? -1.f : 256.f; }
+static_assert(kLazyRescale == 8.f, "sum_limit holds 2^kLazyRescale");
+// probs() with the lazy-rescale test on the weights themselves: while a lane's 16 weights sum
+// to at most 2^kLazyRescale none of them exceeds it, and the reference stands.  Otherwise
+// (some score grew past the reference by more than 4, or the row has no reference yet) the
+// rare path forms the row max over both lanes of the pair, rescales the accumulator and the
+// denominator (which does not hold this sub-block's weights yet), and forms the weights again.
+__device__ __forceinline__ void probs_lazy(const f32x16 &s, f32x16 (&acc)[1][4], float (&m_run)[1],
+                                           float (&l_run)[1], float (&neg)[1], float &limit, bf16x8 (&pf)[1][2],
+                                           const WaveCtx &w) {
+    float ps = weights(s, neg[0], pf, w);
+    if (__builtin_expect(__any(!(ps <= limit)), 0)) {
+        float mx = __builtin_fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
+        float mnew[1] = {fmaxf(m_run[0], max_xor32(mx) * w.c)};
+        rescale<1>(true, mnew, acc, m_run, l_run, neg);
+        limit = sum_limit(m_run[0]);
+        ps = weights(s, neg[0], pf, w);
+    }
+    l_run[0] += ps;
+    // computed here, not sunk past a following branch towards their use
+    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(l_run[0]));
 }
 
 // qk_scores and pv_accum of one head reading through such registers: kr = K tile + klane,
@@ -675,7 +718,7 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     qk_scores<HPW>(K0, 0, qf, s0, w);
     if (masked(0, 0)) mask_scores<HPW>(s0, 0, 0, w);
     row_update<HPW>(s0, acc, m_run, l_run, neg, w);
-    float thr = grow_threshold(m_run[0], w);
+    float limit = sum_limit(m_run[0]);
 
     // Tile t: K(t) in Kc, K(t+1) in Kn, V(t) in Vc; tiles t+2 go to (Kf, Vf).  The loads of
     // tile t+2 are issued unconditionally (past the last tile they re-read tile t1 into a
@@ -683,33 +726,26 @@ __global__ __launch_bounds__(64 * kCausalWaves, 1) void prefill_causal_kernel(Pr
     auto step = [&](int t, uint32_t Kc, uint32_t Kn, uint32_t Vc, char *Kf, char *Vf) {
         const int kb = t * kBN;
         const TileSrc nsrc = tile_src_at(p, ws.b, ws.kvh, min(t + 2, t1) * kBN);
-        float mx;
-        bool grow;
-        // phase A: S(t,1) with P(t,0)
+        // phase A: S(t,1) with P(t,0) and its lazy-rescale test (after PV of P(t-1,1))
         qk_scores_r(Kc, 1, qf, s1);
-        probs<HPW>(s0, neg, l_run, pf, w);
+        probs_lazy(s0[0], acc, m_run, l_run, neg, limit, pf, w);
         if (masked(t, 1)) mask_scores<HPW>(s1, kb, 1, w);
-        // phase B: O += V(t)^T P(t,0) with the growth test of S(t,1)
+        // phase B: O += V(t)^T P(t,0)
         pv_accum_r(Vc, 0, pf, acc);
-        grow = lane_grows(s1[0], thr, mx);
-        rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
         // tiles t+1 have landed everywhere; the buffers of tiles t-1 (V) and t (K) are free
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        // phase C: S(t+1,0) with P(t,1) and the K loads of tile t+2 (the scores of tile t+1
-        // are unused after the last tile)
+        // phase C: S(t+1,0) with P(t,1) and its test, and the K loads of tile t+2 (the scores
+        // of tile t+1 are unused after the last tile)
         qk_scores_r(Kn, 0, qf, s0);
-        probs<HPW>(s1, neg, l_run, pf, w);
+        probs_lazy(s1[0], acc, m_run, l_run, neg, limit, pf, w);
 #pragma unroll
         for (int i = 0; i < 3; ++i) dma16_opaque(nsrc.k, Kf + (wave + kCausalWaves * i) * 1024, kl[i]);
         if (t < t1 && masked(t + 1, 0)) mask_scores<HPW>(s0, kb + kBN, 0, w);
-        // phase D: O += V(t)^T P(t,1) with the growth test of S(t+1,0) and the V^T loads of
-        // tile t+2
+        // phase D: O += V(t)^T P(t,1) and the V^T loads of tile t+2
         pv_accum_r(Vc, 1, pf, acc);
-        grow = lane_grows(s0[0], thr, mx);
 #pragma unroll
         for (int i = 0; i < 2; ++i) dma16_opaque(nsrc.vt, Vf + (wave + kCausalWaves * i) * 1024, vl[i]);
-        if (t < t1) rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
     };
     for (int t = 0; t <= t1; t += 3) {
         step(t, kr0, kr1, vr0, K2, V2);
