@@ -570,26 +570,6 @@ __device__ __forceinline__ uint32_t lds_reg(const char *p) {
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 __device__ __forceinline__ bf16x8 lds_read16(uint32_t a, int off) { return *(lds_bf16x8 *)(a + off); }
 
-// The lazy-rescale test of one sub-block without the row max: a lane's largest raw score
-// against thr = (m + kLazyRescale) / c, the threshold in raw-score units (the scale is
-// positive).  Only the rare rescale needs the max of the row, from both lanes of the pair.
-__device__ __forceinline__ bool lane_grows(const f32x16 &s, float thr, float &mx) {
-    mx = __builtin_fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
-    return mx > thr;
-}
-__device__ __forceinline__ float grow_threshold(float m, const WaveCtx &w) { return (m + kLazyRescale) / w.c; }
-// The rescale of rescale(), for lanes whose largest raw score is mx; thr follows the new max.
-__device__ __forceinline__ void rescale_lane(bool grow, float mx, f32x16 (&acc)[1][4], float (&m_run)[1],
-                                             float (&l_run)[1], float (&neg)[1], float &thr, const WaveCtx &w) {
-    if (__builtin_expect(__any(grow), 0)) {
-        float mnew[1] = {fmaxf(m_run[0], max_xor32(mx) * w.c)};
-        rescale<1>(true, mnew, acc, m_run, l_run, neg);
-        thr = grow_threshold(m_run[0], w);
-    }
-}
-
 // The weights P = 2^(c s - m) of one head's sub-block as probs() forms them, without adding
 // them to the denominator; returns the lane's sum of its 16 weights.
 __device__ __forceinline__ float weights(const f32x16 &s, float neg, bf16x8 (&pf)[1][2], const WaveCtx &w) {
@@ -915,7 +895,7 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
         bool sink_inf[HPW];
         f32x16 acc[HPW][4];
         init_state_from<HPW>(sink, w, acc, m_run, l_run, sink_inf, neg);
-        float thr = grow_threshold(m_run[0], w);
+        float limit = sum_limit(m_run[0]);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int sub = j - 4 + i, k0 = kBQ * sub;
@@ -926,11 +906,8 @@ __global__ __launch_bounds__(64 * kSwaWaves, 1) void prefill_swa_kernel(PrefillP
             f32x16 sc[HPW];
             qk_scores<HPW>(slot, 0, qc, sc, w);
             if (!full) mask_scores<HPW>(sc, k0, 0, w);
-            float mx;
-            const bool grow = lane_grows(sc[0], thr, mx);
-            rescale_lane(grow, mx, acc, m_run, l_run, neg, thr, w);
             bf16x8 pf[HPW][2];
-            probs<HPW>(sc, neg, l_run, pf, w);
+            probs_lazy(sc[0], acc, m_run, l_run, neg, limit, pf, w);
             pv_sub(slot + kSubKBytes, pf, acc, w);
         }
         // slot (j + 1) % 6 held sub-block j - 5, outside this block's band
