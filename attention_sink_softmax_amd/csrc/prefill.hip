@@ -35,10 +35,12 @@
 //     a lane's operand addresses differ only by compile-time offsets.  Tiles are double
 //     (general kernel) or triple (causal kernel) buffered in distinct LDS objects, so the
 //     loads of the next tiles overlap the math of the current one.
-//   * Softmax: the logit scale is folded into one FMA per score (exp2 domain), the
-//     running max is taken on raw scores, and the output accumulator is rescaled only
-//     when a row's max grows by more than 2^8 (the result is exact for any reference
-//     max; this only bounds the size of the unnormalised terms).
+//   * Softmax: the logit scale is folded into one FMA per score (exp2 domain), and the
+//     reference max moves, with a rescale of the output accumulator, only when a row's max
+//     grows by more than 2^8 (the result is exact for any reference max; this only bounds
+//     the size of the unnormalised terms).  The causal and ring kernels detect the growth
+//     on the weights themselves (a lane whose 16 weights sum past 2^8) and form the row max
+//     only inside the rare rescale; the general kernel takes the max of every sub-block.
 //   * Sub-blocks fully inside every row's visible range take a branch-free path; diagonal
 //     and band-edge sub-blocks take a masked path.
 //   * Workgroup ids are remapped so that the workgroups sharing one KV head and position
