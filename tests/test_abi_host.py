@@ -253,6 +253,12 @@ def test_decode_workspace_plan(L):
     # workgroups)
     n = sa.sinkattn_decode_workspace_bytes(0, 0, 8, 64, 4, 262144)
     assert n == 8 * 64 * 16 * 132 * 4
+    # a split never exceeds 16384 keys (the kernel holds the page ids of at most 128 slices per
+    # wave): more sequences keep 16 splits of 16384 keys rather than longer splits
+    for B in (16, 64):
+        assert sa.sinkattn_decode_workspace_bytes(0, 0, B, 64, 4, 262144) == B * 64 * 16 * 132 * 4
+    # few (sequence, KV head) pairs: short splits, here 512 of 512 keys
+    assert sa.sinkattn_decode_workspace_bytes(0, 0, 1, 16, 1, 262144) == 16 * 512 * 132 * 4
     # sliding ring decode: one split per (sequence, KV head), no workspace
     assert sa.sinkattn_decode_workspace_bytes(1, 128, 128, 64, 8, 65536) == 0
     assert sa.sinkattn_decode_workspace_bytes(1, 128, 1, 64, 8, 100) == 0
