@@ -43,11 +43,11 @@ CSRC = os.path.join(ROOT, "attention_sink_softmax_amd", "csrc")
 # stale and `traffic` is reported as null until the counters are taken again.
 TRAFFIC = {
     "ga_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                          "sha256": "22c84aa4e18b6f1c73212f2a4f81a570b8860a34080dc6ae02dcfaf03ae413da",
-                          "read_GB": 3.5696, "written_GB": 0.5369},
+                          "sha256": "0ad3f48061805f92d070cf996575869849d707cfe07f4d1357aba8ff4ed436e4",
+                          "read_GB": 3.5704, "written_GB": 0.5369},
     "swa_prefill_L32768": {"sources": ("prefill.hip", "common.h", "launch.h"),
-                           "sha256": "22c84aa4e18b6f1c73212f2a4f81a570b8860a34080dc6ae02dcfaf03ae413da",
-                           "read_GB": 1.0232, "written_GB": 0.5369},
+                           "sha256": "0ad3f48061805f92d070cf996575869849d707cfe07f4d1357aba8ff4ed436e4",
+                           "read_GB": 1.0234, "written_GB": 0.5369},
     "ga_decode_B8_256K_paged": {"sources": ("decode.hip", "rope.h", "common.h", "launch.h"),
                                 "sha256": "e4ac83f4b6eba6bc677512e1c1646afe51736e2fe76416f4f562c21182fc9ec0",
                                 "read_GB": 5.3749, "written_GB": 0.0046},
