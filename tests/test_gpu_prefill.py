@@ -121,9 +121,12 @@ def test_growing_max_rescales():
     d["k"] = inputs.bf16_bits(k)
     d["v"] = inputs.bf16_bits(inputs.bf16_to_f32(d["v"]) * 0.25)
     for mode, W in ((oracle.GLOBAL, 0), (oracle.SWA, 128)):
-        got = run_prefill(mode, W, d)
-        ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"], mode, W, 192 ** -0.5)
-        assert_parity(got, ref, f"growing logits mode={mode}")
+        # with a sink (every row starts from its sink logit) and without one (every row
+        # starts with no reference, so its first visible keys force the first rescale)
+        for sink in (True, False):
+            got = run_prefill(mode, W, d, sink=sink)
+            ref = oracle.prefill(d["q"], d["k"], d["v"], d["sink"] if sink else None, mode, W, 192 ** -0.5)
+            assert_parity(got, ref, f"growing logits mode={mode} sink={sink}")
 
 
 def test_wide_window_equals_global_bitwise():
