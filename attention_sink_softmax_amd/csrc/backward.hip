@@ -10,20 +10,21 @@
 //
 // Four kernels on one stream:
 //   bwd_pre     D_i and the per-block partial sums of the sink gradient;
-//   bwd_dkdv    one workgroup per 128 keys of a (sequence, KV head): each wave keeps its 32 keys'
-//               K and V operands and its dK, dV accumulators in registers and walks every query
-//               head of the group and every 32-row query tile that sees its keys:
+//   bwd_dkdv    one workgroup per 128 keys of a (sequence, KV head): the two waves of each 32-key
+//               group keep its K and dV, or V and dK, in registers and walk every query head of
+//               the group and every 32-row query tile that sees its keys:
 //                 S = Q K^T, dP = dO V^T (query rows x keys), dS = P (dP - D),
 //                 dV += P^T dO, dK += dS^T Q       (P and dS feed the A operand as they are;
 //                                                    dO and Q arrive through transposing reads);
-//   bwd_dq      one workgroup per 32 query rows of four query heads of one KV head: each wave
-//               keeps its head's Q and dO operands and dQ^T in registers and walks the key tiles:
+//   bwd_dq      one workgroup per 64 query rows of four query heads of one KV head: each wave
+//               keeps its head's Q and dO operands and dQ^T for 32 rows in registers and walks
+//               the key tiles:
 //                 S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
 //   bwd_dsink   sums the sink gradient partials in a fixed order (deterministic).
 // All products are v_mfma_f32_32x32x16_bf16 with float32 accumulation; P and dS enter them as
-// bf16.  Tiles pass through double-buffered LDS (one barrier per tile) with their 16-byte
-// chunks XOR-swizzled by row so that both the row reads and the transposing reads spread over
-// the banks.  Masking is branch-free and only runs on tiles that cross the causal diagonal, the
+// bf16.  Tiles pass through LDS (four buffers in bwd_dkdv, three in bwd_dq, loaded two steps
+// ahead, one barrier per step) with their 16-byte chunks XOR-swizzled by row so that both the
+// row reads and the transposing reads spread over the banks.  Masking is branch-free and only runs on tiles that cross the causal diagonal, the
 // window's edge or the sequence end.
 #include "common.h"
 #include "launch.h"
