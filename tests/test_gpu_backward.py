@@ -29,7 +29,7 @@ def assert_grad(got, ref, what):
     assert max_abs <= bound and rel <= 5e-3, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
 
 
-def run(mode, W, Hq, Hkv, L, B=1, sink_kind="sink", seed=0):
+def run(mode, W, Hq, Hkv, L, B=1, sink_kind="sink", seed=0, scale=SCALE):
     w = inputs.Workload("t", "prefill", 0, B, Hq, Hkv, seqlen=L, seed=seed)
     d = inputs.prefill_inputs(w)
     dout = inputs.normal((B, Hq, L, 128), seed, 5)
@@ -44,10 +44,10 @@ def run(mode, W, Hq, Hkv, L, B=1, sink_kind="sink", seed=0):
     out = torch.empty((B, Hq, L, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
     ws = torch.empty(sa.sinkattn_prefill_chunk_workspace_bytes(B, L, Hq, Hkv, L), dtype=torch.uint8, device="cuda")
-    sa.sinkattn_prefill_ex(mode, W, q, k, v, s, out, ws, lse=lse)
-    dq, dk, dv, ds = sa.prefill_backward(mode, W, q, k, v, s, out, dev_bf16(dout), lse)
+    sa.sinkattn_prefill_ex(mode, W, q, k, v, s, out, ws, lse=lse, scale=scale)
+    dq, dk, dv, ds = sa.prefill_backward(mode, W, q, k, v, s, out, dev_bf16(dout), lse, scale=scale)
     torch.cuda.synchronize()
-    ref = oracle.prefill_backward(d["q"], d["k"], d["v"], sink, dout, mode, W, SCALE)
+    ref = oracle.prefill_backward(d["q"], d["k"], d["v"], sink, dout, mode, W, scale)
     got = (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy(), None if ds is None else ds.cpu().numpy())
     bound = None
     if sink is not None:
@@ -56,7 +56,7 @@ def run(mode, W, Hq, Hkv, L, B=1, sink_kind="sink", seed=0):
         # bf16 weights of the forward's value product): its error is bounded by a small multiple
         # of sum_i exp(sink - LSE_i) |dO_i| |O_i|, a scale of the summands rather than of their
         # (cancelling) sum.  The bar is 2^-6 of that.
-        o_ref, lse_ref = oracle.prefill_chunk(d["q"], d["k"], d["v"], sink, mode, W, SCALE, return_lse=True)
+        o_ref, lse_ref = oracle.prefill_chunk(d["q"], d["k"], d["v"], sink, mode, W, scale, return_lse=True)
         dof = inputs.bf16_to_f32(dout).astype(np.float64)
         with np.errstate(invalid="ignore"):
             ps = np.where(np.isinf(sink)[None, :, None], 0.0, np.exp(sink[None, :, None] - lse_ref))
@@ -89,6 +89,18 @@ def test_backward(mode, W, Hq, Hkv, L, B, sink_kind):
         assert got[3] is None
     else:
         assert_dsink(got[3], ref[3], bound)
+
+
+@pytest.mark.parametrize("mode,W,scale", [(oracle.GLOBAL, 0, 0.125), (oracle.SWA, 128, 0.3)])
+def test_backward_nondefault_scale(mode, W, scale):
+    """A logit scale other than 1/sqrt(192): it enters P's exponent (with the forward's LSE),
+    dq and dk (a factor of the scale each), and the pre-pass's -LSE log2(e) is taken from the
+    forward at the same scale."""
+    print(f"[case] backward mode={mode} W={W} scale={scale}", flush=True)
+    got, ref, sink, bound = run(mode, W, 16, 2, 333, 1, "sink", seed=11 + W, scale=scale)
+    for name, i in (("dq", 0), ("dk", 1), ("dv", 2)):
+        assert_grad(got[i], ref[i], f"scale {scale} {name}")
+    assert_dsink(got[3], ref[3], bound)
 
 
 def test_backward_ga_2k_all_heads():

@@ -125,6 +125,39 @@ def test_growing_scores_ring():
     assert_parity(got.reshape(-1, 128), ref, "growing scores ring")
 
 
+@pytest.mark.parametrize("scale", [0.125, 0.4])
+def test_nondefault_scale(scale):
+    """Logit scales other than 1/sqrt(192), with growing key norms so that the rescale is taken:
+    the scale enters the exponent's FMA and the lazy-rescale threshold (m + 8) / c.  A ring
+    (single-slice kernel) and a paged cache split over several workgroups (merge kernel)."""
+    print(f"[case] decode scale={scale}", flush=True)
+    W, Hq, Hkv = 128, 16, 2
+    lens = np.array([128, 300, 1000], np.int32)
+    B, L = len(lens), int(lens.max())
+    d = growing_keys(seq_data(B, Hq, Hkv, L, seed=51), 100.0)
+    kr = np.zeros((B, Hkv, W, 192), np.uint16)
+    vr = np.zeros((B, Hkv, W, 128), np.uint16)
+    for b in range(B):
+        k1, v1 = inputs.ring_from_sequence(d["k"][b:b + 1], d["v"][b:b + 1], int(lens[b]), W)
+        kr[b], vr[b] = k1[0], v1[0]
+    qn = np.stack([d["q"][b, :, lens[b] - 1] for b in range(B)])
+    out = sa.decode(oracle.SWA, W, dev_bf16(qn), sa.KV_RING, dev_bf16(kr), dev_bf16(vr), dev_i32(lens), L,
+                    dev_f32(d["sink"]), scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(qn, kr, vr, lens, d["sink"], oracle.SWA, W, scale, oracle.RING)
+    assert_parity(host_f32(out), ref, f"ring scale={scale}")
+    lens2 = np.array([700, 5000, 4097], np.int32)
+    L2, Hq2, Hkv2, ps = 5000, 64, 4, 64
+    d2 = growing_keys(seq_data(len(lens2), Hq2, Hkv2, L2, seed=52), 400.0)
+    kp, vp, bt = inputs.pages_from_sequence(d2["k"], d2["v"], L2, ps, len(lens2) * (L2 // ps + 1) + 3, seed=6)
+    qn2 = np.stack([d2["q"][b, :, lens2[b] - 1] for b in range(len(lens2))])
+    out2 = sa.decode(oracle.GLOBAL, 0, dev_bf16(qn2), sa.KV_PAGED, dev_bf16(kp), dev_bf16(vp), dev_i32(lens2), L2,
+                     dev_f32(d2["sink"]), dev_i32(bt), scale=scale)
+    torch.cuda.synchronize()
+    ref2 = oracle.decode(qn2, kp, vp, lens2, d2["sink"], oracle.GLOBAL, 0, scale, oracle.PAGED, bt)
+    assert_parity(host_f32(out2), ref2, f"paged scale={scale}")
+
+
 def test_contiguous_equals_permuted_pages():
     lens = np.array([3000, 2048], np.int32)
     d = seq_data(2, 16, 2, 3000, seed=5)
