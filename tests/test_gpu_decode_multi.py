@@ -171,3 +171,31 @@ def test_q_shape_checked_before_launch():
         sa.sinkattn_decode_fp8(sa.GLOBAL, 0, 4, q1, k8, v8, lens, 100, None, 1.0, 1.0, out4, None, bt)
     with pytest.raises(ValueError):
         sa.sinkattn_decode_multi(sa.GLOBAL, 0, 4, q1[:, :, 0], sa.KV_PAGED, k, v, lens, 100, None, out4, None, bt)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,q_len,L,nsplit", [
+    (128, 16, 4, 1, 1600, 1),   # 512 (sequence, KV head) units: one split over up to 1600 keys
+    (100, 16, 4, 1, 1600, 2),   # two splits of 896 keys
+    (64, 64, 4, 8, 2000, 1),    # 128 columns per KV head in two column chunks, one split
+])
+def test_many_sequences_long_single_split(B, Hq, Hkv, q_len, L, nsplit):
+    """Enough sequences that the plan keeps one (or two) splits per unit over key ranges longer
+    than the unsplit limit of 1024: the split kernel then walks the whole range and writes the
+    final output itself (the sink added in its epilogue).  Inputs are drawn for the decoded
+    tokens only."""
+    need = sa.sinkattn_decode_multi_workspace_bytes(oracle.GLOBAL, 0, B, Hq, Hkv, q_len, L)
+    assert need == (0 if nsplit == 1 else B * Hq * q_len * nsplit * 132 * 4), need
+    print(f"[case] many sequences B={B} Hq={Hq} Hkv={Hkv} q_len={q_len} L={L} nsplit={nsplit}", flush=True)
+    rng = np.random.default_rng(B + q_len)
+    lens = rng.integers(L // 2, L + 1, size=B).astype(np.int32)
+    lens[0], lens[1], lens[2] = L, 1024, 1025
+    ps = 64
+    k = inputs.normal((B, Hkv, L, 192), 60 + B, 1)
+    v = inputs.normal((B, Hkv, L, 128), 60 + B, 2)
+    q = inputs.normal((B, Hq, q_len, 192), 60 + B, 0)
+    sink = inputs.sink_values(Hq, 60 + B)
+    kp, vp, bt = inputs.pages_from_sequence(k, v, L, ps, B * ((L + ps - 1) // ps) + 3, seed=B, permute=True)
+    del k, v
+    got = gpu_multi(oracle.GLOBAL, 0, sa.KV_PAGED, q, kp, vp, lens, L, sink, bt)
+    ref = oracle.decode(q, kp, vp, lens, sink, oracle.GLOBAL, 0, SCALE, oracle.PAGED, bt)
+    assert_parity(got, ref, f"many sequences B={B} q_len={q_len}")
